@@ -1,0 +1,115 @@
+/*
+ * oracle.c -- plain, slow CPU reference of the conventional SSM decode recurrences.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the bench's CPU-baseline leg load
+ * this library; the decode library never calls it and shares no code, header or table with it.
+ *
+ * What it computes is the definition that ReplaySSM must reproduce: the pages state that the
+ * replayed outputs equal those of conventional decoding except for floating-point differences
+ * (fagnersouza.tech post "ReplaySSM: o ganho aparece na carga concorrente...", section
+ * "Cuidados e limites"), and that conventional decoding reads and rewrites the whole state on
+ * every token (same post, lede; ia.goatify.app article, paragraph "ReplaySSM cambia qué se
+ * almacena").
+ *
+ * Arithmetic: fp64 on fp32 inputs, plain loops in the order of the definition, built with
+ * -O2 -ffp-contract=off and no fast-math. OpenMP only spreads independent (batch, head) pairs over
+ * threads; it does not change any result.
+ */
+#include <math.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
+/*
+ * One conventional Mamba-2 decode token for every (b, h) pair.
+ *
+ * Discretisation (the plain Mamba-2 reading of "decay, add an outer product, output"):
+ *     a       = exp(dt[b,h] * A[h])
+ *     S[p][n] = a * S[p][n] + (dt[b,h] * x[b,h,p]) * Bm[b,g,n]
+ *     y[p]    = sum_n S[p][n] * C[b,g,n] + D[h] * x[b,h,p]          (post-update state)
+ * with g = h / (nh / ng).
+ *
+ * Layouts (row-major, last index fastest): x [nb,nh,P], Bm and C [nb,ng,N], dt [nb,nh],
+ * A and D [nh], state [nb,nh,P,N] (fp64, updated in place), y [nb,nh,P] (fp64, written).
+ */
+void orc_m2_step(int nb, int nh, int ng, int P, int N,
+                 const float *A, const float *D,
+                 const float *x, const float *Bm, const float *C, const float *dt,
+                 double *state, double *y)
+{
+    const int hpg = nh / ng;
+    const long pairs = (long)nb * nh;
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < pairs; ++bh) {
+        const long b = bh / nh;
+        const int h = (int)(bh % nh);
+        const int g = h / hpg;
+        const double dtv = (double)dt[bh];
+        const double a = exp(dtv * (double)A[h]);
+        const float *xv = x + bh * P;
+        const float *Bv = Bm + (b * ng + g) * N;
+        const float *Cv = C + (b * ng + g) * N;
+        double *S = state + bh * (long)P * N;
+        for (int p = 0; p < P; ++p) {
+            const double coef = dtv * (double)xv[p];
+            double acc = 0.0;
+            for (int n = 0; n < N; ++n) {
+                const double s = a * S[(long)p * N + n] + coef * (double)Bv[n];
+                S[(long)p * N + n] = s;
+                acc += s * (double)Cv[n];
+            }
+            y[bh * P + p] = acc + (double)D[h] * (double)xv[p];
+        }
+    }
+}
+
+/*
+ * One conventional Gated DeltaNet decode token for every (b, h) pair. The state S is d_v x d_k
+ * (row i is an output channel), so the rank-1 correction multiplies from the right:
+ *     S   <- alpha * S (I - beta k k^T) + beta v k^T
+ *          = alpha * (S - beta (S k) k^T) + beta v k^T
+ *     o    = S q                                                     (post-update state)
+ * Layouts: q, k [nb,nh,dk], v [nb,nh,dv], beta and alpha [nb,nh], state [nb,nh,dv,dk] fp64 in
+ * place, o [nb,nh,dv] fp64.
+ */
+void orc_gdn_step(int nb, int nh, int dk, int dv,
+                  const float *q, const float *k, const float *v,
+                  const float *beta, const float *alpha,
+                  double *state, double *o)
+{
+    const long pairs = (long)nb * nh;
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < pairs; ++bh) {
+        const double be = (double)beta[bh];
+        const double al = (double)alpha[bh];
+        const float *qv = q + bh * dk;
+        const float *kv = k + bh * dk;
+        const float *vv = v + bh * dv;
+        double *S = state + bh * (long)dv * dk;
+        for (int i = 0; i < dv; ++i) {
+            double *row = S + (long)i * dk;
+            double sk = 0.0;
+            for (int j = 0; j < dk; ++j) sk += row[j] * (double)kv[j];
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) {
+                const double s = al * (row[j] - be * sk * (double)kv[j])
+                               + be * (double)vv[i] * (double)kv[j];
+                row[j] = s;
+                acc += s * (double)qv[j];
+            }
+            o[bh * dv + i] = acc;
+        }
+    }
+}
