@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the ReplaySSM decode hot path on one MI355X.
+
+Default workload: Mamba-2 decode of one SSM layer at serving shape -- batch 256, 128 heads,
+head_dim 64, d_state 128 (4 MiB fp32 state per sequence, 1 GiB per layer), ring W = 16, fp32
+state. One step = one decode token for every sequence (one rssm_decode_step launch, the fold of
+a full ring included in the launch that fills it). Inputs come from a pool of 32 pre-generated
+seeded token slots (step t uses slot t mod 32) resident in HBM before timing starts.
+
+Printed: one JSON line. `value` is the algorithmic HBM traffic of the replay decode per second
+(GB/s), the bytes the method must move (checkpoint reads, the fold's read+write, ring reads and
+appends, inputs, outputs) divided by the timed wall time. Also reported: SSM-layer tokens/s, the
+speedup over the conventional read-modify-write kernel on the same input schedule, the roofline
+of the dominant kernel, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s (1e9 bytes)
+METRIC = "SSM decode state GB/s (% of HBM peak) + tokens/s vs conventional, batch 256 W=16"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "checkpoint_replay_buffer_amd", "csrc", "mamba2.hip")
+
+
+# ------------------------------------------------------------------------------------------
+# algorithmic byte model (per (sequence, head) pair and per launch)
+# ------------------------------------------------------------------------------------------
+
+def m2_replay_bytes(P, N, W, gr, length, store_c=True, bf16=False) -> float:
+    """HBM bytes one decode launch must move for one (b, h) pair whose ring holds `length`
+    committed entries before the token. gr = G / H (B and C rows are shared by a group)."""
+    f = 4
+    inputs = (P + 1) * f + 2 * N * f * gr          # x, dt, B, C of the token
+    ring_rd = length * ((P + 1) * f + N * f * gr)  # x, dt, B of the buffered entries
+    y = P * f
+    if length + 1 >= W:                            # the token fills the ring: fold
+        s0 = 2 * P * N * f + (P * N * 2 if bf16 else 0)
+        return s0 + inputs + ring_rd + y
+    s0 = P * N * (2 if bf16 else f)
+    append = (P + 1) * f + N * f * gr * (2 if store_c else 1)
+    return s0 + inputs + ring_rd + append + y
+
+
+def m2_rmw_bytes(P, N, gr) -> float:
+    f = 4
+    return 2 * P * N * f + (P + 1) * f + 2 * N * f * gr + P * f
+
+
+# ------------------------------------------------------------------------------------------
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    for p in (KERNEL_SRC, os.path.join(os.path.dirname(KERNEL_SRC), "dev_common.h")):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this kernel, if the counters were
+    taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("src_hash") != _src_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def run_m2(args, torch, rb, wl):
+    bf16 = args.workload == "m2_serve_bf16"
+    batch = args.batch or 256
+    sh = wl.M2Shape(batch=batch, nheads=128, ngroups=128, head_dim=64, d_state=128, window=16)
+    P, N, W, H, B = sh.head_dim, sh.d_state, sh.window, sh.nheads, sh.batch
+    gr = sh.ngroups / sh.nheads
+    pool_n = 32
+    t0 = time.time()
+    prm = wl.m2_params(sh, 0)
+    s0 = torch.from_numpy(wl.m2_state0(sh, 0)).cuda()
+    pool = []
+    for s in range(pool_n):
+        ins = wl.m2_token_inputs(sh, 0, s)
+        pool.append({k: torch.from_numpy(v[0]).cuda() for k, v in ins.items()})
+    A = torch.from_numpy(prm["A"]).cuda()
+    D = torch.from_numpy(prm["D"]).cuda()
+    gen_s = time.time() - t0
+
+    ctx = rb.Context("mamba2", B, H, P, N, W, bf16_read=bf16, store_c=True)
+    ctx.set_params(A, D)
+    y = torch.empty(B, H, P, device="cuda")
+    K, Wm = args.steps, args.warmup
+
+    # warm-up, then restart from the checkpoint so the timed steps see lengths 0, 1, ..., W-1, ...
+    ctx.init_checkpoint(s0)
+    for t in range(Wm):
+        ctx.decode_step(y, **pool[t % pool_n])
+    ctx.init_checkpoint(s0)
+    torch.cuda.synchronize()
+
+    ev = _events(torch, 2 * K + 2)
+    ev[0].record()
+    for t in range(K):
+        ev[1 + 2 * t].record()
+        ctx.decode_step(y, **pool[t % pool_n])
+        ev[2 + 2 * t].record()
+    ev[-1].record()
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[-1])
+    launch_ms = [ev[1 + 2 * t].elapsed_time(ev[2 + 2 * t]) for t in range(K)]
+    h, l, n, e = ctx.bookkeeping()
+    assert e == 0 and l[0] == K % W, "unexpected bookkeeping after the timed steps"
+
+    alg_bytes = sum(m2_replay_bytes(P, N, W, gr, t % W, True, bf16) for t in range(K)) * B * H
+    state_bytes = sum((2 * P * N * 4 if t % W == W - 1 else P * N * (2 if bf16 else 4))
+                      for t in range(K)) * B * H
+    replay_s = total_ms / 1e3
+
+    # conventional read-modify-write on the same schedule
+    rmw_s = None
+    if not args.no_rmw:
+        cfg = rb.make_config(rb.RSSM_MAMBA2, B, H, sh.ngroups, P, N, W)
+        st = s0.clone()
+        y1 = torch.empty(1, B, H, P, device="cuda")
+        for t in range(Wm):
+            rb.step_baseline(cfg, st, y1, A, D, **{k: v.unsqueeze(0) for k, v in pool[t % pool_n].items()})
+        st.copy_(s0)
+        torch.cuda.synchronize()
+        ev2 = _events(torch, 2)
+        ev2[0].record()
+        for t in range(K):
+            rb.step_baseline(cfg, st, y1, A, D, **{k: v.unsqueeze(0) for k, v in pool[t % pool_n].items()})
+        ev2[1].record()
+        torch.cuda.synchronize()
+        rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+        del st
+
+    kern_s = sum(launch_ms) / 1e3
+    achieved = alg_bytes / kern_s / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(alg_bytes / replay_s / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-read/fp32" if bf16 else "fp32",
+        "data": "synthetic (seeded N(0,1) x, N(0,1)/sqrt(N) B and C, softplus(N(-2,0.5)) dt)",
+        "config": {"workload": f"mamba2_decode_b{B}_h{H}_p{P}_n{N}_w{W}" + ("_bf16read" if bf16 else ""),
+                   "batch": B, "heads": H, "head_dim": P, "d_state": N, "window": W,
+                   "groups": sh.ngroups, "input_pool_slots": pool_n},
+        "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
+        "state_gbs": round(state_bytes / replay_s / 1e9, 1),
+        "tokens_per_s": round(B * K / replay_s, 1),
+        "rmw_ms_per_step": round(rmw_s * 1e3 / K, 5) if rmw_s else None,
+        "rmw_gbs": round(m2_rmw_bytes(P, N, gr) * B * H * K / rmw_s / 1e9, 1) if rmw_s else None,
+        "speedup_vs_rmw": round(rmw_s / replay_s, 3) if rmw_s else None,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_m2_decode",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": _traffic("k_m2_decode_bf16" if bf16 else "k_m2_decode"),
+            "alg_bytes_per_launch": round(alg_bytes / K),
+            "avg_launch_us": round(1e3 * sum(launch_ms) / K, 2),
+        },
+        "input_gen_s": round(gen_s, 1),
+    }
+    return line, (sh, prm)
+
+
+def cpu_baseline_m2(sh, prm, wl, budget_s=12.0):
+    """Time the CPU oracle (conventional fp64 recurrence) on the first steps of a subset of the
+    same seeded schedule, sized to about `budget_s` of CPU time."""
+    import oracle
+    cores = oracle.set_threads(0)
+    nseq = 32
+    sub = slice(0, nseq)
+    s0 = wl.m2_state0(wl.M2Shape(nseq, sh.nheads, sh.ngroups, sh.head_dim, sh.d_state, sh.window), 0)
+    state = s0.astype(np.float64)
+    toks = [wl.m2_token_inputs(sh, 0, s) for s in range(4)]
+    toks = [{k: np.ascontiguousarray(v[0][sub]) for k, v in t.items()} for t in toks]
+    t0 = time.perf_counter()
+    oracle.m2_step(prm["A"], prm["D"], toks[0]["x"], toks[0]["B"], toks[0]["C"], toks[0]["dt"], state)
+    one = time.perf_counter() - t0
+    steps = max(2, min(512, int(budget_s / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    for t in range(steps):
+        k = toks[t % 4]
+        oracle.m2_step(prm["A"], prm["D"], k["x"], k["B"], k["C"], k["dt"], state)
+    el = time.perf_counter() - t0
+    tok_s = nseq * steps / el
+    # the oracle reads and rewrites the fp64 state once per token
+    gbs = 2 * sh.head_dim * sh.d_state * 8 * sh.nheads * tok_s / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s (fp64 state read+write)", "cores": cores,
+            "kind": "oracle", "tokens_per_s": round(tok_s, 1),
+            "sample": f"first {steps} decode steps of sequences 0..{nseq - 1} (all {sh.nheads} heads) "
+                      f"of the same seeded schedule, conventional fp64 recurrence, {el:.1f} s"}
+
+
+def calibrate_copy(torch, nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, so rocprofv3 counter runs can scale FETCH_SIZE /
+    WRITE_SIZE to bytes."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="m2_serve", choices=["m2_serve", "m2_serve_bf16"])
+    ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rmw", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path has no cross-GPU step; see the design notes on sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    from checkpoint_replay_buffer_amd import binding as rb
+    rb.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+    line, (sh, prm) = run_m2(args, torch, rb, wl)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_m2(sh, prm, wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

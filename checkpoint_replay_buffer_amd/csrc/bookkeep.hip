@@ -1,0 +1,99 @@
+// bookkeep.hip -- checkpoint loading and the pointer-only commit / rollback of speculative drafts.
+//
+// Accepting a prefix of the drafts only moves the committed length: no state and no ring data is
+// copied (ia.goatify.app article "NVIDIA y Princeton aceleran modelos híbridos...", paragraph
+// "El retroceso usa un puntero del búfer"). Bookkeeping words are [3][B] int32 (head, len,
+// ndraft), read from bk.in and written to bk.out.
+#include "dev_common.h"
+#include "internal.h"
+
+namespace rssm {
+namespace {
+
+constexpr uint32_t kCommitRange = 1u;
+constexpr uint32_t kRollbackRange = 2u;
+
+// One workgroup per (b, h) tile: copy the initial state of selected sequences into S0 (and its
+// bf16 copy) and reset their bookkeeping.
+__global__ void __launch_bounds__(256) k_init(float *S0, uint16_t *S0b, const float *state,
+                                              const int32_t *mask, Bk bk, uint32_t *err, int B,
+                                              int H, long tile_elems)
+{
+    const int tile = blockIdx.x;
+    const int b = tile / H, h = tile - b * H;
+    const bool sel = mask == nullptr || mask[b] != 0;
+    if (h == 0 && threadIdx.x == 0) {
+        bk.out[b] = sel ? 0 : bk.in[b];
+        bk.out[B + b] = sel ? 0 : bk.in[B + b];
+        bk.out[2 * B + b] = sel ? 0 : bk.in[2 * B + b];
+        if (mask == nullptr && tile == 0) *err = 0u;
+    }
+    if (!sel) return;
+    const size_t base = (size_t)tile * tile_elems;
+    for (long i = threadIdx.x; i < tile_elems / 4; i += blockDim.x) {
+        const float4 v = ld4_nt(state + base + 4 * i);
+        st4(S0 + base + 4 * i, v);
+        if (S0b) {
+            uint2 w;
+            w.x = pack_bf16x2(v.x, v.y);
+            w.y = pack_bf16x2(v.z, v.w);
+            *reinterpret_cast<uint2 *>(S0b + base + 4 * i) = w;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) k_commit(Bk bk, const int32_t *accepted, uint32_t *err, int B)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int len = bk.in[B + b], nd = bk.in[2 * B + b], acc = accepted[b];
+    const bool ok = acc >= 0 && acc <= nd;
+    bk.out[b] = bk.in[b];
+    bk.out[B + b] = ok ? len + acc : len;
+    bk.out[2 * B + b] = 0;
+    if (!ok) atomicOr(err, kCommitRange);
+}
+
+__global__ void __launch_bounds__(256) k_rollback(Bk bk, const int32_t *new_len, uint32_t *err, int B)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int len = bk.in[B + b], nl = new_len[b];
+    const bool ok = nl >= 0 && nl <= len;
+    bk.out[b] = bk.in[b];
+    bk.out[B + b] = ok ? nl : len;
+    bk.out[2 * B + b] = 0;
+    if (!ok) atomicOr(err, kRollbackRange);
+}
+
+__global__ void k_clear(uint32_t *w) { *w = 0u; }
+
+}  // namespace
+
+hipError_t init_checkpoint(float *S0, uint16_t *S0b, const float *state, const int32_t *mask,
+                           Bk bk, uint32_t *err, int B, int H, long tile_elems, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_init, dim3(B * H), dim3(256), 0, s, S0, S0b, state, mask, bk, err, B, H,
+                       tile_elems);
+    return hipGetLastError();
+}
+
+hipError_t bk_commit(Bk bk, const int32_t *accepted, uint32_t *err, int B, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_commit, dim3((B + 255) / 256), dim3(256), 0, s, bk, accepted, err, B);
+    return hipGetLastError();
+}
+
+hipError_t bk_rollback(Bk bk, const int32_t *new_len, uint32_t *err, int B, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_rollback, dim3((B + 255) / 256), dim3(256), 0, s, bk, new_len, err, B);
+    return hipGetLastError();
+}
+
+hipError_t clear_word(uint32_t *w, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_clear, dim3(1), dim3(1), 0, s, w);
+    return hipGetLastError();
+}
+
+}  // namespace rssm

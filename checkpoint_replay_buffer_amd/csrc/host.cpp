@@ -1,0 +1,336 @@
+// host.cpp -- the C ABI of librssm: argument checks, workspace layout, call-order state and
+// kernel dispatch. Every entry point returns before launching anything when a check fails.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "../../include/rssm.h"
+#include "internal.h"
+
+using namespace rssm;
+
+struct rssm_ctx {
+    rssm_config cfg;
+    char *ws;
+    size_t ws_bytes;
+    int32_t *bk[2];        // [3][B] head, len, ndraft; the live copy is bk[par]
+    uint32_t *err;
+    float *S0;
+    uint16_t *S0b;
+    M2Ring m2;
+    GdnRing gdn;
+    const float *A, *D;
+    int par;
+    bool pending;          // a verify awaits its commit / rollback
+    bool initialized;      // a full rssm_init_checkpoint has run
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+    size_t bk, err, S0, S0b, r0, r1, r2, r3, total;
+};
+
+rssm_status check_config(const rssm_config *c)
+{
+    if (!c) return RSSM_E_ARG;
+    if (c->kind != RSSM_MAMBA2 && c->kind != RSSM_GDN) return RSSM_E_ARG;
+    if (c->batch < 1 || c->nheads < 1 || c->ngroups < 1 || c->dim_v < 1 || c->dim_k < 1)
+        return RSSM_E_SHAPE;
+    if (c->window < 1 || c->window > kMaxWindow) return RSSM_E_SHAPE;
+    if (c->max_draft < 0 || c->max_draft > c->window) return RSSM_E_SHAPE;
+    if (c->nheads % c->ngroups != 0) return RSSM_E_SHAPE;
+    if (c->flags & ~(uint32_t)(RSSM_F_BF16_READ | RSSM_F_STORE_C)) return RSSM_E_ARG;
+    if ((long long)c->batch * c->nheads > 0x7fffffffLL) return RSSM_E_SHAPE;
+    if (c->kind == RSSM_GDN) {
+        if (c->ngroups != c->nheads) return RSSM_E_SHAPE;
+        if (c->flags != 0) return RSSM_E_UNSUPPORTED;
+        if (!gdn_supported(c->dim_v, c->dim_k)) return RSSM_E_UNSUPPORTED;
+    } else {
+        if (!m2_supported(c->dim_v, c->dim_k)) return RSSM_E_UNSUPPORTED;
+        // the fold stages W+1 entries of x and B in LDS: keep it within 64 KiB per workgroup
+        const long lds = 4L * ((c->window + 1L) * (c->dim_v + c->dim_k) + 2L * (c->window + 2));
+        if (lds > 65536) return RSSM_E_UNSUPPORTED;
+    }
+    return RSSM_OK;
+}
+
+Layout layout(const rssm_config *c)
+{
+    const size_t B = c->batch, H = c->nheads, G = c->ngroups, P = c->dim_v, N = c->dim_k,
+                 W = c->window;
+    Layout L{};
+    size_t o = 0;
+    L.bk = o;  o += up(2 * 3 * B * sizeof(int32_t));
+    L.err = o; o += up(sizeof(uint32_t));
+    L.S0 = o;  o += up(B * H * P * N * sizeof(float));
+    L.S0b = o; o += (c->flags & RSSM_F_BF16_READ) ? up(B * H * P * N * 2) : 0;
+    if (c->kind == RSSM_MAMBA2) {
+        L.r0 = o; o += up(B * H * W * P * sizeof(float));                               // x
+        L.r1 = o; o += up(B * G * W * N * sizeof(float));                               // B
+        L.r2 = o; o += (c->flags & RSSM_F_STORE_C) ? up(B * G * W * N * sizeof(float)) : 0;  // C
+        L.r3 = o; o += up(B * H * W * sizeof(float));                                   // dt
+    } else {
+        L.r0 = o; o += up(B * H * W * N * sizeof(float));                               // k
+        L.r1 = o; o += up(B * H * W * P * sizeof(float));                               // v
+        L.r2 = o; o += up(B * H * W * sizeof(float));                                   // beta
+        L.r3 = o; o += up(B * H * W * sizeof(float));                                   // alpha
+    }
+    L.total = o;
+    return L;
+}
+
+hipStream_t strm(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+Bk flip(rssm_ctx *c) { return Bk{c->bk[c->par], c->bk[c->par ^ 1]}; }
+
+rssm_status launched(rssm_ctx *c, hipError_t e, bool flips)
+{
+    if (e != hipSuccess) return RSSM_E_DEVICE;
+    if (flips) c->par ^= 1;
+    return RSSM_OK;
+}
+
+M2Dims m2dims(const rssm_config &c)
+{
+    return M2Dims{c.batch, c.nheads, c.ngroups, c.dim_v, c.dim_k, c.window};
+}
+
+GdnDims gdndims(const rssm_config &c)
+{
+    return GdnDims{c.batch, c.nheads, c.dim_v, c.dim_k, c.window};
+}
+
+rssm_status check_inputs(const rssm_config &c, const rssm_inputs *in)
+{
+    if (!in || in->ntok < 1) return RSSM_E_ARG;
+    if (c.kind == RSSM_MAMBA2) {
+        if (!aligned16(in->x) || !aligned16(in->B) || !aligned16(in->C) || !in->dt) return RSSM_E_ARG;
+    } else {
+        if (!aligned16(in->q) || !aligned16(in->k) || !aligned16(in->v) || !in->beta || !in->alpha)
+            return RSSM_E_ARG;
+    }
+    return RSSM_OK;
+}
+
+rssm_status ready(const rssm_ctx *c)
+{
+    if (!c) return RSSM_E_ARG;
+    if (!c->initialized) return RSSM_E_STATE;
+    if (c->cfg.kind == RSSM_MAMBA2 && (!c->A || !c->D)) return RSSM_E_STATE;
+    return RSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rssm_status rssm_workspace_bytes(const rssm_config *cfg, size_t *bytes)
+{
+    const rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    if (!bytes) return RSSM_E_ARG;
+    *bytes = layout(cfg).total;
+    return RSSM_OK;
+}
+
+rssm_status rssm_create(const rssm_config *cfg, void *dev_ws, size_t bytes, rssm_ctx **out)
+{
+    const rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    if (!out || !dev_ws || (reinterpret_cast<uintptr_t>(dev_ws) & (kAlign - 1)) != 0) return RSSM_E_ARG;
+    const Layout L = layout(cfg);
+    if (bytes < L.total) return RSSM_E_SPACE;
+    rssm_ctx *c = new (std::nothrow) rssm_ctx();
+    if (!c) return RSSM_E_ARG;
+    c->cfg = *cfg;
+    c->ws = static_cast<char *>(dev_ws);
+    c->ws_bytes = bytes;
+    const size_t B = cfg->batch;
+    c->bk[0] = reinterpret_cast<int32_t *>(c->ws + L.bk);
+    c->bk[1] = c->bk[0] + 3 * B;
+    c->err = reinterpret_cast<uint32_t *>(c->ws + L.err);
+    c->S0 = reinterpret_cast<float *>(c->ws + L.S0);
+    c->S0b = (cfg->flags & RSSM_F_BF16_READ) ? reinterpret_cast<uint16_t *>(c->ws + L.S0b) : nullptr;
+    if (cfg->kind == RSSM_MAMBA2) {
+        c->m2.x = reinterpret_cast<float *>(c->ws + L.r0);
+        c->m2.B = reinterpret_cast<float *>(c->ws + L.r1);
+        c->m2.C = (cfg->flags & RSSM_F_STORE_C) ? reinterpret_cast<float *>(c->ws + L.r2) : nullptr;
+        c->m2.dt = reinterpret_cast<float *>(c->ws + L.r3);
+    } else {
+        c->gdn.k = reinterpret_cast<float *>(c->ws + L.r0);
+        c->gdn.v = reinterpret_cast<float *>(c->ws + L.r1);
+        c->gdn.beta = reinterpret_cast<float *>(c->ws + L.r2);
+        c->gdn.alpha = reinterpret_cast<float *>(c->ws + L.r3);
+    }
+    *out = c;
+    return RSSM_OK;
+}
+
+void rssm_destroy(rssm_ctx *ctx) { delete ctx; }
+
+rssm_status rssm_set_params(rssm_ctx *ctx, const float *A, const float *D)
+{
+    if (!ctx || !A || !D) return RSSM_E_ARG;
+    if (ctx->cfg.kind != RSSM_MAMBA2) return RSSM_E_UNSUPPORTED;
+    ctx->A = A;
+    ctx->D = D;
+    return RSSM_OK;
+}
+
+rssm_status rssm_init_checkpoint(rssm_ctx *ctx, const float *state, const int32_t *seq_mask,
+                                 void *stream)
+{
+    if (!ctx || !aligned16(state)) return RSSM_E_ARG;
+    if (seq_mask && !ctx->initialized) return RSSM_E_STATE;   // the first load must cover all
+    const rssm_config &c = ctx->cfg;
+    const hipError_t e = init_checkpoint(ctx->S0, ctx->S0b, state, seq_mask, flip(ctx), ctx->err,
+                                         c.batch, c.nheads, (long)c.dim_v * c.dim_k, strm(stream));
+    const rssm_status s = launched(ctx, e, true);
+    if (s == RSSM_OK) {
+        ctx->initialized = true;
+        ctx->pending = false;
+    }
+    return s;
+}
+
+rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream)
+{
+    rssm_status s = ready(ctx);
+    if (s != RSSM_OK) return s;
+    const rssm_config &c = ctx->cfg;
+    if ((s = check_inputs(c, in)) != RSSM_OK) return s;
+    if (in->ntok != 1 || !aligned16(y)) return RSSM_E_ARG;
+    if (ctx->pending) return RSSM_E_STATE;
+    if (c.kind == RSSM_MAMBA2) {
+        M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
+                     in->x, in->B, in->C, in->dt, y, 1};
+        return launched(ctx, m2_decode(a, ctx->S0b != nullptr, strm(stream)), true);
+    }
+    GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
+                  in->alpha, y};
+    return launched(ctx, gdn_decode(a, strm(stream)), true);
+}
+
+rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream)
+{
+    rssm_status s = ready(ctx);
+    if (s != RSSM_OK) return s;
+    if (ctx->pending) return RSSM_E_STATE;
+    const rssm_config &c = ctx->cfg;
+    if (c.kind == RSSM_MAMBA2) {
+        M2FoldArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, min_len, nullptr};
+        return launched(ctx, m2_fold(a, ctx->S0b != nullptr, strm(stream)), true);
+    }
+    GdnFoldArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, min_len, nullptr};
+    return launched(ctx, gdn_fold(a, strm(stream)), true);
+}
+
+rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream)
+{
+    rssm_status s = ready(ctx);
+    if (s != RSSM_OK) return s;
+    const rssm_config &c = ctx->cfg;
+    if (c.kind != RSSM_MAMBA2) return RSSM_E_UNSUPPORTED;
+    if ((s = check_inputs(c, in)) != RSSM_OK) return s;
+    if (!aligned16(y)) return RSSM_E_ARG;
+    if (in->ntok > c.max_draft || in->ntok > c.window) return RSSM_E_ARG;
+    if (ctx->pending) return RSSM_E_STATE;
+    M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
+                 in->x, in->B, in->C, in->dt, y, in->ntok};
+    s = launched(ctx, m2_verify(a, ctx->S0b != nullptr, strm(stream)), true);
+    if (s == RSSM_OK) ctx->pending = true;
+    return s;
+}
+
+rssm_status rssm_verify_commit(rssm_ctx *ctx, const int32_t *accepted, void *stream)
+{
+    if (!ctx || !accepted) return RSSM_E_ARG;
+    if (!ctx->pending) return RSSM_E_STATE;
+    const rssm_status s = launched(ctx, bk_commit(flip(ctx), accepted, ctx->err, ctx->cfg.batch,
+                                                  strm(stream)), true);
+    if (s == RSSM_OK) ctx->pending = false;
+    return s;
+}
+
+rssm_status rssm_rollback(rssm_ctx *ctx, const int32_t *new_len, void *stream)
+{
+    if (!ctx || !new_len) return RSSM_E_ARG;
+    if (!ctx->initialized) return RSSM_E_STATE;
+    const rssm_status s = launched(ctx, bk_rollback(flip(ctx), new_len, ctx->err, ctx->cfg.batch,
+                                                    strm(stream)), true);
+    if (s == RSSM_OK) ctx->pending = false;
+    return s;
+}
+
+rssm_status rssm_step_baseline(const rssm_config *cfg, float *state, const rssm_inputs *in,
+                               const float *A, const float *D, float *y, float *snapshots,
+                               void *stream)
+{
+    rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    if ((s = check_inputs(*cfg, in)) != RSSM_OK) return s;
+    if (!aligned16(state) || !aligned16(y) || (snapshots && !aligned16(snapshots))) return RSSM_E_ARG;
+    if (cfg->kind == RSSM_MAMBA2) {
+        if (!A || !D) return RSSM_E_ARG;
+        M2RmwArgs a{m2dims(*cfg), state, snapshots, A, D, in->x, in->B, in->C, in->dt, y, in->ntok};
+        return m2_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+    }
+    GdnRmwArgs a{gdndims(*cfg), state, snapshots, in->q, in->k, in->v, in->beta, in->alpha, y,
+                 in->ntok};
+    return gdn_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+}
+
+rssm_status rssm_materialize(rssm_ctx *ctx, float *state_out, void *stream)
+{
+    rssm_status s = ready(ctx);
+    if (s != RSSM_OK) return s;
+    if (!aligned16(state_out)) return RSSM_E_ARG;
+    const rssm_config &c = ctx->cfg;
+    const Bk bk{ctx->bk[ctx->par], nullptr};
+    if (c.kind == RSSM_MAMBA2) {
+        M2FoldArgs a{m2dims(c), bk, ctx->S0, nullptr, ctx->m2, ctx->A, 1, state_out};
+        return launched(ctx, m2_fold(a, false, strm(stream)), false);
+    }
+    GdnFoldArgs a{gdndims(c), bk, ctx->S0, ctx->gdn, 1, state_out};
+    return launched(ctx, gdn_fold(a, strm(stream)), false);
+}
+
+rssm_status rssm_read_bookkeeping(rssm_ctx *ctx, int32_t *head, int32_t *len, int32_t *ndraft,
+                                  uint32_t *dev_err, void *stream)
+{
+    if (!ctx) return RSSM_E_ARG;
+    const hipStream_t st = strm(stream);
+    const size_t B = ctx->cfg.batch;
+    const int32_t *live = ctx->bk[ctx->par];
+    hipError_t e = hipSuccess;
+    if (head && e == hipSuccess) e = hipMemcpyAsync(head, live, B * 4, hipMemcpyDeviceToHost, st);
+    if (len && e == hipSuccess) e = hipMemcpyAsync(len, live + B, B * 4, hipMemcpyDeviceToHost, st);
+    if (ndraft && e == hipSuccess) e = hipMemcpyAsync(ndraft, live + 2 * B, B * 4, hipMemcpyDeviceToHost, st);
+    if (dev_err && e == hipSuccess) e = hipMemcpyAsync(dev_err, ctx->err, 4, hipMemcpyDeviceToHost, st);
+    if (dev_err && e == hipSuccess) e = clear_word(ctx->err, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    return e == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+}
+
+const char *rssm_status_str(rssm_status s)
+{
+    switch (s) {
+    case RSSM_OK: return "ok";
+    case RSSM_E_ARG: return "invalid argument (null or misaligned pointer, bad value)";
+    case RSSM_E_SHAPE: return "invalid or inconsistent dimensions";
+    case RSSM_E_SPACE: return "workspace too small";
+    case RSSM_E_STATE: return "call-order misuse";
+    case RSSM_E_DEVICE: return "HIP launch or copy failed";
+    case RSSM_E_UNSUPPORTED: return "shape or option without a compiled kernel";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// internal.h -- kernel argument blocks and launcher entry points of librssm (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rssm {
+
+constexpr int kMaxWindow = 64;   // largest ring length W
+
+// Bookkeeping is double-buffered: every launch that changes it reads bk_in and writes bk_out
+// (each [3][B] int32: head, len, ndraft). All head-workgroups of a sequence read bk_in while one
+// of them writes bk_out, so no launch both reads and writes the same word.
+struct Bk {
+    const int32_t *in;
+    int32_t *out;
+};
+
+struct M2Ring {
+    float *x;     // [B,H,W,P]
+    float *B;     // [B,G,W,N]
+    float *C;     // [B,G,W,N] or nullptr (not stored)
+    float *dt;    // [B,H,W]
+};
+
+struct M2Dims {
+    int B, H, G, P, N, W;
+};
+
+// Mamba-2 decode / verify (ntok tokens, token-major inputs).
+struct M2StepArgs {
+    M2Dims d;
+    Bk bk;
+    float *S0;          // [B,H,P,N]
+    uint16_t *S0b;      // bf16 copy or nullptr
+    M2Ring ring;
+    const float *A, *D; // [H]
+    const float *x, *Bm, *C, *dt;
+    float *y;
+    int ntok;
+};
+
+// Mamba-2 consolidation (write S0) or materialisation (write out).
+struct M2FoldArgs {
+    M2Dims d;
+    Bk bk;
+    float *S0;
+    uint16_t *S0b;
+    M2Ring ring;
+    const float *A;
+    int min_len;
+    float *out;         // materialise target, nullptr when consolidating
+};
+
+struct M2RmwArgs {
+    M2Dims d;
+    float *state;
+    float *snap;        // nullptr = in place
+    const float *A, *D;
+    const float *x, *Bm, *C, *dt;
+    float *y;
+    int ntok;
+};
+
+struct GdnRing {
+    float *k;      // [B,H,W,dk]
+    float *v;      // [B,H,W,dv]
+    float *beta;   // [B,H,W]
+    float *alpha;  // [B,H,W]
+};
+
+struct GdnDims {
+    int B, H, DV, DK, W;
+};
+
+struct GdnStepArgs {
+    GdnDims d;
+    Bk bk;
+    float *S0;
+    GdnRing ring;
+    const float *q, *k, *v, *beta, *alpha;
+    float *o;
+};
+
+struct GdnFoldArgs {
+    GdnDims d;
+    Bk bk;
+    float *S0;
+    GdnRing ring;
+    int min_len;
+    float *out;
+};
+
+struct GdnRmwArgs {
+    GdnDims d;
+    float *state;
+    float *snap;
+    const float *q, *k, *v, *beta, *alpha;
+    float *o;
+    int ntok;
+};
+
+// ---- launchers (return hipSuccess or the launch error) ----
+bool m2_supported(int P, int N);
+hipError_t m2_decode(const M2StepArgs &a, bool bf16, hipStream_t s);
+hipError_t m2_verify(const M2StepArgs &a, bool bf16, hipStream_t s);
+hipError_t m2_fold(const M2FoldArgs &a, bool bf16, hipStream_t s);
+hipError_t m2_rmw(const M2RmwArgs &a, hipStream_t s);
+
+bool gdn_supported(int DV, int DK);
+hipError_t gdn_decode(const GdnStepArgs &a, hipStream_t s);
+hipError_t gdn_fold(const GdnFoldArgs &a, hipStream_t s);
+hipError_t gdn_rmw(const GdnRmwArgs &a, hipStream_t s);
+
+hipError_t init_checkpoint(float *S0, uint16_t *S0b, const float *state, const int32_t *mask,
+                           Bk bk, uint32_t *err, int B, int H, long tile_elems, hipStream_t s);
+hipError_t bk_commit(Bk bk, const int32_t *accepted, uint32_t *err, int B, hipStream_t s);
+hipError_t bk_rollback(Bk bk, const int32_t *new_len, uint32_t *err, int B, hipStream_t s);
+hipError_t clear_word(uint32_t *w, hipStream_t s);
+
+}  // namespace rssm

@@ -1,0 +1,648 @@
+// mamba2.hip -- Mamba-2 ReplaySSM decode kernels for gfx950.
+//
+// Per (sequence b, head h) the state is a P x N fp32 checkpoint S0 plus a ring of the last W
+// tokens' inputs. Writing Lam_m = exp(A sum_{i<m} dt_i) for the decay over m buffered entries and
+// w_j = dt_j exp(A sum_{i>j} dt_i) for entry j's weight, the state after the entries is
+//     S = Lam_m S0 + sum_j w_j x_j B_j^T,
+// so the output of the newest entry, y = S C + D x, is
+//     y = Lam_m (S0 C) + sum_j w_j (B_j . C) x_j + D x                                   (replay)
+// which reads S0 once and never writes it. Folding the entries (consolidation) writes that S
+// back as the new S0. The normal step appends to the buffer and reads the checkpoint; only a
+// full buffer is consolidated (ia.goatify.app article "NVIDIA y Princeton aceleran modelos
+// híbridos...", paragraph "El checkpoint reduce escrituras de estado").
+//
+// One workgroup per (b, h) tile. The S0 stream is the only large traffic: its 16-byte loads are
+// issued first, the small per-tile work (ring staging in LDS, decay weights, B_j . C dots with
+// lane-group butterflies) runs while they are in flight, and the row sums of S0 C use a
+// reduce-scatter butterfly over the lanes of a row.
+#include "dev_common.h"
+#include "internal.h"
+
+namespace rssm {
+namespace {
+
+// weight of entry j among m entries with step sizes sdt[0..m-1]: dt_j exp(A sum_{i>j} dt_i)
+__device__ __forceinline__ float m2_weight(const float *sdt, int j, int m, float A)
+{
+    float s = 0.f;
+    for (int i = j + 1; i < m; ++i) s += sdt[i];
+    return sdt[j] * expf(A * s);
+}
+
+// decay of the whole window of m entries: exp(A sum_i dt_i)
+__device__ __forceinline__ float m2_window_decay(const float *sdt, int m, float A)
+{
+    float s = 0.f;
+    for (int i = 0; i < m; ++i) s += sdt[i];
+    return expf(A * s);
+}
+
+__device__ __forceinline__ float dot_row(const float4 &v, const float *cc)
+{
+    return v.x * cc[0] + v.y * cc[1] + v.z * cc[2] + v.w * cc[3];
+}
+__device__ __forceinline__ float dot_row(const uint2 &v, const float *cc)
+{
+    return bf16_lo(v.x) * cc[0] + bf16_hi(v.x) * cc[1] + bf16_lo(v.y) * cc[2] + bf16_hi(v.y) * cc[3];
+}
+__device__ __forceinline__ float dot_row(const uint4 &v, const float *cc)
+{
+    return bf16_lo(v.x) * cc[0] + bf16_hi(v.x) * cc[1] + bf16_lo(v.y) * cc[2] + bf16_hi(v.y) * cc[3]
+         + bf16_lo(v.z) * cc[4] + bf16_hi(v.z) * cc[5] + bf16_lo(v.w) * cc[6] + bf16_hi(v.w) * cc[7];
+}
+
+template <int EPL>
+__device__ __forceinline__ void load_cols(float (&cc)[EPL], const float *src)
+{
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+        const float4 v = ld4(src + e);
+        cc[e] = v.x; cc[e + 1] = v.y; cc[e + 2] = v.z; cc[e + 3] = v.w;
+    }
+}
+
+// bf16 read-copy layout: 16-byte loads (8 values) when the tile has enough of them for every
+// lane, else 8-byte loads.
+template <int P, int N>
+struct Bf16Epl {
+    static constexpr int value = (P * N / 8 >= TileShape<P, N>::TPB) ? 8 : 4;
+};
+
+template <int EPL> struct RawBf16;
+template <> struct RawBf16<8> { using type = uint4; };
+template <> struct RawBf16<4> { using type = uint2; };
+
+// Per-tile context of one (b, h) workgroup.
+struct Tile {
+    int b, h, g, t, W;
+    size_t bh, bg;            // tile index and (b, group) index
+    size_t rh, rg_;           // ring row bases: (b,h) and (b,g) times W
+    bool own_group;           // first head of its group: writes the group's B / C ring rows
+    float Ah, Dh;
+};
+
+__device__ __forceinline__ Tile make_tile(const M2Dims &d, const float *A, const float *D)
+{
+    Tile c;
+    const int tile = blockIdx.x;
+    c.b = tile / d.H;
+    c.h = tile - c.b * d.H;
+    const int hpg = d.H / d.G;
+    c.g = c.h / hpg;
+    c.t = threadIdx.x;
+    c.W = d.W;
+    c.bh = (size_t)tile;
+    c.bg = (size_t)c.b * d.G + c.g;
+    c.rh = c.bh * d.W;
+    c.rg_ = c.bg * d.W;
+    c.own_group = (c.h - c.g * hpg) == 0;
+    c.Ah = A ? A[c.h] : 0.f;
+    c.Dh = D ? D[c.h] : 0.f;
+    return c;
+}
+
+// LDS floats used by the fold core for a ring of length W.
+__host__ __device__ constexpr int fold_lds_floats(int W, int P, int N)
+{
+    return (W + 1) * (P + N) + 2 * (W + 2);
+}
+
+// Fold n = nring (+1 with a current token) entries into the lane's R x 4 block of the
+// checkpoint held in acc:  acc <- Lam_n acc + sum_j w_j x_j B_j^T.  Ring entries start at ring
+// slot `head`; the current token (xt, Bt, dtt), if xt != nullptr, is the newest entry.
+// All threads of the workgroup must call it (it synchronises).
+template <int P, int N, int R>
+__device__ __forceinline__ void m2_fold_core(float4 (&acc)[R], float *smem,
+                             const M2Ring &ring, const Tile &c, int head, int nring,
+                             const float *xt, const float *Bt, float dtt)
+{
+    constexpr int TPB = TileShape<P, N>::TPB;
+    using M = RowMap<P, N, TPB, 4>;
+    static_assert(R == M::R, "fold block");
+    const int W = c.W, t = c.t;
+    const int rg = t / M::LPR, c0 = (t - rg * M::LPR) * 4;
+    const int n = nring + (xt ? 1 : 0);
+    float *sh_u = smem;                     // [n][P]: x_j, then w_j x_j
+    float *sh_B = sh_u + (W + 1) * P;       // [n][N]
+    float *sh_dt = sh_B + (W + 1) * N;      // [n]
+    float *sh_w = sh_dt + (W + 2);          // [n] weights, [W+1] window decay
+
+    for (int j = t; j < n; j += TPB) sh_dt[j] = j < nring ? ring.dt[c.rh + (head + j) % W] : dtt;
+    constexpr int PF = P / 4, NF = N / 4;
+    for (int i = t; i < n * PF; i += TPB) {
+        const int j = i / PF, q = (i - j * PF) * 4;
+        const float4 v = j < nring ? ld4(ring.x + (c.rh + (head + j) % W) * P + q) : ld4(xt + q);
+        st4(sh_u + j * P + q, v);
+    }
+    for (int i = t; i < n * NF; i += TPB) {
+        const int j = i / NF, q = (i - j * NF) * 4;
+        const float4 v = j < nring ? ld4(ring.B + (c.rg_ + (head + j) % W) * N + q) : ld4(Bt + q);
+        st4(sh_B + j * N + q, v);
+    }
+    __syncthreads();
+    for (int j = t; j < n; j += TPB) sh_w[j] = m2_weight(sh_dt, j, n, c.Ah);
+    if (t == TPB - 1) sh_w[W + 1] = m2_window_decay(sh_dt, n, c.Ah);
+    __syncthreads();
+    for (int i = t; i < n * P; i += TPB) sh_u[i] *= sh_w[i / P];
+    __syncthreads();
+    const float lam = sh_w[W + 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        acc[r].x *= lam; acc[r].y *= lam; acc[r].z *= lam; acc[r].w *= lam;
+    }
+    const int p0 = rg * R;
+    for (int j = 0; j < n; ++j) {
+        const float4 bv = ld4(sh_B + j * N + c0);
+        const float *u = sh_u + j * P + p0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float ur = u[r];
+            acc[r].x += ur * bv.x; acc[r].y += ur * bv.y;
+            acc[r].z += ur * bv.z; acc[r].w += ur * bv.w;
+        }
+    }
+}
+
+// Store the lane's block of a folded checkpoint (and its bf16 read copy).
+template <int P, int N>
+__device__ __forceinline__ void store_tile(const float4 (&acc)[Map4<P, N>::R],
+                                           float *dst, uint16_t *dstb, int t)
+{
+    using M = RowMap<P, N, TileShape<P, N>::TPB, 4>;
+    const int rg = t / M::LPR, c0 = (t - rg * M::LPR) * 4;
+    const size_t off = (size_t)(rg * M::R) * N + c0;
+#pragma unroll
+    for (int r = 0; r < M::R; ++r) st4_nt(dst + off + (size_t)r * N, acc[r]);
+    if (dstb) {
+#pragma unroll
+        for (int r = 0; r < M::R; ++r) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[r].x, acc[r].y);
+            w.y = pack_bf16x2(acc[r].z, acc[r].w);
+            *reinterpret_cast<uint2 *>(dstb + off + (size_t)r * N) = w;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// decode: replay path (the token does not fill the ring)
+// ------------------------------------------------------------------------------------------
+template <int P, int N, bool BF16>
+__device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile &c, int head, int len, float *smem)
+{
+    constexpr int TPB = TileShape<P, N>::TPB;
+    constexpr int EPL = BF16 ? Bf16Epl<P, N>::value : 4;
+    using M = RowMap<P, N, TPB, EPL>;
+    constexpr int R = M::R, LPR = M::LPR;
+    using RawT = typename std::conditional<BF16, typename RawBf16<EPL>::type, float4>::type;
+    const int W = c.W, t = c.t, m = len + 1;
+    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * EPL;
+    float *sh_x = smem;            // [m][P]
+    float *sh_dt = sh_x + W * P;   // [m]
+    float *sh_cf = sh_dt + W;      // [m]  w_j (B_j . C)
+    float *sh_lam = sh_cf + W;     // window decay
+
+    // 1. checkpoint block: issued first, consumed last
+    RawT raw[R];
+    {
+        const size_t off = c.bh * (size_t)(P * N) + (size_t)(rg * R) * N + c0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if constexpr (!BF16) raw[r] = ld4_nt(a.S0 + off + (size_t)r * N);
+            else if constexpr (EPL == 8) raw[r] = ldu4_nt(a.S0b + off + (size_t)r * N);
+            else raw[r] = ldu2_nt(a.S0b + off + (size_t)r * N);
+        }
+    }
+    const float *xt = a.x + c.bh * P;
+    const float *Bt = a.Bm + c.bg * N;
+    const float *Ct = a.C + c.bg * N;
+    const float dtt = a.dt[c.bh];
+    const int slot = (head + len) % W;
+    float cc[EPL];
+    load_cols<EPL>(cc, Ct + c0);
+
+    // 2. stage step sizes and x rows of the m entries; append this token's dt and x
+    for (int j = t; j < m; j += TPB) sh_dt[j] = j < len ? a.ring.dt[c.rh + (head + j) % W] : dtt;
+    if (t == 0) a.ring.dt[c.rh + slot] = dtt;
+    constexpr int PF = P / 4;
+    for (int i = t; i < m * PF; i += TPB) {
+        const int j = i / PF, q = (i - j * PF) * 4;
+        float4 v;
+        if (j < len) {
+            v = ld4(a.ring.x + (c.rh + (head + j) % W) * P + q);
+        } else {
+            v = ld4(xt + q);
+            st4(a.ring.x + (c.rh + slot) * P + q, v);
+        }
+        st4(sh_x + j * P + q, v);
+    }
+    if (a.ring.C && c.own_group && rg == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4)
+            st4(a.ring.C + (c.rg_ + slot) * N + c0 + e, make_float4(cc[e], cc[e + 1], cc[e + 2], cc[e + 3]));
+    }
+    __syncthreads();
+
+    // 3. w_j (B_j . C) for every entry; row group rg takes entries rg, rg + RG, ...
+    for (int j = rg; j < m; j += M::RG) {
+        const float *Bj = j < len ? a.ring.B + (c.rg_ + (head + j) % W) * N : Bt;
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+            const float4 v = ld4(Bj + c0 + e);
+            if (j == len && c.own_group) st4(a.ring.B + (c.rg_ + slot) * N + c0 + e, v);
+            part += v.x * cc[e] + v.y * cc[e + 1] + v.z * cc[e + 2] + v.w * cc[e + 3];
+        }
+        const float s = group_sum<LPR>(part);
+        if (cg == 0) sh_cf[j] = m2_weight(sh_dt, j, m, c.Ah) * s;
+    }
+    if (t == TPB - 1) sh_lam[0] = m2_window_decay(sh_dt, m, c.Ah);
+    __syncthreads();
+
+    // 4. z = S0 C, then y = Lam z + sum_j w_j (B_j . C) x_j + D x
+    float part[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[r] = dot_row(raw[r], cc);
+    int rsel;
+    const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
+    if (row_writer<R, LPR>(cg)) {
+        const int p = rg * R + rsel;
+        float corr = 0.f;
+        for (int j = 0; j < m; ++j) corr += sh_cf[j] * sh_x[j * P + p];
+        a.y[c.bh * P + p] = sh_lam[0] * z + corr + c.Dh * sh_x[len * P + p];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// decode: fold path (the token fills the ring; with len == W after a full commit the ring is
+// already full and the token is the (W+1)-th entry)
+// ------------------------------------------------------------------------------------------
+template <int P, int N, bool BF16>
+__device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &c, int head, int len, float *smem)
+{
+    constexpr int TPB = TileShape<P, N>::TPB;
+    using M = RowMap<P, N, TPB, 4>;
+    constexpr int R = M::R, LPR = M::LPR;
+    const int t = c.t;
+    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
+    float *S0 = a.S0 + c.bh * (size_t)(P * N);
+    float4 acc[R];
+    {
+        const size_t off = (size_t)(rg * R) * N + c0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = ld4_nt(S0 + off + (size_t)r * N);
+    }
+    const float *xt = a.x + c.bh * P;
+    const float *Bt = a.Bm + c.bg * N;
+    float cc[4];
+    load_cols<4>(cc, a.C + c.bg * N + c0);
+    m2_fold_core<P, N>(acc, smem, a.ring, c, head, len, xt, Bt, a.dt[c.bh]);
+    store_tile<P, N>(acc, S0, BF16 ? a.S0b + c.bh * (size_t)(P * N) : nullptr, t);
+    float part[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[r] = dot_row(acc[r], cc);
+    int rsel;
+    const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
+    if (row_writer<R, LPR>(cg)) {
+        const int p = rg * R + rsel;
+        a.y[c.bh * P + p] = z + c.Dh * xt[p];
+    }
+}
+
+template <int P, int N, bool BF16>
+__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs a)
+{
+    extern __shared__ float smem[];
+    const Tile c = make_tile(a.d, a.A, a.D);
+    const int B = a.d.B, W = c.W;
+    const int head = a.bk.in[c.b];
+    const int len = a.bk.in[B + c.b];
+    const bool fold = len + 1 >= W;
+    if (fold) m2_fold_decode<P, N, BF16>(a, c, head, len, smem);
+    else m2_replay_decode<P, N, BF16>(a, c, head, len, smem);
+    if (c.h == 0 && c.t == 0) {
+        a.bk.out[c.b] = fold ? (head + len + 1) % W : head;
+        a.bk.out[B + c.b] = fold ? 0 : len + 1;
+        a.bk.out[2 * B + c.b] = 0;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// consolidation / materialisation
+// ------------------------------------------------------------------------------------------
+template <int P, int N, bool BF16>
+__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_fold(M2FoldArgs a)
+{
+    constexpr int TPB = TileShape<P, N>::TPB;
+    using M = RowMap<P, N, TPB, 4>;
+    extern __shared__ float smem[];
+    const Tile c = make_tile(a.d, a.A, nullptr);
+    const int B = a.d.B, W = c.W;
+    const int head = a.bk.in[c.b];
+    const int len = a.bk.in[B + c.b];
+    const int nd = a.bk.in[2 * B + c.b];
+    const bool fold = len >= (a.min_len > 1 ? a.min_len : 1);
+    if (!a.out && c.h == 0 && c.t == 0) {
+        a.bk.out[c.b] = fold ? (head + len) % W : head;
+        a.bk.out[B + c.b] = fold ? 0 : len;
+        a.bk.out[2 * B + c.b] = nd;
+    }
+    float *S0 = a.S0 + c.bh * (size_t)(P * N);
+    if (!fold) {
+        if (a.out) {
+            float *dst = a.out + c.bh * (size_t)(P * N);
+            for (int i = c.t; i < P * N / 4; i += TPB) st4(dst + 4 * i, ld4(S0 + 4 * i));
+        }
+        return;
+    }
+    const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
+    float4 acc[M::R];
+    const size_t off = (size_t)(rg * M::R) * N + c0;
+#pragma unroll
+    for (int r = 0; r < M::R; ++r) acc[r] = ld4_nt(S0 + off + (size_t)r * N);
+    m2_fold_core<P, N>(acc, smem, a.ring, c, head, len, nullptr, nullptr, 0.f);
+    if (a.out) store_tile<P, N>(acc, a.out + c.bh * (size_t)(P * N), nullptr, c.t);
+    else store_tile<P, N>(acc, S0, BF16 ? a.S0b + c.bh * (size_t)(P * N) : nullptr, c.t);
+}
+
+// ------------------------------------------------------------------------------------------
+// speculative verify: K drafts, outputs only, S0 streamed once
+// ------------------------------------------------------------------------------------------
+template <int P, int N, int EPL, typename RawT>
+__device__ __forceinline__ void m2_verify_outputs(const M2StepArgs &a, const Tile &c, const RawT *raw,
+                                  int head_e, int len_e, float *smem)
+{
+    constexpr int TPB = TileShape<P, N>::TPB;
+    using M = RowMap<P, N, TPB, EPL>;
+    constexpr int R = M::R, LPR = M::LPR;
+    const int W = c.W, t = c.t, K = a.ntok;
+    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * EPL;
+    const size_t BH = (size_t)a.d.B * a.d.H, BG = (size_t)a.d.B * a.d.G;
+    const int ne = len_e + K;
+    float *sh_x = smem;            // [ne][P]
+    float *sh_B = sh_x + W * P;    // [ne][N]
+    float *sh_dt = sh_B + W * N;   // [ne]
+    float *sh_cf = sh_dt + W;      // [ne]
+    float *sh_lam = sh_cf + W;
+
+    for (int j = t; j < ne; j += TPB)
+        sh_dt[j] = j < len_e ? a.ring.dt[c.rh + (head_e + j) % W] : a.dt[(j - len_e) * BH + c.bh];
+    constexpr int PF = P / 4, NF = N / 4;
+    for (int i = t; i < ne * PF; i += TPB) {
+        const int j = i / PF, q = (i - j * PF) * 4;
+        const float4 v = j < len_e ? ld4(a.ring.x + (c.rh + (head_e + j) % W) * P + q)
+                                   : ld4(a.x + ((j - len_e) * BH + c.bh) * P + q);
+        st4(sh_x + j * P + q, v);
+    }
+    for (int i = t; i < ne * NF; i += TPB) {
+        const int j = i / NF, q = (i - j * NF) * 4;
+        const float4 v = j < len_e ? ld4(a.ring.B + (c.rg_ + (head_e + j) % W) * N + q)
+                                   : ld4(a.Bm + ((j - len_e) * BG + c.bg) * N + q);
+        st4(sh_B + j * N + q, v);
+    }
+    __syncthreads();
+
+    for (int k = 0; k < K; ++k) {
+        const int mk = len_e + k + 1;
+        float cc[EPL];
+        load_cols<EPL>(cc, a.C + (k * BG + c.bg) * N + c0);
+        float part[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) part[r] = dot_row(raw[r], cc);
+        int rsel;
+        const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
+        for (int j = rg; j < mk; j += M::RG) {
+            float pp = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) pp += sh_B[j * N + c0 + e] * cc[e];
+            const float s = group_sum<LPR>(pp);
+            if (cg == 0) sh_cf[j] = m2_weight(sh_dt, j, mk, c.Ah) * s;
+        }
+        if (t == TPB - 1) sh_lam[0] = m2_window_decay(sh_dt, mk, c.Ah);
+        __syncthreads();
+        if (row_writer<R, LPR>(cg)) {
+            const int p = rg * R + rsel;
+            float corr = 0.f;
+            for (int j = 0; j < mk; ++j) corr += sh_cf[j] * sh_x[j * P + p];
+            a.y[(k * BH + c.bh) * P + p] = sh_lam[0] * z + corr + c.Dh * sh_x[(len_e + k) * P + p];
+        }
+        __syncthreads();
+    }
+
+    // append the drafts as entries len_e .. len_e + K - 1 (every ring read is done)
+    for (int i = t; i < K * PF; i += TPB) {
+        const int k = i / PF, q = (i - k * PF) * 4;
+        st4(a.ring.x + (c.rh + (head_e + len_e + k) % W) * P + q, ld4(sh_x + (len_e + k) * P + q));
+    }
+    if (c.own_group) {
+        for (int i = t; i < K * NF; i += TPB) {
+            const int k = i / NF, q = (i - k * NF) * 4;
+            const size_t row = (c.rg_ + (head_e + len_e + k) % W) * N + q;
+            st4(a.ring.B + row, ld4(sh_B + (len_e + k) * N + q));
+            if (a.ring.C) st4(a.ring.C + row, ld4(a.C + (k * BG + c.bg) * N + q));
+        }
+    }
+    for (int k = t; k < K; k += TPB) a.ring.dt[c.rh + (head_e + len_e + k) % W] = sh_dt[len_e + k];
+}
+
+template <int P, int N, bool BF16>
+__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_verify(M2StepArgs a)
+{
+    constexpr int TPB = TileShape<P, N>::TPB;
+    extern __shared__ float smem[];
+    const Tile c = make_tile(a.d, a.A, a.D);
+    const int B = a.d.B, W = c.W, K = a.ntok;
+    const int head = a.bk.in[c.b];
+    const int len = a.bk.in[B + c.b];
+    const bool prefold = len + K > W;
+    const int head_e = prefold ? (head + len) % W : head;
+    const int len_e = prefold ? 0 : len;
+    const size_t off0 = c.bh * (size_t)(P * N);
+    if (prefold || !BF16) {
+        using M = RowMap<P, N, TPB, 4>;
+        const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
+        float4 acc[M::R];
+        const size_t off = off0 + (size_t)(rg * M::R) * N + c0;
+#pragma unroll
+        for (int r = 0; r < M::R; ++r) acc[r] = ld4_nt(a.S0 + off + (size_t)r * N);
+        if (prefold) {
+            m2_fold_core<P, N>(acc, smem, a.ring, c, head, len, nullptr, nullptr, 0.f);
+            store_tile<P, N>(acc, a.S0 + off0, BF16 ? a.S0b + off0 : nullptr, c.t);
+            __syncthreads();
+        }
+        m2_verify_outputs<P, N, 4>(a, c, acc, head_e, len_e, smem);
+    } else {
+        constexpr int EPL = Bf16Epl<P, N>::value;
+        using M = RowMap<P, N, TPB, EPL>;
+        using RawT = typename RawBf16<EPL>::type;
+        const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * EPL;
+        RawT raw[M::R];
+        const size_t off = off0 + (size_t)(rg * M::R) * N + c0;
+#pragma unroll
+        for (int r = 0; r < M::R; ++r) {
+            if constexpr (EPL == 8) raw[r] = ldu4_nt(a.S0b + off + (size_t)r * N);
+            else raw[r] = ldu2_nt(a.S0b + off + (size_t)r * N);
+        }
+        m2_verify_outputs<P, N, EPL>(a, c, raw, head_e, len_e, smem);
+    }
+    if (c.h == 0 && c.t == 0) {
+        a.bk.out[c.b] = head_e;
+        a.bk.out[B + c.b] = len_e;
+        a.bk.out[2 * B + c.b] = K;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// conventional read-modify-write comparator
+// ------------------------------------------------------------------------------------------
+template <int P, int N>
+__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_rmw(M2RmwArgs a)
+{
+    constexpr int TPB = TileShape<P, N>::TPB;
+    using M = RowMap<P, N, TPB, 4>;
+    constexpr int R = M::R, LPR = M::LPR;
+    const Tile c = make_tile(a.d, a.A, a.D);
+    const int t = c.t;
+    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
+    const size_t BH = (size_t)a.d.B * a.d.H, BG = (size_t)a.d.B * a.d.G;
+    const size_t off = c.bh * (size_t)(P * N) + (size_t)(rg * R) * N + c0;
+    float4 S[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) S[r] = ld4_nt(a.state + off + (size_t)r * N);
+    for (int k = 0; k < a.ntok; ++k) {
+        const float dtv = a.dt[k * BH + c.bh];
+        const float dec = expf(dtv * c.Ah);
+        const float *xk = a.x + (k * BH + c.bh) * P;
+        const float4 bv = ld4(a.Bm + (k * BG + c.bg) * N + c0);
+        float cc[4];
+        load_cols<4>(cc, a.C + (k * BG + c.bg) * N + c0);
+        float part[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float coef = dtv * xk[rg * R + r];
+            S[r].x = dec * S[r].x + coef * bv.x;
+            S[r].y = dec * S[r].y + coef * bv.y;
+            S[r].z = dec * S[r].z + coef * bv.z;
+            S[r].w = dec * S[r].w + coef * bv.w;
+            part[r] = dot_row(S[r], cc);
+        }
+        int rsel;
+        const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
+        if (row_writer<R, LPR>(cg)) {
+            const int p = rg * R + rsel;
+            a.y[(k * BH + c.bh) * P + p] = z + c.Dh * xk[p];
+        }
+        if (a.snap) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) st4_nt(a.snap + k * BH * (size_t)(P * N) + off + (size_t)r * N, S[r]);
+        }
+    }
+    if (!a.snap) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) st4_nt(a.state + off + (size_t)r * N, S[r]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------
+template <int P, int N>
+size_t decode_lds(int W)
+{
+    const size_t replay = (size_t)W * P + 3 * W + 4;
+    const size_t fold = fold_lds_floats(W, P, N);
+    return 4 * (replay > fold ? replay : fold);
+}
+
+template <int P, int N>
+size_t verify_lds(int W)
+{
+    const size_t out = (size_t)W * (P + N) + 2 * W + 4;
+    const size_t fold = fold_lds_floats(W, P, N);
+    return 4 * (out > fold ? out : fold);
+}
+
+template <int P, int N>
+hipError_t go_decode(const M2StepArgs &a, bool bf16, hipStream_t s)
+{
+    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    const size_t lds = decode_lds<P, N>(a.d.W);
+    if (bf16) hipLaunchKernelGGL((k_m2_decode<P, N, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_m2_decode<P, N, false>), grid, block, lds, s, a);
+    return hipGetLastError();
+}
+
+template <int P, int N>
+hipError_t go_verify(const M2StepArgs &a, bool bf16, hipStream_t s)
+{
+    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    const size_t lds = verify_lds<P, N>(a.d.W);
+    if (bf16) hipLaunchKernelGGL((k_m2_verify<P, N, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_m2_verify<P, N, false>), grid, block, lds, s, a);
+    return hipGetLastError();
+}
+
+template <int P, int N>
+hipError_t go_fold(const M2FoldArgs &a, bool bf16, hipStream_t s)
+{
+    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    const size_t lds = 4 * (size_t)fold_lds_floats(a.d.W, P, N);
+    if (bf16) hipLaunchKernelGGL((k_m2_fold<P, N, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_m2_fold<P, N, false>), grid, block, lds, s, a);
+    return hipGetLastError();
+}
+
+template <int P, int N>
+hipError_t go_rmw(const M2RmwArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    hipLaunchKernelGGL((k_m2_rmw<P, N>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// (head_dim P, d_state N) pairs with compiled kernels.
+#define RSSM_M2_SHAPES(X) X(16, 16) X(32, 32) X(64, 64) X(64, 128) X(128, 128)
+
+bool m2_supported(int P, int N)
+{
+#define RSSM_CASE(p, n) if (P == p && N == n) return true;
+    RSSM_M2_SHAPES(RSSM_CASE)
+#undef RSSM_CASE
+    return false;
+}
+
+hipError_t m2_decode(const M2StepArgs &a, bool bf16, hipStream_t s)
+{
+#define RSSM_C(p, n) if (a.d.P == p && a.d.N == n) return go_decode<p, n>(a, bf16, s);
+    RSSM_M2_SHAPES(RSSM_C)
+#undef RSSM_C
+    return hipErrorInvalidValue;
+}
+
+hipError_t m2_verify(const M2StepArgs &a, bool bf16, hipStream_t s)
+{
+#define RSSM_C(p, n) if (a.d.P == p && a.d.N == n) return go_verify<p, n>(a, bf16, s);
+    RSSM_M2_SHAPES(RSSM_C)
+#undef RSSM_C
+    return hipErrorInvalidValue;
+}
+
+hipError_t m2_fold(const M2FoldArgs &a, bool bf16, hipStream_t s)
+{
+#define RSSM_C(p, n) if (a.d.P == p && a.d.N == n) return go_fold<p, n>(a, bf16, s);
+    RSSM_M2_SHAPES(RSSM_C)
+#undef RSSM_C
+    return hipErrorInvalidValue;
+}
+
+hipError_t m2_rmw(const M2RmwArgs &a, hipStream_t s)
+{
+#define RSSM_C(p, n) if (a.d.P == p && a.d.N == n) return go_rmw<p, n>(a, s);
+    RSSM_M2_SHAPES(RSSM_C)
+#undef RSSM_C
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rssm

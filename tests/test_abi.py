@@ -1,0 +1,140 @@
+"""librssm loads, exports every entry point include/rssm.h declares, and rejects bad arguments and
+call-order misuse on the host, before any device work. No GPU needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import checkpoint_replay_buffer_amd.binding as rb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rssm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rb.LIB_PATH):
+        from checkpoint_replay_buffer_amd import build
+        build.build()
+    return rb.load_library()
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rssm_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_match_header(lib):
+    names = _declared()
+    assert set(names) == set(rb.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in range(0, -7, -1):
+        assert rb.status_str(st) not in ("", "unknown status")
+    assert rb.status_str(-99) == "unknown status"
+
+
+def _cfg(**kw):
+    base = dict(kind=rb.RSSM_MAMBA2, batch=256, nheads=128, ngroups=128, dim_v=64, dim_k=128,
+                window=16, max_draft=6, flags=rb.RSSM_F_STORE_C)
+    base.update(kw)
+    return rb.make_config(**base)
+
+
+def _up(v):
+    return (v + 255) // 256 * 256
+
+
+def test_workspace_layout(lib):
+    B, H, G, P, N, W = 256, 128, 128, 64, 128, 16
+    want = _up(2 * 3 * B * 4) + _up(4) + _up(B * H * P * N * 4) + _up(B * H * W * P * 4) \
+        + 2 * _up(B * G * W * N * 4) + _up(B * H * W * 4)
+    assert rb.rssm_workspace_bytes(_cfg()) == want
+    # bf16 read copy adds B*H*P*N*2; no stored C removes one B/C ring
+    assert rb.rssm_workspace_bytes(_cfg(flags=rb.RSSM_F_STORE_C | rb.RSSM_F_BF16_READ)) == \
+        want + _up(B * H * P * N * 2)
+    assert rb.rssm_workspace_bytes(_cfg(flags=0)) == want - _up(B * G * W * N * 4)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kind=3), -1),
+    (dict(window=0), -2),
+    (dict(window=65), -2),
+    (dict(max_draft=17), -2),
+    (dict(max_draft=-1), -2),
+    (dict(ngroups=3), -2),
+    (dict(batch=0), -2),
+    (dict(flags=8), -1),
+    (dict(dim_v=48), -6),
+    (dict(dim_k=96), -6),
+    (dict(kind=rb.RSSM_GDN, dim_v=128, dim_k=128, ngroups=64), -2),
+    (dict(kind=rb.RSSM_GDN, dim_v=128, dim_k=128, flags=rb.RSSM_F_BF16_READ), -6),
+])
+def test_config_errors(lib, kw, status):
+    with pytest.raises(rb.RssmError) as e:
+        rb.rssm_workspace_bytes(_cfg(**kw))
+    assert e.value.status == status
+
+
+FAKE_WS = 1 << 40     # an aligned address; creation never dereferences it
+
+
+def test_create_checks(lib):
+    cfg = _cfg()
+    n = rb.rssm_workspace_bytes(cfg)
+    with pytest.raises(rb.RssmError) as e:
+        rb.rssm_create(cfg, FAKE_WS + 16, n)
+    assert e.value.status == -1
+    with pytest.raises(rb.RssmError) as e:
+        rb.rssm_create(cfg, FAKE_WS, n - 1)
+    assert e.value.status == -3
+    h = rb.rssm_create(cfg, FAKE_WS, n)
+    rb.rssm_destroy(h)
+
+
+def test_call_order_checked_on_host(lib):
+    cfg = _cfg(batch=2, nheads=4, ngroups=4, dim_v=16, dim_k=16, window=4, max_draft=2)
+    h = rb.rssm_create(cfg, FAKE_WS, rb.rssm_workspace_bytes(cfg))
+    try:
+        tok = rb.make_inputs(1, x=FAKE_WS, B=FAKE_WS, C=FAKE_WS, dt=FAKE_WS)
+        # nothing loaded yet
+        for call in (lambda: rb.rssm_decode_step(h, tok, FAKE_WS, stream=0),
+                     lambda: rb.rssm_consolidate(h, 1, stream=0),
+                     lambda: rb.rssm_verify(h, tok, FAKE_WS, stream=0),
+                     lambda: rb.rssm_verify_commit(h, FAKE_WS, stream=0),
+                     lambda: rb.rssm_rollback(h, FAKE_WS, stream=0),
+                     lambda: rb.rssm_materialize(h, FAKE_WS, stream=0),
+                     lambda: rb.rssm_init_checkpoint(h, FAKE_WS, FAKE_WS, stream=0)):
+            with pytest.raises(rb.RssmError) as e:
+                call()
+            assert e.value.status == -4
+        # null / misaligned arguments
+        with pytest.raises(rb.RssmError) as e:
+            rb.rssm_init_checkpoint(h, FAKE_WS + 4, None, stream=0)
+        assert e.value.status == -1
+        with pytest.raises(rb.RssmError) as e:
+            rb.rssm_set_params(h, None, FAKE_WS)
+        assert e.value.status == -1
+    finally:
+        rb.rssm_destroy(h)
+
+
+def test_baseline_argument_checks(lib):
+    cfg = _cfg(batch=2, nheads=4, ngroups=4, dim_v=16, dim_k=16, window=4, max_draft=0)
+    bad = rb.make_inputs(1, x=FAKE_WS + 8, B=FAKE_WS, C=FAKE_WS, dt=FAKE_WS)
+    with pytest.raises(rb.RssmError) as e:
+        rb.rssm_step_baseline(cfg, FAKE_WS, bad, FAKE_WS, FAKE_WS, FAKE_WS, stream=0)
+    assert e.value.status == -1
+    zero = rb.make_inputs(0, x=FAKE_WS, B=FAKE_WS, C=FAKE_WS, dt=FAKE_WS)
+    with pytest.raises(rb.RssmError) as e:
+        rb.rssm_step_baseline(cfg, FAKE_WS, zero, FAKE_WS, FAKE_WS, FAKE_WS, stream=0)
+    assert e.value.status == -1
+    with pytest.raises(rb.RssmError) as e:
+        rb.rssm_step_baseline(cfg, FAKE_WS, rb.make_inputs(1, x=FAKE_WS, B=FAKE_WS, C=FAKE_WS,
+                                                           dt=FAKE_WS),
+                              None, FAKE_WS, FAKE_WS, stream=0)
+    assert e.value.status == -1

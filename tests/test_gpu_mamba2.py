@@ -1,0 +1,435 @@
+"""GPU parity of the Mamba-2 ReplaySSM path (C ABI -> HIP kernels) against the CPU oracle.
+
+Tolerances: normwise relative error (max over output vectors of max|d| / max|ref|) 1e-5 for the
+fp32 paths and 2e-2 for the bf16 read copy; bookkeeping (head, len, ndraft, error bits)
+bit-exact.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from checkpoint_replay_buffer_amd import binding as rb
+from oracle import Bookkeeping, m2_spec_round, m2_step, normwise_err
+from tests.gpu_helpers import dev, host, m2_dev_tokens, say, tok0
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+TOL_BF16 = 2e-2
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _ctx(sh: wl.M2Shape, prm, bf16=False, store_c=True):
+    c = rb.Context("mamba2", sh.batch, sh.nheads, sh.head_dim, sh.d_state, sh.window,
+                   ngroups=sh.ngroups, max_draft=sh.max_draft, bf16_read=bf16, store_c=store_c)
+    A, D = dev(prm["A"]), dev(prm["D"])
+    c.set_params(A, D)
+    return c, A, D
+
+
+def _check_bk(ctx, model: Bookkeeping, err=None):
+    h, l, n, e = ctx.bookkeeping()
+    mh, ml, mn = model.snapshot()
+    assert h == list(mh) and l == list(ml) and n == list(mn), (h, l, n, mh, ml, mn)
+    if err is not None:
+        assert e == err
+    return e
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("G", [4, 1])
+def test_tiny_decode_every_call(bf16, G):
+    """B=2, H=4, P=N=16, W=4, 64 steps: every y, the materialised state after every call and the
+    bookkeeping after every call."""
+    sh = wl.M2Shape(batch=2, nheads=4, ngroups=G, head_dim=16, d_state=16, window=4)
+    say(f"tiny decode bf16={bf16} G={G}")
+    prm = wl.m2_params(sh, 0)
+    s0 = wl.m2_state0(sh, 0)
+    ins = wl.m2_token_inputs(sh, 0, 0, ntok=64)
+    d = m2_dev_tokens(sh, ins, 64)
+    ctx, A, D = _ctx(sh, prm, bf16)
+    ctx.init_checkpoint(dev(s0))
+    model = Bookkeeping(sh.batch, sh.window)
+    ref = s0.astype(np.float64).copy()
+    y = torch.empty(sh.batch, sh.nheads, sh.head_dim, device="cuda")
+    mat = torch.empty(s0.shape, device="cuda")
+    worst = 0.0
+    for t in range(64):
+        tok = {k: v[t] for k, v in d.items()}
+        ctx.decode_step(y, **tok)
+        y_ref = m2_step(prm["A"], prm["D"], ins["x"][t], ins["B"][t], ins["C"][t], ins["dt"][t], ref)
+        model.decode()
+        err = normwise_err(host(y), y_ref)
+        worst = max(worst, err)
+        assert err < (TOL_BF16 if bf16 else TOL), (t, err)
+        _check_bk(ctx, model, 0)
+        ctx.materialize(mat)
+        assert normwise_err(host(mat), ref) < TOL, t
+    say(f"  worst normwise {worst:.3e}")
+
+
+def test_rmw_comparator_tiny():
+    sh = wl.M2Shape(batch=3, nheads=4, ngroups=2, head_dim=16, d_state=16, window=4)
+    prm = wl.m2_params(sh, 2)
+    s0 = wl.m2_state0(sh, 2)
+    ins = wl.m2_token_inputs(sh, 2, 0, ntok=24)
+    d = m2_dev_tokens(sh, ins, 24)
+    cfg = rb.make_config(rb.RSSM_MAMBA2, sh.batch, sh.nheads, sh.ngroups, 16, 16, 4)
+    A, D = dev(prm["A"]), dev(prm["D"])
+    st = dev(s0)
+    ref = s0.astype(np.float64).copy()
+    y = torch.empty(1, sh.batch, sh.nheads, 16, device="cuda")
+    for t in range(24):
+        rb.step_baseline(cfg, st, y, A, D, **{k: v[t:t + 1] for k, v in d.items()})
+        y_ref = m2_step(prm["A"], prm["D"], ins["x"][t], ins["B"][t], ins["C"][t], ins["dt"][t], ref)
+        assert normwise_err(host(y)[0], y_ref) < TOL
+    assert normwise_err(host(st), ref) < TOL
+    # snapshot mode: K tokens from the state, state read-only, one snapshot per token
+    K = 5
+    snaps = torch.empty((K,) + s0.shape, device="cuda")
+    yk = torch.empty(K, sh.batch, sh.nheads, 16, device="cuda")
+    before = host(st).copy()
+    rb.step_baseline(cfg, st, yk, A, D, snapshots=snaps, **{k: v[:K] for k, v in d.items()})
+    assert np.array_equal(host(st), before)
+    r2 = before.astype(np.float64)
+    for k in range(K):
+        y_ref = m2_step(prm["A"], prm["D"], ins["x"][k], ins["B"][k], ins["C"][k], ins["dt"][k], r2)
+        assert normwise_err(host(yk)[k], y_ref) < TOL
+        assert normwise_err(host(snaps)[k], r2) < TOL
+
+
+def test_ragged_lengths_masked_init_consolidate():
+    """Sequences at different buffer fills (masked re-init), grouped B/C, partial folds."""
+    sh = wl.M2Shape(batch=5, nheads=4, ngroups=2, head_dim=32, d_state=32, window=4)
+    prm = wl.m2_params(sh, 3)
+    s0 = wl.m2_state0(sh, 3)
+    ctx, A, D = _ctx(sh, prm)
+    ctx.init_checkpoint(dev(s0))
+    model = Bookkeeping(sh.batch, sh.window)
+    ref = s0.astype(np.float64).copy()
+    y = torch.empty(sh.batch, sh.nheads, sh.head_dim, device="cuda")
+    mat = torch.empty(s0.shape, device="cuda")
+    schedule = ["d", "d", ("mask", [1, 0, 1, 0, 0]), "d", "d", "d", ("cons", 2), "d", "d",
+                ("mask", [0, 0, 0, 1, 1]), "d", "d", "d", "d", "d", ("cons", 1), "d"]
+    for i, op in enumerate(schedule):
+        if op == "d":
+            ins = wl.m2_token_inputs(sh, 3, 10 + i)
+            tok = tok0(m2_dev_tokens(sh, ins, 1))
+            ctx.decode_step(y, **tok)
+            y_ref = m2_step(prm["A"], prm["D"], ins["x"][0], ins["B"][0], ins["C"][0], ins["dt"][0], ref)
+            model.decode()
+            assert normwise_err(host(y), y_ref) < TOL, i
+        elif op[0] == "mask":
+            fresh = wl.m2_state0(sh, 100 + i)
+            m = np.array(op[1], dtype=np.int32)
+            ctx.init_checkpoint(dev(fresh), dev(m))
+            ref[m != 0] = fresh[m != 0]
+            model.init(m)
+        else:
+            ctx.consolidate(op[1])
+            model.consolidate(op[1])
+        _check_bk(ctx, model, 0)
+        ctx.materialize(mat)
+        assert normwise_err(host(mat), ref) < TOL, i
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_speculative_rounds(bf16):
+    """verify K drafts -> causal outputs equal conventional steps from the committed state;
+    commit by pointer; interleaved decodes; discarded drafts."""
+    sh = wl.M2Shape(batch=6, nheads=4, ngroups=4, head_dim=16, d_state=16, window=8, max_draft=3)
+    prm = wl.m2_params(sh, 4)
+    s0 = wl.m2_state0(sh, 4)
+    ctx, A, D = _ctx(sh, prm, bf16)
+    ctx.init_checkpoint(dev(s0))
+    model = Bookkeeping(sh.batch, sh.window, sh.max_draft)
+    ref = s0.astype(np.float64).copy()
+    acc = wl.spec_accepted(sh.batch, 40, sh.max_draft, seed=4)
+    tol = TOL_BF16 if bf16 else TOL
+    yk = torch.empty(3, sh.batch, sh.nheads, 16, device="cuda")
+    y = torch.empty(sh.batch, sh.nheads, 16, device="cuda")
+    mat = torch.empty(s0.shape, device="cuda")
+    for r in range(40):
+        K = 1 + r % 3
+        ins = wl.m2_token_inputs(sh, 4, 200 + r, ntok=K)
+        ctx.verify(yk[:K], **m2_dev_tokens(sh, ins, K))
+        model.verify(K)
+        _check_bk(ctx, model)
+        a = np.minimum(acc[r], K).astype(np.int32)
+        if r % 7 == 6:
+            a[:] = 0
+            ctx.rollback(dev(np.array(model.len, dtype=np.int32)))
+            model.rollback(model.len.copy())
+        else:
+            ctx.commit(dev(a))
+            model.commit(a)
+        y_ref = m2_spec_round(prm["A"], prm["D"], ins, ref, a)
+        assert normwise_err(host(yk[:K]), y_ref) < tol, r
+        _check_bk(ctx, model, 0)
+        ctx.materialize(mat)
+        assert normwise_err(host(mat), ref) < TOL, r
+        if r % 3 == 2:
+            t = wl.m2_token_inputs(sh, 4, 500 + r)
+            ctx.decode_step(y, **tok0(m2_dev_tokens(sh, t, 1)))
+            model.decode()
+            y_ref = m2_step(prm["A"], prm["D"], t["x"][0], t["B"][0], t["C"][0], t["dt"][0], ref)
+            assert normwise_err(host(y), y_ref) < tol, r
+            _check_bk(ctx, model, 0)
+
+
+def test_golden_bookkeeping_trace_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "bookkeeping_w4_k2.json")))
+    sh = wl.M2Shape(batch=g["batch"], nheads=2, ngroups=2, head_dim=16, d_state=16,
+                    window=g["window"], max_draft=g["max_draft"])
+    prm = wl.m2_params(sh, 0)
+    ctx, A, D = _ctx(sh, prm)
+    y = torch.empty(sh.max_draft, sh.batch, sh.nheads, 16, device="cuda")
+    for i, op in enumerate(g["ops"]):
+        kind = op["op"]
+        if kind == "init":
+            ctx.init_checkpoint(dev(wl.m2_state0(sh, 0)))
+        elif kind == "init_mask":
+            ctx.init_checkpoint(dev(wl.m2_state0(sh, 1)), dev(np.array(op["arg"], dtype=np.int32)))
+        elif kind == "decode":
+            ctx.decode_step(y[0], **tok0(m2_dev_tokens(sh, wl.m2_token_inputs(sh, 0, i), 1)))
+        elif kind == "verify":
+            K = op["K"]
+            ctx.verify(y[:K], **m2_dev_tokens(sh, wl.m2_token_inputs(sh, 0, i, ntok=K), K))
+        elif kind == "commit":
+            ctx.commit(dev(np.array(op["arg"], dtype=np.int32)))
+        elif kind == "rollback":
+            ctx.rollback(dev(np.array(op["arg"], dtype=np.int32)))
+        elif kind == "consolidate":
+            ctx.consolidate(op["arg"])
+        if kind == "read_err":
+            assert ctx.bookkeeping()[3] == op["err"], (i, op)
+            continue
+        h, l, n = _peek(ctx)
+        assert (h, l, n) == (op["head"], op["len"], op["ndraft"]), (i, op, h, l, n)
+
+
+def _peek(ctx):
+    """head / len / ndraft without reading (and so without clearing) the error word."""
+    import ctypes
+    B = ctx.cfg.batch
+    arr = ctypes.c_int32 * B
+    h, l, n = arr(), arr(), arr()
+    st = rb.load_library().rssm_read_bookkeeping(ctx.handle, h, l, n, None, rb._stream(None))
+    assert st == 0
+    return list(h), list(l), list(n)
+
+
+def test_rollback_prefix_bit_exact():
+    """Run A: consolidate(W-K+1), verify K drafts, commit a. Run B: same consolidate, verify only
+    the first a drafts, commit a. Outputs of the a drafts, bookkeeping, the materialised state and
+    every later output are bit-identical."""
+    sh = wl.M2Shape(batch=4, nheads=4, ngroups=4, head_dim=64, d_state=128, window=16, max_draft=6)
+    prm = wl.m2_params(sh, 5)
+    s0 = dev(wl.m2_state0(sh, 5))
+    K, a = 6, 4
+    outs = []
+    for run in ("A", "B"):
+        ctx, A, D = _ctx(sh, prm)
+        ctx.init_checkpoint(s0)
+        y = torch.empty(sh.batch, sh.nheads, 64, device="cuda")
+        for t in range(13):
+            ctx.decode_step(y, **tok0(m2_dev_tokens(sh, wl.m2_token_inputs(sh, 5, t), 1)))
+        ctx.consolidate(sh.window - K + 1)
+        ins = wl.m2_token_inputs(sh, 5, 99, ntok=K)
+        n = K if run == "A" else a
+        yk = torch.empty(n, sh.batch, sh.nheads, 64, device="cuda")
+        ctx.verify(yk, **m2_dev_tokens(sh, {k: v[:n] for k, v in ins.items()}, n))
+        ctx.commit(dev(np.full(sh.batch, a, dtype=np.int32)))
+        mat = torch.empty(s0.shape, device="cuda")
+        ctx.materialize(mat)
+        later = []
+        for t in range(5):
+            ctx.decode_step(y, **tok0(m2_dev_tokens(sh, wl.m2_token_inputs(sh, 5, 300 + t), 1)))
+            later.append(host(y).copy())
+        outs.append((host(yk)[:a].copy(), ctx.bookkeeping(), host(mat).copy(), later))
+    (ya, bka, ma, la), (yb, bkb, mb, lb) = outs
+    assert np.array_equal(ya, yb)
+    assert bka == bkb
+    assert np.array_equal(ma, mb)
+    for u, v in zip(la, lb):
+        assert np.array_equal(u, v)
+
+
+def test_rollback_to_shorter_prefix_equals_shorter_run():
+    sh = wl.M2Shape(batch=3, nheads=4, ngroups=4, head_dim=16, d_state=16, window=8)
+    prm = wl.m2_params(sh, 6)
+    s0 = dev(wl.m2_state0(sh, 6))
+    toks = [tok0(m2_dev_tokens(sh, wl.m2_token_inputs(sh, 6, t), 1)) for t in range(5)]
+    res = []
+    for n_dec, rb_len in ((5, [2, 0, 5]), (2, None)):
+        ctx, A, D = _ctx(sh, prm)
+        ctx.init_checkpoint(s0)
+        y = torch.empty(3, 4, 16, device="cuda")
+        for t in range(n_dec):
+            ctx.decode_step(y, **toks[t])
+        if rb_len is not None:
+            ctx.rollback(dev(np.array(rb_len, dtype=np.int32)))
+        mat = torch.empty(s0.shape, device="cuda")
+        ctx.materialize(mat)
+        res.append((host(mat).copy(), ctx.bookkeeping()))
+    # sequence 0 rolled back to 2 equals the 2-token run; 1 (len 0) equals the initial state
+    assert np.array_equal(res[0][0][0], res[1][0][0])
+    assert np.array_equal(res[0][0][1], host(s0)[1])
+    assert res[0][1][1] == [2, 0, 5]
+
+
+def test_out_of_range_commit_and_rollback_raise_bits():
+    sh = wl.M2Shape(batch=4, nheads=2, ngroups=2, head_dim=16, d_state=16, window=4, max_draft=2)
+    prm = wl.m2_params(sh, 7)
+    ctx, A, D = _ctx(sh, prm)
+    ctx.init_checkpoint(dev(wl.m2_state0(sh, 7)))
+    yk = torch.empty(2, 4, 2, 16, device="cuda")
+    ctx.verify(yk, **m2_dev_tokens(sh, wl.m2_token_inputs(sh, 7, 1, ntok=2), 2))
+    ctx.commit(dev(np.array([0, 3, -1, 2], dtype=np.int32)))
+    h, l, n, e = ctx.bookkeeping()
+    assert l == [0, 0, 0, 2] and n == [0, 0, 0, 0] and e == rb.RSSM_DEV_COMMIT_RANGE
+    ctx.rollback(dev(np.array([0, 0, 1, 3], dtype=np.int32)))
+    h, l, n, e = ctx.bookkeeping()
+    assert l == [0, 0, 0, 2] and e == rb.RSSM_DEV_ROLLBACK_RANGE
+    assert ctx.bookkeeping()[3] == 0
+    # host-side call-order checks
+    with pytest.raises(rb.RssmError):
+        ctx.commit(dev(np.zeros(4, dtype=np.int32)))
+    ctx.verify(yk, **m2_dev_tokens(sh, wl.m2_token_inputs(sh, 7, 2, ntok=2), 2))
+    with pytest.raises(rb.RssmError):
+        ctx.decode_step(yk[0], **tok0(m2_dev_tokens(sh, wl.m2_token_inputs(sh, 7, 3), 1)))
+    ctx.rollback(dev(np.zeros(4, dtype=np.int32)))
+
+
+def test_determinism_and_head_permutation():
+    sh = wl.M2Shape(batch=3, nheads=8, ngroups=8, head_dim=64, d_state=128, window=16)
+    prm = wl.m2_params(sh, 8)
+    s0 = wl.m2_state0(sh, 8)
+    ins = wl.m2_token_inputs(sh, 8, 0, ntok=20)
+    perm = np.array([3, 1, 7, 0, 2, 6, 5, 4])
+    runs = []
+    for p in (None, None, perm):
+        pp = {k: v for k, v in prm.items()} if p is None else {k: v[p].copy() for k, v in prm.items()}
+        ss = s0 if p is None else s0[:, p].copy()
+        ii = ins if p is None else {"x": ins["x"][:, :, p].copy(), "B": ins["B"][:, :, p].copy(),
+                                    "C": ins["C"][:, :, p].copy(), "dt": ins["dt"][:, :, p].copy()}
+        ctx, A, D = _ctx(sh, pp)
+        ctx.init_checkpoint(dev(ss))
+        d = m2_dev_tokens(sh, ii, 20)
+        y = torch.empty(sh.batch, sh.nheads, 64, device="cuda")
+        ys = []
+        for t in range(20):
+            ctx.decode_step(y, **{k: v[t] for k, v in d.items()})
+            ys.append(host(y).copy())
+        runs.append(np.stack(ys))
+    assert np.array_equal(runs[0], runs[1])
+    assert np.array_equal(runs[0][:, :, perm], runs[2])
+
+
+# ---------------------------------------------------------------------------------------------
+# serving shape: batch 256, 128 heads, head_dim 64, d_state 128, W = 16, 512 steps
+# ---------------------------------------------------------------------------------------------
+
+SUBSET = np.array([0, 1, 37, 101, 128, 190, 254, 255])
+
+
+@pytest.mark.parametrize("bf16,steps", [(False, 512), (True, 160)])
+def test_serving_shape_sampled(bf16, steps):
+    sh = wl.M2_SERVE
+    say(f"serving shape bf16={bf16} steps={steps}: generating inputs")
+    prm = wl.m2_params(sh, 0)
+    s0 = wl.m2_state0(sh, 0)
+    pool = 32
+    slots = [wl.m2_token_inputs(sh, 0, s) for s in range(pool)]
+    dslots = [tok0(m2_dev_tokens(sh, s, 1)) for s in slots]
+    ctx, A, D = _ctx(sh, prm, bf16)
+    ctx.init_checkpoint(dev(s0))
+    cfg = rb.make_config(rb.RSSM_MAMBA2, sh.batch, sh.nheads, sh.ngroups, sh.head_dim, sh.d_state,
+                         sh.window)
+    st_rmw = dev(s0)
+    y = torch.empty(sh.batch, sh.nheads, sh.head_dim, device="cuda")
+    y2 = torch.empty(1, sh.batch, sh.nheads, sh.head_dim, device="cuda")
+    sub = torch.from_numpy(SUBSET).cuda()
+    ys = torch.empty(steps, len(SUBSET), sh.nheads, sh.head_dim, device="cuda")
+    worst_pair = 0.0
+    say("  running GPU steps")
+    for t in range(steps):
+        tok = dslots[t % pool]
+        ctx.decode_step(y, **tok)
+        ys[t] = y.index_select(0, sub)
+        if not bf16:
+            rb.step_baseline(cfg, st_rmw, y2, A, D, **{k: v.unsqueeze(0) for k, v in tok.items()})
+            if t % 64 == 63:     # replay vs read-modify-write at every sequence
+                worst_pair = max(worst_pair, normwise_err(host(y), host(y2)[0]))
+    mat = torch.empty(s0.shape, device="cuda")
+    ctx.materialize(mat)
+    h, l, n, e = ctx.bookkeeping()
+    assert l == [steps % sh.window] * sh.batch and h == [0] * sh.batch and e == 0
+    say("  oracle on the sampled sequences")
+    ref = s0[SUBSET].astype(np.float64)
+    worst = 0.0
+    ys_h = host(ys)
+    for t in range(steps):
+        s = slots[t % pool]
+        y_ref = m2_step(prm["A"], prm["D"], s["x"][0][SUBSET], s["B"][0][SUBSET], s["C"][0][SUBSET],
+                        s["dt"][0][SUBSET], ref)
+        worst = max(worst, normwise_err(ys_h[t], y_ref))
+    say(f"  worst normwise {worst:.3e} (replay vs rmw {worst_pair:.3e})")
+    assert worst < (TOL_BF16 if bf16 else TOL)
+    assert normwise_err(host(mat)[SUBSET], ref) < TOL
+    if not bf16:
+        assert worst_pair < 2 * TOL
+        assert normwise_err(host(st_rmw)[SUBSET], ref) < TOL
+
+
+@pytest.mark.parametrize("batch", [1, 32])
+def test_bf16_small_batches(batch):
+    sh = wl.M2Shape(batch=batch, nheads=128, ngroups=128, head_dim=64, d_state=128, window=16)
+    prm = wl.m2_params(sh, 9)
+    s0 = wl.m2_state0(sh, 9)
+    ins = wl.m2_token_inputs(sh, 9, 0, ntok=40)
+    d = m2_dev_tokens(sh, ins, 40)
+    ctx, A, D = _ctx(sh, prm, bf16=True)
+    ctx.init_checkpoint(dev(s0))
+    ref = s0.astype(np.float64)
+    y = torch.empty(batch, 128, 64, device="cuda")
+    for t in range(40):
+        ctx.decode_step(y, **{k: v[t] for k, v in d.items()})
+        y_ref = m2_step(prm["A"], prm["D"], ins["x"][t], ins["B"][t], ins["C"][t], ins["dt"][t], ref)
+        assert normwise_err(host(y), y_ref) < TOL_BF16
+
+
+def test_speculative_serving_shape_sampled():
+    """batch 512, K = 6 drafts per round into the W = 16 ring, censored-geometric acceptance:
+    bookkeeping of all 512 sequences bit-exact after every call, outputs of sampled sequences."""
+    sh = wl.M2_SPEC
+    K, rounds = 6, 24
+    prm = wl.m2_params(sh, 0)
+    s0 = wl.m2_state0(sh, 0)
+    acc = wl.spec_accepted(sh.batch, rounds, K, seed=0)
+    ctx, A, D = _ctx(sh, prm)
+    ctx.init_checkpoint(dev(s0))
+    model = Bookkeeping(sh.batch, sh.window, K)
+    sub = np.array([0, 5, 300, 511])
+    ref = s0[sub].astype(np.float64)
+    yk = torch.empty(K, sh.batch, sh.nheads, sh.head_dim, device="cuda")
+    worst = 0.0
+    pool = [wl.m2_token_inputs(sh, 0, s, ntok=K) for s in range(3)]
+    dpool = [m2_dev_tokens(sh, p, K) for p in pool]
+    for r in range(rounds):
+        ins = pool[r % 3]
+        ctx.verify(yk, **dpool[r % 3])
+        model.verify(K)
+        _check_bk(ctx, model, 0)
+        ctx.commit(dev(acc[r]))
+        model.commit(acc[r])
+        _check_bk(ctx, model, 0)
+        sub_ins = {k: v[:, sub] for k, v in ins.items()}
+        y_ref = m2_spec_round(prm["A"], prm["D"], sub_ins, ref, acc[r][sub])
+        worst = max(worst, normwise_err(host(yk)[:, sub], y_ref))
+    say(f"  spec worst normwise {worst:.3e}")
+    assert worst < TOL
