@@ -23,6 +23,11 @@ struct rssm_ctx {
     int par;
     bool pending;          // a verify awaits its commit / rollback
     bool initialized;      // a full rssm_init_checkpoint has run
+    // Bounds lo <= len[b] <= hi over all sequences, kept on the host from the call sequence
+    // (the device-resident commit / rollback arguments only widen them). A decode with
+    // hi + 1 < W cannot fold any sequence and uses the replay-only kernel.
+    int lo, hi;
+    int pending_k;         // draft count of the pending verify
 };
 
 namespace {
@@ -52,6 +57,7 @@ rssm_status check_config(const rssm_config *c)
         if (c->ngroups != c->nheads) return RSSM_E_SHAPE;
         if (c->flags != 0) return RSSM_E_UNSUPPORTED;
         if (!gdn_supported(c->dim_v, c->dim_k)) return RSSM_E_UNSUPPORTED;
+        if (gdn_lds_bytes(c->dim_v, c->dim_k, c->window) > 65536) return RSSM_E_UNSUPPORTED;
     } else {
         if (!m2_supported(c->dim_v, c->dim_k)) return RSSM_E_UNSUPPORTED;
         // the fold stages W+1 entries of x and B in LDS: keep it within 64 KiB per workgroup
@@ -117,6 +123,17 @@ rssm_status check_inputs(const rssm_config &c, const rssm_inputs *in)
             return RSSM_E_ARG;
     }
     return RSSM_OK;
+}
+
+// len bounds after folding every sequence with len >= m (m >= 1)
+void bounds_after_fold(rssm_ctx *c, int m)
+{
+    if (c->lo >= m) {
+        c->lo = c->hi = 0;
+    } else if (c->hi >= m) {
+        c->lo = 0;
+        c->hi = m - 1;
+    }
 }
 
 rssm_status ready(const rssm_ctx *c)
@@ -196,6 +213,8 @@ rssm_status rssm_init_checkpoint(rssm_ctx *ctx, const float *state, const int32_
     if (s == RSSM_OK) {
         ctx->initialized = true;
         ctx->pending = false;
+        ctx->lo = 0;
+        if (!seq_mask) ctx->hi = 0;
     }
     return s;
 }
@@ -208,14 +227,28 @@ rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, voi
     if ((s = check_inputs(c, in)) != RSSM_OK) return s;
     if (in->ntok != 1 || !aligned16(y)) return RSSM_E_ARG;
     if (ctx->pending) return RSSM_E_STATE;
+    const bool mayfold = ctx->hi + 1 >= c.window;
     if (c.kind == RSSM_MAMBA2) {
         M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
                      in->x, in->B, in->C, in->dt, y, 1};
-        return launched(ctx, m2_decode(a, ctx->S0b != nullptr, strm(stream)), true);
+        s = launched(ctx, m2_decode(a, ctx->S0b != nullptr, mayfold, strm(stream)), true);
+    } else {
+        GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
+                      in->alpha, y};
+        s = launched(ctx, gdn_decode(a, strm(stream)), true);
     }
-    GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
-                  in->alpha, y};
-    return launched(ctx, gdn_decode(a, strm(stream)), true);
+    if (s == RSSM_OK) {
+        if (!mayfold) {
+            ++ctx->lo;
+            ++ctx->hi;
+        } else if (ctx->lo + 1 >= c.window) {       // every sequence folded
+            ctx->lo = ctx->hi = 0;
+        } else {                                     // some may have folded, the rest < W
+            ctx->lo = 0;
+            ctx->hi = c.window - 1;
+        }
+    }
+    return s;
 }
 
 rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream)
@@ -226,10 +259,13 @@ rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream)
     const rssm_config &c = ctx->cfg;
     if (c.kind == RSSM_MAMBA2) {
         M2FoldArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, min_len, nullptr};
-        return launched(ctx, m2_fold(a, ctx->S0b != nullptr, strm(stream)), true);
+        s = launched(ctx, m2_fold(a, ctx->S0b != nullptr, strm(stream)), true);
+    } else {
+        GdnFoldArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, min_len, nullptr};
+        s = launched(ctx, gdn_fold(a, strm(stream)), true);
     }
-    GdnFoldArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, min_len, nullptr};
-    return launched(ctx, gdn_fold(a, strm(stream)), true);
+    if (s == RSSM_OK) bounds_after_fold(ctx, min_len > 1 ? min_len : 1);
+    return s;
 }
 
 rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream)
@@ -245,7 +281,11 @@ rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *st
     M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
                  in->x, in->B, in->C, in->dt, y, in->ntok};
     s = launched(ctx, m2_verify(a, ctx->S0b != nullptr, strm(stream)), true);
-    if (s == RSSM_OK) ctx->pending = true;
+    if (s == RSSM_OK) {
+        ctx->pending = true;
+        ctx->pending_k = in->ntok;
+        bounds_after_fold(ctx, c.window - in->ntok + 1);   // sequences with len + K > W fold
+    }
     return s;
 }
 
@@ -255,7 +295,10 @@ rssm_status rssm_verify_commit(rssm_ctx *ctx, const int32_t *accepted, void *str
     if (!ctx->pending) return RSSM_E_STATE;
     const rssm_status s = launched(ctx, bk_commit(flip(ctx), accepted, ctx->err, ctx->cfg.batch,
                                                   strm(stream)), true);
-    if (s == RSSM_OK) ctx->pending = false;
+    if (s == RSSM_OK) {
+        ctx->pending = false;
+        ctx->hi = ctx->hi + ctx->pending_k < ctx->cfg.window ? ctx->hi + ctx->pending_k : ctx->cfg.window;
+    }
     return s;
 }
 
@@ -265,7 +308,10 @@ rssm_status rssm_rollback(rssm_ctx *ctx, const int32_t *new_len, void *stream)
     if (!ctx->initialized) return RSSM_E_STATE;
     const rssm_status s = launched(ctx, bk_rollback(flip(ctx), new_len, ctx->err, ctx->cfg.batch,
                                                     strm(stream)), true);
-    if (s == RSSM_OK) ctx->pending = false;
+    if (s == RSSM_OK) {
+        ctx->pending = false;
+        ctx->lo = 0;
+    }
     return s;
 }
 

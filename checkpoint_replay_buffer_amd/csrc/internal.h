@@ -7,7 +7,7 @@
 
 namespace rssm {
 
-constexpr int kMaxWindow = 64;   // largest ring length W
+constexpr int kMaxWindow = 32;   // largest ring length W (W + 1 entries fit one wave's lanes)
 
 // Bookkeeping is double-buffered: every launch that changes it reads bk_in and writes bk_out
 // (each [3][B] int32: head, len, ndraft). All head-workgroups of a sequence read bk_in while one
@@ -103,12 +103,14 @@ struct GdnRmwArgs {
 
 // ---- launchers (return hipSuccess or the launch error) ----
 bool m2_supported(int P, int N);
-hipError_t m2_decode(const M2StepArgs &a, bool bf16, hipStream_t s);
+// mayfold = false promises that no sequence's ring fills in this step (len + 1 < W for all).
+hipError_t m2_decode(const M2StepArgs &a, bool bf16, bool mayfold, hipStream_t s);
 hipError_t m2_verify(const M2StepArgs &a, bool bf16, hipStream_t s);
 hipError_t m2_fold(const M2FoldArgs &a, bool bf16, hipStream_t s);
 hipError_t m2_rmw(const M2RmwArgs &a, hipStream_t s);
 
 bool gdn_supported(int DV, int DK);
+size_t gdn_lds_bytes(int DV, int DK, int W);
 hipError_t gdn_decode(const GdnStepArgs &a, hipStream_t s);
 hipError_t gdn_fold(const GdnFoldArgs &a, hipStream_t s);
 hipError_t gdn_rmw(const GdnRmwArgs &a, hipStream_t s);

@@ -101,62 +101,79 @@ __device__ __forceinline__ Tile make_tile(const M2Dims &d, const float *A, const
     return c;
 }
 
-// LDS floats used by the fold core for a ring of length W.
+// LDS floats used by the fold core for a ring of length W (x and B rows of up to W+1 entries).
 __host__ __device__ constexpr int fold_lds_floats(int W, int P, int N)
 {
-    return (W + 1) * (P + N) + 2 * (W + 2);
+    return (W + 1) * (P + N);
+}
+
+// Decay weights of n <= 64 entries whose step sizes sit one per lane of the wave (lane l < n holds
+// dt_l, oldest first): returns w_l = dt_l exp(A sum_{i>l} dt_i) on lane l (0 on lanes >= n), and
+// the decay of the whole window exp(A sum_i dt_i) in `lam` on every lane. The suffix sums are a
+// log-step scan with wave shuffles; every lane of the wave must take part.
+__device__ __forceinline__ float wave_weights(float dtl, int n, float A, float &lam)
+{
+    const int lane = threadIdx.x & 63;
+    const float v = lane < n ? dtl : 0.f;
+    float e = __shfl_down(v, 1);        // sum over i > lane, built up by the scan below
+    if (lane == 63) e = 0.f;
+    for (int off = 1; off < n; off <<= 1) {
+        const float o = __shfl_down(e, off);
+        if (lane + off < 64) e += o;
+    }
+    lam = expf(A * __shfl(v + e, 0));
+    return lane < n ? dtl * expf(A * e) : 0.f;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
 // Fold n = nring (+1 with a current token) entries into the lane's R x 4 block of the
 // checkpoint held in acc:  acc <- Lam_n acc + sum_j w_j x_j B_j^T.  Ring entries start at ring
 // slot `head`; the current token (xt, Bt, dtt), if xt != nullptr, is the newest entry.
-// All threads of the workgroup must call it (it synchronises).
+// n <= W + 1 <= 33 entries, so each wave holds every step size in its lanes. All threads of the
+// workgroup must call it; it synchronises once.
 template <int P, int N, int R>
-__device__ __forceinline__ void m2_fold_core(float4 (&acc)[R], float *smem,
-                             const M2Ring &ring, const Tile &c, int head, int nring,
-                             const float *xt, const float *Bt, float dtt)
+__device__ __forceinline__ void m2_fold_core(float4 (&acc)[R], float *smem, const M2Ring &ring,
+                                             const Tile &c, int head, int nring, const float *xt,
+                                             const float *Bt, float dtt)
 {
     constexpr int TPB = TileShape<P, N>::TPB;
-    using M = RowMap<P, N, TPB, 4>;
+    using M = Map4<P, N>;
     static_assert(R == M::R, "fold block");
-    const int W = c.W, t = c.t;
+    const int W = c.W, t = c.t, lane = t & 63;
     const int rg = t / M::LPR, c0 = (t - rg * M::LPR) * 4;
     const int n = nring + (xt ? 1 : 0);
-    float *sh_u = smem;                     // [n][P]: x_j, then w_j x_j
-    float *sh_B = sh_u + (W + 1) * P;       // [n][N]
-    float *sh_dt = sh_B + (W + 1) * N;      // [n]
-    float *sh_w = sh_dt + (W + 2);          // [n] weights, [W+1] window decay
+    float *sh_x = smem;                     // [n][P]
+    float *sh_B = sh_x + (W + 1) * P;       // [n][N]
 
-    for (int j = t; j < n; j += TPB) sh_dt[j] = j < nring ? ring.dt[c.rh + (head + j) % W] : dtt;
+    const float dtl = lane < nring ? ring.dt[c.rh + (head + lane) % W] : dtt;
     constexpr int PF = P / 4, NF = N / 4;
     for (int i = t; i < n * PF; i += TPB) {
         const int j = i / PF, q = (i - j * PF) * 4;
-        const float4 v = j < nring ? ld4(ring.x + (c.rh + (head + j) % W) * P + q) : ld4(xt + q);
-        st4(sh_u + j * P + q, v);
+        st4(sh_x + j * P + q, j < nring ? ld4(ring.x + (c.rh + (head + j) % W) * P + q) : ld4(xt + q));
     }
     for (int i = t; i < n * NF; i += TPB) {
         const int j = i / NF, q = (i - j * NF) * 4;
-        const float4 v = j < nring ? ld4(ring.B + (c.rg_ + (head + j) % W) * N + q) : ld4(Bt + q);
-        st4(sh_B + j * N + q, v);
+        st4(sh_B + j * N + q, j < nring ? ld4(ring.B + (c.rg_ + (head + j) % W) * N + q) : ld4(Bt + q));
     }
+    float lam;
+    const float w = wave_weights(dtl, n, c.Ah, lam);
     __syncthreads();
-    for (int j = t; j < n; j += TPB) sh_w[j] = m2_weight(sh_dt, j, n, c.Ah);
-    if (t == TPB - 1) sh_w[W + 1] = m2_window_decay(sh_dt, n, c.Ah);
-    __syncthreads();
-    for (int i = t; i < n * P; i += TPB) sh_u[i] *= sh_w[i / P];
-    __syncthreads();
-    const float lam = sh_w[W + 1];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         acc[r].x *= lam; acc[r].y *= lam; acc[r].z *= lam; acc[r].w *= lam;
     }
     const int p0 = rg * R;
     for (int j = 0; j < n; ++j) {
+        const float wj = lane_value(w, j);
         const float4 bv = ld4(sh_B + j * N + c0);
-        const float *u = sh_u + j * P + p0;
+        const float *xj = sh_x + j * P + p0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float ur = u[r];
+            const float ur = wj * xj[r];
             acc[r].x += ur * bv.x; acc[r].y += ur * bv.y;
             acc[r].z += ur * bv.z; acc[r].w += ur * bv.w;
         }
@@ -164,11 +181,11 @@ __device__ __forceinline__ void m2_fold_core(float4 (&acc)[R], float *smem,
 }
 
 // Store the lane's block of a folded checkpoint (and its bf16 read copy).
-template <int P, int N>
-__device__ __forceinline__ void store_tile(const float4 (&acc)[Map4<P, N>::R],
-                                           float *dst, uint16_t *dstb, int t)
+template <int P, int N, int R>
+__device__ __forceinline__ void store_tile(const float4 (&acc)[R], float *dst, uint16_t *dstb, int t)
 {
-    using M = RowMap<P, N, TileShape<P, N>::TPB, 4>;
+    using M = Map4<P, N>;
+    static_assert(R == M::R, "fold block");
     const int rg = t / M::LPR, c0 = (t - rg * M::LPR) * 4;
     const size_t off = (size_t)(rg * M::R) * N + c0;
 #pragma unroll
@@ -184,46 +201,74 @@ __device__ __forceinline__ void store_tile(const float4 (&acc)[Map4<P, N>::R],
     }
 }
 
-// ------------------------------------------------------------------------------------------
-// decode: replay path (the token does not fill the ring)
-// ------------------------------------------------------------------------------------------
+// The lane's R rows x EPL columns of the checkpoint read: fp32 S0 or its bf16 copy.
 template <int P, int N, bool BF16>
-__device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile &c, int head, int len, float *smem)
-{
-    constexpr int TPB = TileShape<P, N>::TPB;
-    constexpr int EPL = BF16 ? Bf16Epl<P, N>::value : 4;
-    using M = RowMap<P, N, TPB, EPL>;
-    constexpr int R = M::R, LPR = M::LPR;
+struct ReadTile {
+    static constexpr int EPL = BF16 ? Bf16Epl<P, N>::value : 4;
+    using M = RowMap<P, N, TileShape<P, N>::TPB, EPL>;
     using RawT = typename std::conditional<BF16, typename RawBf16<EPL>::type, float4>::type;
-    const int W = c.W, t = c.t, m = len + 1;
-    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * EPL;
-    float *sh_x = smem;            // [m][P]
-    float *sh_dt = sh_x + W * P;   // [m]
-    float *sh_cf = sh_dt + W;      // [m]  w_j (B_j . C)
-    float *sh_lam = sh_cf + W;     // window decay
+    RawT v[M::R];
 
-    // 1. checkpoint block: issued first, consumed last
-    RawT raw[R];
+    __device__ __forceinline__ void load(const M2StepArgs &a, const Tile &c)
     {
-        const size_t off = c.bh * (size_t)(P * N) + (size_t)(rg * R) * N + c0;
+        const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * EPL;
+        const size_t off = c.bh * (size_t)(P * N) + (size_t)(rg * M::R) * N + c0;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if constexpr (!BF16) raw[r] = ld4_nt(a.S0 + off + (size_t)r * N);
-            else if constexpr (EPL == 8) raw[r] = ldu4_nt(a.S0b + off + (size_t)r * N);
-            else raw[r] = ldu2_nt(a.S0b + off + (size_t)r * N);
+        for (int r = 0; r < M::R; ++r) {
+            if constexpr (!BF16) v[r] = ld4_nt(a.S0 + off + (size_t)r * N);
+            else if constexpr (EPL == 8) v[r] = ldu4_nt(a.S0b + off + (size_t)r * N);
+            else v[r] = ldu2_nt(a.S0b + off + (size_t)r * N);
         }
     }
+};
+
+template <int P, int N, int R>
+__device__ __forceinline__ void load_fp32_tile(float4 (&acc)[R], const float *S0, const Tile &c)
+{
+    using M = Map4<P, N>;
+    const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
+    const size_t off = c.bh * (size_t)(P * N) + (size_t)(rg * M::R) * N + c0;
+#pragma unroll
+    for (int r = 0; r < M::R; ++r) acc[r] = ld4_nt(S0 + off + (size_t)r * N);
+}
+
+// ------------------------------------------------------------------------------------------
+// decode: replay path (the token does not fill the ring). One barrier per tile.
+// ------------------------------------------------------------------------------------------
+template <int P, int N, bool BF16>
+__device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile &c, int head,
+                                                 int len, const ReadTile<P, N, BF16> &tile,
+                                                 float *smem)
+{
+    constexpr int TPB = TileShape<P, N>::TPB;
+    using RT = ReadTile<P, N, BF16>;
+    constexpr int EPL = RT::EPL;
+    using M = typename RT::M;
+    constexpr int R = M::R, LPR = M::LPR, RG = M::RG;
+    const int W = c.W, t = c.t, m = len + 1, lane = t & 63;
+    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * EPL;
+    float *sh_x = smem;            // [m][P]   x of the entries
+    float *sh_s = sh_x + W * P;    // [m]      B_j . C
+    float *sh_w = sh_s + W;        // [m]      decay weights
     const float *xt = a.x + c.bh * P;
     const float *Bt = a.Bm + c.bg * N;
-    const float *Ct = a.C + c.bg * N;
     const float dtt = a.dt[c.bh];
     const int slot = (head + len) % W;
-    float cc[EPL];
-    load_cols<EPL>(cc, Ct + c0);
 
-    // 2. stage step sizes and x rows of the m entries; append this token's dt and x
-    for (int j = t; j < m; j += TPB) sh_dt[j] = j < len ? a.ring.dt[c.rh + (head + j) % W] : dtt;
-    if (t == 0) a.ring.dt[c.rh + slot] = dtt;
+    // all global loads first: C columns, step sizes (one per lane), B rows of this row group's
+    // first two entries, x rows of every entry
+    float cc[EPL];
+    load_cols<EPL>(cc, a.C + c.bg * N + c0);
+    const float dtl = lane < len ? a.ring.dt[c.rh + (head + lane) % W] : dtt;
+    float4 bq[2][EPL / 4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int j = rg + RG * q;
+        const float *Bj = j < len ? a.ring.B + (c.rg_ + (head + j) % W) * N : Bt;
+#pragma unroll
+        for (int e = 0; e < EPL / 4; ++e)
+            bq[q][e] = j < m ? ld4(Bj + c0 + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     constexpr int PF = P / 4;
     for (int i = t; i < m * PF; i += TPB) {
         const int j = i / PF, q = (i - j * PF) * 4;
@@ -232,44 +277,64 @@ __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile
             v = ld4(a.ring.x + (c.rh + (head + j) % W) * P + q);
         } else {
             v = ld4(xt + q);
-            st4(a.ring.x + (c.rh + slot) * P + q, v);
+            st4(a.ring.x + (c.rh + slot) * P + q, v);      // append x
         }
         st4(sh_x + j * P + q, v);
     }
-    if (a.ring.C && c.own_group && rg == 0) {
+    // append B, C, dt of the token (its slot is not one of the entries being read)
+    if (c.own_group) {
+        if (rg == len % RG) {        // the token's B row (already in cache from the load above)
 #pragma unroll
-        for (int e = 0; e < EPL; e += 4)
-            st4(a.ring.C + (c.rg_ + slot) * N + c0 + e, make_float4(cc[e], cc[e + 1], cc[e + 2], cc[e + 3]));
+            for (int e = 0; e < EPL / 4; ++e) st4(a.ring.B + (c.rg_ + slot) * N + c0 + 4 * e, ld4(Bt + c0 + 4 * e));
+        }
+        if (a.ring.C && rg == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; e += 4)
+                st4(a.ring.C + (c.rg_ + slot) * N + c0 + e, make_float4(cc[e], cc[e + 1], cc[e + 2], cc[e + 3]));
+        }
     }
-    __syncthreads();
+    if (t == 0) a.ring.dt[c.rh + slot] = dtt;
 
-    // 3. w_j (B_j . C) for every entry; row group rg takes entries rg, rg + RG, ...
-    for (int j = rg; j < m; j += M::RG) {
+    // decay weights (every wave computes them; wave 0 publishes)
+    float lam;
+    const float w = wave_weights(dtl, m, c.Ah, lam);
+    if (t < m) sh_w[t] = w;
+    // B_j . C for the row group's entries
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int j = rg + RG * q;
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL / 4; ++e)
+            part += bq[q][e].x * cc[4 * e] + bq[q][e].y * cc[4 * e + 1] + bq[q][e].z * cc[4 * e + 2]
+                  + bq[q][e].w * cc[4 * e + 3];
+        const float s = group_sum<LPR>(part);
+        if (cg == 0 && j < m) sh_s[j] = s;
+    }
+    for (int j = rg + 2 * RG; j < m; j += RG) {          // rings longer than 2 RG
         const float *Bj = j < len ? a.ring.B + (c.rg_ + (head + j) % W) * N : Bt;
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; e += 4) {
             const float4 v = ld4(Bj + c0 + e);
-            if (j == len && c.own_group) st4(a.ring.B + (c.rg_ + slot) * N + c0 + e, v);
             part += v.x * cc[e] + v.y * cc[e + 1] + v.z * cc[e + 2] + v.w * cc[e + 3];
         }
         const float s = group_sum<LPR>(part);
-        if (cg == 0) sh_cf[j] = m2_weight(sh_dt, j, m, c.Ah) * s;
+        if (cg == 0) sh_s[j] = s;
     }
-    if (t == TPB - 1) sh_lam[0] = m2_window_decay(sh_dt, m, c.Ah);
     __syncthreads();
 
-    // 4. z = S0 C, then y = Lam z + sum_j w_j (B_j . C) x_j + D x
+    // z = S0 C, then y = Lam z + sum_j w_j (B_j . C) x_j + D x
     float part[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) part[r] = dot_row(raw[r], cc);
+    for (int r = 0; r < R; ++r) part[r] = dot_row(tile.v[r], cc);
     int rsel;
     const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
     if (row_writer<R, LPR>(cg)) {
         const int p = rg * R + rsel;
         float corr = 0.f;
-        for (int j = 0; j < m; ++j) corr += sh_cf[j] * sh_x[j * P + p];
-        a.y[c.bh * P + p] = sh_lam[0] * z + corr + c.Dh * sh_x[len * P + p];
+        for (int j = 0; j < m; ++j) corr += sh_w[j] * sh_s[j] * sh_x[j * P + p];
+        a.y[c.bh * P + p] = lam * z + corr + c.Dh * sh_x[len * P + p];
     }
 }
 
@@ -277,27 +342,20 @@ __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile
 // decode: fold path (the token fills the ring; with len == W after a full commit the ring is
 // already full and the token is the (W+1)-th entry)
 // ------------------------------------------------------------------------------------------
-template <int P, int N, bool BF16>
-__device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &c, int head, int len, float *smem)
+template <int P, int N, bool BF16, int R>
+__device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &c, int head, int len,
+                                               float4 (&acc)[R], float *smem)
 {
-    constexpr int TPB = TileShape<P, N>::TPB;
-    using M = RowMap<P, N, TPB, 4>;
-    constexpr int R = M::R, LPR = M::LPR;
+    using M = Map4<P, N>;
+    static_assert(R == M::R, "fold block");
+    constexpr int LPR = M::LPR;
     const int t = c.t;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
-    float *S0 = a.S0 + c.bh * (size_t)(P * N);
-    float4 acc[R];
-    {
-        const size_t off = (size_t)(rg * R) * N + c0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = ld4_nt(S0 + off + (size_t)r * N);
-    }
     const float *xt = a.x + c.bh * P;
-    const float *Bt = a.Bm + c.bg * N;
     float cc[4];
     load_cols<4>(cc, a.C + c.bg * N + c0);
-    m2_fold_core<P, N>(acc, smem, a.ring, c, head, len, xt, Bt, a.dt[c.bh]);
-    store_tile<P, N>(acc, S0, BF16 ? a.S0b + c.bh * (size_t)(P * N) : nullptr, t);
+    m2_fold_core<P, N>(acc, smem, a.ring, c, head, len, xt, a.Bm + c.bg * N, a.dt[c.bh]);
+    store_tile<P, N>(acc, a.S0 + c.bh * (size_t)(P * N), BF16 ? a.S0b + c.bh * (size_t)(P * N) : nullptr, t);
     float part[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) part[r] = dot_row(acc[r], cc);
@@ -309,17 +367,45 @@ __device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &
     }
 }
 
-template <int P, int N, bool BF16>
+// MAYFOLD = false: the host knows no sequence's ring fills in this step, so the checkpoint read
+// (fp32 or bf16) is issued before anything else. MAYFOLD = true: any mix of replaying and folding
+// sequences; the fp32 tile is still loaded first.
+template <int P, int N, bool BF16, bool MAYFOLD>
 __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs a)
 {
     extern __shared__ float smem[];
     const Tile c = make_tile(a.d, a.A, a.D);
     const int B = a.d.B, W = c.W;
-    const int head = a.bk.in[c.b];
-    const int len = a.bk.in[B + c.b];
-    const bool fold = len + 1 >= W;
-    if (fold) m2_fold_decode<P, N, BF16>(a, c, head, len, smem);
-    else m2_replay_decode<P, N, BF16>(a, c, head, len, smem);
+    bool fold = false;
+    int head, len;
+    if constexpr (!MAYFOLD) {
+        ReadTile<P, N, BF16> tile;
+        tile.load(a, c);
+        head = a.bk.in[c.b];
+        len = a.bk.in[B + c.b];
+        m2_replay_decode<P, N, BF16>(a, c, head, len, tile, smem);
+    } else if constexpr (!BF16) {
+        ReadTile<P, N, false> tile;
+        tile.load(a, c);
+        head = a.bk.in[c.b];
+        len = a.bk.in[B + c.b];
+        fold = len + 1 >= W;
+        if (fold) m2_fold_decode<P, N, false>(a, c, head, len, tile.v, smem);
+        else m2_replay_decode<P, N, false>(a, c, head, len, tile, smem);
+    } else {
+        head = a.bk.in[c.b];
+        len = a.bk.in[B + c.b];
+        fold = len + 1 >= W;
+        if (fold) {
+            float4 acc[Map4<P, N>::R];
+            load_fp32_tile<P, N>(acc, a.S0, c);
+            m2_fold_decode<P, N, true>(a, c, head, len, acc, smem);
+        } else {
+            ReadTile<P, N, true> tile;
+            tile.load(a, c);
+            m2_replay_decode<P, N, true>(a, c, head, len, tile, smem);
+        }
+    }
     if (c.h == 0 && c.t == 0) {
         a.bk.out[c.b] = fold ? (head + len + 1) % W : head;
         a.bk.out[B + c.b] = fold ? 0 : len + 1;
@@ -549,7 +635,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_rmw(M2RmwArgs a)
 template <int P, int N>
 size_t decode_lds(int W)
 {
-    const size_t replay = (size_t)W * P + 3 * W + 4;
+    const size_t replay = (size_t)W * P + 2 * W;
     const size_t fold = fold_lds_floats(W, P, N);
     return 4 * (replay > fold ? replay : fold);
 }
@@ -563,12 +649,14 @@ size_t verify_lds(int W)
 }
 
 template <int P, int N>
-hipError_t go_decode(const M2StepArgs &a, bool bf16, hipStream_t s)
+hipError_t go_decode(const M2StepArgs &a, bool bf16, bool mayfold, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
     const size_t lds = decode_lds<P, N>(a.d.W);
-    if (bf16) hipLaunchKernelGGL((k_m2_decode<P, N, true>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((k_m2_decode<P, N, false>), grid, block, lds, s, a);
+    if (bf16 && mayfold) hipLaunchKernelGGL((k_m2_decode<P, N, true, true>), grid, block, lds, s, a);
+    else if (bf16) hipLaunchKernelGGL((k_m2_decode<P, N, true, false>), grid, block, lds, s, a);
+    else if (mayfold) hipLaunchKernelGGL((k_m2_decode<P, N, false, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_m2_decode<P, N, false, false>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
@@ -613,9 +701,9 @@ bool m2_supported(int P, int N)
     return false;
 }
 
-hipError_t m2_decode(const M2StepArgs &a, bool bf16, hipStream_t s)
+hipError_t m2_decode(const M2StepArgs &a, bool bf16, bool mayfold, hipStream_t s)
 {
-#define RSSM_C(p, n) if (a.d.P == p && a.d.N == n) return go_decode<p, n>(a, bf16, s);
+#define RSSM_C(p, n) if (a.d.P == p && a.d.N == n) return go_decode<p, n>(a, bf16, mayfold, s);
     RSSM_M2_SHAPES(RSSM_C)
 #undef RSSM_C
     return hipErrorInvalidValue;

@@ -91,7 +91,7 @@ typedef struct {
     int32_t ngroups;     /* G (Mamba-2 B/C groups; must be H for GDN) */
     int32_t dim_v;       /* P (Mamba-2 head_dim) or d_v (GDN) */
     int32_t dim_k;       /* N (Mamba-2 d_state) or d_k (GDN) */
-    int32_t window;      /* W, ring length, 1..64 */
+    int32_t window;      /* W, ring length, 1..32 */
     int32_t max_draft;   /* largest K accepted by rssm_verify, 0..W (0 = no speculative use) */
     uint32_t flags;      /* RSSM_F_* */
 } rssm_config;

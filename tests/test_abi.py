@@ -63,7 +63,7 @@ def test_workspace_layout(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(kind=3), -1),
     (dict(window=0), -2),
-    (dict(window=65), -2),
+    (dict(window=33), -2),
     (dict(max_draft=17), -2),
     (dict(max_draft=-1), -2),
     (dict(ngroups=3), -2),

@@ -371,15 +371,36 @@ def test_serving_shape_sampled(bf16, steps):
     assert l == [steps % sh.window] * sh.batch and h == [0] * sh.batch and e == 0
     say("  oracle on the sampled sequences")
     ref = s0[SUBSET].astype(np.float64)
-    worst = 0.0
+    ck = ref.copy()        # the checkpoint the kernel reads: the state at the last fold
+    win_dt = []            # dt of the entries buffered since that fold
+    worst = worst_tok = 0.0
     ys_h = host(ys)
+    W = sh.window
     for t in range(steps):
-        s = slots[t % pool]
-        y_ref = m2_step(prm["A"], prm["D"], s["x"][0][SUBSET], s["B"][0][SUBSET], s["C"][0][SUBSET],
-                        s["dt"][0][SUBSET], ref)
+        s = {k: v[0][SUBSET] for k, v in slots[t % pool].items()}
+        y_ref = m2_step(prm["A"], prm["D"], s["x"], s["B"], s["C"], s["dt"], ref)
         worst = max(worst, normwise_err(ys_h[t], y_ref))
-    say(f"  worst normwise {worst:.3e} (replay vs rmw {worst_pair:.3e})")
-    assert worst < (TOL_BF16 if bf16 else TOL)
+        worst_tok = max(worst_tok, normwise_err(ys_h[t].reshape(len(SUBSET), -1),
+                                                y_ref.reshape(len(SUBSET), -1)))
+        win_dt.append(s["dt"].astype(np.float64))
+        if bf16 and t % W + 1 < W:
+            # bf16 rounding of the checkpoint read: |dy| <= Lam * 2^-8 * sum_n |S0[p,n]| |C_n|
+            lam = np.exp(prm["A"].astype(np.float64)[None, :] * np.sum(win_dt, axis=0))
+            bound = lam[..., None] * 2.0 ** -8 * np.einsum("bhpn,bhn->bhp", np.abs(ck),
+                                                           np.abs(s["C"].astype(np.float64)))
+            slack = TOL * np.max(np.abs(y_ref), axis=-1, keepdims=True)
+            assert np.all(np.abs(ys_h[t] - y_ref) <= bound + slack), t
+        if t % W + 1 == W:
+            ck = ref.copy()
+            win_dt = []
+    say(f"  worst normwise per head {worst:.3e}, per sequence-token {worst_tok:.3e} "
+        f"(replay vs rmw {worst_pair:.3e})")
+    if bf16:
+        # tolerance on the layer output of one token of one sequence (all heads); single heads
+        # whose output is small next to the checkpoint term can exceed it within the bound above
+        assert worst_tok < TOL_BF16
+    else:
+        assert worst < TOL
     assert normwise_err(host(mat)[SUBSET], ref) < TOL
     if not bf16:
         assert worst_pair < 2 * TOL
