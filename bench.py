@@ -195,7 +195,7 @@ def run_m2(args, torch, rb, wl):
         "speedup_vs_rmw": round(rmw_s / replay_s, 3) if rmw_s else None,
         "roofline": {
             "bound": "hbm",
-            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},false> (replay-only steps)",
+            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kUniform> (steps that replay)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -206,7 +206,7 @@ def run_m2(args, torch, rb, wl):
             "launches": len(rep),
         },
         "fold_steps": {
-            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},true> (the step that fills the ring)",
+            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kMayFold> (the step that fills the ring)",
             "achieved_gbs": round(fol_bytes / fol_s / 1e9, 1) if fol else None,
             "alg_bytes_per_launch": round(fol_bytes / len(fol)) if fol else None,
             "avg_launch_us": round(1e6 * fol_s / len(fol), 2) if fol else None,

@@ -128,13 +128,14 @@ __device__ __forceinline__ void gram_dots(const float *sh_k, const float *sh_q, 
 // ------------------------------------------------------------------------------------------
 // replay (the token does not fill the ring)
 // ------------------------------------------------------------------------------------------
-template <int DV, int DK>
+template <int DV, int DK, int R>
 __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c, int head, int len,
-                                           float *smem)
+                                           const float4 (&s)[R], float *smem)
 {
     constexpr int TPB = TileShape<DV, DK>::TPB;
     using M = Map4<DV, DK>;
-    constexpr int R = M::R, LPR = M::LPR;
+    static_assert(R == M::R, "tile block");
+    constexpr int LPR = M::LPR;
     const int W = c.W, t = c.t, m = len + 1, W1 = W + 1;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
     float *sh_k = smem;                 // [m][DK]
@@ -148,24 +149,11 @@ __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c,
     float *sh_cv = sh_bc + W;           // [m] d_j beta_j c_j
     float *sh_g = sh_cv + W;            // [1] gamma
 
-    float4 s[R];
-    {
-        const size_t off = c.bh * (size_t)(DV * DK) + (size_t)(rg * R) * DK + c0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) s[r] = ld4_nt(a.S0 + off + (size_t)r * DK);
-    }
     const float *qt = a.q + c.bh * DK, *kt = a.k + c.bh * DK, *vt = a.v + c.bh * DV;
     const float bet = a.beta[c.bh], alt = a.alpha[c.bh];
     const int slot = (head + len) % W;
     stage_entries<DV, DK, TPB>(a.ring, c, head, len, true, kt, vt, bet, alt, sh_k, sh_v, sh_be, sh_al);
     for (int i = t; i < DK / 4; i += TPB) st4(sh_q + 4 * i, ld4(qt + 4 * i));
-    // append the token (its ring slot is not one of the entries being read)
-    for (int i = t; i < DK / 4; i += TPB) st4(a.ring.k + (c.rh + slot) * DK + 4 * i, ld4(kt + 4 * i));
-    for (int i = t; i < DV / 4; i += TPB) st4(a.ring.v + (c.rh + slot) * DV + 4 * i, ld4(vt + 4 * i));
-    if (t == 0) {
-        a.ring.beta[c.rh + slot] = bet;
-        a.ring.alpha[c.rh + slot] = alt;
-    }
     __syncthreads();
     gram_dots<DK, TPB>(sh_k, sh_q, m, W1, sh_G, sh_u, t);
     __syncthreads();
@@ -207,6 +195,14 @@ __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c,
         float acc = 0.f;
         for (int j = 0; j < m; ++j) acc += sh_cv[j] * sh_v[j * DV + i];
         a.o[c.bh * DV + i] = sh_g[0] * z + acc;
+    }
+    // Append the token as entry len (its slot is none of the entries read above); after the last
+    // barrier, so no barrier waits for these stores.
+    for (int i = t; i < DK / 4; i += TPB) st4(a.ring.k + (c.rh + slot) * DK + 4 * i, ld4(sh_k + len * DK + 4 * i));
+    for (int i = t; i < DV / 4; i += TPB) st4(a.ring.v + (c.rh + slot) * DV + 4 * i, ld4(sh_v + len * DV + 4 * i));
+    if (t == 0) {
+        a.ring.beta[c.rh + slot] = bet;
+        a.ring.alpha[c.rh + slot] = alt;
     }
 }
 
@@ -314,21 +310,16 @@ __device__ __forceinline__ void gdn_store(const float4 (&s)[R], float *dst, int 
     for (int r = 0; r < R; ++r) st4_nt(dst + off + (size_t)r * DK, s[r]);
 }
 
-template <int DV, int DK>
+template <int DV, int DK, int R>
 __device__ __forceinline__ void gdn_fold_decode(const GdnStepArgs &a, const GTile &c, int head,
-                                                int len, float *smem)
+                                                int len, float4 (&s)[R], float *smem)
 {
     using M = Map4<DV, DK>;
-    constexpr int R = M::R, LPR = M::LPR;
+    static_assert(R == M::R, "tile block");
+    constexpr int LPR = M::LPR;
     const int t = c.t;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
     float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
-    float4 s[R];
-    {
-        const size_t off = (size_t)(rg * R) * DK + c0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) s[r] = ld4_nt(S0 + off + (size_t)r * DK);
-    }
     const float *qt = a.q + c.bh * DK;
     const float4 qv = ld4(qt + c0);
     gdn_fold_core<DV, DK>(s, smem, a.ring, c, head, len, true, a.k + c.bh * DK, a.v + c.bh * DV,
@@ -345,14 +336,23 @@ __device__ __forceinline__ void gdn_fold_decode(const GdnStepArgs &a, const GTil
 template <int DV, int DK>
 __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_decode(GdnStepArgs a)
 {
+    using M = Map4<DV, DK>;
     extern __shared__ float smem[];
     const GTile c = make_gtile(a.d);
     const int B = a.d.B, W = c.W;
+    // the checkpoint tile first: both paths read it with the same map
+    float4 s[M::R];
+    {
+        const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
+        const size_t off = c.bh * (size_t)(DV * DK) + (size_t)(rg * M::R) * DK + c0;
+#pragma unroll
+        for (int r = 0; r < M::R; ++r) s[r] = ld4_nt(a.S0 + off + (size_t)r * DK);
+    }
     const int head = a.bk.in[c.b];
     const int len = a.bk.in[B + c.b];
     const bool fold = len + 1 >= W;
-    if (fold) gdn_fold_decode<DV, DK>(a, c, head, len, smem);
-    else gdn_replay<DV, DK>(a, c, head, len, smem);
+    if (fold) gdn_fold_decode<DV, DK>(a, c, head, len, s, smem);
+    else gdn_replay<DV, DK>(a, c, head, len, s, smem);
     if (c.h == 0 && c.t == 0) {
         a.bk.out[c.b] = fold ? (head + len + 1) % W : head;
         a.bk.out[B + c.b] = fold ? 0 : len + 1;

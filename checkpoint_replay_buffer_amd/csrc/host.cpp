@@ -28,6 +28,11 @@ struct rssm_ctx {
     // hi + 1 < W cannot fold any sequence and uses the replay-only kernel.
     int lo, hi;
     int pending_k;         // draft count of the pending verify
+    // Every sequence is at the same ring position (uhead, ulen), known exactly on the host: true
+    // from a full load until a masked load, a commit or a rollback (whose effect depends on
+    // device-resident arguments). Such decodes pass the position as a kernel argument.
+    bool uni;
+    int uhead, ulen;
 };
 
 namespace {
@@ -215,6 +220,8 @@ rssm_status rssm_init_checkpoint(rssm_ctx *ctx, const float *state, const int32_
         ctx->pending = false;
         ctx->lo = 0;
         if (!seq_mask) ctx->hi = 0;
+        ctx->uni = seq_mask == nullptr;
+        ctx->uhead = ctx->ulen = 0;
     }
     return s;
 }
@@ -230,14 +237,21 @@ rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, voi
     const bool mayfold = ctx->hi + 1 >= c.window;
     if (c.kind == RSSM_MAMBA2) {
         M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
-                     in->x, in->B, in->C, in->dt, y, 1};
-        s = launched(ctx, m2_decode(a, ctx->S0b != nullptr, mayfold, strm(stream)), true);
+                     in->x, in->B, in->C, in->dt, y, 1, ctx->uhead, ctx->ulen};
+        const int mode = (ctx->uni && ctx->ulen + 1 < c.window) ? 0 : (mayfold ? 2 : 1);
+        s = launched(ctx, m2_decode(a, ctx->S0b != nullptr, mode, strm(stream)), true);
     } else {
         GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
                       in->alpha, y};
         s = launched(ctx, gdn_decode(a, strm(stream)), true);
     }
     if (s == RSSM_OK) {
+        if (ctx->ulen + 1 >= c.window) {
+            ctx->uhead = (ctx->uhead + ctx->ulen + 1) % c.window;
+            ctx->ulen = 0;
+        } else {
+            ++ctx->ulen;
+        }
         if (!mayfold) {
             ++ctx->lo;
             ++ctx->hi;
@@ -264,7 +278,14 @@ rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream)
         GdnFoldArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, min_len, nullptr};
         s = launched(ctx, gdn_fold(a, strm(stream)), true);
     }
-    if (s == RSSM_OK) bounds_after_fold(ctx, min_len > 1 ? min_len : 1);
+    if (s == RSSM_OK) {
+        const int m = min_len > 1 ? min_len : 1;
+        bounds_after_fold(ctx, m);
+        if (ctx->ulen >= m) {
+            ctx->uhead = (ctx->uhead + ctx->ulen) % c.window;
+            ctx->ulen = 0;
+        }
+    }
     return s;
 }
 
@@ -285,6 +306,10 @@ rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *st
         ctx->pending = true;
         ctx->pending_k = in->ntok;
         bounds_after_fold(ctx, c.window - in->ntok + 1);   // sequences with len + K > W fold
+        if (ctx->ulen + in->ntok > c.window) {
+            ctx->uhead = (ctx->uhead + ctx->ulen) % c.window;
+            ctx->ulen = 0;
+        }
     }
     return s;
 }
@@ -298,6 +323,7 @@ rssm_status rssm_verify_commit(rssm_ctx *ctx, const int32_t *accepted, void *str
     if (s == RSSM_OK) {
         ctx->pending = false;
         ctx->hi = ctx->hi + ctx->pending_k < ctx->cfg.window ? ctx->hi + ctx->pending_k : ctx->cfg.window;
+        ctx->uni = false;
     }
     return s;
 }
@@ -311,6 +337,7 @@ rssm_status rssm_rollback(rssm_ctx *ctx, const int32_t *new_len, void *stream)
     if (s == RSSM_OK) {
         ctx->pending = false;
         ctx->lo = 0;
+        ctx->uni = false;
     }
     return s;
 }

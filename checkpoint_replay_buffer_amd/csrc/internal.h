@@ -39,6 +39,7 @@ struct M2StepArgs {
     const float *x, *Bm, *C, *dt;
     float *y;
     int ntok;
+    int uhead, ulen;    // ring position shared by every sequence (uniform decode mode only)
 };
 
 // Mamba-2 consolidation (write S0) or materialisation (write out).
@@ -103,8 +104,9 @@ struct GdnRmwArgs {
 
 // ---- launchers (return hipSuccess or the launch error) ----
 bool m2_supported(int P, int N);
-// mayfold = false promises that no sequence's ring fills in this step (len + 1 < W for all).
-hipError_t m2_decode(const M2StepArgs &a, bool bf16, bool mayfold, hipStream_t s);
+// Decode kernel choice. 0: every sequence is at ring position (a.uhead, a.ulen) and none fills
+// its ring; 1: no sequence fills its ring; 2: any sequence may fold.
+hipError_t m2_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s);
 hipError_t m2_verify(const M2StepArgs &a, bool bf16, hipStream_t s);
 hipError_t m2_fold(const M2FoldArgs &a, bool bf16, hipStream_t s);
 hipError_t m2_rmw(const M2RmwArgs &a, hipStream_t s);

@@ -234,31 +234,39 @@ __device__ __forceinline__ void load_fp32_tile(float4 (&acc)[R], const float *S0
 
 // ------------------------------------------------------------------------------------------
 // decode: replay path (the token does not fill the ring). One barrier per tile.
+//
+// Vector-load completions are waited for in issue order, so whatever is issued first can be
+// consumed while later loads are still in flight. With EARLY = false the small ring-side loads go
+// out first and the checkpoint read after them: the ring work (LDS staging, decay weights,
+// B_j . C) then overlaps the checkpoint stream. EARLY = true means the caller already issued the
+// checkpoint read (needed when the ring position must first be read from device memory).
 // ------------------------------------------------------------------------------------------
-template <int P, int N, bool BF16>
+template <int P, int N, bool BF16, bool EARLY>
 __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile &c, int head,
-                                                 int len, const ReadTile<P, N, BF16> &tile,
-                                                 float *smem)
+                                                 int len, ReadTile<P, N, BF16> &tile, float *smem)
 {
     constexpr int TPB = TileShape<P, N>::TPB;
     using RT = ReadTile<P, N, BF16>;
     constexpr int EPL = RT::EPL;
     using M = typename RT::M;
     constexpr int R = M::R, LPR = M::LPR, RG = M::RG;
-    const int W = c.W, t = c.t, m = len + 1, lane = t & 63;
+    constexpr int DUP = LPR / R;                          // lanes holding the same finished row
+    constexpr int PF = P / 4;
+    constexpr int XQ = (kMaxWindow * PF + TPB - 1) / TPB; // x-row float4 per thread, at most
+    const int W = c.W, t = c.t, m = len + 1;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * EPL;
     float *sh_x = smem;            // [m][P]   x of the entries
-    float *sh_s = sh_x + W * P;    // [m]      B_j . C
-    float *sh_w = sh_s + W;        // [m]      decay weights
+    float *sh_cf = sh_x + W * P;   // [m]      w_j (B_j . C)
     const float *xt = a.x + c.bh * P;
     const float *Bt = a.Bm + c.bg * N;
     const float dtt = a.dt[c.bh];
     const int slot = (head + len) % W;
 
-    // all global loads first: C columns, step sizes (one per lane), B rows of this row group's
-    // first two entries, x rows of every entry
+    // 1. ring-side loads: C columns, step sizes (one per lane), B rows of this row group's first
+    //    two entries, x rows of every entry
     float cc[EPL];
     load_cols<EPL>(cc, a.C + c.bg * N + c0);
+    const int lane = t & 63;
     const float dtl = lane < len ? a.ring.dt[c.rh + (head + lane) % W] : dtt;
     float4 bq[2][EPL / 4];
 #pragma unroll
@@ -269,21 +277,72 @@ __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile
         for (int e = 0; e < EPL / 4; ++e)
             bq[q][e] = j < m ? ld4(Bj + c0 + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    constexpr int PF = P / 4;
-    for (int i = t; i < m * PF; i += TPB) {
-        const int j = i / PF, q = (i - j * PF) * 4;
-        float4 v;
-        if (j < len) {
-            v = ld4(a.ring.x + (c.rh + (head + j) % W) * P + q);
-        } else {
-            v = ld4(xt + q);
-            st4(a.ring.x + (c.rh + slot) * P + q, v);      // append x
-        }
-        st4(sh_x + j * P + q, v);
+    float4 xs[XQ];
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = t + q * TPB, j = i / PF, o = (i - j * PF) * 4;
+        xs[q] = i < m * PF ? (j < len ? ld4(a.ring.x + (c.rh + (head + j) % W) * P + o) : ld4(xt + o))
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    // append B, C, dt of the token (its slot is not one of the entries being read)
+    // 2. the checkpoint read
+    if constexpr (!EARLY) tile.load(a, c);
+
+    // 3. ring work while the checkpoint streams in
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = t + q * TPB, j = i / PF, o = (i - j * PF) * 4;
+        if (i < m * PF) st4(sh_x + j * P + o, xs[q]);
+    }
+    float lam;
+    const float w = wave_weights(dtl, m, c.Ah, lam);     // w_j on lane j of every wave
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int j = rg + RG * q;
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL / 4; ++e)
+            part += bq[q][e].x * cc[4 * e] + bq[q][e].y * cc[4 * e + 1] + bq[q][e].z * cc[4 * e + 2]
+                  + bq[q][e].w * cc[4 * e + 3];
+        const float sj = group_sum<LPR>(part);
+        const float wj = __shfl(w, j);                   // all lanes active: j < 2 RG <= 32
+        if (cg == 0 && j < m) sh_cf[j] = wj * sj;
+    }
+    for (int q = 2; q * RG < m; ++q) {                   // rings longer than 2 RG (trip count is
+        const int j = rg + RG * q;                       // uniform, so every lane shuffles)
+        const float *Bj = j < len ? a.ring.B + (c.rg_ + (head + j) % W) * N : Bt;
+        float part = 0.f;
+        if (j < m) {
+#pragma unroll
+            for (int e = 0; e < EPL; e += 4) {
+                const float4 v = ld4(Bj + c0 + e);
+                part += v.x * cc[e] + v.y * cc[e + 1] + v.z * cc[e + 2] + v.w * cc[e + 3];
+            }
+        }
+        const float sj = group_sum<LPR>(part);
+        const float wj = __shfl(w, j & 63);
+        if (cg == 0 && j < m) sh_cf[j] = wj * sj;
+    }
+    __syncthreads();
+
+    // 4. z = S0 C; y = Lam z + sum_j w_j (B_j . C) x_j + D x, the sum split over the DUP lanes
+    //    that hold the same row
+    float part[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[r] = dot_row(tile.v[r], cc);
+    int rsel;
+    const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
+    const int p = rg * R + rsel, k = cg & (DUP - 1);
+    float corr = 0.f;
+    for (int j = k; j < m; j += DUP) corr += sh_cf[j] * sh_x[j * P + p];
+    corr = group_sum<DUP>(corr);
+    if (k == 0) a.y[c.bh * P + p] = lam * z + corr + c.Dh * sh_x[len * P + p];
+
+    // 5. Append the token as entry len. Its slot is none of the entries read above. The stores
+    //    come after the barrier: a workgroup barrier waits for the workgroup's outstanding
+    //    stores, so stores issued before it would put their latency on every tile.
+    for (int i = t; i < PF; i += TPB) st4(a.ring.x + (c.rh + slot) * P + 4 * i, ld4(sh_x + len * P + 4 * i));
     if (c.own_group) {
-        if (rg == len % RG) {        // the token's B row (already in cache from the load above)
+        if (rg == len % RG) {        // the token's B row (in cache from the loads above)
 #pragma unroll
             for (int e = 0; e < EPL / 4; ++e) st4(a.ring.B + (c.rg_ + slot) * N + c0 + 4 * e, ld4(Bt + c0 + 4 * e));
         }
@@ -294,48 +353,6 @@ __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile
         }
     }
     if (t == 0) a.ring.dt[c.rh + slot] = dtt;
-
-    // decay weights (every wave computes them; wave 0 publishes)
-    float lam;
-    const float w = wave_weights(dtl, m, c.Ah, lam);
-    if (t < m) sh_w[t] = w;
-    // B_j . C for the row group's entries
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int j = rg + RG * q;
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL / 4; ++e)
-            part += bq[q][e].x * cc[4 * e] + bq[q][e].y * cc[4 * e + 1] + bq[q][e].z * cc[4 * e + 2]
-                  + bq[q][e].w * cc[4 * e + 3];
-        const float s = group_sum<LPR>(part);
-        if (cg == 0 && j < m) sh_s[j] = s;
-    }
-    for (int j = rg + 2 * RG; j < m; j += RG) {          // rings longer than 2 RG
-        const float *Bj = j < len ? a.ring.B + (c.rg_ + (head + j) % W) * N : Bt;
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4) {
-            const float4 v = ld4(Bj + c0 + e);
-            part += v.x * cc[e] + v.y * cc[e + 1] + v.z * cc[e + 2] + v.w * cc[e + 3];
-        }
-        const float s = group_sum<LPR>(part);
-        if (cg == 0) sh_s[j] = s;
-    }
-    __syncthreads();
-
-    // z = S0 C, then y = Lam z + sum_j w_j (B_j . C) x_j + D x
-    float part[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) part[r] = dot_row(tile.v[r], cc);
-    int rsel;
-    const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
-    if (row_writer<R, LPR>(cg)) {
-        const int p = rg * R + rsel;
-        float corr = 0.f;
-        for (int j = 0; j < m; ++j) corr += sh_w[j] * sh_s[j] * sh_x[j * P + p];
-        a.y[c.bh * P + p] = lam * z + corr + c.Dh * sh_x[len * P + p];
-    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -367,10 +384,15 @@ __device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &
     }
 }
 
-// MAYFOLD = false: the host knows no sequence's ring fills in this step, so the checkpoint read
-// (fp32 or bf16) is issued before anything else. MAYFOLD = true: any mix of replaying and folding
-// sequences; the fp32 tile is still loaded first.
-template <int P, int N, bool BF16, bool MAYFOLD>
+// Decode kernel variants, chosen on the host from what it knows about the ring fill:
+//   kUniform  every sequence has the ring position (a.uhead, a.ulen) and none fills its ring:
+//             no device read is needed before the ring loads, which go out before the checkpoint
+//   kReplay   no sequence fills its ring; positions are read from the device, so the checkpoint
+//             read is issued first and the ring loads after the positions arrive
+//   kMayFold  any mix of replaying and folding sequences
+enum DecodeMode { kUniform = 0, kReplay = 1, kMayFold = 2 };
+
+template <int P, int N, bool BF16, int MODE>
 __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs a)
 {
     extern __shared__ float smem[];
@@ -378,12 +400,17 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs
     const int B = a.d.B, W = c.W;
     bool fold = false;
     int head, len;
-    if constexpr (!MAYFOLD) {
+    if constexpr (MODE == kUniform) {
+        ReadTile<P, N, BF16> tile;
+        head = a.uhead;
+        len = a.ulen;
+        m2_replay_decode<P, N, BF16, false>(a, c, head, len, tile, smem);
+    } else if constexpr (MODE == kReplay) {
         ReadTile<P, N, BF16> tile;
         tile.load(a, c);
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
-        m2_replay_decode<P, N, BF16>(a, c, head, len, tile, smem);
+        m2_replay_decode<P, N, BF16, true>(a, c, head, len, tile, smem);
     } else if constexpr (!BF16) {
         ReadTile<P, N, false> tile;
         tile.load(a, c);
@@ -391,7 +418,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs
         len = a.bk.in[B + c.b];
         fold = len + 1 >= W;
         if (fold) m2_fold_decode<P, N, false>(a, c, head, len, tile.v, smem);
-        else m2_replay_decode<P, N, false>(a, c, head, len, tile, smem);
+        else m2_replay_decode<P, N, false, true>(a, c, head, len, tile, smem);
     } else {
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
@@ -402,8 +429,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs
             m2_fold_decode<P, N, true>(a, c, head, len, acc, smem);
         } else {
             ReadTile<P, N, true> tile;
-            tile.load(a, c);
-            m2_replay_decode<P, N, true>(a, c, head, len, tile, smem);
+            m2_replay_decode<P, N, true, false>(a, c, head, len, tile, smem);
         }
     }
     if (c.h == 0 && c.t == 0) {
@@ -635,7 +661,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_rmw(M2RmwArgs a)
 template <int P, int N>
 size_t decode_lds(int W)
 {
-    const size_t replay = (size_t)W * P + 2 * W;
+    const size_t replay = (size_t)W * P + W;
     const size_t fold = fold_lds_floats(W, P, N);
     return 4 * (replay > fold ? replay : fold);
 }
@@ -649,14 +675,21 @@ size_t verify_lds(int W)
 }
 
 template <int P, int N>
-hipError_t go_decode(const M2StepArgs &a, bool bf16, bool mayfold, hipStream_t s)
+hipError_t go_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
     const size_t lds = decode_lds<P, N>(a.d.W);
-    if (bf16 && mayfold) hipLaunchKernelGGL((k_m2_decode<P, N, true, true>), grid, block, lds, s, a);
-    else if (bf16) hipLaunchKernelGGL((k_m2_decode<P, N, true, false>), grid, block, lds, s, a);
-    else if (mayfold) hipLaunchKernelGGL((k_m2_decode<P, N, false, true>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((k_m2_decode<P, N, false, false>), grid, block, lds, s, a);
+#define RSSM_GO(b, md) hipLaunchKernelGGL((k_m2_decode<P, N, b, md>), grid, block, lds, s, a)
+    if (bf16) {
+        if (mode == kUniform) RSSM_GO(true, kUniform);
+        else if (mode == kReplay) RSSM_GO(true, kReplay);
+        else RSSM_GO(true, kMayFold);
+    } else {
+        if (mode == kUniform) RSSM_GO(false, kUniform);
+        else if (mode == kReplay) RSSM_GO(false, kReplay);
+        else RSSM_GO(false, kMayFold);
+    }
+#undef RSSM_GO
     return hipGetLastError();
 }
 
@@ -701,9 +734,9 @@ bool m2_supported(int P, int N)
     return false;
 }
 
-hipError_t m2_decode(const M2StepArgs &a, bool bf16, bool mayfold, hipStream_t s)
+hipError_t m2_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s)
 {
-#define RSSM_C(p, n) if (a.d.P == p && a.d.N == n) return go_decode<p, n>(a, bf16, mayfold, s);
+#define RSSM_C(p, n) if (a.d.P == p && a.d.N == n) return go_decode<p, n>(a, bf16, mode, s);
     RSSM_M2_SHAPES(RSSM_C)
 #undef RSSM_C
     return hipErrorInvalidValue;
