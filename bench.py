@@ -218,6 +218,284 @@ def run_m2(args, torch, rb, wl):
     return line, (sh, prm)
 
 
+def m2_verify_bytes(P, N, W, gr, K, length, store_c=True) -> tuple[float, bool]:
+    """HBM bytes of one verify launch for one (b, h) pair with `length` committed entries, and
+    whether it folds them first (length + K > W)."""
+    f = 4
+    drafts = K * ((P + 1) * f + 2 * N * f * gr)
+    ring = length * ((P + 1) * f + N * f * gr)
+    outs = K * P * f
+    append = K * ((P + 1) * f + N * f * gr * (2 if store_c else 1))
+    fold = length + K > W
+    s0 = (2 if fold else 1) * P * N * f
+    return s0 + ring + drafts + outs + append, fold
+
+
+def run_m2_spec(args, torch, rb, wl):
+    """Speculative decoding: K = 6 drafts per round into the W = 16 ring, verify (outputs of all
+    drafts, checkpoint streamed once) then a pointer commit of the seeded accepted prefix, against
+    the conventional round (state read once, one snapshot written per draft, pointer commit)."""
+    sh = wl.M2_SPEC
+    P, N, W, H, B, K = sh.head_dim, sh.d_state, sh.window, sh.nheads, sh.batch, sh.max_draft
+    gr = sh.ngroups / sh.nheads
+    rounds, Wm, S = args.steps or 256, args.warmup, 4
+    t0 = time.time()
+    prm = wl.m2_params(sh, 0)
+    s0 = torch.from_numpy(wl.m2_state0(sh, 0)).cuda()
+    pool = []
+    for s in range(S):
+        ins = wl.m2_token_inputs(sh, 0, s, ntok=K)
+        pool.append({k: torch.from_numpy(v).cuda() for k, v in ins.items()})
+    acc_h = wl.spec_accepted(B, rounds + Wm, K, p=0.35, seed=0)
+    acc = torch.from_numpy(acc_h).cuda()
+    A = torch.from_numpy(prm["A"]).cuda()
+    D = torch.from_numpy(prm["D"]).cuda()
+    gen_s = time.time() - t0
+
+    ctx = rb.Context("mamba2", B, H, P, N, W, max_draft=K, store_c=True)
+    ctx.set_params(A, D)
+    yk = torch.empty(K, B, H, P, device="cuda")
+    ctx.init_checkpoint(s0)
+    for r in range(Wm):
+        ctx.verify(yk, **pool[r % S])
+        ctx.commit(acc[rounds + r])
+    ctx.init_checkpoint(s0)
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for r in range(rounds):
+        ctx.verify(yk, **pool[r % S])
+        ctx.commit(acc[r])
+    ev[1].record()
+    torch.cuda.synchronize()
+    replay_s = ev[0].elapsed_time(ev[1]) / 1e3
+    h, l, n, e = ctx.bookkeeping()
+    assert e == 0
+    # per-launch durations of the verify kernel (second pass)
+    ctx.init_checkpoint(s0)
+    torch.cuda.synchronize()
+    evl = _events(torch, 2 * rounds)
+    for r in range(rounds):
+        evl[2 * r].record()
+        ctx.verify(yk, **pool[r % S])
+        evl[2 * r + 1].record()
+        ctx.commit(acc[r])
+    torch.cuda.synchronize()
+    verify_ms = [evl[2 * r].elapsed_time(evl[2 * r + 1]) for r in range(rounds)]
+    del ctx
+
+    # exact algorithmic bytes from the ring lengths the rounds produce
+    L = np.zeros(B, dtype=np.int64)
+    vbytes, folds = 0.0, 0
+    for r in range(rounds):
+        per = [m2_verify_bytes(P, N, W, gr, int(x), K) for x in L]
+        vbytes += sum(p[0] for p in per) * H
+        fold = L + K > W
+        folds += int(fold.sum())
+        L = np.where(fold, 0, L) + acc_h[r]
+    cbytes = 3 * 4 * B * 2 * rounds + B * 4 * rounds          # commits
+    alg_bytes = vbytes + cbytes
+
+    # conventional comparator: snapshots into a 2K+1 slot pool, pointer commit
+    cfg = rb.make_config(rb.RSSM_MAMBA2, B, H, sh.ngroups, P, N, W, K)
+    spool = torch.empty((2 * K + 1, B, H, P, N), device="cuda")
+    slot_of = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def conv_round(r, a_row):
+        rb.step_baseline_spec(cfg, spool, slot_of, yk, A, D, **pool[r % S])
+        rb.rssm_baseline_commit(cfg, slot_of, a_row, K)
+
+    spool[2 * K].copy_(s0)
+    slot_of.fill_(2 * K)
+    for r in range(Wm):
+        conv_round(r, acc[rounds + r])
+    spool[2 * K].copy_(s0)
+    slot_of.fill_(2 * K)
+    torch.cuda.synchronize()
+    ev2 = _events(torch, 2)
+    ev2[0].record()
+    for r in range(rounds):
+        conv_round(r, acc[r])
+    ev2[1].record()
+    torch.cuda.synchronize()
+    conv_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+    del spool
+    conv_bytes = (P * N * 4 * (1 + K) + K * ((P + 1) * 4 + 2 * N * 4 * gr) + K * P * 4) * B * H * rounds
+
+    vk_s = sum(verify_ms) / 1e3
+    achieved = vbytes / vk_s / 1e9
+    accepted = int(acc_h[:rounds].sum())
+    return {
+        "metric": "speculative verify+commit state GB/s (% of HBM peak) + accepted tokens/s vs "
+                  "conventional per-draft snapshots, batch 512 K=6 W=16",
+        "value": round(alg_bytes / replay_s / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": rounds, "warmup": Wm,
+        "ms_per_step": round(replay_s * 1e3 / rounds, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded drafts; accepted ~ min(Geometric(0.35) failures, 6))",
+        "config": {"workload": f"mamba2_spec_b{B}_h{H}_p{P}_n{N}_w{W}_k{K}", "batch": B,
+                   "heads": H, "head_dim": P, "d_state": N, "window": W, "drafts": K,
+                   "rounds": rounds, "draft_pool_slots": S},
+        "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
+        "accepted_tokens_per_s": round(accepted / replay_s, 1),
+        "mean_accepted": round(accepted / (rounds * B), 3),
+        "fold_fraction": round(folds / (rounds * B), 4),
+        "conv_ms_per_round": round(conv_s * 1e3 / rounds, 5),
+        "conv_gbs": round(conv_bytes / conv_s / 1e9, 1),
+        "speedup_vs_conventional": round(conv_s / replay_s, 3),
+        "roofline": {"bound": "hbm", "kernel": "k_m2_verify<64,128,false>",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic("verify"),
+                     "alg_bytes_per_launch": round(vbytes / rounds),
+                     "avg_launch_us": round(1e6 * vk_s / rounds, 2), "launches": rounds},
+        "input_gen_s": round(gen_s, 1),
+    }, (sh, prm)
+
+
+def gdn_bytes(DV, DK, W, length) -> float:
+    f = 4
+    token = (2 * DK + DV + 2) * f
+    ring = length * (DK + DV + 2) * f
+    o = DV * f
+    if length + 1 >= W:
+        return 2 * DV * DK * f + token + ring + o
+    return DV * DK * f + token + ring + (DK + DV + 2) * f + o
+
+
+def run_gdn(args, torch, rb, wl):
+    """Gated DeltaNet decode: batch 256, 32 heads, d_k = d_v = 128, W = 16."""
+    sh = wl.GDN_SERVE
+    DV, DK, W, H, B = sh.d_v, sh.d_k, sh.window, sh.nheads, sh.batch
+    K, Wm, S = args.steps, args.warmup, 32
+    t0 = time.time()
+    s0 = torch.from_numpy(wl.gdn_state0(sh, 0)).cuda()
+    pool = []
+    for s in range(S):
+        ins = wl.gdn_token_inputs(sh, 0, s)
+        pool.append({k: torch.from_numpy(v[0]).cuda() for k, v in ins.items()})
+    gen_s = time.time() - t0
+    ctx = rb.Context("gdn", B, H, DV, DK, W)
+    o = torch.empty(B, H, DV, device="cuda")
+    ctx.init_checkpoint(s0)
+    for t in range(Wm):
+        ctx.decode_step(o, **pool[t % S])
+    ctx.init_checkpoint(s0)
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for t in range(K):
+        ctx.decode_step(o, **pool[t % S])
+    ev[1].record()
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[1])
+    ctx.init_checkpoint(s0)
+    torch.cuda.synchronize()
+    evl = _events(torch, 2 * K)
+    for t in range(K):
+        evl[2 * t].record()
+        ctx.decode_step(o, **pool[t % S])
+        evl[2 * t + 1].record()
+    torch.cuda.synchronize()
+    launch_ms = [evl[2 * t].elapsed_time(evl[2 * t + 1]) for t in range(K)]
+    alg = sum(gdn_bytes(DV, DK, W, t % W) for t in range(K)) * B * H
+    cfg = rb.make_config(rb.RSSM_GDN, B, H, H, DV, DK, W)
+    st = s0.clone()
+    o1 = torch.empty(1, B, H, DV, device="cuda")
+    for t in range(Wm):
+        rb.step_baseline(cfg, st, o1, **{k: v.unsqueeze(0) for k, v in pool[t % S].items()})
+    st.copy_(s0)
+    torch.cuda.synchronize()
+    ev2 = _events(torch, 2)
+    ev2[0].record()
+    for t in range(K):
+        rb.step_baseline(cfg, st, o1, **{k: v.unsqueeze(0) for k, v in pool[t % S].items()})
+    ev2[1].record()
+    torch.cuda.synchronize()
+    rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+    rmw_bytes = (2 * DV * DK * 4 + (2 * DK + DV + 2) * 4 + DV * 4) * B * H * K
+    rep = [t for t in range(K) if t % W != W - 1]
+    fol = [t for t in range(K) if t % W == W - 1]
+    rep_b = sum(gdn_bytes(DV, DK, W, t % W) for t in rep) * B * H
+    fol_b = sum(gdn_bytes(DV, DK, W, t % W) for t in fol) * B * H
+    rep_s = sum(launch_ms[t] for t in rep) / 1e3
+    fol_s = sum(launch_ms[t] for t in fol) / 1e3
+    replay_s = total_ms / 1e3
+    return {
+        "metric": "GDN decode state GB/s (% of HBM peak) + tokens/s vs conventional, batch 256 W=16",
+        "value": round(alg / replay_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(total_ms / K, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded; q, k L2-normalised N(0,1), v N(0,1), beta sigmoid, alpha exp(-softplus))",
+        "config": {"workload": f"gdn_decode_b{B}_h{H}_dk{DK}_dv{DV}_w{W}", "batch": B, "heads": H,
+                   "d_k": DK, "d_v": DV, "window": W, "input_pool_slots": S},
+        "pct_hbm_peak": round(100 * alg / replay_s / 1e9 / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(B * K / replay_s, 1),
+        "rmw_ms_per_step": round(rmw_s * 1e3 / K, 5),
+        "rmw_gbs": round(rmw_bytes / rmw_s / 1e9, 1),
+        "speedup_vs_rmw": round(rmw_s / replay_s, 3),
+        "roofline": {"bound": "hbm", "kernel": "k_gdn_decode<128,128> (steps that replay)",
+                     "achieved": round(rep_b / rep_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(rep_b / rep_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic("gdn_replay"),
+                     "alg_bytes_per_launch": round(rep_b / len(rep)),
+                     "avg_launch_us": round(1e6 * rep_s / len(rep), 2), "launches": len(rep)},
+        "fold_steps": {"achieved_gbs": round(fol_b / fol_s / 1e9, 1) if fol else None,
+                       "avg_launch_us": round(1e6 * fol_s / len(fol), 2) if fol else None,
+                       "launches": len(fol)},
+        "input_gen_s": round(gen_s, 1),
+    }, sh
+
+
+def cpu_baseline_gdn(sh, wl, budget_s=8.0):
+    import oracle
+    cores = oracle.set_threads(0)
+    state = wl.gdn_state0(sh, 0).astype(np.float64)
+    toks = [{k: np.ascontiguousarray(v[0]) for k, v in wl.gdn_token_inputs(sh, 0, s).items()}
+            for s in range(4)]
+    for _ in range(2):
+        t0 = time.perf_counter()
+        oracle.gdn_step(*(toks[0][k] for k in ("q", "k", "v", "beta", "alpha")), state)
+        one = time.perf_counter() - t0
+    steps = max(2, min(512, int(budget_s / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    for t in range(steps):
+        oracle.gdn_step(*(toks[t % 4][k] for k in ("q", "k", "v", "beta", "alpha")), state)
+    el = time.perf_counter() - t0
+    tok_s = sh.batch * steps / el
+    return {"value": round(2 * sh.d_v * sh.d_k * 8 * sh.nheads * tok_s / 1e9, 3),
+            "unit": "GB/s (fp64 state read+write)", "cores": cores, "kind": "oracle",
+            "tokens_per_s": round(tok_s, 1),
+            "sample": f"first {steps} decode steps of all {sh.batch} sequences, conventional fp64 "
+                      f"recurrence, {el:.1f} s"}
+
+
+def cpu_baseline_m2_spec(sh, prm, wl, budget_s=8.0):
+    import oracle
+    cores = oracle.set_threads(0)
+    nseq = 64
+    K = sh.max_draft
+    small = wl.M2Shape(nseq, sh.nheads, sh.ngroups, sh.head_dim, sh.d_state, sh.window, K)
+    state = wl.m2_state0(sh, 0)[:nseq].astype(np.float64)
+    drafts = [{k: np.ascontiguousarray(v[:, :nseq]) for k, v in wl.m2_token_inputs(sh, 0, s, ntok=K).items()}
+              for s in range(2)]
+    acc = wl.spec_accepted(sh.batch, 512, K, seed=0)[:, :nseq]
+    t0 = time.perf_counter()
+    oracle.m2_spec_round(prm["A"], prm["D"], drafts[0], state, acc[0])
+    one = time.perf_counter() - t0
+    rounds = max(2, min(256, int(budget_s / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    for r in range(rounds):
+        oracle.m2_spec_round(prm["A"], prm["D"], drafts[r % 2], state, acc[r])
+    el = time.perf_counter() - t0
+    del small
+    return {"value": round(int(acc[:rounds].sum()) / el, 1), "unit": "accepted tokens/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"first {rounds} rounds of sequences 0..{nseq - 1} (all heads), conventional fp64 "
+                      f"recurrence with a state copy per draft, {el:.1f} s"}
+
+
 def cpu_baseline_m2(sh, prm, wl, budget_s=12.0):
     """Time the CPU oracle (conventional fp64 recurrence) on the first steps of a subset of the
     same seeded schedule, sized to about `budget_s` of CPU time."""
@@ -261,9 +539,11 @@ def calibrate_copy(torch, nbytes=1 << 30, reps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (decode tokens; verify rounds for m2_spec); default 512 / 256")
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", default="m2_serve", choices=["m2_serve", "m2_serve_bf16"])
+    ap.add_argument("--workload", default="m2_serve",
+                    choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve"])
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rmw", action="store_true")
@@ -284,9 +564,20 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy(torch)
-    line, (sh, prm) = run_m2(args, torch, rb, wl)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_m2(sh, prm, wl)
+    if args.workload == "m2_spec":
+        line, (sh, prm) = run_m2_spec(args, torch, rb, wl)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_m2_spec(sh, prm, wl)
+    elif args.workload == "gdn_serve":
+        args.steps = args.steps or 512
+        line, sh = run_gdn(args, torch, rb, wl)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_gdn(sh, wl)
+    else:
+        args.steps = args.steps or 512
+        line, (sh, prm) = run_m2(args, torch, rb, wl)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_m2(sh, prm, wl)
     print(json.dumps(line), flush=True)
 
 

@@ -28,8 +28,8 @@ RSSM_F_STORE_C = 2
 
 EXPORTS = ("rssm_workspace_bytes", "rssm_create", "rssm_destroy", "rssm_set_params",
            "rssm_init_checkpoint", "rssm_decode_step", "rssm_consolidate", "rssm_verify",
-           "rssm_verify_commit", "rssm_rollback", "rssm_step_baseline", "rssm_materialize",
-           "rssm_read_bookkeeping", "rssm_status_str")
+           "rssm_verify_commit", "rssm_rollback", "rssm_step_baseline", "rssm_step_baseline_spec",
+           "rssm_baseline_commit", "rssm_materialize", "rssm_read_bookkeeping", "rssm_status_str")
 
 
 class RssmError(RuntimeError):
@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "rssm_verify_commit": (I32, [P, P, P]),
         "rssm_rollback": (I32, [P, P, P]),
         "rssm_step_baseline": (I32, [cfgp, P, inp, P, P, P, P, P]),
+        "rssm_step_baseline_spec": (I32, [cfgp, P, P, inp, P, P, P, P]),
+        "rssm_baseline_commit": (I32, [cfgp, P, P, I32, P]),
         "rssm_materialize": (I32, [P, P, P]),
         "rssm_read_bookkeeping": (I32, [P, P, P, P, ctypes.POINTER(U32), P]),
         "rssm_status_str": (ctypes.c_char_p, [I32]),
@@ -184,6 +186,20 @@ def rssm_step_baseline(cfg: rssm_config, state, inputs: rssm_inputs, A, D, y, sn
                                            _stream(stream)))
 
 
+def rssm_step_baseline_spec(cfg: rssm_config, pool, slot_of, inputs: rssm_inputs, A, D, y,
+                            stream=None) -> None:
+    _chk("rssm_step_baseline_spec",
+         load_library().rssm_step_baseline_spec(ctypes.byref(cfg), _ptr(pool), _ptr(slot_of),
+                                                ctypes.byref(inputs), _ptr(A), _ptr(D), _ptr(y),
+                                                _stream(stream)))
+
+
+def rssm_baseline_commit(cfg: rssm_config, slot_of, accepted, ndraft: int, stream=None) -> None:
+    _chk("rssm_baseline_commit",
+         load_library().rssm_baseline_commit(ctypes.byref(cfg), _ptr(slot_of), _ptr(accepted),
+                                             int(ndraft), _stream(stream)))
+
+
 def rssm_materialize(ctx: int, state_out, stream=None) -> None:
     _chk("rssm_materialize", load_library().rssm_materialize(ctx, _ptr(state_out), _stream(stream)))
 
@@ -278,6 +294,13 @@ class Context:
             self.close()
         except Exception:
             pass
+
+
+def step_baseline_spec(cfg: rssm_config, pool, slot_of, y, A, D, stream=None, **kw):
+    """Conventional speculative round over the drafts in kw (leading token axis K): snapshots into
+    the slot pool [2K+1, B, H, P, N] from each sequence's committed slot."""
+    ntok = next(iter(kw.values())).shape[0]
+    rssm_step_baseline_spec(cfg, pool, slot_of, make_inputs(ntok, **kw), A, D, y, stream)
 
 
 def step_baseline(cfg: rssm_config, state, y, A=None, D=None, snapshots=None, stream=None, **kw):

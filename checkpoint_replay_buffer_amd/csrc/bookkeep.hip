@@ -66,6 +66,16 @@ __global__ void __launch_bounds__(256) k_rollback(Bk bk, const int32_t *new_len,
     if (!ok) atomicOr(err, kRollbackRange);
 }
 
+// Conventional speculative comparator: point each sequence at the snapshot taken after its
+// accepted drafts (slot (slot_of < K ? K : 0) + accepted - 1); nothing is copied.
+__global__ void __launch_bounds__(256) k_slot_commit(int32_t *slot_of, const int32_t *accepted, int B, int K)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int acc = accepted[b], sl = slot_of[b];
+    if (acc >= 1 && acc <= K) slot_of[b] = (sl < K ? K : 0) + acc - 1;
+}
+
 __global__ void k_clear(uint32_t *w) { *w = 0u; }
 
 }  // namespace
@@ -87,6 +97,12 @@ hipError_t bk_commit(Bk bk, const int32_t *accepted, uint32_t *err, int B, hipSt
 hipError_t bk_rollback(Bk bk, const int32_t *new_len, uint32_t *err, int B, hipStream_t s)
 {
     hipLaunchKernelGGL(k_rollback, dim3((B + 255) / 256), dim3(256), 0, s, bk, new_len, err, B);
+    return hipGetLastError();
+}
+
+hipError_t slot_commit(int32_t *slot_of, const int32_t *accepted, int B, int K, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_slot_commit, dim3((B + 255) / 256), dim3(256), 0, s, slot_of, accepted, B, K);
     return hipGetLastError();
 }
 

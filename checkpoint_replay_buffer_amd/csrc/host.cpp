@@ -352,12 +352,36 @@ rssm_status rssm_step_baseline(const rssm_config *cfg, float *state, const rssm_
     if (!aligned16(state) || !aligned16(y) || (snapshots && !aligned16(snapshots))) return RSSM_E_ARG;
     if (cfg->kind == RSSM_MAMBA2) {
         if (!A || !D) return RSSM_E_ARG;
-        M2RmwArgs a{m2dims(*cfg), state, snapshots, A, D, in->x, in->B, in->C, in->dt, y, in->ntok};
+        M2RmwArgs a{m2dims(*cfg), state, snapshots, A, D, in->x, in->B, in->C, in->dt, y, in->ntok,
+                    nullptr};
         return m2_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
     }
     GdnRmwArgs a{gdndims(*cfg), state, snapshots, in->q, in->k, in->v, in->beta, in->alpha, y,
                  in->ntok};
     return gdn_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+}
+
+rssm_status rssm_step_baseline_spec(const rssm_config *cfg, float *pool, const int32_t *slot_of,
+                                    const rssm_inputs *in, const float *A, const float *D, float *y,
+                                    void *stream)
+{
+    rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    if (cfg->kind != RSSM_MAMBA2) return RSSM_E_UNSUPPORTED;
+    if ((s = check_inputs(*cfg, in)) != RSSM_OK) return s;
+    if (!aligned16(pool) || !aligned16(y) || !slot_of || !A || !D) return RSSM_E_ARG;
+    M2RmwArgs a{m2dims(*cfg), pool, nullptr, A, D, in->x, in->B, in->C, in->dt, y, in->ntok, slot_of};
+    return m2_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+}
+
+rssm_status rssm_baseline_commit(const rssm_config *cfg, int32_t *slot_of, const int32_t *accepted,
+                                 int32_t ndraft, void *stream)
+{
+    const rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    if (!slot_of || !accepted || ndraft < 1) return RSSM_E_ARG;
+    return slot_commit(slot_of, accepted, cfg->batch, ndraft, strm(stream)) == hipSuccess
+               ? RSSM_OK : RSSM_E_DEVICE;
 }
 
 rssm_status rssm_materialize(rssm_ctx *ctx, float *state_out, void *stream)

@@ -56,12 +56,13 @@ struct M2FoldArgs {
 
 struct M2RmwArgs {
     M2Dims d;
-    float *state;
-    float *snap;        // nullptr = in place
+    float *state;       // [B,H,P,N]; with slot_of: the slot pool [2 ntok + 1][B,H,P,N]
+    float *snap;        // nullptr = in place (ignored with slot_of)
     const float *A, *D;
     const float *x, *Bm, *C, *dt;
     float *y;
     int ntok;
+    const int32_t *slot_of;   // [B] committed slot per sequence, or nullptr
 };
 
 struct GdnRing {
@@ -121,6 +122,7 @@ hipError_t init_checkpoint(float *S0, uint16_t *S0b, const float *state, const i
                            Bk bk, uint32_t *err, int B, int H, long tile_elems, hipStream_t s);
 hipError_t bk_commit(Bk bk, const int32_t *accepted, uint32_t *err, int B, hipStream_t s);
 hipError_t bk_rollback(Bk bk, const int32_t *new_len, uint32_t *err, int B, hipStream_t s);
+hipError_t slot_commit(int32_t *slot_of, const int32_t *accepted, int B, int K, hipStream_t s);
 hipError_t clear_word(uint32_t *w, hipStream_t s);
 
 }  // namespace rssm

@@ -616,11 +616,22 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_rmw(M2RmwArgs a)
     const Tile c = make_tile(a.d, a.A, a.D);
     const int t = c.t;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
-    const size_t BH = (size_t)a.d.B * a.d.H, BG = (size_t)a.d.B * a.d.G;
-    const size_t off = c.bh * (size_t)(P * N) + (size_t)(rg * R) * N + c0;
+    const size_t BH = (size_t)a.d.B * a.d.H, BG = (size_t)a.d.B * a.d.G, PN = (size_t)P * N;
+    const size_t off = (size_t)(rg * R) * N + c0;       // lane block within a tile
+    // source tile and the first snapshot tile (snapshot k is k * BH tiles further)
+    const float *src;
+    float *snap0;
+    if (a.slot_of) {
+        const int sl = a.slot_of[c.b];
+        src = a.state + ((size_t)sl * BH + c.bh) * PN;
+        snap0 = a.state + ((size_t)(sl < a.ntok ? a.ntok : 0) * BH + c.bh) * PN;
+    } else {
+        src = a.state + c.bh * PN;
+        snap0 = a.snap ? a.snap + c.bh * PN : nullptr;
+    }
     float4 S[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) S[r] = ld4_nt(a.state + off + (size_t)r * N);
+    for (int r = 0; r < R; ++r) S[r] = ld4_nt(src + off + (size_t)r * N);
     for (int k = 0; k < a.ntok; ++k) {
         const float dtv = a.dt[k * BH + c.bh];
         const float dec = expf(dtv * c.Ah);
@@ -644,14 +655,14 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_rmw(M2RmwArgs a)
             const int p = rg * R + rsel;
             a.y[(k * BH + c.bh) * P + p] = z + c.Dh * xk[p];
         }
-        if (a.snap) {
+        if (snap0) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) st4_nt(a.snap + k * BH * (size_t)(P * N) + off + (size_t)r * N, S[r]);
+            for (int r = 0; r < R; ++r) st4_nt(snap0 + k * BH * PN + off + (size_t)r * N, S[r]);
         }
     }
-    if (!a.snap) {
+    if (!snap0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) st4_nt(a.state + off + (size_t)r * N, S[r]);
+        for (int r = 0; r < R; ++r) st4_nt(a.state + c.bh * PN + off + (size_t)r * N, S[r]);
     }
 }
 

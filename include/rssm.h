@@ -164,6 +164,25 @@ rssm_status rssm_step_baseline(const rssm_config *cfg, float *state, const rssm_
                                const float *A, const float *D, float *y, float *snapshots,
                                void *stream);
 
+/* Conventional speculative round, the comparator for rssm_verify + rssm_verify_commit (Mamba-2).
+ * Done conventionally, a rollback needs a copy of the state after every step (news.hamidun.com
+ * item "NVIDIA présente ReplaySSM...", section "D'où vient le problème de l'état"); this keeps
+ * one snapshot per draft and commits by pointer. `pool` holds 2K+1 state slots
+ * [2K+1][B,H,dim_v,dim_k] (K = in->ntok); slot_of[b] ([B] int32, device, values 0..2K) names the
+ * slot with sequence b's committed state. Each sequence runs the K drafts from that state and
+ * writes the state after draft k to slot o_b + k, o_b = K if slot_of[b] < K else 0 (the half
+ * that does not hold its committed state), and y [K,B,H,dim_v] receives every draft's output.
+ * Slot values outside 0..2K are undefined behaviour (the caller owns slot_of). */
+rssm_status rssm_step_baseline_spec(const rssm_config *cfg, float *pool, const int32_t *slot_of,
+                                    const rssm_inputs *in, const float *A, const float *D,
+                                    float *y, void *stream);
+
+/* Commit of the conventional comparator: for every b with 1 <= accepted[b] <= ndraft, point
+ * slot_of[b] at the snapshot after accepted[b] drafts (o_b + accepted[b] - 1, o_b as above);
+ * 0 keeps the committed state. No state is copied. accepted [B] int32, device. */
+rssm_status rssm_baseline_commit(const rssm_config *cfg, int32_t *slot_of, const int32_t *accepted,
+                                 int32_t ndraft, void *stream);
+
 /* Write the current state of every sequence (S0 with its committed entries folded in) to
  * state_out [B,H,dim_v,dim_k] without changing the context. */
 rssm_status rssm_materialize(rssm_ctx *ctx, float *state_out, void *stream);

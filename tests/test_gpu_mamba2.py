@@ -454,3 +454,31 @@ def test_speculative_serving_shape_sampled():
         worst = max(worst, normwise_err(host(yk)[:, sub], y_ref))
     say(f"  spec worst normwise {worst:.3e}")
     assert worst < TOL
+
+
+def test_snapshot_comparator_rounds():
+    """The conventional speculative comparator: per-draft snapshots in a slot pool, commit by
+    pointing each sequence at its accepted snapshot; outputs and committed states against the
+    oracle's recomputation from the accepted prefix."""
+    sh = wl.M2Shape(batch=5, nheads=2, ngroups=2, head_dim=16, d_state=16, window=8, max_draft=3)
+    K = 3
+    prm = wl.m2_params(sh, 11)
+    s0 = wl.m2_state0(sh, 11)
+    cfg = rb.make_config(rb.RSSM_MAMBA2, sh.batch, sh.nheads, sh.ngroups, 16, 16, sh.window, K)
+    A, D = dev(prm["A"]), dev(prm["D"])
+    pool = torch.zeros((2 * K + 1,) + s0.shape, device="cuda")
+    pool[2 * K] = dev(s0)
+    slot_of = torch.full((sh.batch,), 2 * K, dtype=torch.int32, device="cuda")
+    acc = wl.spec_accepted(sh.batch, 12, K, seed=11)
+    ref = s0.astype(np.float64).copy()
+    yk = torch.empty(K, sh.batch, sh.nheads, 16, device="cuda")
+    for r in range(12):
+        ins = wl.m2_token_inputs(sh, 11, r, ntok=K)
+        rb.step_baseline_spec(cfg, pool, slot_of, yk, A, D, **m2_dev_tokens(sh, ins, K))
+        rb.rssm_baseline_commit(cfg, slot_of, dev(acc[r]), K)
+        y_ref = m2_spec_round(prm["A"], prm["D"], ins, ref, acc[r])
+        assert normwise_err(host(yk), y_ref) < TOL, r
+        sl = host(slot_of)
+        st = host(pool)
+        committed = np.stack([st[sl[b], b] for b in range(sh.batch)])
+        assert normwise_err(committed, ref) < TOL, r
