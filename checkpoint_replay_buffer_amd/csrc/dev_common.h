@@ -34,46 +34,86 @@ using Map4 = RowMap<P, N, TileShape<P, N>::TPB, 4>;
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
-// Sum over the LANES consecutive lanes of an aligned lane group (xor butterfly).
-template <int LANES>
+// Value of the butterfly partner at distance X (a power of two <= 16) within aligned groups of 2X
+// lanes. Distances 1 and 2 are xor partners (DPP quad permutes); 4 and 8 use the DPP mirrors
+// inside 8- and 16-lane rows (lane i <-> 7 - i, 15 - i), whose partner differs from i in bit
+// log2(X) and in the bits below it; 16 is an xor swizzle within 32-lane groups. For the sums
+// and reduce-scatters below this is as good as a plain xor: each step merges two disjoint lane
+// sets that agree on every bit above X, and the steps together reach all lanes of the group.
+// Every lane of the group must be active. DPP = false uses plain shuffles through the LDS
+// crossbar instead, which is faster where the VALU is the busier unit (the read-modify-write
+// comparators, measured).
+template <int X, bool DPP = true>
+__device__ __forceinline__ float bfly(float v)
+{
+    const int i = __float_as_int(v);
+    int r;
+    if constexpr (!DPP) r = __shfl_xor(i, X);
+    else if constexpr (X == 1) r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true);       // [1,0,3,2]
+    else if constexpr (X == 2) r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+    else if constexpr (X == 4) r = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, true); // half-row mirror
+    else if constexpr (X == 8) r = __builtin_amdgcn_mov_dpp(i, 0x140, 0xF, 0xF, true); // row mirror
+    else if constexpr (X == 16) r = __builtin_amdgcn_ds_swizzle(i, 0x401F);            // xor 16
+    else r = __shfl_xor(i, X);
+    return __int_as_float(r);
+}
+
+// Sum over the LANES consecutive lanes of an aligned lane group (butterfly).
+template <int LANES, bool DPP = true>
 __device__ __forceinline__ float group_sum(float s)
 {
-#pragma unroll
-    for (int st = 0; st < ilog2(LANES); ++st) s += __shfl_xor(s, LANES >> (st + 1));
+    if constexpr (LANES >= 32) s += bfly<16, DPP>(s);
+    if constexpr (LANES >= 16) s += bfly<8, DPP>(s);
+    if constexpr (LANES >= 8) s += bfly<4, DPP>(s);
+    if constexpr (LANES >= 4) s += bfly<2, DPP>(s);
+    if constexpr (LANES >= 2) s += bfly<1, DPP>(s);
+    static_assert(LANES <= 32, "lane groups up to 32");
     return s;
+}
+
+// One halving step of the reduce-scatter below: a lane holding C row partials keeps half of them
+// (the upper half when bit X of its column index is set) and adds the partner's values for that
+// half. Recurses down to one row per lane.
+template <int C, int X, int R, bool DPP>
+__device__ __forceinline__ void rs_halve(float (&v)[R], int cg, int &base)
+{
+    if constexpr (C > 1) {
+        const bool up = (cg & X) != 0;
+#pragma unroll
+        for (int i = 0; i < C / 2; ++i) {
+            // The empty asm makes lo / hi opaque register values, so the lane-dependent choice
+            // below stays a select instead of becoming a dynamic index into v (which would push
+            // the array to scratch memory).
+            float lo = v[i], hi = v[i + C / 2];
+            asm volatile("" : "+v"(lo), "+v"(hi));
+            const float send = up ? lo : hi;
+            const float keep = up ? hi : lo;
+            v[i] = keep + bfly<X, DPP>(send);
+        }
+        base += up ? C / 2 : 0;
+        rs_halve<C / 2, X / 2, R, DPP>(v, cg, base);
+    }
+}
+
+template <int X, bool DPP>
+__device__ __forceinline__ float sum_down(float s)
+{
+    if constexpr (X >= 1) return sum_down<X / 2, DPP>(s + bfly<X, DPP>(s));
+    else return s;
 }
 
 // Row sums of an R-row partial-dot block spread over LPR lanes: a reduce-scatter butterfly.
 // Each of the first log2(R) exchange steps halves the number of rows a lane keeps; the rest are
 // plain sums. On return every lane holds the full sum of row `rsel` (an index in 0..R-1), and
 // the LPR/R lanes with equal (cg & ~(LPR/R - 1)) hold the same row.
-template <int R, int LPR>
+template <int R, int LPR, bool DPP = true>
 __device__ __forceinline__ float row_reduce_scatter(float (&v)[R], int cg, int &rsel)
 {
+    static_assert(LPR <= 32 && R <= LPR, "row map");
     int base = 0;
-#pragma unroll
-    for (int st = 0; st < ilog2(R); ++st) {
-        const int c = R >> st;            // rows still held
-        const int X = LPR >> (st + 1);    // partner distance
-        const bool up = (cg & X) != 0;
-#pragma unroll
-        for (int i = 0; i < c / 2; ++i) {
-            // The empty asm makes lo / hi opaque register values, so the lane-dependent choice
-            // below stays a select instead of becoming a dynamic index into v (which would push
-            // the array to scratch memory).
-            float lo = v[i], hi = v[i + c / 2];
-            asm volatile("" : "+v"(lo), "+v"(hi));
-            const float send = up ? lo : hi;
-            const float keep = up ? hi : lo;
-            v[i] = keep + __shfl_xor(send, X);
-        }
-        base += up ? c / 2 : 0;
-    }
-    float s = v[0];
-#pragma unroll
-    for (int st = ilog2(R); st < ilog2(LPR); ++st) s += __shfl_xor(s, LPR >> (st + 1));
+    rs_halve<R, LPR / 2, R, DPP>(v, cg, base);
     rsel = base;
-    return s;
+    return sum_down<LPR / (2 * R), DPP>(v[0]);
 }
 
 // The one lane of each duplicate set that writes the row result.

@@ -126,80 +126,138 @@ __device__ __forceinline__ void gram_dots(const float *sh_k, const float *sh_q, 
 }
 
 // ------------------------------------------------------------------------------------------
-// replay (the token does not fill the ring)
+// replay (the token does not fill the ring). Two barriers per tile.
 // ------------------------------------------------------------------------------------------
-template <int DV, int DK, int R>
+
+// Exclusive suffix products across the lanes of a wave: lane l < n gets prod_{l<i<n} a_i (lane i
+// holds a_i); `all` receives prod_{i<n} a_i on every lane. Every lane of the wave takes part.
+__device__ __forceinline__ float wave_suffix_prod(float al, int n, float &all)
+{
+    const int lane = threadIdx.x & 63;
+    const float v = lane < n ? al : 1.f;
+    float e = __shfl_down(v, 1);
+    if (lane == 63) e = 1.f;
+    for (int off = 1; off < n; off <<= 1) {
+        const float o = __shfl_down(e, off);
+        if (lane + off < 64) e *= o;
+    }
+    all = __shfl(v * e, 0);
+    return e;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// LOAD = true: the checkpoint tile s is read here, after the ring loads went out (the ring position
+// is known without a device read); LOAD = false: the caller already issued it.
+template <int DV, int DK, int R, bool LOAD>
 __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c, int head, int len,
-                                           const float4 (&s)[R], float *smem)
+                                           float4 (&s)[R], float *smem)
 {
     constexpr int TPB = TileShape<DV, DK>::TPB;
     using M = Map4<DV, DK>;
     static_assert(R == M::R, "tile block");
-    constexpr int LPR = M::LPR;
-    const int W = c.W, t = c.t, m = len + 1, W1 = W + 1;
+    constexpr int LPR = M::LPR, DUP = LPR / R;
+    constexpr int KF = DK / 4, VF = DV / 4;
+    constexpr int XQ = (16 * (KF + VF) + TPB - 1) / TPB;   // float4 staged in registers (W <= 16)
+    const int W = c.W, t = c.t, m = len + 1, W1 = W + 1, lane = t & 63;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
     float *sh_k = smem;                 // [m][DK]
     float *sh_v = sh_k + W * DK;        // [m][DV]
     float *sh_q = sh_v + W * DV;        // [DK]
-    float *sh_G = sh_q + DK;            // [m][W1]
-    float *sh_u = sh_G + W * W1;        // [m] k_j . q
-    float *sh_be = sh_u + W;            // [m]
-    float *sh_al = sh_be + W;           // [m]
-    float *sh_bc = sh_al + W;           // [m] beta_j c_j
-    float *sh_cv = sh_bc + W;           // [m] d_j beta_j c_j
-    float *sh_g = sh_cv + W;            // [1] gamma
+    float *sh_G = sh_q + DK;            // [m][W1]  k_l . k_i, l < i
+    float *sh_u = sh_G + W * W1;        // [m]      k_j . q
 
     const float *qt = a.q + c.bh * DK, *kt = a.k + c.bh * DK, *vt = a.v + c.bh * DV;
     const float bet = a.beta[c.bh], alt = a.alpha[c.bh];
     const int slot = (head + len) % W;
-    stage_entries<DV, DK, TPB>(a.ring, c, head, len, true, kt, vt, bet, alt, sh_k, sh_v, sh_be, sh_al);
-    for (int i = t; i < DK / 4; i += TPB) st4(sh_q + 4 * i, ld4(qt + 4 * i));
+    // ring-side loads: beta / alpha of entry `lane` (every wave), k and v rows of all entries
+    const float bel = lane < len ? a.ring.beta[c.rh + (head + lane) % W] : bet;
+    const float all = lane < len ? a.ring.alpha[c.rh + (head + lane) % W] : alt;
+    float4 xs[XQ];
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = t + q * TPB;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < m * KF) {
+            const int j = i / KF, o = (i - j * KF) * 4;
+            v = j < len ? ld4(a.ring.k + (c.rh + (head + j) % W) * DK + o) : ld4(kt + o);
+        } else if (i < m * (KF + VF)) {
+            const int i2 = i - m * KF, j = i2 / VF, o = (i2 - j * VF) * 4;
+            v = j < len ? ld4(a.ring.v + (c.rh + (head + j) % W) * DV + o) : ld4(vt + o);
+        }
+        xs[q] = v;
+    }
+    const float4 qv = ld4(qt + c0);
+    if constexpr (LOAD) {
+        const size_t off = c.bh * (size_t)(DV * DK) + (size_t)(rg * R) * DK + c0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[r] = ld4_nt(a.S0 + off + (size_t)r * DK);
+    }
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = t + q * TPB;
+        if (i < m * KF) {
+            const int j = i / KF, o = (i - j * KF) * 4;
+            st4(sh_k + j * DK + o, xs[q]);
+        } else if (i < m * (KF + VF)) {
+            const int i2 = i - m * KF, j = i2 / VF, o = (i2 - j * VF) * 4;
+            st4(sh_v + j * DV + o, xs[q]);
+        }
+    }
+    for (int i = t + XQ * TPB; i < m * (KF + VF); i += TPB) {   // longer rings
+        if (i < m * KF) {
+            const int j = i / KF, o = (i - j * KF) * 4;
+            st4(sh_k + j * DK + o, j < len ? ld4(a.ring.k + (c.rh + (head + j) % W) * DK + o) : ld4(kt + o));
+        } else {
+            const int i2 = i - m * KF, j = i2 / VF, o = (i2 - j * VF) * 4;
+            st4(sh_v + j * DV + o, j < len ? ld4(a.ring.v + (c.rh + (head + j) % W) * DV + o) : ld4(vt + o));
+        }
+    }
+    if (rg == 0) st4(sh_q + c0, qv);
     __syncthreads();
     gram_dots<DK, TPB>(sh_k, sh_q, m, W1, sh_G, sh_u, t);
     __syncthreads();
-    // back substitution for c_j (one wave, lane j holds entry j)
-    if (t < 64) {
-        float val = t < m ? sh_u[t] : 0.f;
-        for (int i = m - 1; i >= 0; --i) {
-            const float ci = __shfl(val, i);
-            if (t < i) val -= sh_be[i] * sh_G[t * W1 + i] * ci;
-        }
-        if (t < m) {
-            float d = 1.f;
-            for (int i = t + 1; i < m; ++i) d *= sh_al[i];
-            const float bc = sh_be[t] * val;
-            sh_bc[t] = bc;
-            sh_cv[t] = d * bc;
-        }
-        if (t == 0) {
-            float g = 1.f;
-            for (int i = 0; i < m; ++i) g *= sh_al[i];
-            sh_g[0] = g;
-        }
+
+    // c_j by back substitution, in every wave (lane j ends with c_j): c_j = u_j - sum_{i>j}
+    // beta_i G[j][i] c_i. The broadcast of c_i is a readlane, so the loop carries one FMA.
+    float val = lane < m ? sh_u[lane] : 0.f;
+    for (int i = m - 1; i >= 0; --i) {
+        const float ci = lane_value(val, i) * lane_value(bel, i);
+        if (lane < i) val -= sh_G[lane * W1 + i] * ci;
     }
-    __syncthreads();
+    float gam;
+    const float d = wave_suffix_prod(all, m, gam);        // prod_{i>j} alpha_i on lane j
+    const float bc = bel * val;                           // beta_j c_j
+    const float cv = d * bc;
+
     // r = q - sum_j beta_j c_j k_j on the lane's columns, then S0 r
-    float4 rv = ld4(sh_q + c0);
+    float4 rv = qv;
     for (int j = 0; j < m; ++j) {
-        const float bc = sh_bc[j];
+        const float b = lane_value(bc, j);
         const float4 kj = ld4(sh_k + j * DK + c0);
-        rv.x -= bc * kj.x; rv.y -= bc * kj.y; rv.z -= bc * kj.z; rv.w -= bc * kj.w;
+        rv.x -= b * kj.x; rv.y -= b * kj.y; rv.z -= b * kj.z; rv.w -= b * kj.w;
     }
     float part[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) part[r] = s[r].x * rv.x + s[r].y * rv.y + s[r].z * rv.z + s[r].w * rv.w;
     int rsel;
     const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
-    if (row_writer<R, LPR>(cg)) {
-        const int i = rg * R + rsel;
-        float acc = 0.f;
-        for (int j = 0; j < m; ++j) acc += sh_cv[j] * sh_v[j * DV + i];
-        a.o[c.bh * DV + i] = sh_g[0] * z + acc;
+    const int row = rg * R + rsel, k = cg & (DUP - 1);
+    float acc = 0.f;
+    for (int j = 0; j < m; ++j) {                         // split over the DUP lanes of the row
+        const float w = lane_value(cv, j);
+        if ((j & (DUP - 1)) == k) acc += w * sh_v[j * DV + row];
     }
+    acc = group_sum<DUP>(acc);
+    if (k == 0) a.o[c.bh * DV + row] = gam * z + acc;
+
     // Append the token as entry len (its slot is none of the entries read above); after the last
     // barrier, so no barrier waits for these stores.
-    for (int i = t; i < DK / 4; i += TPB) st4(a.ring.k + (c.rh + slot) * DK + 4 * i, ld4(sh_k + len * DK + 4 * i));
-    for (int i = t; i < DV / 4; i += TPB) st4(a.ring.v + (c.rh + slot) * DV + 4 * i, ld4(sh_v + len * DV + 4 * i));
+    for (int i = t; i < KF; i += TPB) st4(a.ring.k + (c.rh + slot) * DK + 4 * i, ld4(sh_k + len * DK + 4 * i));
+    for (int i = t; i < VF; i += TPB) st4(a.ring.v + (c.rh + slot) * DV + 4 * i, ld4(sh_v + len * DV + 4 * i));
     if (t == 0) {
         a.ring.beta[c.rh + slot] = bet;
         a.ring.alpha[c.rh + slot] = alt;
@@ -333,26 +391,36 @@ __device__ __forceinline__ void gdn_fold_decode(const GdnStepArgs &a, const GTil
     if (row_writer<R, LPR>(cg)) a.o[c.bh * DV + rg * R + rsel] = z;
 }
 
-template <int DV, int DK>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_decode(GdnStepArgs a)
+// Decode variants, chosen on the host as for Mamba-2: 0 = every sequence at the ring position
+// (a.uhead, a.ulen) with no fold (ring loads before the checkpoint read), 1 = no sequence folds
+// (positions read from the device), 2 = any sequence may fold.
+template <int DV, int DK, int MODE>
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB))
+k_gdn_decode(GdnStepArgs a)
 {
     using M = Map4<DV, DK>;
     extern __shared__ float smem[];
     const GTile c = make_gtile(a.d);
     const int B = a.d.B, W = c.W;
-    // the checkpoint tile first: both paths read it with the same map
     float4 s[M::R];
-    {
+    int head, len;
+    bool fold = false;
+    if constexpr (MODE == 0) {
+        head = a.uhead;
+        len = a.ulen;
+        gdn_replay<DV, DK, M::R, true>(a, c, head, len, s, smem);
+    } else {
+        // the checkpoint tile first: both paths read it with the same map
         const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
         const size_t off = c.bh * (size_t)(DV * DK) + (size_t)(rg * M::R) * DK + c0;
 #pragma unroll
         for (int r = 0; r < M::R; ++r) s[r] = ld4_nt(a.S0 + off + (size_t)r * DK);
+        head = a.bk.in[c.b];
+        len = a.bk.in[B + c.b];
+        if constexpr (MODE == 2) fold = len + 1 >= W;
+        if (fold) gdn_fold_decode<DV, DK>(a, c, head, len, s, smem);
+        else gdn_replay<DV, DK, M::R, false>(a, c, head, len, s, smem);
     }
-    const int head = a.bk.in[c.b];
-    const int len = a.bk.in[B + c.b];
-    const bool fold = len + 1 >= W;
-    if (fold) gdn_fold_decode<DV, DK>(a, c, head, len, s, smem);
-    else gdn_replay<DV, DK>(a, c, head, len, s, smem);
     if (c.h == 0 && c.t == 0) {
         a.bk.out[c.b] = fold ? (head + len + 1) % W : head;
         a.bk.out[B + c.b] = fold ? 0 : len + 1;
@@ -419,7 +487,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
 #pragma unroll
         for (int r = 0; r < R; ++r) part[r] = S[r].x * kv.x + S[r].y * kv.y + S[r].z * kv.z + S[r].w * kv.w;
         int rsel;
-        const float sk = row_reduce_scatter<R, LPR>(part, cg, rsel);
+        const float sk = row_reduce_scatter<R, LPR, false>(part, cg, rsel);
         if (row_writer<R, LPR>(cg)) sh_sk[rg * R + rsel] = sk;
         __syncthreads();
 #pragma unroll
@@ -432,7 +500,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
             part[r] = S[r].x * qv.x + S[r].y * qv.y + S[r].z * qv.z + S[r].w * qv.w;
         }
         __syncthreads();
-        const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
+        const float z = row_reduce_scatter<R, LPR, false>(part, cg, rsel);
         if (row_writer<R, LPR>(cg)) a.o[tk * DV + rg * R + rsel] = z;
         if (a.snap) {
 #pragma unroll
@@ -449,17 +517,19 @@ template <int DV, int DK>
 size_t gdn_decode_lds(int W)
 {
     const size_t W1 = W + 1;
-    const size_t replay = (size_t)W * (DK + DV) + DK + W * W1 + 5 * W + 4;
+    const size_t replay = (size_t)W * (DK + DV) + DK + W * W1 + W;
     const size_t fold = gdn_fold_lds<DV, DK>(W);
     return 4 * (replay > fold ? replay : fold);
 }
 
 template <int DV, int DK>
-hipError_t go_decode(const GdnStepArgs &a, hipStream_t s)
+hipError_t go_decode(const GdnStepArgs &a, int mode, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(TileShape<DV, DK>::TPB);
     const size_t lds = gdn_decode_lds<DV, DK>(a.d.W);
-    hipLaunchKernelGGL((k_gdn_decode<DV, DK>), grid, block, lds, s, a);
+    if (mode == 0) hipLaunchKernelGGL((k_gdn_decode<DV, DK, 0>), grid, block, lds, s, a);
+    else if (mode == 1) hipLaunchKernelGGL((k_gdn_decode<DV, DK, 1>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_gdn_decode<DV, DK, 2>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
@@ -501,9 +571,9 @@ size_t gdn_lds_bytes(int DV, int DK, int W)
     return 0;
 }
 
-hipError_t gdn_decode(const GdnStepArgs &a, hipStream_t s)
+hipError_t gdn_decode(const GdnStepArgs &a, int mode, hipStream_t s)
 {
-#define RSSM_C(v, k) if (a.d.DV == v && a.d.DK == k) return go_decode<v, k>(a, s);
+#define RSSM_C(v, k) if (a.d.DV == v && a.d.DK == k) return go_decode<v, k>(a, mode, s);
     RSSM_GDN_SHAPES(RSSM_C)
 #undef RSSM_C
     return hipErrorInvalidValue;

@@ -242,8 +242,9 @@ rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, voi
         s = launched(ctx, m2_decode(a, ctx->S0b != nullptr, mode, strm(stream)), true);
     } else {
         GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
-                      in->alpha, y};
-        s = launched(ctx, gdn_decode(a, strm(stream)), true);
+                      in->alpha, y, ctx->uhead, ctx->ulen};
+        const int mode = (ctx->uni && ctx->ulen + 1 < c.window) ? 0 : (mayfold ? 2 : 1);
+        s = launched(ctx, gdn_decode(a, mode, strm(stream)), true);
     }
     if (s == RSSM_OK) {
         if (ctx->ulen + 1 >= c.window) {

@@ -83,6 +83,7 @@ struct GdnStepArgs {
     GdnRing ring;
     const float *q, *k, *v, *beta, *alpha;
     float *o;
+    int uhead, ulen;    // ring position shared by every sequence (mode 0 only)
 };
 
 struct GdnFoldArgs {
@@ -114,7 +115,7 @@ hipError_t m2_rmw(const M2RmwArgs &a, hipStream_t s);
 
 bool gdn_supported(int DV, int DK);
 size_t gdn_lds_bytes(int DV, int DK, int W);
-hipError_t gdn_decode(const GdnStepArgs &a, hipStream_t s);
+hipError_t gdn_decode(const GdnStepArgs &a, int mode, hipStream_t s);   // mode as m2_decode
 hipError_t gdn_fold(const GdnFoldArgs &a, hipStream_t s);
 hipError_t gdn_rmw(const GdnRmwArgs &a, hipStream_t s);
 

@@ -650,7 +650,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_rmw(M2RmwArgs a)
             part[r] = dot_row(S[r], cc);
         }
         int rsel;
-        const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
+        const float z = row_reduce_scatter<R, LPR, false>(part, cg, rsel);
         if (row_writer<R, LPR>(cg)) {
             const int p = rg * R + rsel;
             a.y[(k * BH + c.bh) * P + p] = z + c.Dh * xk[p];
