@@ -65,9 +65,8 @@ rssm_status check_config(const rssm_config *c)
         if (gdn_lds_bytes(c->dim_v, c->dim_k, c->window) > 65536) return RSSM_E_UNSUPPORTED;
     } else {
         if (!m2_supported(c->dim_v, c->dim_k)) return RSSM_E_UNSUPPORTED;
-        // the fold stages W+1 entries of x and B in LDS: keep it within 64 KiB per workgroup
-        const long lds = 4L * ((c->window + 1L) * (c->dim_v + c->dim_k) + 2L * (c->window + 2));
-        if (lds > 65536) return RSSM_E_UNSUPPORTED;
+        // ring entries staged in LDS by the fold and verify kernels: within 64 KiB per workgroup
+        if (m2_lds_bytes(c->dim_v, c->dim_k, c->window) > 65536) return RSSM_E_UNSUPPORTED;
     }
     return RSSM_OK;
 }

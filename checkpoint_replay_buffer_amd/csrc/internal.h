@@ -110,6 +110,7 @@ bool m2_supported(int P, int N);
 // its ring; 1: no sequence fills its ring; 2: any sequence may fold.
 hipError_t m2_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s);
 hipError_t m2_verify(const M2StepArgs &a, bool bf16, hipStream_t s);
+size_t m2_lds_bytes(int P, int N, int W);   // dynamic LDS of the largest Mamba-2 kernel
 hipError_t m2_fold(const M2FoldArgs &a, bool bf16, hipStream_t s);
 hipError_t m2_rmw(const M2RmwArgs &a, hipStream_t s);
 

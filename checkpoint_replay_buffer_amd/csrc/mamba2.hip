@@ -21,22 +21,6 @@
 namespace rssm {
 namespace {
 
-// weight of entry j among m entries with step sizes sdt[0..m-1]: dt_j exp(A sum_{i>j} dt_i)
-__device__ __forceinline__ float m2_weight(const float *sdt, int j, int m, float A)
-{
-    float s = 0.f;
-    for (int i = j + 1; i < m; ++i) s += sdt[i];
-    return sdt[j] * expf(A * s);
-}
-
-// decay of the whole window of m entries: exp(A sum_i dt_i)
-__device__ __forceinline__ float m2_window_decay(const float *sdt, int m, float A)
-{
-    float s = 0.f;
-    for (int i = 0; i < m; ++i) s += sdt[i];
-    return expf(A * s);
-}
-
 __device__ __forceinline__ float dot_row(const float4 &v, const float *cc)
 {
     return v.x * cc[0] + v.y * cc[1] + v.z * cc[2] + v.w * cc[3];
@@ -479,69 +463,132 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_fold(M2FoldArgs a
 
 // ------------------------------------------------------------------------------------------
 // speculative verify: K drafts, outputs only, S0 streamed once
+//
+// The drafts become entries len_e .. len_e + K - 1 after the ring's len_e committed entries.
+// Draft k sees the m_k = len_e + k + 1 entries up to and including itself (causal), so
+//     y_k = Lam_{m_k} (S0 C_k) + sum_{j < m_k} w_{j,m_k} (B_j . C_k) x_j + D x_{len_e+k}.
+// As in the replay decode, the ring and draft rows are loaded first and staged in LDS, and the
+// checkpoint read is issued after them, so the decay weights, the B_j . C_k dots and the
+// per-draft coefficients are computed while the checkpoint streams in. Two barriers per tile.
 // ------------------------------------------------------------------------------------------
-template <int P, int N, int EPL, typename RawT>
-__device__ __forceinline__ void m2_verify_outputs(const M2StepArgs &a, const Tile &c, const RawT *raw,
-                                  int head_e, int len_e, float *smem)
+
+// LDS floats of the verify outputs: x [W][P], B [W][N], C [W][N] (K <= W drafts), the weights
+// and coefficients [W][W] each, the window decays [W].
+__host__ __device__ constexpr int verify_lds_floats(int W, int P, int N)
+{
+    return W * (P + 2 * N) + 2 * W * W + W;
+}
+
+// LOADED = true: the tile already holds the checkpoint (folded just before); otherwise it is read
+// here after the ring and draft loads went out.
+template <int P, int N, bool BF16, bool LOADED>
+__device__ __forceinline__ void m2_verify_outputs(const M2StepArgs &a, const Tile &c, int head_e,
+                                                  int len_e, ReadTile<P, N, BF16> &tile, float *smem)
 {
     constexpr int TPB = TileShape<P, N>::TPB;
-    using M = RowMap<P, N, TPB, EPL>;
+    using RT = ReadTile<P, N, BF16>;
+    constexpr int EPL = RT::EPL;
+    using M = typename RT::M;
     constexpr int R = M::R, LPR = M::LPR;
-    const int W = c.W, t = c.t, K = a.ntok;
+    constexpr int DUP = LPR / R;
+    constexpr int PF = P / 4, NF = N / 4;
+    constexpr int XQ = (kMaxWindow * PF + TPB - 1) / TPB;
+    constexpr int BQ = (kMaxWindow * NF + TPB - 1) / TPB;
+    const int W = c.W, t = c.t, K = a.ntok, ne = len_e + K;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * EPL;
     const size_t BH = (size_t)a.d.B * a.d.H, BG = (size_t)a.d.B * a.d.G;
-    const int ne = len_e + K;
-    float *sh_x = smem;            // [ne][P]
-    float *sh_B = sh_x + W * P;    // [ne][N]
-    float *sh_dt = sh_B + W * N;   // [ne]
-    float *sh_cf = sh_dt + W;      // [ne]
-    float *sh_lam = sh_cf + W;
+    float *sh_x = smem;                // [ne][P]
+    float *sh_B = sh_x + W * P;        // [ne][N]
+    float *sh_C = sh_B + W * N;        // [K][N]
+    float *sh_w = sh_C + W * N;        // [K][W]  w_{j, m_k}
+    float *sh_cf = sh_w + W * W;       // [K][W]  w_{j, m_k} (B_j . C_k)
+    float *sh_lam = sh_cf + W * W;     // [K]     Lam_{m_k}
 
-    for (int j = t; j < ne; j += TPB)
-        sh_dt[j] = j < len_e ? a.ring.dt[c.rh + (head_e + j) % W] : a.dt[(j - len_e) * BH + c.bh];
-    constexpr int PF = P / 4, NF = N / 4;
-    for (int i = t; i < ne * PF; i += TPB) {
-        const int j = i / PF, q = (i - j * PF) * 4;
-        const float4 v = j < len_e ? ld4(a.ring.x + (c.rh + (head_e + j) % W) * P + q)
-                                   : ld4(a.x + ((j - len_e) * BH + c.bh) * P + q);
-        st4(sh_x + j * P + q, v);
+    // 1. ring and draft rows, step sizes (entry j on lane j of every wave), then the checkpoint
+    const int lane = t & 63;
+    const float dtl = lane < len_e ? a.ring.dt[c.rh + (head_e + lane) % W]
+                                   : (lane < ne ? a.dt[(lane - len_e) * BH + c.bh] : 0.f);
+    float4 xs[XQ], bs[BQ], cs[BQ];
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = t + q * TPB, j = i / PF, o = (i - j * PF) * 4;
+        xs[q] = i >= ne * PF ? make_float4(0.f, 0.f, 0.f, 0.f)
+              : (j < len_e ? ld4(a.ring.x + (c.rh + (head_e + j) % W) * P + o)
+                           : ld4(a.x + ((j - len_e) * BH + c.bh) * P + o));
     }
-    for (int i = t; i < ne * NF; i += TPB) {
-        const int j = i / NF, q = (i - j * NF) * 4;
-        const float4 v = j < len_e ? ld4(a.ring.B + (c.rg_ + (head_e + j) % W) * N + q)
-                                   : ld4(a.Bm + ((j - len_e) * BG + c.bg) * N + q);
-        st4(sh_B + j * N + q, v);
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) {
+        const int i = t + q * TPB, j = i / NF, o = (i - j * NF) * 4;
+        bs[q] = i >= ne * NF ? make_float4(0.f, 0.f, 0.f, 0.f)
+              : (j < len_e ? ld4(a.ring.B + (c.rg_ + (head_e + j) % W) * N + o)
+                           : ld4(a.Bm + ((j - len_e) * BG + c.bg) * N + o));
+        cs[q] = i < K * NF ? ld4(a.C + (j * BG + c.bg) * N + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if constexpr (!LOADED) tile.load(a, c);
+
+    // 2. staging and decay weights while the checkpoint is in flight
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = t + q * TPB;
+        if (i < ne * PF) st4(sh_x + 4 * i, xs[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) {
+        const int i = t + q * TPB;
+        if (i < ne * NF) st4(sh_B + 4 * i, bs[q]);
+        if (i < K * NF) st4(sh_C + 4 * i, cs[q]);
+    }
+    constexpr int NW = TPB / 64;
+    for (int k = t / 64; k < K; k += NW) {               // one wave per draft
+        const int mk = len_e + k + 1;
+        float lam;
+        const float w = wave_weights(dtl, mk, c.Ah, lam);
+        if (lane < mk) sh_w[k * W + lane] = w;
+        if (lane == 0) sh_lam[k] = lam;
     }
     __syncthreads();
 
+    // 3. coefficients w_{j, m_k} (B_j . C_k), j < m_k: one dot per lane group
+    {
+        constexpr int LPD = NF < 16 ? NF : 16;           // lanes per dot
+        constexpr int EPD = N / LPD;                     // floats per lane, a multiple of 4
+        const int grp = t / LPD, gl = t - grp * LPD;
+        for (int d = grp; d < K * ne; d += TPB / LPD) {
+            const int k = d / ne, j = d - k * ne;
+            if (j <= len_e + k) {                        // uniform over the lane group
+                const float *bj = sh_B + j * N + gl * EPD, *ck = sh_C + k * N + gl * EPD;
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPD; e += 4) {
+                    const float4 u = ld4(bj + e), v = ld4(ck + e);
+                    s += u.x * v.x + u.y * v.y + u.z * v.z + u.w * v.w;
+                }
+                s = group_sum<LPD>(s);
+                if (gl == 0) sh_cf[k * W + j] = sh_w[k * W + j] * s;
+            }
+        }
+    }
+    __syncthreads();
+
+    // 4. per draft: z = S0 C_k (row reduce-scatter), the buffer sum split over the DUP lanes that
+    //    hold the same row
+    const int kd = cg & (DUP - 1);
     for (int k = 0; k < K; ++k) {
-        const int mk = len_e + k + 1;
         float cc[EPL];
-        load_cols<EPL>(cc, a.C + (k * BG + c.bg) * N + c0);
+        load_cols<EPL>(cc, sh_C + k * N + c0);
         float part[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) part[r] = dot_row(raw[r], cc);
+        for (int r = 0; r < R; ++r) part[r] = dot_row(tile.v[r], cc);
         int rsel;
         const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
-        for (int j = rg; j < mk; j += M::RG) {
-            float pp = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) pp += sh_B[j * N + c0 + e] * cc[e];
-            const float s = group_sum<LPR>(pp);
-            if (cg == 0) sh_cf[j] = m2_weight(sh_dt, j, mk, c.Ah) * s;
-        }
-        if (t == TPB - 1) sh_lam[0] = m2_window_decay(sh_dt, mk, c.Ah);
-        __syncthreads();
-        if (row_writer<R, LPR>(cg)) {
-            const int p = rg * R + rsel;
-            float corr = 0.f;
-            for (int j = 0; j < mk; ++j) corr += sh_cf[j] * sh_x[j * P + p];
-            a.y[(k * BH + c.bh) * P + p] = sh_lam[0] * z + corr + c.Dh * sh_x[(len_e + k) * P + p];
-        }
-        __syncthreads();
+        const int p = rg * R + rsel, mk = len_e + k + 1;
+        float corr = 0.f;
+        for (int j = kd; j < mk; j += DUP) corr += sh_cf[k * W + j] * sh_x[j * P + p];
+        corr = group_sum<DUP>(corr);
+        if (kd == 0) a.y[(k * BH + c.bh) * P + p] = sh_lam[k] * z + corr + c.Dh * sh_x[(len_e + k) * P + p];
     }
 
-    // append the drafts as entries len_e .. len_e + K - 1 (every ring read is done)
+    // 5. append the drafts as entries len_e .. len_e + K - 1 (every ring read is done)
     for (int i = t; i < K * PF; i += TPB) {
         const int k = i / PF, q = (i - k * PF) * 4;
         st4(a.ring.x + (c.rh + (head_e + len_e + k) % W) * P + q, ld4(sh_x + (len_e + k) * P + q));
@@ -551,16 +598,15 @@ __device__ __forceinline__ void m2_verify_outputs(const M2StepArgs &a, const Til
             const int k = i / NF, q = (i - k * NF) * 4;
             const size_t row = (c.rg_ + (head_e + len_e + k) % W) * N + q;
             st4(a.ring.B + row, ld4(sh_B + (len_e + k) * N + q));
-            if (a.ring.C) st4(a.ring.C + row, ld4(a.C + (k * BG + c.bg) * N + q));
+            if (a.ring.C) st4(a.ring.C + row, ld4(sh_C + k * N + q));
         }
     }
-    for (int k = t; k < K; k += TPB) a.ring.dt[c.rh + (head_e + len_e + k) % W] = sh_dt[len_e + k];
+    for (int k = t; k < K; k += TPB) a.ring.dt[c.rh + (head_e + len_e + k) % W] = a.dt[k * BH + c.bh];
 }
 
 template <int P, int N, bool BF16>
 __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_verify(M2StepArgs a)
 {
-    constexpr int TPB = TileShape<P, N>::TPB;
     extern __shared__ float smem[];
     const Tile c = make_tile(a.d, a.A, a.D);
     const int B = a.d.B, W = c.W, K = a.ntok;
@@ -569,33 +615,18 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_verify(M2StepArgs
     const bool prefold = len + K > W;
     const int head_e = prefold ? (head + len) % W : head;
     const int len_e = prefold ? 0 : len;
-    const size_t off0 = c.bh * (size_t)(P * N);
-    if (prefold || !BF16) {
-        using M = RowMap<P, N, TPB, 4>;
-        const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
-        float4 acc[M::R];
-        const size_t off = off0 + (size_t)(rg * M::R) * N + c0;
-#pragma unroll
-        for (int r = 0; r < M::R; ++r) acc[r] = ld4_nt(a.S0 + off + (size_t)r * N);
-        if (prefold) {
-            m2_fold_core<P, N>(acc, smem, a.ring, c, head, len, nullptr, nullptr, 0.f);
-            store_tile<P, N>(acc, a.S0 + off0, BF16 ? a.S0b + off0 : nullptr, c.t);
-            __syncthreads();
-        }
-        m2_verify_outputs<P, N, 4>(a, c, acc, head_e, len_e, smem);
+    if (prefold) {
+        // fold the committed entries first; the drafts then read the folded fp32 tile
+        ReadTile<P, N, false> tile;
+        load_fp32_tile<P, N>(tile.v, a.S0, c);
+        m2_fold_core<P, N>(tile.v, smem, a.ring, c, head, len, nullptr, nullptr, 0.f);
+        const size_t off0 = c.bh * (size_t)(P * N);
+        store_tile<P, N>(tile.v, a.S0 + off0, BF16 ? a.S0b + off0 : nullptr, c.t);
+        __syncthreads();
+        m2_verify_outputs<P, N, false, true>(a, c, head_e, len_e, tile, smem);
     } else {
-        constexpr int EPL = Bf16Epl<P, N>::value;
-        using M = RowMap<P, N, TPB, EPL>;
-        using RawT = typename RawBf16<EPL>::type;
-        const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * EPL;
-        RawT raw[M::R];
-        const size_t off = off0 + (size_t)(rg * M::R) * N + c0;
-#pragma unroll
-        for (int r = 0; r < M::R; ++r) {
-            if constexpr (EPL == 8) raw[r] = ldu4_nt(a.S0b + off + (size_t)r * N);
-            else raw[r] = ldu2_nt(a.S0b + off + (size_t)r * N);
-        }
-        m2_verify_outputs<P, N, EPL>(a, c, raw, head_e, len_e, smem);
+        ReadTile<P, N, BF16> tile;
+        m2_verify_outputs<P, N, BF16, false>(a, c, head_e, len_e, tile, smem);
     }
     if (c.h == 0 && c.t == 0) {
         a.bk.out[c.b] = head_e;
@@ -680,7 +711,7 @@ size_t decode_lds(int W)
 template <int P, int N>
 size_t verify_lds(int W)
 {
-    const size_t out = (size_t)W * (P + N) + 2 * W + 4;
+    const size_t out = verify_lds_floats(W, P, N);
     const size_t fold = fold_lds_floats(W, P, N);
     return 4 * (out > fold ? out : fold);
 }
@@ -743,6 +774,14 @@ bool m2_supported(int P, int N)
     RSSM_M2_SHAPES(RSSM_CASE)
 #undef RSSM_CASE
     return false;
+}
+
+size_t m2_lds_bytes(int P, int N, int W)
+{
+    // the largest of the decode, verify and fold layouts (every kernel's is at most this)
+    const size_t v = verify_lds_floats(W, P, N), f = fold_lds_floats(W, P, N), d = (size_t)W * P + W;
+    const size_t m = v > f ? v : f;
+    return 4 * (m > d ? m : d);
 }
 
 hipError_t m2_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s)
