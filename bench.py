@@ -65,22 +65,22 @@ def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def _src_hash() -> str:
+def _src_hash(files) -> str:
     h = hashlib.sha256()
-    for p in (KERNEL_SRC, os.path.join(os.path.dirname(KERNEL_SRC), "dev_common.h")):
-        h.update(open(p, "rb").read())
+    for f in files:
+        h.update(open(os.path.join(os.path.dirname(KERNEL_SRC), f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def _traffic(kernel_key: str):
     """HBM bytes per launch measured with rocprofv3 counters for this kernel, if the counters were
-    taken on the current kernel source; else None."""
+    taken on the current kernel source (the hash of the files it was built from); else None."""
     try:
         t = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
         return None
     e = t.get(kernel_key)
-    if not e or e.get("src_hash") != _src_hash():
+    if not e or e.get("src_hash") != _src_hash(e.get("files", ())):
         return None
     return e.get("bytes_per_launch")
 
@@ -208,6 +208,7 @@ def run_m2(args, torch, rb, wl):
         "fold_steps": {
             "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kMayFold> (the step that fills the ring)",
             "achieved_gbs": round(fol_bytes / fol_s / 1e9, 1) if fol else None,
+            "traffic": _traffic("decode_fold_bf16" if bf16 else "decode_fold"),
             "alg_bytes_per_launch": round(fol_bytes / len(fol)) if fol else None,
             "avg_launch_us": round(1e6 * fol_s / len(fol), 2) if fol else None,
             "launches": len(fol),
@@ -435,13 +436,16 @@ def run_gdn(args, torch, rb, wl):
         "rmw_ms_per_step": round(rmw_s * 1e3 / K, 5),
         "rmw_gbs": round(rmw_bytes / rmw_s / 1e9, 1),
         "speedup_vs_rmw": round(rmw_s / replay_s, 3),
-        "roofline": {"bound": "hbm", "kernel": "k_gdn_decode<128,128> (steps that replay)",
+        "roofline": {"bound": "hbm", "kernel": "k_gdn_decode<128,128,kUniform> (steps that replay)",
                      "achieved": round(rep_b / rep_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(rep_b / rep_s / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("gdn_replay"),
                      "alg_bytes_per_launch": round(rep_b / len(rep)),
                      "avg_launch_us": round(1e6 * rep_s / len(rep), 2), "launches": len(rep)},
-        "fold_steps": {"achieved_gbs": round(fol_b / fol_s / 1e9, 1) if fol else None,
+        "fold_steps": {"kernel": "k_gdn_decode<128,128,kMayFold> (the step that fills the ring)",
+                       "achieved_gbs": round(fol_b / fol_s / 1e9, 1) if fol else None,
+                       "traffic": _traffic("gdn_fold"),
+                       "alg_bytes_per_launch": round(fol_b / len(fol)) if fol else None,
                        "avg_launch_us": round(1e6 * fol_s / len(fol), 2) if fol else None,
                        "launches": len(fol)},
         "input_gen_s": round(gen_s, 1),
