@@ -13,11 +13,13 @@
 // The Gram entries and k_j . q are independent dot products; the solve is m steps of one wave.
 // The checkpoint is read once (S0 r) and never written.
 //
-// Fold (WY form of the product of the rank-1 corrections), with gamma_t = prod_{i<=t} alpha_i:
-//     y_t = beta_t (k_t - sum_{i<t} (k_i . k_t) y_i)
-//     u_t = beta_t (v_t - sum_{i<t} (gamma_t / gamma_i) (k_i . k_t) u_i)
-//     S0 <- gamma S0 + sum_t ((gamma / gamma_t) u_t - gamma S0 y_t) k_t^T.
-// Both recurrences run down columns independently; S0 y_t uses the row reduce-scatter.
+// Fold (WY form of the product of the rank-1 corrections). With G_it = k_i . k_t, the n x n
+// lower-triangular T of the substitution y_t = beta_t (k_t - sum_{i<t} G_it y_i), i.e. y = T K,
+// and d_q = prod_{i>q} alpha_i, gamma = prod_i alpha_i, the second recurrence
+// u_t = beta_t (v_t - sum_{i<t} (gamma_t / gamma_i) G_it u_i) becomes the same substitution on
+// the rows d_q v_q once u_t is scaled by d_t, so the folded state is
+//     S0 <- gamma S0 + C^T K,     C = T Z,     Z_q = d_q v_q - gamma S0 k_q,
+// in which every decay factor is at most 1. S0 K^T, T Z and C^T K run on the matrix cores.
 #include "dev_common.h"
 #include "internal.h"
 
@@ -99,7 +101,7 @@ __device__ __forceinline__ void stage_entries(const GdnRing &ring, const GTile &
 
 // Gram entries G[l][i] = k_l . k_i (l < i < n), row stride W1; with q != nullptr also
 // u_j = k_j . q into sh_u. Lane groups of LPD lanes take one dot each.
-template <int DK, int TPB>
+template <int DK, int TPB, int KSTR = DK>
 __device__ __forceinline__ void gram_dots(const float *sh_k, const float *sh_q, int n, int W1,
                                           float *sh_G, float *sh_u, int t)
 {
@@ -112,10 +114,10 @@ __device__ __forceinline__ void gram_dots(const float *sh_k, const float *sh_q, 
         int l, i = -1;
         if (d < nq) {
             l = d;
-            s = lds_dot<DK, TPB>(sh_k + l * DK, sh_q, lane);
+            s = lds_dot<DK, TPB>(sh_k + l * KSTR, sh_q, lane);
         } else {
             upper_pair(d - nq, l, i);
-            s = lds_dot<DK, TPB>(sh_k + l * DK, sh_k + i * DK, lane);
+            s = lds_dot<DK, TPB>(sh_k + l * KSTR, sh_k + i * KSTR, lane);
         }
         s = group_sum<LPD>(s);
         if (lane == 0) {
@@ -264,131 +266,268 @@ __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c,
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// fold on the matrix cores (v_mfma_f32_16x16x4_f32)
+//
+// Operand layouts of the instruction, lane l: A[l % 16][l / 16]; B[l / 16][l % 16]; accumulator
+// register r holds D[4 (l / 16) + r][l % 16]. Lane (g, c) = (l / 16, l % 16) of wave w keeps,
+// for each of its i-blocks ib (16 rows of S) and each k-block kb (16 columns), the float4
+//     S[16 ib + c][16 kb + 4 g + r],  r = 0..3.
+// Taking the inner index of step r of k-block kb to be 16 kb + 4 g + r, that float4 is the B
+// operand of K S0^T (the transpose of S0 K^T) and also the accumulator of K^T C (the transpose of
+// C^T K), so the tile stays in registers. The accumulator of K S0^T is the B operand of T Z, and
+// the accumulator of T Z the B operand of K^T C. Blocks of 16 entries; at most two (W <= 32).
+// ------------------------------------------------------------------------------------------
+template <int DV, int DK>
+struct FoldMap {
+    static constexpr int TPB = TileShape<DV, DK>::TPB, NW = TPB / 64;
+    static constexpr int IB = DV / 16, KB = DK / 16, IBW = IB / NW;   // i-blocks per wave
+    static constexpr int KS = DK + 4, VS = DV + 4;                      // padded LDS row strides
+    static_assert(IBW >= 1 && IBW * NW == IB, "fold map");
+};
+
+// LDS rows of the fold: the window rounded up to whole 16-entry blocks.
+__host__ __device__ constexpr int fold_rows(int W) { return (W + 15) / 16 * 16; }
+
 template <int DV, int DK>
 __host__ __device__ constexpr int gdn_fold_lds(int W)
 {
-    // k, v, Y, U: (W+1) rows each; e [DV][W+1]; G [(W+1)^2]; beta, alpha, decay ratios, gamma
-    return (W + 1) * (2 * DK + 2 * DV) + DV * (W + 1) + (W + 1) * (W + 1) + 3 * (W + 1) + 4;
+    // K [WP][DK+4], V [WP][DV+4], T [WP][WP+4], Gram [W][W+1], d [WP], gamma
+    return fold_rows(W) * (DK + 4 + DV + 4 + fold_rows(W) + 4 + 1) + W * (W + 1) + 1;
 }
 
-// Fold n entries (ring entries [0, nring) and optionally the token) into the lane's block of the
-// checkpoint held in s. All threads call it.
-template <int DV, int DK, int R>
-__device__ __forceinline__ void gdn_fold_core(float4 (&s)[R], float *smem, const GdnRing &ring,
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Element offset, inside a tile, of the float4 S[16 ib' + c][16 kb + 4 g] of the thread's i-block
+// ib (ib' = w IBW + ib) at kb = 0.
+template <int DV, int DK>
+__device__ __forceinline__ int fold_offset(int t, int ib)
+{
+    using F = FoldMap<DV, DK>;
+    const int w = t >> 6, l = t & 63;
+    return (16 * (w * F::IBW + ib) + (l & 15)) * DK + 4 * (l >> 4);
+}
+
+// T by forward substitution, in one wave: T[t][q] = beta_t ([t == q] - sum_{i<t} G_iq' T[i][q])
+// with G_it = sh_G[i W1 + t]. Column q is lane group q / LPC (LPC = 64 / np lanes, each summing
+// every LPC-th i); rows n..np-1 are zero. beta_t is on lane t (`bel`).
+template <int LPC>
+__device__ __forceinline__ void t_solve(const float *sh_G, int W1, float bel, int n, int np,
+                                        float *sh_T, int TS)
+{
+    const int lane = threadIdx.x & 63, q = lane / LPC, part = lane - q * LPC;
+    for (int t = 0; t < n; ++t) {
+        float acc = 0.f;
+        for (int i = part; i < t; i += LPC) acc += sh_G[i * W1 + t] * sh_T[i * TS + q];
+        acc = group_sum<LPC>(acc);
+        const float b = lane_value(bel, t);
+        if (part == 0) sh_T[t * TS + q] = b * ((t == q ? 1.f : 0.f) - acc);
+        // row t is read by every lane of the wave in the next steps
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    for (int t = n; t < np; ++t)
+        if (part == 0) sh_T[t * TS + q] = 0.f;
+}
+
+// Fold n = nring (+1 with the token) >= 1 entries (ring entries [0, nring) from slot `head`, then
+// the token (kt, vt, bet, alt) if tok) into the tile, which is read from S0t (fold layout) after
+// the entries' loads went out. All threads call it; three barriers.
+template <int DV, int DK, int IBW, int KB>
+__device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem, const GdnRing &ring,
                                               const GTile &c, int head, int nring, bool tok,
-                                              const float *kt, const float *vt, float bet, float alt)
+                                              const float *kt, const float *vt, float bet,
+                                              float alt, const float *S0t)
 {
-    constexpr int TPB = TileShape<DV, DK>::TPB;
-    using M = Map4<DV, DK>;
-    static_assert(R == M::R, "fold block");
-    constexpr int LPR = M::LPR;
-    static_assert(TPB >= DK + DV, "one thread per Y / U column");
-    const int W = c.W, t = c.t, W1 = W + 1;
-    const int n = nring + (tok ? 1 : 0);
-    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
-    float *sh_k = smem;                 // [n][DK]
-    float *sh_v = sh_k + W1 * DK;       // [n][DV]
-    float *sh_Y = sh_v + W1 * DV;       // [n][DK]
-    float *sh_U = sh_Y + W1 * DK;       // [n][DV]
-    float *sh_e = sh_U + W1 * DV;       // [DV][W1]  (S0 y_t)
-    float *sh_G = sh_e + DV * W1;       // [W1][W1]
-    float *sh_be = sh_G + W1 * W1;      // [n]
-    float *sh_al = sh_be + W1;          // [n]
-    float *sh_dr = sh_al + W1;          // [n] prod_{i>t} alpha_i
-    float *sh_g = sh_dr + W1;           // gamma
+    using F = FoldMap<DV, DK>;
+    static_assert(IBW == F::IBW && KB == F::KB, "fold block");
+    constexpr int TPB = F::TPB, KS = F::KS, VS = F::VS, KF = DK / 4, VF = DV / 4;
+    constexpr int XQ = (kMaxWindow * (KF + VF) + TPB - 1) / TPB;
+    const int W = c.W, t = c.t, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
+    const int n = nring + (tok ? 1 : 0), NT = (n + 15) >> 4, np = NT * 16;
+    const int WP = fold_rows(W), TS = WP + 4, W1 = W + 1;
+    float *sh_k = smem;                 // [WP][KS]
+    float *sh_v = sh_k + WP * KS;       // [WP][VS]
+    float *sh_T = sh_v + WP * VS;       // [WP][TS]
+    float *sh_G = sh_T + WP * TS;       // [W][W1]
+    float *sh_d = sh_G + W * W1;        // [WP]
+    float *sh_g = sh_d + WP;            // gamma
 
-    stage_entries<DV, DK, TPB>(ring, c, head, nring, tok, kt, vt, bet, alt, sh_k, sh_v, sh_be, sh_al);
-    __syncthreads();
-    gram_dots<DK, TPB>(sh_k, nullptr, n, W1, sh_G, nullptr, t);
-    for (int j = t; j < n; j += TPB) {
-        float d = 1.f;
-        for (int i = j + 1; i < n; ++i) d *= sh_al[i];
-        sh_dr[j] = d;
-    }
-    if (t == TPB - 1) {
-        float g = 1.f;
-        for (int i = 0; i < n; ++i) g *= sh_al[i];
-        sh_g[0] = g;
-    }
-    __syncthreads();
-    if (t < DK) {                       // column t of Y
-        for (int q = 0; q < n; ++q) {
-            float y = sh_k[q * DK + t];
-            for (int i = 0; i < q; ++i) y -= sh_G[i * W1 + q] * sh_Y[i * DK + t];
-            sh_Y[q * DK + t] = sh_be[q] * y;
+    // 1. the entries' loads, then the tile's; stage the entries (zero rows up to the block end)
+    float4 xs[XQ];
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = t + q * TPB;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < n * KF) {
+            const int j = i / KF, o = (i - j * KF) * 4;
+            v = j < nring ? ld4(ring.k + (c.rh + (head + j) % W) * DK + o) : ld4(kt + o);
+        } else if (i < n * (KF + VF)) {
+            const int i2 = i - n * KF, j = i2 / VF, o = (i2 - j * VF) * 4;
+            v = j < nring ? ld4(ring.v + (c.rh + (head + j) % W) * DV + o) : ld4(vt + o);
         }
-    } else if (t < DK + DV) {           // column t - DK of U
-        const int col = t - DK;
-        for (int q = 0; q < n; ++q) {
-            float u = sh_v[q * DV + col];
-            float ratio = 1.f;          // gamma_q / gamma_i = prod_{i < i' <= q} alpha_i'
-            for (int i = q - 1; i >= 0; --i) {
-                ratio *= sh_al[i + 1];
-                u -= ratio * sh_G[i * W1 + q] * sh_U[i * DV + col];
+        xs[q] = v;
+    }
+    float bel = 0.f, all = 1.f;
+    if (wv == 0) {
+        bel = lane < nring ? ring.beta[c.rh + (head + lane) % W] : (lane < n ? bet : 0.f);
+        all = lane < nring ? ring.alpha[c.rh + (head + lane) % W] : (lane < n ? alt : 1.f);
+    }
+#pragma unroll
+    for (int ib = 0; ib < IBW; ++ib) {
+        const float *src = S0t + fold_offset<DV, DK>(t, ib);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
+    }
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = t + q * TPB;
+        if (i < n * KF) {
+            const int j = i / KF, o = (i - j * KF) * 4;
+            st4(sh_k + j * KS + o, xs[q]);
+        } else if (i < n * (KF + VF)) {
+            const int i2 = i - n * KF, j = i2 / VF, o = (i2 - j * VF) * 4;
+            st4(sh_v + j * VS + o, xs[q]);
+        }
+    }
+    for (int i = t; i < (np - n) * (KF + VF); i += TPB) {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < (np - n) * KF) {
+            const int j = i / KF;
+            st4(sh_k + (n + j) * KS + (i - j * KF) * 4, z);
+        } else {
+            const int i2 = i - (np - n) * KF, j = i2 / VF;
+            st4(sh_v + (n + j) * VS + (i2 - j * VF) * 4, z);
+        }
+    }
+    __syncthreads();
+
+    // 2. Gram entries (every wave), decay ratios (wave 0), K S0^T of the wave's i-blocks
+    gram_dots<DK, TPB, KS>(sh_k, nullptr, n, W1, sh_G, nullptr, t);
+    if (wv == 0) {
+        float gam;
+        const float d = wave_suffix_prod(all, n, gam);
+        if (lane < np) sh_d[lane] = lane < n ? d : 0.f;
+        if (lane == 0) sh_g[0] = gam;
+    }
+    v4f fz[IBW][2];
+#pragma unroll
+    for (int ib = 0; ib < IBW; ++ib) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            if (tb < NT) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const float4 kv = ld4(sh_k + (16 * tb + cl) * KS + 16 * kb + 4 * g);
+                    acc = mfma4(kv.x, s[ib][kb].x, acc);
+                    acc = mfma4(kv.y, s[ib][kb].y, acc);
+                    acc = mfma4(kv.z, s[ib][kb].z, acc);
+                    acc = mfma4(kv.w, s[ib][kb].w, acc);
+                }
             }
-            sh_U[q * DV + col] = sh_be[q] * u;
+            fz[ib][tb] = acc;            // (S0 k_q)[i] for q = 16 tb + 4 g + r, i = 16 ib' + c
         }
     }
     __syncthreads();
-    // e_t = S0 y_t for every t
-    for (int q = 0; q < n; ++q) {
-        const float4 y = ld4(sh_Y + q * DK + c0);
-        float part[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) part[r] = s[r].x * y.x + s[r].y * y.y + s[r].z * y.z + s[r].w * y.w;
-        int rsel;
-        const float e = row_reduce_scatter<R, LPR>(part, cg, rsel);
-        if (row_writer<R, LPR>(cg)) sh_e[(rg * R + rsel) * W1 + q] = e;
+
+    // 3. T (wave 0)
+    if (wv == 0) {
+        if (NT == 1) t_solve<4>(sh_G, W1, bel, n, np, sh_T, TS);
+        else t_solve<2>(sh_G, W1, bel, n, np, sh_T, TS);
     }
     __syncthreads();
-    const float g = sh_g[0];
+
+    // 4. Z = d_q v_q - gamma S0 k_q, C = T Z, S0 <- gamma S0 + C^T K
+    const float gam = sh_g[0];
+    v4f cz[IBW][2];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        s[r].x *= g; s[r].y *= g; s[r].z *= g; s[r].w *= g;
+    for (int ib = 0; ib < IBW; ++ib) {
+        const int i = 16 * (wv * IBW + ib) + cl;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            if (tb < NT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int q = 16 * tb + 4 * g + r;
+                    fz[ib][tb][r] = sh_d[q] * sh_v[q * VS + i] - gam * fz[ib][tb][r];
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            if (tt < NT) {
+#pragma unroll
+                for (int tb = 0; tb <= tt; ++tb) {
+                    const float4 tv = ld4(sh_T + (16 * tt + cl) * TS + 16 * tb + 4 * g);
+                    acc = mfma4(tv.x, fz[ib][tb][0], acc);
+                    acc = mfma4(tv.y, fz[ib][tb][1], acc);
+                    acc = mfma4(tv.z, fz[ib][tb][2], acc);
+                    acc = mfma4(tv.w, fz[ib][tb][3], acc);
+                }
+            }
+            cz[ib][tt] = acc;            // C[t][i] for t = 16 tt + 4 g + r, i = 16 ib' + c
+        }
     }
-    for (int q = 0; q < n; ++q) {
-        const float4 kq = ld4(sh_k + q * DK + c0);
-        const float dq = sh_dr[q];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int i = rg * R + r;
-            const float cf = dq * sh_U[q * DV + i] - g * sh_e[i * W1 + q];
-            s[r].x += cf * kq.x; s[r].y += cf * kq.y; s[r].z += cf * kq.z; s[r].w += cf * kq.w;
+    for (int ib = 0; ib < IBW; ++ib) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            v4f acc = {gam * s[ib][kb].x, gam * s[ib][kb].y, gam * s[ib][kb].z, gam * s[ib][kb].w};
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                if (tt < NT) {
+                    const float *kr = sh_k + (16 * tt + 4 * g) * KS + 16 * kb + cl;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc = mfma4(kr[r * KS], cz[ib][tt][r], acc);
+                }
+            }
+            s[ib][kb] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
 }
 
-template <int DV, int DK, int R>
-__device__ __forceinline__ void gdn_store(const float4 (&s)[R], float *dst, int t)
+template <int DV, int DK, int IBW, int KB>
+__device__ __forceinline__ void fold_store(const float4 (&s)[IBW][KB], float *dst, int t)
 {
-    using M = Map4<DV, DK>;
-    const int rg = t / M::LPR, c0 = (t - rg * M::LPR) * 4;
-    const size_t off = (size_t)(rg * R) * DK + c0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) st4_nt(dst + off + (size_t)r * DK, s[r]);
+    for (int ib = 0; ib < IBW; ++ib) {
+        float *p = dst + fold_offset<DV, DK>(t, ib);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) st4_nt(p + 16 * kb, s[ib][kb]);
+    }
 }
 
-template <int DV, int DK, int R>
+// decode step whose token fills the ring: fold the ring and the token, store, o = S q
+template <int DV, int DK>
 __device__ __forceinline__ void gdn_fold_decode(const GdnStepArgs &a, const GTile &c, int head,
-                                                int len, float4 (&s)[R], float *smem)
+                                                int len, float *smem)
 {
-    using M = Map4<DV, DK>;
-    static_assert(R == M::R, "tile block");
-    constexpr int LPR = M::LPR;
-    const int t = c.t;
-    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
+    using F = FoldMap<DV, DK>;
+    const int t = c.t, lane = t & 63, g = lane >> 4;
     float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
     const float *qt = a.q + c.bh * DK;
-    const float4 qv = ld4(qt + c0);
-    gdn_fold_core<DV, DK>(s, smem, a.ring, c, head, len, true, a.k + c.bh * DK, a.v + c.bh * DV,
-                          a.beta[c.bh], a.alpha[c.bh]);
-    gdn_store<DV, DK>(s, S0, t);
-    float part[R];
+    float4 s[F::IBW][F::KB];
+    gdn_fold_mfma<DV, DK>(s, smem, a.ring, c, head, len, true, a.k + c.bh * DK, a.v + c.bh * DV,
+                          a.beta[c.bh], a.alpha[c.bh], S0);
+    fold_store<DV, DK>(s, S0, t);
 #pragma unroll
-    for (int r = 0; r < R; ++r) part[r] = s[r].x * qv.x + s[r].y * qv.y + s[r].z * qv.z + s[r].w * qv.w;
-    int rsel;
-    const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
-    if (row_writer<R, LPR>(cg)) a.o[c.bh * DV + rg * R + rsel] = z;
+    for (int ib = 0; ib < F::IBW; ++ib) {
+        float p = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < F::KB; ++kb) {
+            const float4 qv = ld4(qt + 16 * kb + 4 * g);
+            p += s[ib][kb].x * qv.x + s[ib][kb].y * qv.y + s[ib][kb].z * qv.z + s[ib][kb].w * qv.w;
+        }
+        p += __shfl_xor(p, 16);
+        p += __shfl_xor(p, 32);
+        if (g == 0) a.o[c.bh * DV + 16 * ((t >> 6) * F::IBW + ib) + (lane & 15)] = p;
+    }
 }
 
 // Decode variants, chosen on the host as for Mamba-2: 0 = every sequence at the ring position
@@ -409,17 +548,22 @@ k_gdn_decode(GdnStepArgs a)
         head = a.uhead;
         len = a.ulen;
         gdn_replay<DV, DK, M::R, true>(a, c, head, len, s, smem);
-    } else {
-        // the checkpoint tile first: both paths read it with the same map
+    } else if constexpr (MODE == 1) {
+        // the checkpoint tile first, then the ring position
         const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
         const size_t off = c.bh * (size_t)(DV * DK) + (size_t)(rg * M::R) * DK + c0;
 #pragma unroll
         for (int r = 0; r < M::R; ++r) s[r] = ld4_nt(a.S0 + off + (size_t)r * DK);
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
-        if constexpr (MODE == 2) fold = len + 1 >= W;
-        if (fold) gdn_fold_decode<DV, DK>(a, c, head, len, s, smem);
-        else gdn_replay<DV, DK, M::R, false>(a, c, head, len, s, smem);
+        gdn_replay<DV, DK, M::R, false>(a, c, head, len, s, smem);
+    } else {
+        // the ring position first: the fold and the replay read the tile with different maps
+        head = a.bk.in[c.b];
+        len = a.bk.in[B + c.b];
+        fold = len + 1 >= W;
+        if (fold) gdn_fold_decode<DV, DK>(a, c, head, len, smem);
+        else gdn_replay<DV, DK, M::R, true>(a, c, head, len, s, smem);
     }
     if (c.h == 0 && c.t == 0) {
         a.bk.out[c.b] = fold ? (head + len + 1) % W : head;
@@ -453,13 +597,10 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_fold(GdnFoldAr
         }
         return;
     }
-    const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
-    float4 s[M::R];
-    const size_t off = (size_t)(rg * M::R) * DK + c0;
-#pragma unroll
-    for (int r = 0; r < M::R; ++r) s[r] = ld4_nt(S0 + off + (size_t)r * DK);
-    gdn_fold_core<DV, DK>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f);
-    gdn_store<DV, DK>(s, a.out ? a.out + c.bh * (size_t)(DV * DK) : S0, c.t);
+    using F = FoldMap<DV, DK>;
+    float4 s[F::IBW][F::KB];
+    gdn_fold_mfma<DV, DK>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f, S0);
+    fold_store<DV, DK>(s, a.out ? a.out + c.bh * (size_t)(DV * DK) : S0, c.t);
 }
 
 // conventional read-modify-write comparator
