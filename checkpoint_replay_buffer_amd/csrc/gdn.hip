@@ -334,10 +334,16 @@ __device__ __forceinline__ void t_solve(const float *sh_G, int W1, float bel, in
         if (part == 0) sh_T[t * TS + q] = 0.f;
 }
 
-// Fold n = nring (+1 with the token) >= 1 entries (ring entries [0, nring) from slot `head`, then
-// the token (kt, vt, bet, alt) if tok) into the tile, which is read from S0t (fold layout) after
-// the entries' loads went out. All threads call it; three barriers.
-template <int DV, int DK, int IBW, int KB>
+// Fold n = nring (+1 with the token) entries, 1 <= n <= 16 NTM, (ring entries [0, nring) from
+// slot `head`, then the token (kt, vt, bet, alt) if tok) into the tile, which is read from S0t
+// (fold layout) after the entries' loads went out. All threads call it; three barriers.
+//
+// Every MFMA chain runs a compile-time number of steps (NTM blocks of 16 entries; rows past n are
+// zero), and its accumulator is first read in the same straight-line code that issued the chain:
+// a conditional chain followed by a read on the other side of a branch was given too few wait
+// states by the compiler (the read saw a stale accumulator register), so no chain sits in a
+// branch and no chain result is read across one.
+template <int DV, int DK, int NTM, int IBW, int KB>
 __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem, const GdnRing &ring,
                                               const GTile &c, int head, int nring, bool tok,
                                               const float *kt, const float *vt, float bet,
@@ -345,10 +351,12 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
 {
     using F = FoldMap<DV, DK>;
     static_assert(IBW == F::IBW && KB == F::KB, "fold block");
+    static_assert(NTM == 1 || NTM == 2, "one or two 16-entry blocks");
     constexpr int TPB = F::TPB, KS = F::KS, VS = F::VS, KF = DK / 4, VF = DV / 4;
     constexpr int XQ = (kMaxWindow * (KF + VF) + TPB - 1) / TPB;
+    constexpr int NP = 16 * NTM;        // entry rows, zero past n
     const int W = c.W, t = c.t, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
-    const int n = nring + (tok ? 1 : 0), NT = (n + 15) >> 4, np = NT * 16;
+    const int n = nring + (tok ? 1 : 0);
     const int WP = fold_rows(W), TS = WP + 4, W1 = W + 1;
     float *sh_k = smem;                 // [WP][KS]
     float *sh_v = sh_k + WP * KS;       // [WP][VS]
@@ -357,7 +365,8 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
     float *sh_d = sh_G + W * W1;        // [WP]
     float *sh_g = sh_d + WP;            // gamma
 
-    // 1. the entries' loads, then the tile's; stage the entries (zero rows up to the block end)
+    // 1. the entries' loads, then the tile's; stage the entries (zero rows up to NP), decay
+    //    ratios d_q and gamma (wave 0)
     float4 xs[XQ];
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
@@ -394,98 +403,82 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
             st4(sh_v + j * VS + o, xs[q]);
         }
     }
-    for (int i = t; i < (np - n) * (KF + VF); i += TPB) {
+    for (int i = t; i < (NP - n) * (KF + VF); i += TPB) {
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < (np - n) * KF) {
+        if (i < (NP - n) * KF) {
             const int j = i / KF;
             st4(sh_k + (n + j) * KS + (i - j * KF) * 4, z);
         } else {
-            const int i2 = i - (np - n) * KF, j = i2 / VF;
+            const int i2 = i - (NP - n) * KF, j = i2 / VF;
             st4(sh_v + (n + j) * VS + (i2 - j * VF) * 4, z);
         }
     }
-    __syncthreads();
-
-    // 2. Gram entries (every wave), decay ratios (wave 0), K S0^T of the wave's i-blocks
-    gram_dots<DK, TPB, KS>(sh_k, nullptr, n, W1, sh_G, nullptr, t);
     if (wv == 0) {
         float gam;
         const float d = wave_suffix_prod(all, n, gam);
-        if (lane < np) sh_d[lane] = lane < n ? d : 0.f;
+        if (lane < NP) sh_d[lane] = lane < n ? d : 0.f;
         if (lane == 0) sh_g[0] = gam;
     }
-    v4f fz[IBW][2];
+    __syncthreads();
+
+    // 2. Gram entries (every wave); Z = d_q v_q - gamma S0 k_q for the wave's i-blocks, with
+    //    S0 k_q from K S0^T on the matrix cores
+    gram_dots<DK, TPB, KS>(sh_k, nullptr, n, W1, sh_G, nullptr, t);
+    const float gam = sh_g[0];
+    v4f fz[IBW][NTM];
 #pragma unroll
     for (int ib = 0; ib < IBW; ++ib) {
+        const int i = 16 * (wv * IBW + ib) + cl;
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < NTM; ++tb) {
             v4f acc = {0.f, 0.f, 0.f, 0.f};
-            if (tb < NT) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const float4 kv = ld4(sh_k + (16 * tb + cl) * KS + 16 * kb + 4 * g);
-                    acc = mfma4(kv.x, s[ib][kb].x, acc);
-                    acc = mfma4(kv.y, s[ib][kb].y, acc);
-                    acc = mfma4(kv.z, s[ib][kb].z, acc);
-                    acc = mfma4(kv.w, s[ib][kb].w, acc);
-                }
+            for (int kb = 0; kb < KB; ++kb) {
+                const float4 kv = ld4(sh_k + (16 * tb + cl) * KS + 16 * kb + 4 * g);
+                acc = mfma4(kv.x, s[ib][kb].x, acc);
+                acc = mfma4(kv.y, s[ib][kb].y, acc);
+                acc = mfma4(kv.z, s[ib][kb].z, acc);
+                acc = mfma4(kv.w, s[ib][kb].w, acc);
             }
-            fz[ib][tb] = acc;            // (S0 k_q)[i] for q = 16 tb + 4 g + r, i = 16 ib' + c
+            // acc[r] = (S0 k_q)[i] for q = 16 tb + 4 g + r
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int q = 16 * tb + 4 * g + r;
+                fz[ib][tb][r] = sh_d[q] * sh_v[q * VS + i] - gam * acc[r];
+            }
         }
     }
     __syncthreads();
 
     // 3. T (wave 0)
-    if (wv == 0) {
-        if (NT == 1) t_solve<4>(sh_G, W1, bel, n, np, sh_T, TS);
-        else t_solve<2>(sh_G, W1, bel, n, np, sh_T, TS);
-    }
+    if (wv == 0) t_solve<64 / NP>(sh_G, W1, bel, n, NP, sh_T, TS);
     __syncthreads();
 
-    // 4. Z = d_q v_q - gamma S0 k_q, C = T Z, S0 <- gamma S0 + C^T K
-    const float gam = sh_g[0];
-    v4f cz[IBW][2];
+    // 4. C = T Z, then S0 <- gamma S0 + C^T K
 #pragma unroll
     for (int ib = 0; ib < IBW; ++ib) {
-        const int i = 16 * (wv * IBW + ib) + cl;
+        v4f cz[NTM];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            if (tb < NT) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int q = 16 * tb + 4 * g + r;
-                    fz[ib][tb][r] = sh_d[q] * sh_v[q * VS + i] - gam * fz[ib][tb][r];
-                }
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < NTM; ++tt) {
             v4f acc = {0.f, 0.f, 0.f, 0.f};
-            if (tt < NT) {
 #pragma unroll
-                for (int tb = 0; tb <= tt; ++tb) {
-                    const float4 tv = ld4(sh_T + (16 * tt + cl) * TS + 16 * tb + 4 * g);
-                    acc = mfma4(tv.x, fz[ib][tb][0], acc);
-                    acc = mfma4(tv.y, fz[ib][tb][1], acc);
-                    acc = mfma4(tv.z, fz[ib][tb][2], acc);
-                    acc = mfma4(tv.w, fz[ib][tb][3], acc);
-                }
+            for (int tb = 0; tb <= tt; ++tb) {
+                const float4 tv = ld4(sh_T + (16 * tt + cl) * TS + 16 * tb + 4 * g);
+                acc = mfma4(tv.x, fz[ib][tb][0], acc);
+                acc = mfma4(tv.y, fz[ib][tb][1], acc);
+                acc = mfma4(tv.z, fz[ib][tb][2], acc);
+                acc = mfma4(tv.w, fz[ib][tb][3], acc);
             }
-            cz[ib][tt] = acc;            // C[t][i] for t = 16 tt + 4 g + r, i = 16 ib' + c
+            cz[tt] = acc;                // C[t][i] for t = 16 tt + 4 g + r, i = 16 ib' + c
         }
-    }
-#pragma unroll
-    for (int ib = 0; ib < IBW; ++ib) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             v4f acc = {gam * s[ib][kb].x, gam * s[ib][kb].y, gam * s[ib][kb].z, gam * s[ib][kb].w};
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                if (tt < NT) {
-                    const float *kr = sh_k + (16 * tt + 4 * g) * KS + 16 * kb + cl;
+            for (int tt = 0; tt < NTM; ++tt) {
+                const float *kr = sh_k + (16 * tt + 4 * g) * KS + 16 * kb + cl;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc = mfma4(kr[r * KS], cz[ib][tt][r], acc);
-                }
+                for (int r = 0; r < 4; ++r) acc = mfma4(kr[r * KS], cz[tt][r], acc);
             }
             s[ib][kb] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
@@ -503,8 +496,9 @@ __device__ __forceinline__ void fold_store(const float4 (&s)[IBW][KB], float *ds
     }
 }
 
-// decode step whose token fills the ring: fold the ring and the token, store, o = S q
-template <int DV, int DK>
+// decode step whose token fills the ring: fold the ring and the token, store, o = S q (all in
+// one straight-line region after the fold's MFMA chains)
+template <int DV, int DK, int NTM>
 __device__ __forceinline__ void gdn_fold_decode(const GdnStepArgs &a, const GTile &c, int head,
                                                 int len, float *smem)
 {
@@ -513,8 +507,8 @@ __device__ __forceinline__ void gdn_fold_decode(const GdnStepArgs &a, const GTil
     float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
     const float *qt = a.q + c.bh * DK;
     float4 s[F::IBW][F::KB];
-    gdn_fold_mfma<DV, DK>(s, smem, a.ring, c, head, len, true, a.k + c.bh * DK, a.v + c.bh * DV,
-                          a.beta[c.bh], a.alpha[c.bh], S0);
+    gdn_fold_mfma<DV, DK, NTM>(s, smem, a.ring, c, head, len, true, a.k + c.bh * DK,
+                               a.v + c.bh * DV, a.beta[c.bh], a.alpha[c.bh], S0);
     fold_store<DV, DK>(s, S0, t);
 #pragma unroll
     for (int ib = 0; ib < F::IBW; ++ib) {
@@ -528,6 +522,18 @@ __device__ __forceinline__ void gdn_fold_decode(const GdnStepArgs &a, const GTil
         p += __shfl_xor(p, 32);
         if (g == 0) a.o[c.bh * DV + 16 * ((t >> 6) * F::IBW + ib) + (lane & 15)] = p;
     }
+}
+
+// Consolidation or materialisation of one tile: fold, then store (same straight-line region).
+template <int DV, int DK, int NTM>
+__device__ __forceinline__ void gdn_fold_tile(const GdnFoldArgs &a, const GTile &c, int head,
+                                              int len, float *smem)
+{
+    using F = FoldMap<DV, DK>;
+    float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
+    float4 s[F::IBW][F::KB];
+    gdn_fold_mfma<DV, DK, NTM>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f, S0);
+    fold_store<DV, DK>(s, a.out ? a.out + c.bh * (size_t)(DV * DK) : S0, c.t);
 }
 
 // Decode variants, chosen on the host as for Mamba-2: 0 = every sequence at the ring position
@@ -562,8 +568,9 @@ k_gdn_decode(GdnStepArgs a)
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
         fold = len + 1 >= W;
-        if (fold) gdn_fold_decode<DV, DK>(a, c, head, len, smem);
-        else gdn_replay<DV, DK, M::R, true>(a, c, head, len, s, smem);
+        if (!fold) gdn_replay<DV, DK, M::R, true>(a, c, head, len, s, smem);
+        else if (W > 16) gdn_fold_decode<DV, DK, 2>(a, c, head, len, smem);
+        else gdn_fold_decode<DV, DK, 1>(a, c, head, len, smem);
     }
     if (c.h == 0 && c.t == 0) {
         a.bk.out[c.b] = fold ? (head + len + 1) % W : head;
@@ -597,10 +604,8 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_fold(GdnFoldAr
         }
         return;
     }
-    using F = FoldMap<DV, DK>;
-    float4 s[F::IBW][F::KB];
-    gdn_fold_mfma<DV, DK>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f, S0);
-    fold_store<DV, DK>(s, a.out ? a.out + c.bh * (size_t)(DV * DK) : S0, c.t);
+    if (W > 16) gdn_fold_tile<DV, DK, 2>(a, c, head, len, smem);
+    else gdn_fold_tile<DV, DK, 1>(a, c, head, len, smem);
 }
 
 // conventional read-modify-write comparator

@@ -23,7 +23,7 @@ def _step_ref(ins, t, ref, sel=slice(None)):
                     ins["alpha"][t][sel], ref)
 
 
-@pytest.mark.parametrize("d,W", [(16, 4), (64, 16), (128, 16), (128, 1)])
+@pytest.mark.parametrize("d,W", [(16, 4), (64, 16), (128, 16), (128, 1), (16, 20), (64, 24), (128, 32)])
 def test_decode_every_call(d, W):
     sh = wl.GDNShape(batch=3, nheads=3, d_k=d, d_v=d, window=W)
     T = 3 * W + 5 if W > 1 else 9
@@ -52,16 +52,21 @@ def test_decode_every_call(d, W):
     say(f"  worst normwise {worst:.3e}")
 
 
-def test_consolidate_and_masked_init():
-    sh = wl.GDNShape(batch=4, nheads=2, d_k=64, d_v=64, window=8)
+@pytest.mark.parametrize("d,W", [(64, 8), (128, 24)])
+def test_consolidate_and_masked_init(d, W):
+    """Masked re-init, consolidation with a threshold, materialisation after every operation. At
+    W = 24 the consolidation folds up to 23 entries (two 16-entry blocks)."""
+    sh = wl.GDNShape(batch=4, nheads=2, d_k=d, d_v=d, window=W)
+    say(f"gdn consolidate d={d} W={W}")
     s0 = wl.gdn_state0(sh, 1)
     ctx = _ctx(sh)
     ctx.init_checkpoint(dev(s0))
     model = Bookkeeping(sh.batch, sh.window)
     ref = s0.astype(np.float64).copy()
-    o = torch.empty(sh.batch, sh.nheads, 64, device="cuda")
+    o = torch.empty(sh.batch, sh.nheads, d, device="cuda")
     mat = torch.empty(s0.shape, device="cuda")
-    sched = ["d"] * 5 + [("mask", [0, 1, 0, 1])] + ["d"] * 2 + [("cons", 3)] + ["d"] * 9 + [("cons", 1)]
+    sched = (["d"] * (W - 3) + [("mask", [0, 1, 0, 1])] + ["d"] * 2 + [("cons", 3)] + ["d"] * (W + 1)
+             + [("cons", 1)])
     for i, op in enumerate(sched):
         if op == "d":
             ins = wl.gdn_token_inputs(sh, 1, 50 + i)
