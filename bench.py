@@ -88,7 +88,8 @@ def _traffic(kernel_key: str):
 def run_m2(args, torch, rb, wl):
     bf16 = args.workload == "m2_serve_bf16"
     batch = args.batch or 256
-    sh = wl.M2Shape(batch=batch, nheads=128, ngroups=128, head_dim=64, d_state=128, window=16)
+    sh = wl.M2Shape(batch=batch, nheads=128, ngroups=args.groups or 128, head_dim=64, d_state=128,
+                    window=16)
     P, N, W, H, B = sh.head_dim, sh.d_state, sh.window, sh.nheads, sh.batch
     gr = sh.ngroups / sh.nheads
     pool_n = 32
@@ -103,7 +104,7 @@ def run_m2(args, torch, rb, wl):
     D = torch.from_numpy(prm["D"]).cuda()
     gen_s = time.time() - t0
 
-    ctx = rb.Context("mamba2", B, H, P, N, W, bf16_read=bf16, store_c=True)
+    ctx = rb.Context("mamba2", B, H, P, N, W, ngroups=sh.ngroups, bf16_read=bf16, store_c=True)
     ctx.set_params(A, D)
     y = torch.empty(B, H, P, device="cuda")
     K, Wm = args.steps, args.warmup
@@ -184,7 +185,8 @@ def run_m2(args, torch, rb, wl):
         "vs_baseline": None,
         "dtype": "bf16-read/fp32" if bf16 else "fp32",
         "data": "synthetic (seeded N(0,1) x, N(0,1)/sqrt(N) B and C, softplus(N(-2,0.5)) dt)",
-        "config": {"workload": f"mamba2_decode_b{B}_h{H}_p{P}_n{N}_w{W}" + ("_bf16read" if bf16 else ""),
+        "config": {"workload": f"mamba2_decode_b{B}_h{H}_p{P}_n{N}_w{W}"
+                               + (f"_g{sh.ngroups}" if sh.ngroups != H else "") + ("_bf16read" if bf16 else ""),
                    "batch": B, "heads": H, "head_dim": P, "d_state": N, "window": W,
                    "groups": sh.ngroups, "input_pool_slots": pool_n},
         "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
@@ -549,6 +551,8 @@ def main():
     ap.add_argument("--workload", default="m2_serve",
                     choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve"])
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
+    ap.add_argument("--groups", type=int, default=0,
+                    help="Mamba-2 B/C groups (default: one per head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rmw", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")

@@ -337,10 +337,15 @@ def test_determinism_and_head_permutation():
 SUBSET = np.array([0, 1, 37, 101, 128, 190, 254, 255])
 
 
-@pytest.mark.parametrize("bf16,steps", [(False, 512), (True, 160)])
-def test_serving_shape_sampled(bf16, steps):
-    sh = wl.M2_SERVE
-    say(f"serving shape bf16={bf16} steps={steps}: generating inputs")
+@pytest.mark.parametrize("bf16,steps,G", [(False, 512, 128), (True, 160, 128), (False, 128, 8),
+                                          (False, 128, 1)])
+def test_serving_shape_sampled(bf16, steps, G):
+    """Serving shape (batch 256, 128 heads, 64x128, W = 16): sampled sequences against the oracle
+    at every step, all sequences against the read-modify-write kernel; also with B/C shared by
+    groups of heads (G = 8, G = 1)."""
+    sh = wl.M2_SERVE if G == 128 else wl.M2Shape(batch=256, nheads=128, ngroups=G, head_dim=64,
+                                                   d_state=128, window=16)
+    say(f"serving shape bf16={bf16} steps={steps} G={G}: generating inputs")
     prm = wl.m2_params(sh, 0)
     s0 = wl.m2_state0(sh, 0)
     pool = 32
