@@ -27,7 +27,7 @@ RSSM_F_BF16_READ = 1
 RSSM_F_STORE_C = 2
 
 EXPORTS = ("rssm_workspace_bytes", "rssm_create", "rssm_destroy", "rssm_set_params",
-           "rssm_init_checkpoint", "rssm_decode_step", "rssm_consolidate", "rssm_verify",
+           "rssm_init_checkpoint", "rssm_decode_step", "rssm_consolidate", "rssm_prefill", "rssm_verify",
            "rssm_verify_commit", "rssm_rollback", "rssm_step_baseline", "rssm_step_baseline_spec",
            "rssm_baseline_commit", "rssm_materialize", "rssm_read_bookkeeping", "rssm_status_str")
 
@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "rssm_init_checkpoint": (I32, [P, P, P, P]),
         "rssm_decode_step": (I32, [P, inp, P, P]),
         "rssm_consolidate": (I32, [P, I32, P]),
+        "rssm_prefill": (I32, [P, inp, P, P]),
         "rssm_verify": (I32, [P, inp, P, P]),
         "rssm_verify_commit": (I32, [P, P, P]),
         "rssm_rollback": (I32, [P, P, P]),
@@ -164,6 +165,10 @@ def rssm_decode_step(ctx: int, inputs: rssm_inputs, y, stream=None) -> None:
 
 def rssm_consolidate(ctx: int, min_len: int, stream=None) -> None:
     _chk("rssm_consolidate", load_library().rssm_consolidate(ctx, int(min_len), _stream(stream)))
+
+
+def rssm_prefill(ctx: int, inputs: rssm_inputs, y, stream=None) -> None:
+    _chk("rssm_prefill", load_library().rssm_prefill(ctx, ctypes.byref(inputs), _ptr(y), _stream(stream)))
 
 
 def rssm_verify(ctx: int, inputs: rssm_inputs, y, stream=None) -> None:
@@ -264,6 +269,11 @@ class Context:
 
     def decode_step(self, y, stream=None, **kw):
         rssm_decode_step(self.handle, self._inputs(1, **kw), _f32(y, "y"), stream)
+
+    def prefill(self, y, stream=None, **kw):
+        """T prompt tokens (token-major inputs, leading dimension T) into the checkpoint."""
+        ntok = next(iter(kw.values())).shape[0]
+        rssm_prefill(self.handle, self._inputs(ntok, **kw), _f32(y, "y"), stream)
 
     def verify(self, y, stream=None, **kw):
         ntok = next(iter(kw.values())).shape[0]

@@ -42,6 +42,18 @@ struct M2StepArgs {
     int uhead, ulen;    // ring position shared by every sequence (uniform decode mode only)
 };
 
+// Mamba-2 prefill of T prompt tokens (token-major inputs) into the checkpoint.
+struct M2PrefillArgs {
+    M2Dims d;
+    Bk bk;
+    float *S0;          // [B,H,P,N]
+    uint16_t *S0b;      // bf16 copy or nullptr
+    const float *A, *D; // [H]
+    const float *x, *Bm, *C, *dt;
+    float *y;           // [T,B,H,P]
+    int T;
+};
+
 // Mamba-2 consolidation (write S0) or materialisation (write out).
 struct M2FoldArgs {
     M2Dims d;
@@ -111,6 +123,7 @@ bool m2_supported(int P, int N);
 hipError_t m2_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s);
 hipError_t m2_verify(const M2StepArgs &a, bool bf16, hipStream_t s);
 size_t m2_lds_bytes(int P, int N, int W);   // dynamic LDS of the largest Mamba-2 kernel
+hipError_t m2_prefill(const M2PrefillArgs &a, bool bf16, hipStream_t s);
 hipError_t m2_fold(const M2FoldArgs &a, bool bf16, hipStream_t s);
 hipError_t m2_rmw(const M2RmwArgs &a, hipStream_t s);
 

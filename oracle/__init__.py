@@ -564,11 +564,18 @@ class GDNReplay:
 # Comparison metric
 # ----------------------------------------------------------------------------------------------
 
-def normwise_err(got, ref) -> float:
-    """max over output vectors (last axis) of max|got - ref| / max|ref|."""
+def normwise_err(got, ref, head_floor=None) -> float:
+    """max over output vectors (last axis) of max|got - ref| / max|ref|.
+
+    With head_floor (arrays [..., H, P]: the heads of one sequence-token in the last two axes),
+    each head vector's denominator is at least head_floor times the largest |ref| over all heads of
+    the same sequence-token: a head whose output nearly cancels is judged against the scale of the
+    layer output it belongs to rather than against its own near-zero magnitude."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     num = np.max(np.abs(got - ref), axis=-1)
     den = np.max(np.abs(ref), axis=-1)
+    if head_floor is not None:
+        den = np.maximum(den, head_floor * np.max(den, axis=-1, keepdims=True))
     den = np.where(den == 0, 1.0, den)
     return float(np.max(num / den)) if num.size else 0.0

@@ -20,6 +20,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
 TOL_BF16 = 2e-2
+HEAD_FLOOR = 0.01   # full-batch serving checks: a head's denominator >= 1 % of the token's largest head
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -369,7 +370,7 @@ def test_serving_shape_sampled(bf16, steps, G):
         if not bf16:
             rb.step_baseline(cfg, st_rmw, y2, A, D, **{k: v.unsqueeze(0) for k, v in tok.items()})
             if t % 64 == 63:     # replay vs read-modify-write at every sequence
-                worst_pair = max(worst_pair, normwise_err(host(y), host(y2)[0]))
+                worst_pair = max(worst_pair, normwise_err(host(y), host(y2)[0], HEAD_FLOOR))
     mat = torch.empty(s0.shape, device="cuda")
     ctx.materialize(mat)
     h, l, n, e = ctx.bookkeeping()
@@ -384,7 +385,7 @@ def test_serving_shape_sampled(bf16, steps, G):
     for t in range(steps):
         s = {k: v[0][SUBSET] for k, v in slots[t % pool].items()}
         y_ref = m2_step(prm["A"], prm["D"], s["x"], s["B"], s["C"], s["dt"], ref)
-        worst = max(worst, normwise_err(ys_h[t], y_ref))
+        worst = max(worst, normwise_err(ys_h[t], y_ref, HEAD_FLOOR))
         worst_tok = max(worst_tok, normwise_err(ys_h[t].reshape(len(SUBSET), -1),
                                                 y_ref.reshape(len(SUBSET), -1)))
         win_dt.append(s["dt"].astype(np.float64))

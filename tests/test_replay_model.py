@@ -254,3 +254,17 @@ def test_replay_model_follows_golden_trace(oracle_lib):
             continue
         h, l, nd = rp.bk.snapshot()
         assert list(h) == op["head"] and list(l) == op["len"] and list(nd) == op["ndraft"], op
+
+
+def test_normwise_head_floor():
+    """The head floor changes only heads whose output is small next to the sequence-token's
+    largest head: a near-cancelled head is judged against the layer scale."""
+    from oracle import normwise_err
+    ref = np.array([[[1.0, -2.0], [1e-4, 2e-4]]])          # [token, H=2, P=2]
+    got = ref.copy()
+    got[0, 1, 0] += 1e-6                                   # absolute error 1e-6 on the small head
+    assert abs(normwise_err(got, ref) - 1e-6 / 2e-4) < 1e-12
+    assert abs(normwise_err(got, ref, head_floor=0.01) - 1e-6 / 0.02) < 1e-12
+    got2 = ref.copy()
+    got2[0, 0, 1] += 1e-6                                  # a large head is unaffected
+    assert normwise_err(got2, ref, head_floor=0.01) == normwise_err(got2, ref)
