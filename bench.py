@@ -367,6 +367,103 @@ def gdn_bytes(DV, DK, W, length) -> float:
     return DV * DK * f + token + ring + (DK + DV + 2) * f + o
 
 
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+
+
+def m2_prefill_bytes(P, N, gr, T) -> float:
+    """HBM bytes of one prefill of T tokens for one (b, h) pair: the checkpoint read and written
+    once, every token's x, dt, B, C read, every output written."""
+    f = 4
+    return 2 * P * N * f + T * ((P + 1) * f + 2 * N * f * gr) + T * P * f
+
+
+def m2_prefill_flops(P, N, T) -> float:
+    """Matrix-core flops of one prefill for one (b, h) pair, per 16-token chunk: S C^T and the
+    rank-16 update (2 * 16 * P * N each), C B^T (2 * 16 * 16 * N) and M X (2 * 16 * 16 * P)."""
+    chunks = (T + 15) // 16
+    return chunks * (2 * 2 * 16 * P * N + 2 * 16 * 16 * N + 2 * 16 * 16 * P)
+
+
+def run_m2_prefill(args, torch, rb, wl):
+    """Prefill: a T-token prompt per sequence into the checkpoint (batch 256, 128 heads, 64 x 128),
+    against the conventional sequential scan (state read once, the T updates applied in order in
+    registers, state written once)."""
+    T = args.prompt
+    sh = wl.M2Shape(batch=args.batch or 256, nheads=128, ngroups=args.groups or 128, head_dim=64,
+                    d_state=128, window=16)
+    P, N, W, H, B = sh.head_dim, sh.d_state, sh.window, sh.nheads, sh.batch
+    gr = sh.ngroups / sh.nheads
+    K, Wm, S = args.steps, args.warmup, 32
+    t0 = time.time()
+    prm = wl.m2_params(sh, 0)
+    s0 = torch.from_numpy(wl.m2_state0(sh, 0)).cuda()
+    pool = [{k: torch.from_numpy(v[0]).cuda() for k, v in wl.m2_token_inputs(sh, 0, s).items()}
+            for s in range(S)]
+    prompt = {k: torch.stack([pool[t % S][k] for t in range(T)]) for k in pool[0]}
+    del pool
+    A = torch.from_numpy(prm["A"]).cuda()
+    D = torch.from_numpy(prm["D"]).cuda()
+    gen_s = time.time() - t0
+    ctx = rb.Context("mamba2", B, H, P, N, W, ngroups=sh.ngroups)
+    ctx.set_params(A, D)
+    y = torch.empty(T, B, H, P, device="cuda")
+    ctx.init_checkpoint(s0)
+    for _ in range(Wm):
+        ctx.prefill(y, **prompt)
+    torch.cuda.synchronize()
+    ev = _events(torch, 2 * K)
+    for k in range(K):
+        ev[2 * k].record()
+        ctx.prefill(y, **prompt)
+        ev[2 * k + 1].record()
+    torch.cuda.synchronize()
+    ms = [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(K)]
+    pre_s = sum(ms) / 1e3
+    # conventional sequential scan on the same prompt
+    cfg = rb.make_config(rb.RSSM_MAMBA2, B, H, sh.ngroups, P, N, W)
+    st = s0.clone()
+    for _ in range(Wm):
+        rb.step_baseline(cfg, st, y, A, D, **prompt)
+    torch.cuda.synchronize()
+    ev2 = _events(torch, 2)
+    ev2[0].record()
+    for _ in range(K):
+        rb.step_baseline(cfg, st, y, A, D, **prompt)
+    ev2[1].record()
+    torch.cuda.synchronize()
+    conv_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+    bytes_call = m2_prefill_bytes(P, N, gr, T) * B * H
+    flops_call = m2_prefill_flops(P, N, T) * B * H
+    gbs = bytes_call * K / pre_s / 1e9
+    tfl = flops_call * K / pre_s / 1e12
+    hbm_frac, mfma_frac = gbs / HBM_PEAK_GBS, tfl / MFMA_FP32_PEAK_TFLOPS
+    bound_hbm = hbm_frac >= mfma_frac
+    return {
+        "metric": "SSM prefill tokens/s (prompt into the checkpoint) vs the conventional sequential scan",
+        "value": round(B * T * K / pre_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(1e3 * pre_s / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded; prompt token t is pool slot t mod 32 of the decode inputs)",
+        "config": {"workload": f"mamba2_prefill_b{B}_h{H}_p{P}_n{N}_t{T}"
+                               + (f"_g{sh.ngroups}" if sh.ngroups != H else ""),
+                   "batch": B, "heads": H, "head_dim": P, "d_state": N, "prompt": T,
+                   "groups": sh.ngroups},
+        "alg_gbs": round(gbs, 1), "mfma_tflops": round(tfl, 2),
+        "conventional_ms": round(1e3 * conv_s / K, 4),
+        "speedup_vs_conventional": round(conv_s / pre_s, 3),
+        "roofline": {"bound": "hbm" if bound_hbm else "mfma", "kernel": "k_m2_prefill<64,128,false>",
+                     "achieved": round(gbs if bound_hbm else tfl, 2),
+                     "peak": HBM_PEAK_GBS if bound_hbm else MFMA_FP32_PEAK_TFLOPS,
+                     "unit": "GB/s" if bound_hbm else "TFLOP/s",
+                     "frac": round(hbm_frac if bound_hbm else mfma_frac, 4),
+                     "other": {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4)},
+                     "traffic": _traffic("prefill"), "alg_bytes_per_launch": round(bytes_call),
+                     "flops_per_launch": round(flops_call),
+                     "avg_launch_us": round(1e6 * pre_s / K, 2), "launches": K},
+        "input_gen_s": round(gen_s, 1),
+    }, (sh, prm)
+
+
 def run_gdn(args, torch, rb, wl):
     """Gated DeltaNet decode: batch 256, 32 heads, d_k = d_v = 128, W = 16."""
     sh = wl.GDN_SERVE
@@ -549,7 +646,8 @@ def main():
                     help="timed steps (decode tokens; verify rounds for m2_spec); default 512 / 256")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="m2_serve",
-                    choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve"])
+                    choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve", "m2_prefill"])
+    ap.add_argument("--prompt", type=int, default=512, help="prompt tokens (m2_prefill)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
     ap.add_argument("--groups", type=int, default=0,
                     help="Mamba-2 B/C groups (default: one per head)")
@@ -576,6 +674,15 @@ def main():
         line, (sh, prm) = run_m2_spec(args, torch, rb, wl)
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_m2_spec(sh, prm, wl)
+    elif args.workload == "m2_prefill":
+        args.steps = args.steps or 8
+        args.warmup = min(args.warmup, 2)
+        line, (sh, prm) = run_m2_prefill(args, torch, rb, wl)
+        if not args.no_cpu_baseline:
+            cb = cpu_baseline_m2(sh, prm, wl)
+            cb["gbs_fp64_state"] = cb["value"]
+            cb["value"], cb["unit"] = cb["tokens_per_s"], "tokens/s"
+            line["cpu_baseline"] = cb
     elif args.workload == "gdn_serve":
         args.steps = args.steps or 512
         line, sh = run_gdn(args, torch, rb, wl)

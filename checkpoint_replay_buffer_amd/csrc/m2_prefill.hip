@@ -39,11 +39,16 @@ struct PrefillMap {
     static_assert(IBW >= 1 && IBW * NW == IB, "prefill map");
 };
 
-// LDS floats: x [16][P+4], B and C [16][N+4], M [16][20], Lam, w[15][.] and dt [16] each
+// LDS floats: two staging buffers, each x [16][P+4], B and C [16][N+4], dt [16]
+template <int P, int N>
+__host__ __device__ constexpr int prefill_buf_floats()
+{
+    return kChunk * (P + 4) + 2 * kChunk * (N + 4) + kChunk;
+}
 template <int P, int N>
 __host__ __device__ constexpr int prefill_lds_floats()
 {
-    return kChunk * (P + 4) + 2 * kChunk * (N + 4) + kChunk * 20 + 3 * kChunk;
+    return 2 * prefill_buf_floats<P, N>();
 }
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c)
@@ -52,7 +57,7 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c)
 }
 
 // The fp32 MFMA adds its four products to the accumulator in sequence, so a chain over d_state
-// is a sequential sum of N terms. The long products (S C^T, C B^T) keep NA independent chains
+// is a sequential sum of N terms. The long products (S C^T, B C^T) keep NA independent chains
 // over interleaved k-blocks and add them as a tree: shorter sequential sums (the outputs of heads
 // whose terms nearly cancel are sensitive to it), and independent work for the matrix cores.
 template <int NA>
@@ -73,21 +78,90 @@ __device__ __forceinline__ void mfma_settle()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// sum_{lo < i <= hi} d[i] over the 16 step sizes of a chunk, in increasing i. The indices are
+// lane-dependent, so the terms outside the range are added as exact zeros instead of indexing
+// the register array (which would move it to scratch memory).
+__device__ __forceinline__ float range_sum(const float (&d)[kChunk], int lo, int hi)
+{
+    float e = 0.f;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) e += (i > lo && i <= hi) ? d[i] : 0.f;
+    return e;
+}
+
+// The chunk's rows of x, B, C and dt held in registers between their load and their LDS store.
+// The lane-dependent part of every address is fixed for the whole prompt and computed once; a
+// chunk only moves the (uniform) base pointers.
+template <int P, int N>
+struct ChunkRows {
+    static constexpr int TPB = TileShape<P, N>::TPB, PF = P / 4, NF = N / 4;
+    static constexpr int XQ = (kChunk * PF + TPB - 1) / TPB, BQ = (kChunk * NF + TPB - 1) / TPB;
+    float4 x[XQ], b[BQ], c[BQ];
+    float dt;
+    size_t xo[XQ], bo[BQ];   // element offsets from the chunk's first row
+    int xj[XQ], bj[BQ];      // token of the row within the chunk (kChunk: no row)
+
+    __device__ __forceinline__ void init(size_t BH, size_t BG, int t)
+    {
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int i = t + q * TPB, j = i / PF, o = (i - j * PF) * 4;
+            xj[q] = i < kChunk * PF ? j : kChunk;
+            xo[q] = (size_t)j * BH * P + o;
+        }
+#pragma unroll
+        for (int q = 0; q < BQ; ++q) {
+            const int i = t + q * TPB, j = i / NF, o = (i - j * NF) * 4;
+            bj[q] = i < kChunk * NF ? j : kChunk;
+            bo[q] = (size_t)j * BG * N + o;
+        }
+    }
+
+    // rows of tokens t0 .. t0 + ct - 1; xb, bb, cb, db point at token t0's row of this tile
+    __device__ __forceinline__ void load(const float *xb, const float *bb, const float *cb,
+                                         const float *db, size_t BH, int ct, int t)
+    {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) x[q] = xj[q] < ct ? ld4(xb + xo[q]) : z;
+#pragma unroll
+        for (int q = 0; q < BQ; ++q) {
+            b[q] = bj[q] < ct ? ld4(bb + bo[q]) : z;
+            c[q] = bj[q] < ct ? ld4(cb + bo[q]) : z;
+        }
+        dt = t < ct ? db[(size_t)t * BH] : 0.f;
+    }
+
+    __device__ __forceinline__ void store(float *sh_x, float *sh_B, float *sh_C, float *sh_dt, int t) const
+    {
+        constexpr int XS = P + 4, BS = N + 4;
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int i = t + q * TPB, j = i / PF, o = (i - j * PF) * 4;
+            if (i < kChunk * PF) st4(sh_x + j * XS + o, x[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < BQ; ++q) {
+            const int i = t + q * TPB, j = i / NF, o = (i - j * NF) * 4;
+            if (i < kChunk * NF) {
+                st4(sh_B + j * BS + o, b[q]);
+                st4(sh_C + j * BS + o, c[q]);
+            }
+        }
+        if (t < kChunk) sh_dt[t] = dt;
+    }
+};
+
+// One barrier per chunk: the chunk's rows (prefetched into registers during the previous chunk)
+// go to one of two LDS buffers; every wave then works from LDS and its registers only.
 template <int P, int N, bool BF16>
 __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2PrefillArgs a)
 {
     using F = PrefillMap<P, N>;
-    constexpr int TPB = F::TPB, IBW = F::IBW, KB = F::KB, XS = F::XS, BS = F::BS;
-    constexpr int PF = P / 4, NF = N / 4, MS = 20;
+    constexpr int IBW = F::IBW, KB = F::KB, XS = F::XS, BS = F::BS;
     constexpr int NA = KB >= 4 ? 4 : KB;   // independent accumulators of the d_state products
+    constexpr int BUF = prefill_buf_floats<P, N>();
     extern __shared__ float smem[];
-    float *sh_x = smem;                    // [16][XS]
-    float *sh_B = sh_x + kChunk * XS;      // [16][BS]
-    float *sh_C = sh_B + kChunk * BS;      // [16][BS]
-    float *sh_M = sh_C + kChunk * BS;      // [16][MS]  w[t][j] (B_j . C_t)
-    float *sh_L = sh_M + kChunk * MS;      // [16]      Lam_t
-    float *sh_wf = sh_L + kChunk;          // [16]      w[15][j]
-    float *sh_dt = sh_wf + kChunk;         // [16]
 
     const int B = a.d.B, H = a.d.H, G = a.d.G, T = a.T;
     const int tile = blockIdx.x, b = tile / H, h = tile - b * H, g0 = h / (H / G);
@@ -96,6 +170,12 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2Prefill
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
     const float Ah = a.A[h], Dh = a.D[h];
 
+    // token-0 rows of this tile; a chunk adds t0 rows of stride BH (x, dt) or BG (B, C)
+    const float *x0 = a.x + bh * P, *b0 = a.Bm + bg * N, *c0 = a.C + bg * N, *d0 = a.dt + bh;
+    float *y0 = a.y + bh * P;
+    ChunkRows<P, N> rows;
+    rows.init(BH, BG, t);
+    rows.load(x0, b0, c0, d0, BH, T < kChunk ? T : kChunk, t);
     float4 s[IBW][KB];
     float *S0 = a.S0 + bh * (size_t)(P * N);
     int off[IBW];
@@ -106,59 +186,79 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2Prefill
         for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(S0 + off[ib] + 16 * kb);
     }
 
-    for (int t0 = 0; t0 < T; t0 += kChunk) {
+    int buf = 0;
+    for (int t0 = 0; t0 < T; t0 += kChunk, buf ^= 1) {
         const int ct = T - t0 < kChunk ? T - t0 : kChunk;
-        // 1. the chunk's rows (zero past its last token)
-        for (int i = t; i < kChunk * (PF + 2 * NF); i += TPB) {
-            if (i < kChunk * PF) {
-                const int j = i / PF, o = (i - j * PF) * 4;
-                st4(sh_x + j * XS + o, j < ct ? ld4(a.x + ((size_t)(t0 + j) * BH + bh) * P + o)
-                                              : make_float4(0.f, 0.f, 0.f, 0.f));
-            } else {
-                const int i2 = i - kChunk * PF, which = i2 / (kChunk * NF);
-                const int i3 = i2 - which * kChunk * NF, j = i3 / NF, o = (i3 - j * NF) * 4;
-                const float *src = which == 0 ? a.Bm : a.C;
-                st4((which == 0 ? sh_B : sh_C) + j * BS + o,
-                    j < ct ? ld4(src + ((size_t)(t0 + j) * BG + bg) * N + o)
-                           : make_float4(0.f, 0.f, 0.f, 0.f));
-            }
-        }
-        if (t < kChunk) sh_dt[t] = t < ct ? a.dt[(size_t)(t0 + t) * BH + bh] : 0.f;
+        float *sh_x = smem + buf * BUF;
+        float *sh_B = sh_x + kChunk * XS;
+        float *sh_C = sh_B + kChunk * BS;
+        float *sh_dt = sh_C + kChunk * BS;
+        rows.store(sh_x, sh_B, sh_C, sh_dt, t);
         __syncthreads();
-
-        // 2. wave 0: the weights w[tt][j] (tt = 4 g + r, j = c) and Lam, then C B^T on the matrix
-        //    cores and M = w o (C B^T); every wave: Z = C S^T for its i-blocks (S at the chunk start)
-        if (wv == 0) {
-            float w[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tt = 4 * g + r, j = cl;
-                float e = 0.f;
-                for (int i = j + 1; i <= tt; ++i) e += sh_dt[i];
-                w[r] = j <= tt ? sh_dt[j] * expf(Ah * e) : 0.f;
-                if (j == 0) sh_L[tt] = expf(Ah * (e + sh_dt[0]));
-                if (tt == kChunk - 1) sh_wf[j] = w[r];
-            }
-            v4f gp[NA];
-#pragma unroll
-            for (int q = 0; q < NA; ++q) gp[q] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float4 cv = ld4(sh_C + cl * BS + 16 * kb + 4 * g);   // A: C[tt = c][k]
-                const float4 bv = ld4(sh_B + cl * BS + 16 * kb + 4 * g);   // B: B[j = c][k]
-                v4f &q = gp[kb % NA];
-                q = mfma4(cv.x, bv.x, q);
-                q = mfma4(cv.y, bv.y, q);
-                q = mfma4(cv.z, bv.z, q);
-                q = mfma4(cv.w, bv.w, q);
-            }
-            const v4f gc = tree_sum<NA>(gp);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sh_M[(4 * g + r) * MS + cl] = w[r] * gc[r];
+        if (t0 + kChunk < T) {             // the next chunk's rows, in flight during this chunk
+            const size_t t1 = t0 + kChunk;
+            rows.load(x0 + t1 * BH * P, b0 + t1 * BG * N, c0 + t1 * BG * N, d0 + t1 * BH, BH,
+                      T - (int)t1 < kChunk ? T - (int)t1 : kChunk, t);
         }
-        v4f z[IBW];
+
+        // 1. decay weights, per lane: M-operand weights w[t = c][j = 4 g + r], the decays Lam of
+        //    the output rows t = 4 g + r, and the decay of the whole chunk
+        float d[kChunk];
+#pragma unroll
+        for (int q = 0; q < kChunk; q += 4) {
+            const float4 v = ld4(sh_dt + q);
+            d[q] = v.x; d[q + 1] = v.y; d[q + 2] = v.z; d[q + 3] = v.w;
+        }
+        // this lane's step sizes d[4 g .. 4 g + 3] without indexing d by a lane-dependent value
+        const float4 dq = ld4(sh_dt + 4 * g);
+        const float dg[4] = {dq.x, dq.y, dq.z, dq.w};
+        // sum_{j<i<=t} d_i for j = 4 g + r, by adding d_{j+1} to the sum from j + 1 down
+        float sm[4], su[4];
+        sm[3] = range_sum(d, 4 * g + 3, cl);            // upper end t = c (M operand)
+        su[3] = range_sum(d, 4 * g + 3, kChunk - 1);    // upper end 15 (fold weights)
+#pragma unroll
+        for (int r = 2; r >= 0; --r) {
+            sm[r] = sm[r + 1] + (4 * g + r + 1 <= cl ? dg[r + 1] : 0.f);
+            su[r] = su[r + 1] + dg[r + 1];
+        }
+        float wm[4], wf[4], lam[4];
+        float pre = range_sum(d, -1, 4 * g - 1);        // sum_{i < 4 g} d_i
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            wm[r] = 4 * g + r <= cl ? dg[r] * expf(Ah * sm[r]) : 0.f;
+            wf[r] = dg[r] * expf(Ah * su[r]);
+            pre += dg[r];
+            lam[r] = expf(Ah * pre);                    // exp(A sum_{i <= 4 g + r} d_i)
+        }
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) tot += d[i];
+        const float lam_end = expf(Ah * tot);
+
+        // 2. (B C^T)[j][t] on the matrix cores; its accumulator register r on lane (g, c) holds
+        //    B_{4g+r} . C_c, which is the A operand M[t = c][j = 4 g + r] of M X once weighted
+        v4f gp[NA];
+#pragma unroll
+        for (int q = 0; q < NA; ++q) gp[q] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const float4 bv = ld4(sh_B + cl * BS + 16 * kb + 4 * g);   // A: B[j = c][k]
+            const float4 cv = ld4(sh_C + cl * BS + 16 * kb + 4 * g);   // B: C[t = c][k]
+            v4f &q = gp[kb % NA];
+            q = mfma4(bv.x, cv.x, q);
+            q = mfma4(bv.y, cv.y, q);
+            q = mfma4(bv.z, cv.z, q);
+            q = mfma4(bv.w, cv.w, q);
+        }
+        const v4f bc = tree_sum<NA>(gp);
+        float ma[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ma[r] = wm[r] * bc[r];
+
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
+            const int i = 16 * (wv * IBW + ib) + cl;
+            // 3. Z = C S^T (S at the chunk start)
             v4f zp[NA];
 #pragma unroll
             for (int q = 0; q < NA; ++q) zp[q] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -171,41 +271,32 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2Prefill
                 q = mfma4(cv.z, s[ib][kb].z, q);
                 q = mfma4(cv.w, s[ib][kb].w, q);
             }
-            z[ib] = tree_sum<NA>(zp);      // (S C_tt)[i] for tt = 4 g + r, i = 16 ib' + c
-        }
-        __syncthreads();
-
-        // 3. outputs Y = Lam o Z + M X + D X; then S <- Lam_15 S + B^T (w X) (transposed form)
-        const float lam_end = sh_L[kChunk - 1];
-#pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            const int i = 16 * (wv * IBW + ib) + cl;
+            const v4f z = tree_sum<NA>(zp);  // (S C_tt)[i] for tt = 4 g + r, i = 16 ib' + c
+            // 4. Y = Lam o Z + M X + D X
             float xj[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) xj[r] = sh_x[(4 * g + r) * XS + i];   // X[j = 4 g + r][i]
-            const float4 mv = ld4(sh_M + cl * MS + 4 * g);                    // M[tt = c][4 g + r]
             v4f acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma4(mv.x, xj[0], acc);
-            acc = mfma4(mv.y, xj[1], acc);
-            acc = mfma4(mv.z, xj[2], acc);
-            acc = mfma4(mv.w, xj[3], acc);
+            acc = mfma4(ma[0], xj[0], acc);
+            acc = mfma4(ma[1], xj[1], acc);
+            acc = mfma4(ma[2], xj[2], acc);
+            acc = mfma4(ma[3], xj[3], acc);
             float yv[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tt = 4 * g + r;
-                yv[r] = sh_L[tt] * z[ib][r] + acc[r] + Dh * sh_x[tt * XS + i];
-            }
-            // keep the reads of the accumulator here, next to its chain, rather than sunk into the
-            // conditional stores below
+            for (int r = 0; r < 4; ++r) yv[r] = lam[r] * z[r] + acc[r] + Dh * xj[r];
+            // keep the reads of the accumulators here, next to their chains, rather than sunk into
+            // the conditional stores below
             asm volatile("" ::"v"(yv[0]), "v"(yv[1]), "v"(yv[2]), "v"(yv[3]));
+            float *yc = y0 + (size_t)t0 * BH * P + i;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tt = 4 * g + r;
-                if (tt < ct) a.y[((size_t)(t0 + tt) * BH + bh) * P + i] = yv[r];
+                if (tt < ct) yc[(size_t)tt * BH * P] = yv[r];
             }
+            // 5. S <- Lam_15 S + B^T (w X): B operand w[15][j] x_j[i] for j = 4 g + r
             float wx[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wx[r] = sh_wf[4 * g + r] * xj[r];
+            for (int r = 0; r < 4; ++r) wx[r] = wf[r] * xj[r];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 v4f u = {lam_end * s[ib][kb].x, lam_end * s[ib][kb].y, lam_end * s[ib][kb].z,
@@ -219,7 +310,6 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2Prefill
             }
         }
         mfma_settle();
-        __syncthreads();
     }
 
     // the final state is the new checkpoint (and its bf16 read copy); the ring is empty
