@@ -29,7 +29,8 @@ RSSM_F_STORE_C = 2
 EXPORTS = ("rssm_workspace_bytes", "rssm_create", "rssm_destroy", "rssm_set_params",
            "rssm_init_checkpoint", "rssm_decode_step", "rssm_consolidate", "rssm_prefill", "rssm_verify",
            "rssm_verify_commit", "rssm_rollback", "rssm_step_baseline", "rssm_step_baseline_spec",
-           "rssm_baseline_commit", "rssm_materialize", "rssm_read_bookkeeping", "rssm_status_str")
+           "rssm_baseline_commit", "rssm_seq_state_bytes", "rssm_fork", "rssm_export", "rssm_import",
+           "rssm_materialize", "rssm_read_bookkeeping", "rssm_status_str")
 
 
 class RssmError(RuntimeError):
@@ -83,6 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "rssm_step_baseline": (I32, [cfgp, P, inp, P, P, P, P, P]),
         "rssm_step_baseline_spec": (I32, [cfgp, P, P, inp, P, P, P, P]),
         "rssm_baseline_commit": (I32, [cfgp, P, P, I32, P]),
+        "rssm_seq_state_bytes": (I32, [cfgp, ctypes.POINTER(SZ)]),
+        "rssm_fork": (I32, [P, P, P, I32, P]),
+        "rssm_export": (I32, [P, P, I32, P, P]),
+        "rssm_import": (I32, [P, P, I32, P, P]),
         "rssm_materialize": (I32, [P, P, P]),
         "rssm_read_bookkeeping": (I32, [P, P, P, P, ctypes.POINTER(U32), P]),
         "rssm_status_str": (ctypes.c_char_p, [I32]),
@@ -205,6 +210,24 @@ def rssm_baseline_commit(cfg: rssm_config, slot_of, accepted, ndraft: int, strea
                                              int(ndraft), _stream(stream)))
 
 
+def rssm_seq_state_bytes(cfg: rssm_config) -> int:
+    n = ctypes.c_size_t(0)
+    _chk("rssm_seq_state_bytes", load_library().rssm_seq_state_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def rssm_fork(ctx: int, src, dst, n: int, stream=None) -> None:
+    _chk("rssm_fork", load_library().rssm_fork(ctx, _ptr(src), _ptr(dst), int(n), _stream(stream)))
+
+
+def rssm_export(ctx: int, seq, n: int, buf, stream=None) -> None:
+    _chk("rssm_export", load_library().rssm_export(ctx, _ptr(seq), int(n), _ptr(buf), _stream(stream)))
+
+
+def rssm_import(ctx: int, seq, n: int, buf, stream=None) -> None:
+    _chk("rssm_import", load_library().rssm_import(ctx, _ptr(seq), int(n), _ptr(buf), _stream(stream)))
+
+
 def rssm_materialize(ctx: int, state_out, stream=None) -> None:
     _chk("rssm_materialize", load_library().rssm_materialize(ctx, _ptr(state_out), _stream(stream)))
 
@@ -287,6 +310,20 @@ class Context:
 
     def consolidate(self, min_len: int, stream=None):
         rssm_consolidate(self.handle, min_len, stream)
+
+    def seq_state_bytes(self) -> int:
+        return rssm_seq_state_bytes(self.cfg)
+
+    def fork(self, src, dst, stream=None):
+        """Sequence dst[i] becomes a copy of sequence src[i] (int32 device tensors)."""
+        rssm_fork(self.handle, src, dst, src.numel(), stream)
+
+    def export(self, seq, buf, stream=None):
+        """Packed state of sequences seq (int32 device tensor) into buf (uint8 device tensor)."""
+        rssm_export(self.handle, seq, seq.numel(), buf, stream)
+
+    def import_(self, seq, buf, stream=None):
+        rssm_import(self.handle, seq, seq.numel(), buf, stream)
 
     def materialize(self, out, stream=None):
         rssm_materialize(self.handle, _f32(out, "out"), stream)

@@ -148,6 +148,63 @@ rssm_status ready(const rssm_ctx *c)
     return RSSM_OK;
 }
 
+// The per-sequence segments of the workspace arrays and their packed-slot layout.
+SeqCopyArgs seq_args(const rssm_ctx *c, int mode, int n, const int32_t *src, const int32_t *dst,
+                     char *buf)
+{
+    const rssm_config &g = c->cfg;
+    const size_t H = g.nheads, G = g.ngroups, P = g.dim_v, N = g.dim_k, W = g.window;
+    SeqCopyArgs a{};
+    a.mode = mode;
+    a.n = n;
+    a.B = g.batch;
+    a.src = src;
+    a.dst = dst;
+    a.buf = buf;
+    a.err = c->err;
+    auto add = [&](void *base, size_t bytes) {
+        if (!base) return;
+        a.base[a.nseg] = static_cast<char *>(base);
+        a.seg_bytes[a.nseg] = bytes;
+        a.unit_log2[a.nseg] = bytes % 16 == 0 ? 4 : 2;
+        ++a.nseg;
+    };
+    add(c->S0, H * P * N * sizeof(float));
+    add(c->S0b, H * P * N * sizeof(uint16_t));
+    if (g.kind == RSSM_MAMBA2) {
+        add(c->m2.x, H * W * P * sizeof(float));
+        add(c->m2.B, G * W * N * sizeof(float));
+        add(c->m2.C, G * W * N * sizeof(float));
+        add(c->m2.dt, H * W * sizeof(float));
+    } else {
+        add(c->gdn.k, H * W * N * sizeof(float));
+        add(c->gdn.v, H * W * P * sizeof(float));
+        add(c->gdn.beta, H * W * sizeof(float));
+        add(c->gdn.alpha, H * W * sizeof(float));
+    }
+    uint64_t off = 0, units = 0;
+    for (int k = 0; k < a.nseg; ++k) {
+        a.pack_off[k] = off;
+        off += (a.seg_bytes[k] + 15) / 16 * 16;
+        a.unit_prefix[k] = units;
+        units += a.seg_bytes[k] >> a.unit_log2[k];
+    }
+    a.unit_prefix[a.nseg] = units;
+    a.pack_bytes = kSeqHeader + off;
+    return a;
+}
+
+rssm_status seq_checks(const rssm_ctx *ctx, int32_t n, const void *idx, const void *buf, bool need_buf)
+{
+    rssm_status s = ready(ctx);
+    if (s != RSSM_OK) return s;
+    if (n < 0 || n > ctx->cfg.batch || n > 65535) return RSSM_E_ARG;
+    if (n > 0 && !idx) return RSSM_E_ARG;
+    if (need_buf && n > 0 && !aligned16(buf)) return RSSM_E_ARG;
+    if (ctx->pending) return RSSM_E_STATE;
+    return RSSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -417,6 +474,56 @@ rssm_status rssm_materialize(rssm_ctx *ctx, float *state_out, void *stream)
     }
     GdnFoldArgs a{gdndims(c), bk, ctx->S0, ctx->gdn, 1, state_out};
     return launched(ctx, gdn_fold(a, strm(stream)), false);
+}
+
+rssm_status rssm_seq_state_bytes(const rssm_config *cfg, size_t *bytes)
+{
+    if (!cfg || !bytes) return RSSM_E_ARG;
+    const rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    rssm_ctx c{};
+    c.cfg = *cfg;
+    // any non-null bases give the segment sizes
+    char dummy[16];
+    c.S0 = reinterpret_cast<float *>(dummy);
+    c.S0b = (cfg->flags & RSSM_F_BF16_READ) ? reinterpret_cast<uint16_t *>(dummy) : nullptr;
+    float *f = reinterpret_cast<float *>(dummy);
+    c.m2 = M2Ring{f, f, (cfg->flags & RSSM_F_STORE_C) ? f : nullptr, f};
+    c.gdn = GdnRing{f, f, f, f};
+    *bytes = seq_args(&c, kSeqExport, 0, nullptr, nullptr, nullptr).pack_bytes;
+    return RSSM_OK;
+}
+
+rssm_status rssm_fork(rssm_ctx *ctx, const int32_t *src, const int32_t *dst, int32_t n, void *stream)
+{
+    rssm_status s = seq_checks(ctx, n, src, nullptr, false);
+    if (s != RSSM_OK) return s;
+    if (n > 0 && !dst) return RSSM_E_ARG;
+    const SeqCopyArgs a = seq_args(ctx, kSeqFork, n, src, dst, nullptr);
+    return launched(ctx, seq_copy(a, flip(ctx), strm(stream)), true);
+}
+
+rssm_status rssm_export(rssm_ctx *ctx, const int32_t *seq, int32_t n, void *buf, void *stream)
+{
+    rssm_status s = seq_checks(ctx, n, seq, buf, true);
+    if (s != RSSM_OK) return s;
+    const SeqCopyArgs a = seq_args(ctx, kSeqExport, n, seq, nullptr, static_cast<char *>(buf));
+    return launched(ctx, seq_copy(a, Bk{ctx->bk[ctx->par], nullptr}, strm(stream)), false);
+}
+
+rssm_status rssm_import(rssm_ctx *ctx, const int32_t *seq, int32_t n, const void *buf, void *stream)
+{
+    rssm_status s = seq_checks(ctx, n, seq, buf, true);
+    if (s != RSSM_OK) return s;
+    const SeqCopyArgs a = seq_args(ctx, kSeqImport, n, nullptr, seq,
+                                   const_cast<char *>(static_cast<const char *>(buf)));
+    s = launched(ctx, seq_copy(a, flip(ctx), strm(stream)), true);
+    if (s == RSSM_OK) {                       // the imported lengths are device data
+        ctx->lo = 0;
+        ctx->hi = ctx->cfg.window;
+        ctx->uni = false;
+    }
+    return s;
 }
 
 rssm_status rssm_read_bookkeeping(rssm_ctx *ctx, int32_t *head, int32_t *len, int32_t *ndraft,

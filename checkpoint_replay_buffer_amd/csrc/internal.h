@@ -42,6 +42,25 @@ struct M2StepArgs {
     int uhead, ulen;    // ring position shared by every sequence (uniform decode mode only)
 };
 
+// Per-sequence state copies (fork, export to / import from a packed buffer).
+enum SeqMode { kSeqFork = 0, kSeqExport = 1, kSeqImport = 2 };
+constexpr int kSeqMaxSeg = 6;              // checkpoint, read copy and up to four ring arrays
+constexpr size_t kSeqHeader = 16;          // packed slot: head, len, ndraft, 0, then the segments
+constexpr uint32_t kDevIndexRange = 8u;    // device error bit: a sequence index out of range
+
+struct SeqCopyArgs {
+    int mode, n, B, nseg;
+    const int32_t *src, *dst;              // fork: src[n], dst[n]; export: src = sequences; import: dst
+    char *base[kSeqMaxSeg];                // array bases in the workspace
+    uint64_t seg_bytes[kSeqMaxSeg];        // bytes of one sequence in each array
+    uint64_t pack_off[kSeqMaxSeg];         // offsets of the segments in a packed slot (after the header)
+    int unit_log2[kSeqMaxSeg];             // 4 (16-byte units) or 2 (4-byte units)
+    uint64_t unit_prefix[kSeqMaxSeg + 1];  // cumulative units over the segments
+    char *buf;                             // packed slots (export / import)
+    uint64_t pack_bytes;                   // bytes of one packed slot
+    uint32_t *err;
+};
+
 // Mamba-2 prefill of T prompt tokens (token-major inputs) into the checkpoint.
 struct M2PrefillArgs {
     M2Dims d;
@@ -124,6 +143,7 @@ hipError_t m2_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s);
 hipError_t m2_verify(const M2StepArgs &a, bool bf16, hipStream_t s);
 size_t m2_lds_bytes(int P, int N, int W);   // dynamic LDS of the largest Mamba-2 kernel
 hipError_t m2_prefill(const M2PrefillArgs &a, bool bf16, hipStream_t s);
+hipError_t seq_copy(const SeqCopyArgs &a, Bk bk, hipStream_t s);
 hipError_t m2_fold(const M2FoldArgs &a, bool bf16, hipStream_t s);
 hipError_t m2_rmw(const M2RmwArgs &a, hipStream_t s);
 

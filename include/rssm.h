@@ -74,7 +74,9 @@ enum {
 /* Device error word bits (sticky until read). */
 enum {
     RSSM_DEV_COMMIT_RANGE = 1u,    /* accepted[b] outside [0, ndraft[b]]; len left unchanged */
-    RSSM_DEV_ROLLBACK_RANGE = 2u   /* new_len[b] outside [0, len[b]]; len left unchanged */
+    RSSM_DEV_ROLLBACK_RANGE = 2u,  /* new_len[b] outside [0, len[b]]; len left unchanged */
+    RSSM_DEV_INDEX_RANGE = 8u      /* a fork / export / import sequence index outside [0, B); that
+                                      pair is skipped */
 };
 
 enum { RSSM_MAMBA2 = 1, RSSM_GDN = 2 };
@@ -193,6 +195,31 @@ rssm_status rssm_step_baseline_spec(const rssm_config *cfg, float *pool, const i
  * 0 keeps the committed state. No state is copied. accepted [B] int32, device. */
 rssm_status rssm_baseline_commit(const rssm_config *cfg, int32_t *slot_of, const int32_t *accepted,
                                  int32_t ndraft, void *stream);
+
+/* Per-sequence state snapshots for prefix caching and continuous batching (news.hamidun.com item
+ * "NVIDIA présente ReplaySSM...", sections "D'où vient le problème de l'état" and "Ce que les
+ * ingénieurs d'inférence doivent vérifier"). A sequence's state is its checkpoint (and bf16 read
+ * copy), its ring and its head / len / ndraft; copies of it need no recomputation. All three calls
+ * require no pending verify (RSSM_E_STATE); 0 <= n <= min(batch, 65535) (RSSM_E_ARG); index
+ * arrays are [n] int32 in device memory, and an index outside [0, batch) sets
+ * RSSM_DEV_INDEX_RANGE and skips that pair. */
+
+/* Bytes of one packed sequence slot (16-byte header with head, len, ndraft, then the state
+ * arrays, each padded to 16 bytes); the layout is only meaningful to a context with the same
+ * configuration. Host only. */
+rssm_status rssm_seq_state_bytes(const rssm_config *cfg, size_t *bytes);
+
+/* Make sequence dst[i] a copy of sequence src[i] (state and bookkeeping), i < n. The dst indices
+ * must be distinct and none may be a src of another pair (otherwise the result is undefined). */
+rssm_status rssm_fork(rssm_ctx *ctx, const int32_t *src, const int32_t *dst, int32_t n, void *stream);
+
+/* Write the state of sequence seq[i] into packed slot i of buf (device, 16-byte aligned,
+ * n * rssm_seq_state_bytes bytes, caller-owned). The context is not changed. */
+rssm_status rssm_export(rssm_ctx *ctx, const int32_t *seq, int32_t n, void *buf, void *stream);
+
+/* Replace the state of sequence seq[i] by packed slot i of buf (as written by rssm_export of a
+ * context with the same configuration). seq indices must be distinct. */
+rssm_status rssm_import(rssm_ctx *ctx, const int32_t *seq, int32_t n, const void *buf, void *stream);
 
 /* Write the current state of every sequence (S0 with its committed entries folded in) to
  * state_out [B,H,dim_v,dim_k] without changing the context. */

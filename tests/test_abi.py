@@ -108,6 +108,10 @@ def test_call_order_checked_on_host(lib):
                      lambda: rb.rssm_verify_commit(h, FAKE_WS, stream=0),
                      lambda: rb.rssm_rollback(h, FAKE_WS, stream=0),
                      lambda: rb.rssm_materialize(h, FAKE_WS, stream=0),
+                     lambda: rb.rssm_prefill(h, tok, FAKE_WS, stream=0),
+                     lambda: rb.rssm_fork(h, FAKE_WS, FAKE_WS, 1, stream=0),
+                     lambda: rb.rssm_export(h, FAKE_WS, 1, FAKE_WS, stream=0),
+                     lambda: rb.rssm_import(h, FAKE_WS, 1, FAKE_WS, stream=0),
                      lambda: rb.rssm_init_checkpoint(h, FAKE_WS, FAKE_WS, stream=0)):
             with pytest.raises(rb.RssmError) as e:
                 call()
@@ -138,3 +142,27 @@ def test_baseline_argument_checks(lib):
                                                            dt=FAKE_WS),
                               None, FAKE_WS, FAKE_WS, stream=0)
     assert e.value.status == -1
+
+
+@pytest.mark.parametrize("kind,flags,dims", [
+    (rb.RSSM_MAMBA2, 0, (3, 4, 2, 16, 16, 5)),
+    (rb.RSSM_MAMBA2, rb.RSSM_F_BF16_READ | rb.RSSM_F_STORE_C, (2, 128, 128, 64, 128, 16)),
+    (rb.RSSM_GDN, 0, (2, 3, 3, 64, 64, 7)),
+])
+def test_seq_state_bytes(lib, kind, flags, dims):
+    """A packed sequence slot: a 16-byte header (head, len, ndraft) and each state array's share of
+    one sequence, padded to 16 bytes, in the order checkpoint, read copy, ring arrays."""
+    B, H, G, V, K, W = dims
+    cfg = rb.make_config(kind, B, H, G, V, K, W, 0, flags)
+    pad = lambda n: (n + 15) // 16 * 16
+    segs = [H * V * K * 4]
+    if flags & rb.RSSM_F_BF16_READ:
+        segs.append(H * V * K * 2)
+    if kind == rb.RSSM_MAMBA2:
+        segs += [H * W * V * 4, G * W * K * 4]
+        if flags & rb.RSSM_F_STORE_C:
+            segs.append(G * W * K * 4)
+        segs.append(H * W * 4)
+    else:
+        segs += [H * W * K * 4, H * W * V * 4, H * W * 4, H * W * 4]
+    assert rb.rssm_seq_state_bytes(cfg) == 16 + sum(pad(n) for n in segs)
