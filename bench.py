@@ -464,6 +464,58 @@ def run_m2_prefill(args, torch, rb, wl):
     }, (sh, prm)
 
 
+def run_m2_fork(args, torch, rb, wl):
+    """Per-sequence state copies at the Mamba-2 serving shape (batch 256, 128 heads, 64 x 128,
+    W = 16, C kept): fork half of the sequences onto the other half, export them to a packed
+    buffer and import them back. Bytes: each copied sequence's state read once and written once."""
+    sh = wl.M2Shape(batch=args.batch or 256, nheads=128, ngroups=args.groups or 128, head_dim=64,
+                    d_state=128, window=16)
+    P, N, W, H, B = sh.head_dim, sh.d_state, sh.window, sh.nheads, sh.batch
+    K, Wm = args.steps, args.warmup
+    prm = wl.m2_params(sh, 0)
+    ctx = rb.Context("mamba2", B, H, P, N, W, ngroups=sh.ngroups)
+    ctx.set_params(torch.from_numpy(prm["A"]).cuda(), torch.from_numpy(prm["D"]).cuda())
+    ctx.init_checkpoint(torch.from_numpy(wl.m2_state0(sh, 0)).cuda())
+    half = B // 2
+    src = torch.arange(half, dtype=torch.int32, device="cuda")
+    dst = src + half
+    nb = ctx.seq_state_bytes()
+    buf = torch.empty(half * nb, dtype=torch.uint8, device="cuda")
+    seg = nb - 16                                  # state bytes of one sequence (incl. padding)
+
+    def timed(fn):
+        for _ in range(Wm):
+            fn()
+        torch.cuda.synchronize()
+        ev = _events(torch, 2)
+        ev[0].record()
+        for _ in range(K):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / 1e3 / K
+
+    t_fork = timed(lambda: ctx.fork(src, dst))
+    t_exp = timed(lambda: ctx.export(src, buf))
+    t_imp = timed(lambda: ctx.import_(dst, buf))
+    moved = 2 * half * seg
+    gbs = moved / t_fork / 1e9
+    return {
+        "metric": "per-sequence state copy GB/s (fork / export / import), % of HBM peak",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(1e3 * t_fork, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic (seeded checkpoint)",
+        "config": {"workload": f"mamba2_fork_b{B}_h{H}_p{P}_n{N}_w{W}", "batch": B, "heads": H,
+                   "head_dim": P, "d_state": N, "window": W, "sequences_copied": half,
+                   "state_bytes_per_sequence": seg},
+        "export_gbs": round(moved / t_exp / 1e9, 1), "import_gbs": round(moved / t_imp / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_seq_copy (fork)", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "alg_bytes_per_launch": moved,
+                     "avg_launch_us": round(1e6 * t_fork, 2), "launches": K},
+    }
+
+
 def run_gdn(args, torch, rb, wl):
     """Gated DeltaNet decode: batch 256, 32 heads, d_k = d_v = 128, W = 16."""
     sh = wl.GDN_SERVE
@@ -646,7 +698,8 @@ def main():
                     help="timed steps (decode tokens; verify rounds for m2_spec); default 512 / 256")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="m2_serve",
-                    choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve", "m2_prefill"])
+                    choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve", "m2_prefill",
+                             "m2_fork"])
     ap.add_argument("--prompt", type=int, default=512, help="prompt tokens (m2_prefill)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
     ap.add_argument("--groups", type=int, default=0,
@@ -683,6 +736,10 @@ def main():
             cb["gbs_fp64_state"] = cb["value"]
             cb["value"], cb["unit"] = cb["tokens_per_s"], "tokens/s"
             line["cpu_baseline"] = cb
+    elif args.workload == "m2_fork":
+        args.steps = args.steps or 20
+        args.warmup = min(args.warmup, 3)
+        line = run_m2_fork(args, torch, rb, wl)
     elif args.workload == "gdn_serve":
         args.steps = args.steps or 512
         line, sh = run_gdn(args, torch, rb, wl)

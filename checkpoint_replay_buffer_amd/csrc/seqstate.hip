@@ -20,6 +20,13 @@ namespace {
 
 __device__ __forceinline__ bool in_range(int v, int B) { return v >= 0 && v < B; }
 
+// each byte is read and written once: streaming (non-temporal) 16-byte accesses
+__device__ __forceinline__ void copy16_nt(char *dst, const char *src)
+{
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(src));
+    __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(dst));
+}
+
 // source and destination (sequence or buffer slot) of pair p; false when an index is out of range
 __device__ __forceinline__ bool pair_of(const SeqCopyArgs &a, int p, int &s, int &d)
 {
@@ -55,7 +62,7 @@ __global__ void __launch_bounds__(256) k_seq_copy(SeqCopyArgs a)
         char *dst = to_buf ? a.buf + (size_t)d * a.pack_bytes + kSeqHeader + a.pack_off[k] + off
                            : a.base[k] + (size_t)d * a.seg_bytes[k] + off;
         if (a.unit_log2[k] == 4)
-            *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+            copy16_nt(dst, src);
         else
             *reinterpret_cast<uint32_t *>(dst) = *reinterpret_cast<const uint32_t *>(src);
     }
