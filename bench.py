@@ -511,7 +511,7 @@ def run_m2_fork(args, torch, rb, wl):
         "export_gbs": round(moved / t_exp / 1e9, 1), "import_gbs": round(moved / t_imp / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "k_seq_copy (fork)", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "alg_bytes_per_launch": moved,
+                     "traffic": _traffic("fork"), "alg_bytes_per_launch": moved,
                      "avg_launch_us": round(1e6 * t_fork, 2), "launches": K},
     }
 
