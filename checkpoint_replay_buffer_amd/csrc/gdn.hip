@@ -22,6 +22,7 @@
 // in which every decay factor is at most 1. S0 K^T, T Z and C^T K run on the matrix cores.
 #include "dev_common.h"
 #include "internal.h"
+#include "mfma_tile.h"
 
 namespace rssm {
 namespace {
@@ -267,24 +268,12 @@ __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c,
 }
 
 // ------------------------------------------------------------------------------------------
-// fold on the matrix cores (v_mfma_f32_16x16x4_f32)
-//
-// Operand layouts of the instruction, lane l: A[l % 16][l / 16]; B[l / 16][l % 16]; accumulator
-// register r holds D[4 (l / 16) + r][l % 16]. Lane (g, c) = (l / 16, l % 16) of wave w keeps,
-// for each of its i-blocks ib (16 rows of S) and each k-block kb (16 columns), the float4
-//     S[16 ib + c][16 kb + 4 g + r],  r = 0..3.
-// Taking the inner index of step r of k-block kb to be 16 kb + 4 g + r, that float4 is the B
-// operand of K S0^T (the transpose of S0 K^T) and also the accumulator of K^T C (the transpose of
-// C^T K), so the tile stays in registers. The accumulator of K S0^T is the B operand of T Z, and
-// the accumulator of T Z the B operand of K^T C. Blocks of 16 entries; at most two (W <= 32).
+// fold on the matrix cores (tile layout: mfma_tile.h). The accumulator of K S0^T is the B operand
+// of T Z, and the accumulator of T Z the B operand of K^T C. Blocks of 16 entries; at most two
+// (W <= 32).
 // ------------------------------------------------------------------------------------------
 template <int DV, int DK>
-struct FoldMap {
-    static constexpr int TPB = TileShape<DV, DK>::TPB, NW = TPB / 64;
-    static constexpr int IB = DV / 16, KB = DK / 16, IBW = IB / NW;   // i-blocks per wave
-    static constexpr int KS = DK + 4, VS = DV + 4;                      // padded LDS row strides
-    static_assert(IBW >= 1 && IBW * NW == IB, "fold map");
-};
+using FoldMap = MfmaTile<DV, DK>;
 
 // LDS rows of the fold: the window rounded up to whole 16-entry blocks.
 __host__ __device__ constexpr int fold_rows(int W) { return (W + 15) / 16 * 16; }
@@ -294,44 +283,6 @@ __host__ __device__ constexpr int gdn_fold_lds(int W)
 {
     // K [WP][DK+4], V [WP][DV+4], T [WP][WP+4], Gram [W][W+1], d [WP], gamma
     return fold_rows(W) * (DK + 4 + DV + 4 + fold_rows(W) + 4 + 1) + W * (W + 1) + 1;
-}
-
-__device__ __forceinline__ v4f mfma4(float a, float b, v4f c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Element offset, inside a tile, of the float4 S[16 ib' + c][16 kb + 4 g] of the thread's i-block
-// ib (ib' = w IBW + ib) at kb = 0.
-template <int DV, int DK>
-__device__ __forceinline__ int fold_offset(int t, int ib)
-{
-    using F = FoldMap<DV, DK>;
-    const int w = t >> 6, l = t & 63;
-    return (16 * (w * F::IBW + ib) + (l & 15)) * DK + 4 * (l >> 4);
-}
-
-// T by forward substitution, in one wave: T[t][q] = beta_t ([t == q] - sum_{i<t} G_iq' T[i][q])
-// with G_it = sh_G[i W1 + t]. Column q is lane group q / LPC (LPC = 64 / np lanes, each summing
-// every LPC-th i); rows n..np-1 are zero. beta_t is on lane t (`bel`).
-template <int LPC>
-__device__ __forceinline__ void t_solve(const float *sh_G, int W1, float bel, int n, int np,
-                                        float *sh_T, int TS)
-{
-    const int lane = threadIdx.x & 63, q = lane / LPC, part = lane - q * LPC;
-    for (int t = 0; t < n; ++t) {
-        float acc = 0.f;
-        for (int i = part; i < t; i += LPC) acc += sh_G[i * W1 + t] * sh_T[i * TS + q];
-        acc = group_sum<LPC>(acc);
-        const float b = lane_value(bel, t);
-        if (part == 0) sh_T[t * TS + q] = b * ((t == q ? 1.f : 0.f) - acc);
-        // row t is read by every lane of the wave in the next steps
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    for (int t = n; t < np; ++t)
-        if (part == 0) sh_T[t * TS + q] = 0.f;
 }
 
 // Fold n = nring (+1 with the token) entries, 1 <= n <= 16 NTM, (ring entries [0, nring) from
@@ -352,7 +303,7 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
     using F = FoldMap<DV, DK>;
     static_assert(IBW == F::IBW && KB == F::KB, "fold block");
     static_assert(NTM == 1 || NTM == 2, "one or two 16-entry blocks");
-    constexpr int TPB = F::TPB, KS = F::KS, VS = F::VS, KF = DK / 4, VF = DV / 4;
+    constexpr int TPB = F::TPB, KS = F::CS, VS = F::RS, KF = DK / 4, VF = DV / 4;
     constexpr int XQ = (kMaxWindow * (KF + VF) + TPB - 1) / TPB;
     constexpr int NP = 16 * NTM;        // entry rows, zero past n
     const int W = c.W, t = c.t, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
@@ -388,7 +339,7 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
     }
 #pragma unroll
     for (int ib = 0; ib < IBW; ++ib) {
-        const float *src = S0t + fold_offset<DV, DK>(t, ib);
+        const float *src = S0t + mfma_tile_offset<DV, DK>(t, ib);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
     }
@@ -490,7 +441,7 @@ __device__ __forceinline__ void fold_store(const float4 (&s)[IBW][KB], float *ds
 {
 #pragma unroll
     for (int ib = 0; ib < IBW; ++ib) {
-        float *p = dst + fold_offset<DV, DK>(t, ib);
+        float *p = dst + mfma_tile_offset<DV, DK>(t, ib);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) st4_nt(p + 16 * kb, s[ib][kb]);
     }

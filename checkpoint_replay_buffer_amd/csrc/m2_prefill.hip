@@ -25,19 +25,12 @@
 // the transpose of the rank-16 update.
 #include "dev_common.h"
 #include "internal.h"
+#include "mfma_tile.h"
 
 namespace rssm {
 namespace {
 
 constexpr int kChunk = 16;
-
-template <int P, int N>
-struct PrefillMap {
-    static constexpr int TPB = TileShape<P, N>::TPB, NW = TPB / 64;
-    static constexpr int IB = P / 16, KB = N / 16, IBW = IB / NW;   // i-blocks per wave
-    static constexpr int XS = P + 4, BS = N + 4;                      // padded LDS row strides
-    static_assert(IBW >= 1 && IBW * NW == IB, "prefill map");
-};
 
 // LDS floats: two staging buffers, each x [16][P+4], B and C [16][N+4], dt [16]
 template <int P, int N>
@@ -49,33 +42,6 @@ template <int P, int N>
 __host__ __device__ constexpr int prefill_lds_floats()
 {
     return 2 * prefill_buf_floats<P, N>();
-}
-
-__device__ __forceinline__ v4f mfma4(float a, float b, v4f c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// The fp32 MFMA adds its four products to the accumulator in sequence, so a chain over d_state
-// is a sequential sum of N terms. The long products (S C^T, B C^T) keep NA independent chains
-// over interleaved k-blocks and add them as a tree: shorter sequential sums (the outputs of heads
-// whose terms nearly cancel are sensitive to it), and independent work for the matrix cores.
-template <int NA>
-__device__ __forceinline__ v4f tree_sum(const v4f (&p)[NA])
-{
-    if constexpr (NA == 1) return p[0];
-    else if constexpr (NA == 2) return p[0] + p[1];
-    else return (p[0] + p[1]) + (p[2] + p[3]);
-}
-
-// Wait states after an MFMA chain whose accumulators are next read on the far side of a branch
-// (the loop back-edge, the loop exit): 16 here, more than an 8-pass 16x16x4 f32 result needs, and
-// the scheduling barriers keep the chain ahead of them.
-__device__ __forceinline__ void mfma_settle()
-{
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 // sum_{lo < i <= hi} d[i] over the 16 step sizes of a chunk, in increasing i. The indices are
@@ -157,8 +123,8 @@ struct ChunkRows {
 template <int P, int N, bool BF16>
 __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2PrefillArgs a)
 {
-    using F = PrefillMap<P, N>;
-    constexpr int IBW = F::IBW, KB = F::KB, XS = F::XS, BS = F::BS;
+    using F = MfmaTile<P, N>;
+    constexpr int IBW = F::IBW, KB = F::KB, XS = F::RS, BS = F::CS;
     constexpr int NA = KB >= 4 ? 4 : KB;   // independent accumulators of the d_state products
     constexpr int BUF = prefill_buf_floats<P, N>();
     extern __shared__ float smem[];
