@@ -464,6 +464,92 @@ def run_m2_prefill(args, torch, rb, wl):
     }, (sh, prm)
 
 
+def gdn_prefill_bytes(DV, DK, T) -> float:
+    """HBM bytes of one Gated DeltaNet prefill of T tokens for one (b, h) pair: the checkpoint read
+    and written once, every token's q, k, v, beta, alpha read, every output written."""
+    f = 4
+    return 2 * DV * DK * f + T * (2 * DK + DV + 2) * f + T * DV * f
+
+
+def gdn_prefill_flops(DV, DK, T) -> float:
+    """Matrix-core flops of one Gated DeltaNet prefill for one (b, h) pair, per 16-token chunk:
+    K S^T, Q S^T and the rank-16 update (2 * 16 * DV * DK each), K K^T and Q K^T (2 * 16 * 16 * DK
+    each), U = A T (2 * 16^3), U F, (U o R) V and T Z (2 * 16 * 16 * DV each)."""
+    chunks = (T + 15) // 16
+    return chunks * (3 * 2 * 16 * DV * DK + 2 * 2 * 256 * DK + 2 * 4096 + 3 * 2 * 256 * DV)
+
+
+def run_gdn_prefill(args, torch, rb, wl):
+    """Gated DeltaNet prefill: a T-token prompt per sequence into the checkpoint (batch 256, 32
+    heads, 128 x 128), against the conventional sequential scan (state read once, the T updates
+    applied in order in registers, state written once)."""
+    T = args.prompt
+    sh = wl.GDNShape(batch=args.batch or 256, nheads=32, d_k=128, d_v=128, window=16)
+    DV, DK, W, H, B = sh.d_v, sh.d_k, sh.window, sh.nheads, sh.batch
+    K, Wm, S = args.steps, args.warmup, 32
+    t0 = time.time()
+    s0 = torch.from_numpy(wl.gdn_state0(sh, 0)).cuda()
+    pool = [{k: torch.from_numpy(v[0]).cuda() for k, v in wl.gdn_token_inputs(sh, 0, s).items()}
+            for s in range(S)]
+    prompt = {k: torch.stack([pool[t % S][k] for t in range(T)]) for k in pool[0]}
+    del pool
+    gen_s = time.time() - t0
+    ctx = rb.Context("gdn", B, H, DV, DK, W)
+    o = torch.empty(T, B, H, DV, device="cuda")
+    ctx.init_checkpoint(s0)
+    for _ in range(Wm):
+        ctx.prefill(o, **prompt)
+    torch.cuda.synchronize()
+    ev = _events(torch, 2 * K)
+    for k in range(K):
+        ev[2 * k].record()
+        ctx.prefill(o, **prompt)
+        ev[2 * k + 1].record()
+    torch.cuda.synchronize()
+    ms = [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(K)]
+    pre_s = sum(ms) / 1e3
+    cfg = rb.make_config(rb.RSSM_GDN, B, H, H, DV, DK, W)
+    st = s0.clone()
+    for _ in range(Wm):
+        rb.step_baseline(cfg, st, o, **prompt)
+    torch.cuda.synchronize()
+    ev2 = _events(torch, 2)
+    ev2[0].record()
+    for _ in range(K):
+        rb.step_baseline(cfg, st, o, **prompt)
+    ev2[1].record()
+    torch.cuda.synchronize()
+    conv_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+    bytes_call = gdn_prefill_bytes(DV, DK, T) * B * H
+    flops_call = gdn_prefill_flops(DV, DK, T) * B * H
+    gbs = bytes_call * K / pre_s / 1e9
+    tfl = flops_call * K / pre_s / 1e12
+    hbm_frac, mfma_frac = gbs / HBM_PEAK_GBS, tfl / MFMA_FP32_PEAK_TFLOPS
+    bound_hbm = hbm_frac >= mfma_frac
+    return {
+        "metric": "SSM prefill tokens/s (prompt into the checkpoint) vs the conventional sequential scan",
+        "value": round(B * T * K / pre_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(1e3 * pre_s / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded; prompt token t is pool slot t mod 32 of the decode inputs)",
+        "config": {"workload": f"gdn_prefill_b{B}_h{H}_dk{DK}_dv{DV}_t{T}",
+                   "batch": B, "heads": H, "d_k": DK, "d_v": DV, "prompt": T},
+        "alg_gbs": round(gbs, 1), "mfma_tflops": round(tfl, 2),
+        "conventional_ms": round(1e3 * conv_s / K, 4),
+        "speedup_vs_conventional": round(conv_s / pre_s, 3),
+        "roofline": {"bound": "hbm" if bound_hbm else "mfma", "kernel": "k_gdn_prefill<128,128>",
+                     "achieved": round(gbs if bound_hbm else tfl, 2),
+                     "peak": HBM_PEAK_GBS if bound_hbm else MFMA_FP32_PEAK_TFLOPS,
+                     "unit": "GB/s" if bound_hbm else "TFLOP/s",
+                     "frac": round(hbm_frac if bound_hbm else mfma_frac, 4),
+                     "other": {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4)},
+                     "traffic": _traffic("gdn_prefill"), "alg_bytes_per_launch": round(bytes_call),
+                     "flops_per_launch": round(flops_call),
+                     "avg_launch_us": round(1e6 * pre_s / K, 2), "launches": K},
+        "input_gen_s": round(gen_s, 1),
+    }, sh
+
+
 def run_m2_fork(args, torch, rb, wl):
     """Per-sequence state copies at the Mamba-2 serving shape (batch 256, 128 heads, 64 x 128,
     W = 16, C kept): fork half of the sequences onto the other half, export them to a packed
@@ -699,8 +785,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="m2_serve",
                     choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve", "m2_prefill",
-                             "m2_fork"])
-    ap.add_argument("--prompt", type=int, default=512, help="prompt tokens (m2_prefill)")
+                             "gdn_prefill", "m2_fork"])
+    ap.add_argument("--prompt", type=int, default=512, help="prompt tokens (m2_prefill, gdn_prefill)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
     ap.add_argument("--groups", type=int, default=0,
                     help="Mamba-2 B/C groups (default: one per head)")
@@ -733,6 +819,15 @@ def main():
         line, (sh, prm) = run_m2_prefill(args, torch, rb, wl)
         if not args.no_cpu_baseline:
             cb = cpu_baseline_m2(sh, prm, wl)
+            cb["gbs_fp64_state"] = cb["value"]
+            cb["value"], cb["unit"] = cb["tokens_per_s"], "tokens/s"
+            line["cpu_baseline"] = cb
+    elif args.workload == "gdn_prefill":
+        args.steps = args.steps or 8
+        args.warmup = min(args.warmup, 2)
+        line, sh = run_gdn_prefill(args, torch, rb, wl)
+        if not args.no_cpu_baseline:
+            cb = cpu_baseline_gdn(sh, wl)
             cb["gbs_fp64_state"] = cb["value"]
             cb["value"], cb["unit"] = cb["tokens_per_s"], "tokens/s"
             line["cpu_baseline"] = cb

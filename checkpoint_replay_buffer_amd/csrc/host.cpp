@@ -351,14 +351,19 @@ rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *s
     rssm_status s = ready(ctx);
     if (s != RSSM_OK) return s;
     const rssm_config &c = ctx->cfg;
-    if (c.kind != RSSM_MAMBA2) return RSSM_E_UNSUPPORTED;
     if ((s = check_inputs(c, in)) != RSSM_OK) return s;
     if (!aligned16(y)) return RSSM_E_ARG;
     if (ctx->pending) return RSSM_E_STATE;
     if (ctx->hi > 0 && (s = rssm_consolidate(ctx, 1, stream)) != RSSM_OK) return s;
-    M2PrefillArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->A, ctx->D,
-                    in->x, in->B, in->C, in->dt, y, in->ntok};
-    s = launched(ctx, m2_prefill(a, ctx->S0b != nullptr, strm(stream)), true);
+    if (c.kind == RSSM_MAMBA2) {
+        M2PrefillArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->A, ctx->D,
+                        in->x, in->B, in->C, in->dt, y, in->ntok};
+        s = launched(ctx, m2_prefill(a, ctx->S0b != nullptr, strm(stream)), true);
+    } else {
+        GdnPrefillArgs a{gdndims(c), flip(ctx), ctx->S0, in->q, in->k, in->v, in->beta, in->alpha,
+                         y, in->ntok};
+        s = launched(ctx, gdn_prefill(a, strm(stream)), true);
+    }
     if (s == RSSM_OK) {
         ctx->lo = ctx->hi = 0;
         ctx->ulen = 0;

@@ -126,6 +126,16 @@ struct GdnFoldArgs {
     float *out;
 };
 
+// Gated DeltaNet prefill of T prompt tokens (token-major inputs) into the checkpoint.
+struct GdnPrefillArgs {
+    GdnDims d;
+    Bk bk;
+    float *S0;          // [B,H,dv,dk]
+    const float *q, *k, *v, *beta, *alpha;
+    float *o;           // [T,B,H,dv]
+    int T;
+};
+
 struct GdnRmwArgs {
     GdnDims d;
     float *state;
@@ -152,6 +162,7 @@ size_t gdn_lds_bytes(int DV, int DK, int W);
 hipError_t gdn_decode(const GdnStepArgs &a, int mode, hipStream_t s);   // mode as m2_decode
 hipError_t gdn_fold(const GdnFoldArgs &a, hipStream_t s);
 hipError_t gdn_rmw(const GdnRmwArgs &a, hipStream_t s);
+hipError_t gdn_prefill(const GdnPrefillArgs &a, hipStream_t s);
 
 hipError_t init_checkpoint(float *S0, uint16_t *S0b, const float *state, const int32_t *mask,
                            Bk bk, uint32_t *err, int B, int H, long tile_elems, hipStream_t s);

@@ -140,15 +140,16 @@ rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, voi
  * Requires no pending verify. */
 rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream);
 
-/* Prefill (Mamba-2): run T = in->ntok prompt tokens (in: x [T,B,H,P], B and C [T,B,G,N],
- * dt [T,B,H]) through the recurrence from each sequence's current state and make the final state
+/* Prefill: run T = in->ntok prompt tokens (Mamba-2 in: x [T,B,H,P], B and C [T,B,G,N],
+ * dt [T,B,H]; Gated DeltaNet in: q and k [T,B,H,dim_k], v [T,B,H,dim_v], beta and alpha [T,B,H])
+ * through the recurrence from each sequence's current state and make the final state
  * the checkpoint (ia.goatify.app article "NVIDIA y Princeton aceleran modelos hibridos...",
  * paragraph "ReplaySSM cambia que se almacena": the decode path starts from a checkpoint plus
  * recent inputs). y [T,B,H,dim_v] (required) receives every prompt token's output, the same as T
  * decode steps would give. Buffered entries are folded first (one consolidation launch when any
  * sequence may hold some); afterwards len = ndraft = 0 for every sequence and the bf16 read copy,
  * if any, is refreshed. The checkpoint is read and written once for the whole prompt. Requires no
- * pending verify (RSSM_E_STATE); RSSM_E_UNSUPPORTED for Gated DeltaNet. */
+ * pending verify (RSSM_E_STATE). */
 rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream);
 
 /* Speculative verify of K = in->ntok drafts (1 <= K <= max_draft): sequences whose drafts would
