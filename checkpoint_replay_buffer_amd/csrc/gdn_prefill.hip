@@ -23,10 +23,10 @@ namespace rssm {
 namespace {
 
 constexpr int kChunk = 16;
-constexpr int kGS = kChunk + 1, kTS = kChunk + 4;   // strides of the Gram and the T / A blocks
+constexpr int kTS = kChunk + 4;   // row stride of the 16 x 16 blocks in LDS
 
 // LDS floats: two staging buffers (q and k [16][d_k+4], v [16][d_v+4], beta and alpha [16]),
-// then the Gram [16][17], T [16][20] and A [16][20] of the current chunk
+// then the Gram, T, A and R blocks [16][20] and Gam [16] of the current chunk
 template <int DV, int DK>
 __host__ __device__ constexpr int gp_buf_floats()
 {
@@ -35,17 +35,52 @@ __host__ __device__ constexpr int gp_buf_floats()
 template <int DV, int DK>
 __host__ __device__ constexpr int gp_lds_floats()
 {
-    return 2 * gp_buf_floats<DV, DK>() + kChunk * kGS + 2 * kChunk * kTS;
+    return 2 * gp_buf_floats<DV, DK>() + 4 * kChunk * kTS + kChunk;
 }
 
-// prod_{lo < i <= hi} a[i] over the 16 decays of a chunk; lane-dependent bounds with constant
-// register indices (factors outside the range are exact ones)
-__device__ __forceinline__ float range_prod(const float (&a)[kChunk], int lo, int hi)
+// T of the chunk by forward substitution, T[t][q] = beta_t ([t == q] - sum_{i<t} G_it T[i][q]),
+// one column per lane (q = lane % 16) held in registers; the Gram rows and the betas are read
+// from LDS at addresses common to the wave. Padding rows have k = 0 and beta = 0, so their rows of
+// T are zero.
+__device__ __forceinline__ void chunk_t_solve(const float *sh_G, const float *sh_be, float *sh_T)
 {
-    float p = 1.f;
+    const int lane = threadIdx.x & 63, q = lane & 15;
+    float tq[kChunk];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) p *= (i > lo && i <= hi) ? a[i] : 1.f;
-    return p;
+    for (int t = 0; t < kChunk; ++t) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < t; ++i) acc = fmaf(sh_G[t * kTS + i], tq[i], acc);
+        tq[t] = sh_be[t] * ((t == q ? 1.f : 0.f) - acc);
+    }
+    if (lane < kChunk) {
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) sh_T[t * kTS + q] = tq[t];
+    }
+}
+
+// Decays of the chunk, lane t < 16: R[t][q] = prod_{q<i<=t} alpha_i (1 for q >= t), taken as a
+// running product from q = t down, and Gam_t = prod_{i<=t} alpha_i.
+__device__ __forceinline__ void chunk_decays(const float *sh_al, float *sh_R, float *sh_gam)
+{
+    const int t = threadIdx.x & 63;
+    float al[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; i += 4) {
+        const float4 x = ld4(sh_al + i);
+        al[i] = x.x; al[i + 1] = x.y; al[i + 2] = x.z; al[i + 3] = x.w;
+    }
+    float p = 1.f, row[kChunk];
+#pragma unroll
+    for (int q = kChunk - 1; q >= 0; --q) {
+        if (q < kChunk - 1 && q + 1 <= t) p *= al[q + 1];
+        row[q] = p;
+    }
+    if (t < kChunk) {
+#pragma unroll
+        for (int q = 0; q < kChunk; q += 4) st4(sh_R + t * kTS + q, make_float4(row[q], row[q + 1], row[q + 2], row[q + 3]));
+        sh_gam[t] = p * al[0];
+    }
 }
 
 // The chunk's q, k, v rows and beta, alpha held in registers between their load and their LDS
@@ -123,9 +158,11 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
     constexpr int NA = KB >= 4 ? 4 : KB;   // independent accumulators of the d_k products
     constexpr int BUF = gp_buf_floats<DV, DK>();
     extern __shared__ float smem[];
-    float *sh_G = smem + 2 * BUF;          // [16][kGS]  k_i . k_t
-    float *sh_T = sh_G + kChunk * kGS;     // [16][kTS]  T
+    float *sh_G = smem + 2 * BUF;          // [16][kTS]  k_i . k_t
+    float *sh_T = sh_G + kChunk * kTS;     // [16][kTS]  T
     float *sh_A = sh_T + kChunk * kTS;     // [16][kTS]  q_t . k_t' for t' <= t, else 0
+    float *sh_R = sh_A + kChunk * kTS;     // [16][kTS]  R[t][q]
+    float *sh_gam = sh_R + kChunk * kTS;   // [16]       Gam_t
 
     const int B = a.d.B, H = a.d.H, T = a.T;
     const int tile = blockIdx.x, b = tile / H, h = tile - b * H;
@@ -163,7 +200,50 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
                       a0 + t1 * BH, BH, T - (int)t1 < kChunk ? T - (int)t1 : kChunk, t);
         }
 
-        // 1. every wave: F = K S^T and Qs = Q S^T for its i-blocks (S at the chunk start)
+        // 1. the chunk's S-independent blocks first, so that their latency overlaps the other
+        //    waves' matrix work: wave 0 the Gram block and T, wave 1 the masked Q K^T, the last
+        //    wave the decays (one wave does all three when it is alone)
+        if (wv == 0) {
+            v4f gp[NA];
+#pragma unroll
+            for (int p = 0; p < NA; ++p) gp[p] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);   // A: K[c][k], B: K[c][k]
+                v4f &p = gp[kb % NA];
+                p = mfma4(kv.x, kv.x, p);
+                p = mfma4(kv.y, kv.y, p);
+                p = mfma4(kv.z, kv.z, p);
+                p = mfma4(kv.w, kv.w, p);
+            }
+            const v4f gk = tree_sum<NA>(gp);   // k_{4g+r} . k_c
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sh_G[(4 * g + r) * kTS + cl] = gk[r];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            chunk_t_solve(sh_G, sh_be, sh_T);
+        }
+        if (wv == (NW > 1 ? 1 : 0)) {
+            v4f ap[NA];
+#pragma unroll
+            for (int p = 0; p < NA; ++p) ap[p] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const float4 qv = ld4(sh_q + cl * KS + 16 * kb + 4 * g);   // A: Q[c][k]
+                const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);   // B: K[c][k]
+                v4f &p = ap[kb % NA];
+                p = mfma4(qv.x, kv.x, p);
+                p = mfma4(qv.y, kv.y, p);
+                p = mfma4(qv.z, kv.z, p);
+                p = mfma4(qv.w, kv.w, p);
+            }
+            const v4f qk = tree_sum<NA>(ap);   // q_{4g+r} . k_c
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sh_A[(4 * g + r) * kTS + cl] = cl <= 4 * g + r ? qk[r] : 0.f;
+        }
+        if (wv == NW - 1) chunk_decays(sh_al, sh_R, sh_gam);
+        //    every wave: F = K S^T and Qs = Q S^T for its i-blocks (S at the chunk start)
         v4f fz[IBW], qs[IBW];
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
@@ -188,67 +268,13 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
             qs[ib] = tree_sum<NA>(qp);     // (S q_t)[i] for t = 4 g + r
         }
         mfma_settle();
-        //    wave 0: the Gram block and T; wave 1 (wave 0 when alone): the masked Q K^T
-        if (wv == 0) {
-            v4f gp[NA];
-#pragma unroll
-            for (int p = 0; p < NA; ++p) gp[p] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);   // A: K[c][k], B: K[c][k]
-                v4f &p = gp[kb % NA];
-                p = mfma4(kv.x, kv.x, p);
-                p = mfma4(kv.y, kv.y, p);
-                p = mfma4(kv.z, kv.z, p);
-                p = mfma4(kv.w, kv.w, p);
-            }
-            const v4f gk = tree_sum<NA>(gp);   // k_{4g+r} . k_c
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sh_G[(4 * g + r) * kGS + cl] = gk[r];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const float bel = lane < kChunk ? sh_be[lane] : 0.f;
-            t_solve<64 / kChunk>(sh_G, kGS, bel, ct, kChunk, sh_T, kTS);
-        }
-        if (wv == (NW > 1 ? 1 : 0)) {
-            v4f ap[NA];
-#pragma unroll
-            for (int p = 0; p < NA; ++p) ap[p] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float4 qv = ld4(sh_q + cl * KS + 16 * kb + 4 * g);   // A: Q[c][k]
-                const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);   // B: K[c][k]
-                v4f &p = ap[kb % NA];
-                p = mfma4(qv.x, kv.x, p);
-                p = mfma4(qv.y, kv.y, p);
-                p = mfma4(qv.z, kv.z, p);
-                p = mfma4(qv.w, kv.w, p);
-            }
-            const v4f qk = tree_sum<NA>(ap);   // q_{4g+r} . k_c
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sh_A[(4 * g + r) * kTS + cl] = cl <= 4 * g + r ? qk[r] : 0.f;
-        }
         __syncthreads();
 
         // 2. decays per lane: R[t = c][q = 4 g + r], Gam of the output rows t = 4 g + r, the fold's
         //    R[15][q = 4 g + r] and gam
-        float alv[kChunk];
-#pragma unroll
-        for (int i = 0; i < kChunk; i += 4) {
-            const float4 x = ld4(sh_al + i);
-            alv[i] = x.x; alv[i + 1] = x.y; alv[i + 2] = x.z; alv[i + 3] = x.w;
-        }
-        float rr[4], gm[4], rf[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            rr[r] = range_prod(alv, 4 * g + r, cl);
-            gm[r] = range_prod(alv, -1, 4 * g + r);
-            rf[r] = range_prod(alv, 4 * g + r, kChunk - 1);
-        }
-        float gam = 1.f;
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) gam *= alv[i];
+        const float4 rr = ld4(sh_R + cl * kTS + 4 * g), gm = ld4(sh_gam + 4 * g);
+        const float4 rf = ld4(sh_R + (kChunk - 1) * kTS + 4 * g);
+        const float gam = sh_gam[kChunk - 1];
 
         // 3. U = A T, as U^T = T^T A^T so that lane (g, c) ends with U[t = c][q = 4 g + r], the A
         //    operand of U F
@@ -256,12 +282,9 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             ut = mfma4(sh_T[(4 * g + r) * kTS + cl], sh_A[cl * kTS + 4 * g + r], ut);
-        float ua[4], ur[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            ua[r] = ut[r];
-            ur[r] = ut[r] * rr[r];
-        }
+        const float ua[4] = {ut[0], ut[1], ut[2], ut[3]};
+        const float ur[4] = {ut[0] * rr.x, ut[1] * rr.y, ut[2] * rr.z, ut[3] * rr.w};
+        const float gmv[4] = {gm.x, gm.y, gm.z, gm.w}, rfv[4] = {rf.x, rf.y, rf.z, rf.w};
 
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
@@ -278,7 +301,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
             }
             float ov[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ov[r] = gm[r] * (qs[ib][r] - uf[r]) + uv[r];
+            for (int r = 0; r < 4; ++r) ov[r] = gmv[r] * (qs[ib][r] - uf[r]) + uv[r];
             // keep these reads next to their chains rather than sunk into the stores below
             asm volatile("" ::"v"(ov[0]), "v"(ov[1]), "v"(ov[2]), "v"(ov[3]));
             float *oc = o0 + (size_t)t0 * BH * DV + i;
@@ -288,7 +311,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
             // 5. fold of the chunk: Z = R[15] o V - gam F, C = T Z, S <- gam S + C^T K
             float zf[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) zf[r] = rf[r] * vq[r] - gam * fz[ib][r];
+            for (int r = 0; r < 4; ++r) zf[r] = rfv[r] * vq[r] - gam * fz[ib][r];
             const float4 tv = ld4(sh_T + cl * kTS + 4 * g);                  // T[t = c][4 g + r]
             v4f cz = {0.f, 0.f, 0.f, 0.f};
             cz = mfma4(tv.x, zf[0], cz);
