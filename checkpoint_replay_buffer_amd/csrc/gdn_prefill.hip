@@ -83,11 +83,19 @@ __device__ __forceinline__ void chunk_decays(const float *sh_al, float *sh_R, fl
     }
 }
 
+// Waves per (b, h) workgroup: 4 for 128 x 128 (two i-blocks per wave, so that two workgroups share
+// a compute unit and fill each other's barriers), else the tile's usual count.
+template <int DV, int DK>
+struct GpShape {
+    static constexpr int NW = DV * DK >= 128 * 128 ? 4 : TileShape<DV, DK>::TPB / 64;
+    static constexpr int TPB = 64 * NW;
+};
+
 // The chunk's q, k, v rows and beta, alpha held in registers between their load and their LDS
 // store; the lane-dependent part of each address is computed once per prompt.
 template <int DV, int DK>
 struct GdnRows {
-    static constexpr int TPB = TileShape<DV, DK>::TPB, KF = DK / 4, VF = DV / 4;
+    static constexpr int TPB = GpShape<DV, DK>::TPB, KF = DK / 4, VF = DV / 4;
     static constexpr int KQ = (kChunk * KF + TPB - 1) / TPB, VQ = (kChunk * VF + TPB - 1) / TPB;
     float4 q[KQ], k[KQ], v[VQ];
     float be, al;
@@ -151,9 +159,9 @@ struct GdnRows {
 };
 
 template <int DV, int DK>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPrefillArgs a)
+__global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPrefillArgs a)
 {
-    using F = MfmaTile<DV, DK>;
+    using F = MfmaTile<DV, DK, GpShape<DV, DK>::NW>;
     constexpr int NW = F::NW, IBW = F::IBW, KB = F::KB, KS = F::CS, VS = F::RS;
     constexpr int NA = KB >= 4 ? 4 : KB;   // independent accumulators of the d_k products
     constexpr int BUF = gp_buf_floats<DV, DK>();
@@ -179,7 +187,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
     float *S0 = a.S0 + bh * (size_t)(DV * DK);
 #pragma unroll
     for (int ib = 0; ib < IBW; ++ib) {
-        const float *src = S0 + mfma_tile_offset<DV, DK>(t, ib);
+        const float *src = S0 + mfma_tile_offset<DV, DK, F::NW>(t, ib);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
     }
@@ -335,7 +343,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
     // the final state is the new checkpoint; the ring is empty
 #pragma unroll
     for (int ib = 0; ib < IBW; ++ib) {
-        float *dst = S0 + mfma_tile_offset<DV, DK>(t, ib);
+        float *dst = S0 + mfma_tile_offset<DV, DK, F::NW>(t, ib);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) st4_nt(dst + 16 * kb, s[ib][kb]);
     }
@@ -349,7 +357,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_prefill(GdnPre
 template <int DV, int DK>
 hipError_t go_gdn_prefill(const GdnPrefillArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(TileShape<DV, DK>::TPB);
+    const dim3 grid(a.d.B * a.d.H), block(GpShape<DV, DK>::TPB);
     const size_t lds = 4 * (size_t)gp_lds_floats<DV, DK>();
     hipLaunchKernelGGL((k_gdn_prefill<DV, DK>), grid, block, lds, s, a);
     return hipGetLastError();

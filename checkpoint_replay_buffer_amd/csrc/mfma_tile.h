@@ -17,9 +17,9 @@
 
 namespace rssm {
 
-template <int ROWS, int COLS>
+template <int ROWS, int COLS, int NWAVES = TileShape<ROWS, COLS>::TPB / 64>
 struct MfmaTile {
-    static constexpr int TPB = TileShape<ROWS, COLS>::TPB, NW = TPB / 64;
+    static constexpr int TPB = 64 * NWAVES, NW = NWAVES;
     static constexpr int IB = ROWS / 16, KB = COLS / 16, IBW = IB / NW;   // i-blocks per wave
     static constexpr int RS = ROWS + 4, CS = COLS + 4;   // padded LDS strides of ROWS / COLS rows
     static_assert(IBW >= 1 && IBW * NW == IB, "tile map");
@@ -27,10 +27,10 @@ struct MfmaTile {
 
 // Element offset, inside a tile, of the float4 S[16 ib' + c][4 g] of thread t's i-block ib (add
 // 16 kb for k-block kb).
-template <int ROWS, int COLS>
+template <int ROWS, int COLS, int NWAVES = TileShape<ROWS, COLS>::TPB / 64>
 __device__ __forceinline__ int mfma_tile_offset(int t, int ib)
 {
-    using F = MfmaTile<ROWS, COLS>;
+    using F = MfmaTile<ROWS, COLS, NWAVES>;
     const int w = t >> 6, l = t & 63;
     return (16 * (w * F::IBW + ib) + (l & 15)) * COLS + 4 * (l >> 4);
 }
