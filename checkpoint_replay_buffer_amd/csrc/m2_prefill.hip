@@ -31,8 +31,10 @@ namespace rssm {
 namespace {
 
 constexpr int kChunk = 16;
+constexpr int kMS = kChunk + 4;   // row stride of the 16 x 16 blocks in LDS
 
-// LDS floats: two staging buffers, each x [16][P+4], B and C [16][N+4], dt [16]
+// LDS floats: two staging buffers, each x [16][P+4], B and C [16][N+4], dt [16]; then one 16 x 16
+// partial of B C^T per wave, the weights w[t][j] [16][20], w[15][j] [16] and Lam_t [16]
 template <int P, int N>
 __host__ __device__ constexpr int prefill_buf_floats()
 {
@@ -41,7 +43,7 @@ __host__ __device__ constexpr int prefill_buf_floats()
 template <int P, int N>
 __host__ __device__ constexpr int prefill_lds_floats()
 {
-    return 2 * prefill_buf_floats<P, N>();
+    return 2 * prefill_buf_floats<P, N>() + (MfmaTile<P, N>::NW + 1) * kChunk * kMS + 2 * kChunk;
 }
 
 // sum_{lo < i <= hi} d[i] over the 16 step sizes of a chunk, in increasing i. The indices are
@@ -53,6 +55,63 @@ __device__ __forceinline__ float range_sum(const float (&d)[kChunk], int lo, int
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) e += (i > lo && i <= hi) ? d[i] : 0.f;
     return e;
+}
+
+// Decay weights of the chunk, one wave; lane (g, c) takes t = c and j = 4 g + r:
+//     w[t][j] = dt_j exp(A sum_{j<i<=t} dt_i) (0 for j > t)  -> sh_wm[t][j]
+//     w[15][j], Lam_t = exp(A sum_{i<=t} dt_i) for t = 4 g + r   -> sh_wf, sh_lam (lanes c = 0)
+__device__ __forceinline__ void chunk_weights(const float *sh_dt, float Ah, float *sh_wm,
+                                              float *sh_wf, float *sh_lam)
+{
+    const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+    float d[kChunk];
+#pragma unroll
+    for (int q = 0; q < kChunk; q += 4) {
+        const float4 v = ld4(sh_dt + q);
+        d[q] = v.x; d[q + 1] = v.y; d[q + 2] = v.z; d[q + 3] = v.w;
+    }
+    // this lane's step sizes d[4 g .. 4 g + 3] without indexing d by a lane-dependent value
+    const float4 dq = ld4(sh_dt + 4 * g);
+    const float dg[4] = {dq.x, dq.y, dq.z, dq.w};
+    // sum_{j<i<=t} d_i for j = 4 g + r, by adding d_{j+1} to the sum from j + 1 down
+    float sm[4], su[4];
+    sm[3] = range_sum(d, 4 * g + 3, cl);            // upper end t = c
+    su[3] = range_sum(d, 4 * g + 3, kChunk - 1);    // upper end 15 (fold weights)
+#pragma unroll
+    for (int r = 2; r >= 0; --r) {
+        sm[r] = sm[r + 1] + (4 * g + r + 1 <= cl ? dg[r + 1] : 0.f);
+        su[r] = su[r + 1] + dg[r + 1];
+    }
+    float wm[4], wf[4], lam[4];
+    float pre = range_sum(d, -1, 4 * g - 1);        // sum_{i < 4 g} d_i
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        wm[r] = 4 * g + r <= cl ? dg[r] * expf(Ah * sm[r]) : 0.f;
+        wf[r] = dg[r] * expf(Ah * su[r]);
+        pre += dg[r];
+        lam[r] = expf(Ah * pre);                    // exp(A sum_{i <= 4 g + r} d_i)
+    }
+    st4(sh_wm + cl * kMS + 4 * g, make_float4(wm[0], wm[1], wm[2], wm[3]));
+    if (cl == 0) {
+        st4(sh_wf + 4 * g, make_float4(wf[0], wf[1], wf[2], wf[3]));
+        st4(sh_lam + 4 * g, make_float4(lam[0], lam[1], lam[2], lam[3]));
+    }
+}
+
+// Sum of the per-wave partials of B C^T, as a pairwise tree.
+template <int NW>
+__device__ __forceinline__ float4 sum_partials(const float4 (&p)[NW])
+{
+    if constexpr (NW == 1) {
+        return p[0];
+    } else {
+        float4 h[NW / 2];
+#pragma unroll
+        for (int w = 0; w < NW / 2; ++w)
+            h[w] = make_float4(p[2 * w].x + p[2 * w + 1].x, p[2 * w].y + p[2 * w + 1].y,
+                               p[2 * w].z + p[2 * w + 1].z, p[2 * w].w + p[2 * w + 1].w);
+        return sum_partials<NW / 2>(h);
+    }
 }
 
 // The chunk's rows of x, B, C and dt held in registers between their load and their LDS store.
@@ -118,16 +177,25 @@ struct ChunkRows {
     }
 };
 
-// One barrier per chunk: the chunk's rows (prefetched into registers during the previous chunk)
-// go to one of two LDS buffers; every wave then works from LDS and its registers only.
+// Two barriers per chunk: the chunk's rows (prefetched into registers during the previous chunk)
+// go to one of two LDS buffers; the waves then form the blocks that do not depend on the state
+// (B C^T split over the waves by k-blocks, the decay weights) next to their C S^T products, and
+// after the second barrier every wave has what it needs for its outputs and its part of the
+// update.
 template <int P, int N, bool BF16>
-__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2PrefillArgs a)
+__global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2PrefillArgs a)
 {
     using F = MfmaTile<P, N>;
-    constexpr int IBW = F::IBW, KB = F::KB, XS = F::RS, BS = F::CS;
+    constexpr int NW = F::NW, IBW = F::IBW, KB = F::KB, XS = F::RS, BS = F::CS;
     constexpr int NA = KB >= 4 ? 4 : KB;   // independent accumulators of the d_state products
+    constexpr int KBW = KB / NW;           // k-blocks of B C^T per wave
+    static_assert(KBW * NW == KB, "B C^T split");
     constexpr int BUF = prefill_buf_floats<P, N>();
     extern __shared__ float smem[];
+    float *sh_P = smem + 2 * BUF;          // [NW][16][kMS]  partials of B C^T
+    float *sh_wm = sh_P + NW * kChunk * kMS;   // [16][kMS]  w[t][j] (0 for j > t)
+    float *sh_wf = sh_wm + kChunk * kMS;   // [16]       w[15][j]
+    float *sh_lam = sh_wf + kChunk;        // [16]       Lam_t
 
     const int B = a.d.B, H = a.d.H, G = a.d.G, T = a.T;
     const int tile = blockIdx.x, b = tile / H, h = tile - b * H, g0 = h / (H / G);
@@ -167,64 +235,29 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2Prefill
                       T - (int)t1 < kChunk ? T - (int)t1 : kChunk, t);
         }
 
-        // 1. decay weights, per lane: M-operand weights w[t = c][j = 4 g + r], the decays Lam of
-        //    the output rows t = 4 g + r, and the decay of the whole chunk
-        float d[kChunk];
+        // 1. S-independent blocks first: every wave its share of B C^T (k-blocks wv KBW ..
+        //    wv KBW + KBW - 1), the last wave the decay weights of the chunk
+        {
+            v4f pp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < kChunk; q += 4) {
-            const float4 v = ld4(sh_dt + q);
-            d[q] = v.x; d[q + 1] = v.y; d[q + 2] = v.z; d[q + 3] = v.w;
+            for (int kq = 0; kq < KBW; ++kq) {
+                const int kb = wv * KBW + kq;
+                const float4 bv = ld4(sh_B + cl * BS + 16 * kb + 4 * g);   // A: B[j = c][k]
+                const float4 cv = ld4(sh_C + cl * BS + 16 * kb + 4 * g);   // B: C[t = c][k]
+                pp = mfma4(bv.x, cv.x, pp);
+                pp = mfma4(bv.y, cv.y, pp);
+                pp = mfma4(bv.z, cv.z, pp);
+                pp = mfma4(bv.w, cv.w, pp);
+            }
+            // register r of lane (g, c) holds B_{4g+r} . C_c over this share: stored at
+            // [c][4 g + r], where every wave's lane (g, c) reads it back
+            st4(sh_P + wv * kChunk * kMS + cl * kMS + 4 * g, make_float4(pp[0], pp[1], pp[2], pp[3]));
         }
-        // this lane's step sizes d[4 g .. 4 g + 3] without indexing d by a lane-dependent value
-        const float4 dq = ld4(sh_dt + 4 * g);
-        const float dg[4] = {dq.x, dq.y, dq.z, dq.w};
-        // sum_{j<i<=t} d_i for j = 4 g + r, by adding d_{j+1} to the sum from j + 1 down
-        float sm[4], su[4];
-        sm[3] = range_sum(d, 4 * g + 3, cl);            // upper end t = c (M operand)
-        su[3] = range_sum(d, 4 * g + 3, kChunk - 1);    // upper end 15 (fold weights)
-#pragma unroll
-        for (int r = 2; r >= 0; --r) {
-            sm[r] = sm[r + 1] + (4 * g + r + 1 <= cl ? dg[r + 1] : 0.f);
-            su[r] = su[r + 1] + dg[r + 1];
-        }
-        float wm[4], wf[4], lam[4];
-        float pre = range_sum(d, -1, 4 * g - 1);        // sum_{i < 4 g} d_i
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            wm[r] = 4 * g + r <= cl ? dg[r] * expf(Ah * sm[r]) : 0.f;
-            wf[r] = dg[r] * expf(Ah * su[r]);
-            pre += dg[r];
-            lam[r] = expf(Ah * pre);                    // exp(A sum_{i <= 4 g + r} d_i)
-        }
-        float tot = 0.f;
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) tot += d[i];
-        const float lam_end = expf(Ah * tot);
-
-        // 2. (B C^T)[j][t] on the matrix cores; its accumulator register r on lane (g, c) holds
-        //    B_{4g+r} . C_c, which is the A operand M[t = c][j = 4 g + r] of M X once weighted
-        v4f gp[NA];
-#pragma unroll
-        for (int q = 0; q < NA; ++q) gp[q] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const float4 bv = ld4(sh_B + cl * BS + 16 * kb + 4 * g);   // A: B[j = c][k]
-            const float4 cv = ld4(sh_C + cl * BS + 16 * kb + 4 * g);   // B: C[t = c][k]
-            v4f &q = gp[kb % NA];
-            q = mfma4(bv.x, cv.x, q);
-            q = mfma4(bv.y, cv.y, q);
-            q = mfma4(bv.z, cv.z, q);
-            q = mfma4(bv.w, cv.w, q);
-        }
-        const v4f bc = tree_sum<NA>(gp);
-        float ma[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ma[r] = wm[r] * bc[r];
-
+        if (wv == NW - 1) chunk_weights(sh_dt, Ah, sh_wm, sh_wf, sh_lam);
+        //    every wave: Z = C S^T for its i-blocks (S at the chunk start)
+        v4f z[IBW];
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
-            const int i = 16 * (wv * IBW + ib) + cl;
-            // 3. Z = C S^T (S at the chunk start)
             v4f zp[NA];
 #pragma unroll
             for (int q = 0; q < NA; ++q) zp[q] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -237,8 +270,27 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2Prefill
                 q = mfma4(cv.z, s[ib][kb].z, q);
                 q = mfma4(cv.w, s[ib][kb].w, q);
             }
-            const v4f z = tree_sum<NA>(zp);  // (S C_tt)[i] for tt = 4 g + r, i = 16 ib' + c
-            // 4. Y = Lam o Z + M X + D X
+            z[ib] = tree_sum<NA>(zp);        // (S C_tt)[i] for tt = 4 g + r, i = 16 ib' + c
+        }
+        mfma_settle();
+        __syncthreads();
+
+        // 2. M[t = c][j = 4 g + r] = w[t][j] (B_j . C_t), the A operand of M X; Lam of the output
+        //    rows t = 4 g + r; the fold weights w[15][j = 4 g + r] and Lam_15
+        float4 bcs[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) bcs[w] = ld4(sh_P + w * kChunk * kMS + cl * kMS + 4 * g);
+        const float4 bc = sum_partials<NW>(bcs);
+        const float4 wm = ld4(sh_wm + cl * kMS + 4 * g);
+        const float ma[4] = {wm.x * bc.x, wm.y * bc.y, wm.z * bc.z, wm.w * bc.w};
+        const float4 lm = ld4(sh_lam + 4 * g), wq = ld4(sh_wf + 4 * g);
+        const float lam[4] = {lm.x, lm.y, lm.z, lm.w}, wf[4] = {wq.x, wq.y, wq.z, wq.w};
+        const float lam_end = sh_lam[kChunk - 1];
+
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib) {
+            const int i = 16 * (wv * IBW + ib) + cl;
+            // 3. Y = Lam o Z + M X + D X
             float xj[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) xj[r] = sh_x[(4 * g + r) * XS + i];   // X[j = 4 g + r][i]
@@ -249,7 +301,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2Prefill
             acc = mfma4(ma[3], xj[3], acc);
             float yv[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) yv[r] = lam[r] * z[r] + acc[r] + Dh * xj[r];
+            for (int r = 0; r < 4; ++r) yv[r] = lam[r] * z[ib][r] + acc[r] + Dh * xj[r];
             // keep the reads of the accumulators here, next to their chains, rather than sunk into
             // the conditional stores below
             asm volatile("" ::"v"(yv[0]), "v"(yv[1]), "v"(yv[2]), "v"(yv[3]));
@@ -259,7 +311,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_prefill(M2Prefill
                 const int tt = 4 * g + r;
                 if (tt < ct) yc[(size_t)tt * BH * P] = yv[r];
             }
-            // 5. S <- Lam_15 S + B^T (w X): B operand w[15][j] x_j[i] for j = 4 g + r
+            // 4. S <- Lam_15 S + B^T (w X): B operand w[15][j] x_j[i] for j = 4 g + r
             float wx[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) wx[r] = wf[r] * xj[r];
