@@ -85,6 +85,29 @@ def _traffic(kernel_key: str):
     return e.get("bytes_per_launch")
 
 
+def _graph_time(torch, nsteps, step, reps_warm, reps):
+    """Capture `nsteps` consecutive calls step(t) into one HIP graph (torch's capture stream; the
+    library launches on torch's current stream), replay it reps_warm times, then time `reps`
+    replays between two events. Returns the timed milliseconds."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for t in range(nsteps):
+            step(t)
+    for _ in range(reps_warm):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for _ in range(reps):
+        g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    del g
+    return ms
+
+
 def run_m2(args, torch, rb, wl):
     bf16 = args.workload == "m2_serve_bf16"
     batch = args.batch or 256
@@ -117,15 +140,16 @@ def run_m2(args, torch, rb, wl):
     torch.cuda.synchronize()
 
     # timed region: K steps bracketed by events only (wall time of the whole job)
-    ev = _events(torch, 2)
-    ev[0].record()
-    for t in range(K):
-        ctx.decode_step(y, **pool[t % pool_n])
-    ev[1].record()
-    torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[1])
-    h, l, n, e = ctx.bookkeeping()
-    assert e == 0 and l[0] == K % W, "unexpected bookkeeping after the timed steps"
+    if not args.graph:
+        ev = _events(torch, 2)
+        ev[0].record()
+        for t in range(K):
+            ctx.decode_step(y, **pool[t % pool_n])
+        ev[1].record()
+        torch.cuda.synchronize()
+        total_ms = ev[0].elapsed_time(ev[1])
+        h, l, n, e = ctx.bookkeeping()
+        assert e == 0 and l[0] == K % W, "unexpected bookkeeping after the timed steps"
 
     # the same K steps again with an event pair around every launch (per-kernel durations on the
     # stream the kernels run on)
@@ -139,6 +163,15 @@ def run_m2(args, torch, rb, wl):
     torch.cuda.synchronize()
     launch_ms = [evl[2 * t].elapsed_time(evl[2 * t + 1]) for t in range(K)]
 
+    if args.graph:
+        # the timed steps as replays of one captured window of pool_n = 2 W decode steps from an
+        # empty ring (the window ends where it started: same ring position, same bookkeeping buffer)
+        ctx.init_checkpoint(s0)
+        total_ms = _graph_time(torch, pool_n, lambda t: ctx.decode_step(y, **pool[t]), 1,
+                               K // pool_n)
+        h, l, n, e = ctx.bookkeeping()
+        assert e == 0 and l[0] == 0, "unexpected bookkeeping after the graph replays"
+
     alg_bytes = sum(m2_replay_bytes(P, N, W, gr, t % W, True, bf16) for t in range(K)) * B * H
     state_bytes = sum((2 * P * N * 4 if t % W == W - 1 else P * N * (2 if bf16 else 4))
                       for t in range(K)) * B * H
@@ -150,17 +183,22 @@ def run_m2(args, torch, rb, wl):
         cfg = rb.make_config(rb.RSSM_MAMBA2, B, H, sh.ngroups, P, N, W)
         st = s0.clone()
         y1 = torch.empty(1, B, H, P, device="cuda")
+        pool1 = [{k: v.unsqueeze(0) for k, v in pool[t].items()} for t in range(pool_n)]
         for t in range(Wm):
-            rb.step_baseline(cfg, st, y1, A, D, **{k: v.unsqueeze(0) for k, v in pool[t % pool_n].items()})
+            rb.step_baseline(cfg, st, y1, A, D, **pool1[t % pool_n])
         st.copy_(s0)
         torch.cuda.synchronize()
-        ev2 = _events(torch, 2)
-        ev2[0].record()
-        for t in range(K):
-            rb.step_baseline(cfg, st, y1, A, D, **{k: v.unsqueeze(0) for k, v in pool[t % pool_n].items()})
-        ev2[1].record()
-        torch.cuda.synchronize()
-        rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+        if args.graph:
+            rmw_s = _graph_time(torch, pool_n, lambda t: rb.step_baseline(cfg, st, y1, A, D, **pool1[t]),
+                                1, K // pool_n) / 1e3
+        else:
+            ev2 = _events(torch, 2)
+            ev2[0].record()
+            for t in range(K):
+                rb.step_baseline(cfg, st, y1, A, D, **pool1[t % pool_n])
+            ev2[1].record()
+            torch.cuda.synchronize()
+            rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
         del st
 
     # dominant kernel: the replay-only decode launches (no sequence folds); the launches whose
@@ -186,9 +224,11 @@ def run_m2(args, torch, rb, wl):
         "dtype": "bf16-read/fp32" if bf16 else "fp32",
         "data": "synthetic (seeded N(0,1) x, N(0,1)/sqrt(N) B and C, softplus(N(-2,0.5)) dt)",
         "config": {"workload": f"mamba2_decode_b{B}_h{H}_p{P}_n{N}_w{W}"
-                               + (f"_g{sh.ngroups}" if sh.ngroups != H else "") + ("_bf16read" if bf16 else ""),
+                               + (f"_g{sh.ngroups}" if sh.ngroups != H else "") + ("_bf16read" if bf16 else "")
+                               + ("_graph" if args.graph else ""),
                    "batch": B, "heads": H, "head_dim": P, "d_state": N, "window": W,
-                   "groups": sh.ngroups, "input_pool_slots": pool_n},
+                   "groups": sh.ngroups, "input_pool_slots": pool_n,
+                   "launch": "hip graph of 2 W steps, replayed" if args.graph else "eager"},
         "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
         "state_gbs": round(state_bytes / replay_s / 1e9, 1),
         "tokens_per_s": round(B * K / replay_s, 1),
@@ -604,7 +644,7 @@ def run_m2_fork(args, torch, rb, wl):
 
 def run_gdn(args, torch, rb, wl):
     """Gated DeltaNet decode: batch 256, 32 heads, d_k = d_v = 128, W = 16."""
-    sh = wl.GDN_SERVE
+    sh = wl.GDNShape(batch=args.batch or 256, nheads=32, d_k=128, d_v=128, window=16)
     DV, DK, W, H, B = sh.d_v, sh.d_k, sh.window, sh.nheads, sh.batch
     K, Wm, S = args.steps, args.warmup, 32
     t0 = time.time()
@@ -621,13 +661,14 @@ def run_gdn(args, torch, rb, wl):
         ctx.decode_step(o, **pool[t % S])
     ctx.init_checkpoint(s0)
     torch.cuda.synchronize()
-    ev = _events(torch, 2)
-    ev[0].record()
-    for t in range(K):
-        ctx.decode_step(o, **pool[t % S])
-    ev[1].record()
-    torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[1])
+    if not args.graph:
+        ev = _events(torch, 2)
+        ev[0].record()
+        for t in range(K):
+            ctx.decode_step(o, **pool[t % S])
+        ev[1].record()
+        torch.cuda.synchronize()
+        total_ms = ev[0].elapsed_time(ev[1])
     ctx.init_checkpoint(s0)
     torch.cuda.synchronize()
     evl = _events(torch, 2 * K)
@@ -637,21 +678,30 @@ def run_gdn(args, torch, rb, wl):
         evl[2 * t + 1].record()
     torch.cuda.synchronize()
     launch_ms = [evl[2 * t].elapsed_time(evl[2 * t + 1]) for t in range(K)]
+    if args.graph:
+        ctx.init_checkpoint(s0)
+        total_ms = _graph_time(torch, S, lambda t: ctx.decode_step(o, **pool[t]), 1, K // S)
+        h, l, n, e = ctx.bookkeeping()
+        assert e == 0 and l[0] == 0, "unexpected bookkeeping after the graph replays"
     alg = sum(gdn_bytes(DV, DK, W, t % W) for t in range(K)) * B * H
     cfg = rb.make_config(rb.RSSM_GDN, B, H, H, DV, DK, W)
     st = s0.clone()
     o1 = torch.empty(1, B, H, DV, device="cuda")
+    pool1 = [{k: v.unsqueeze(0) for k, v in pool[t].items()} for t in range(S)]
     for t in range(Wm):
-        rb.step_baseline(cfg, st, o1, **{k: v.unsqueeze(0) for k, v in pool[t % S].items()})
+        rb.step_baseline(cfg, st, o1, **pool1[t % S])
     st.copy_(s0)
     torch.cuda.synchronize()
-    ev2 = _events(torch, 2)
-    ev2[0].record()
-    for t in range(K):
-        rb.step_baseline(cfg, st, o1, **{k: v.unsqueeze(0) for k, v in pool[t % S].items()})
-    ev2[1].record()
-    torch.cuda.synchronize()
-    rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+    if args.graph:
+        rmw_s = _graph_time(torch, S, lambda t: rb.step_baseline(cfg, st, o1, **pool1[t]), 1, K // S) / 1e3
+    else:
+        ev2 = _events(torch, 2)
+        ev2[0].record()
+        for t in range(K):
+            rb.step_baseline(cfg, st, o1, **pool1[t % S])
+        ev2[1].record()
+        torch.cuda.synchronize()
+        rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
     rmw_bytes = (2 * DV * DK * 4 + (2 * DK + DV + 2) * 4 + DV * 4) * B * H * K
     rep = [t for t in range(K) if t % W != W - 1]
     fol = [t for t in range(K) if t % W == W - 1]
@@ -666,8 +716,9 @@ def run_gdn(args, torch, rb, wl):
         "warmup": Wm, "ms_per_step": round(total_ms / K, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
         "data": "synthetic (seeded; q, k L2-normalised N(0,1), v N(0,1), beta sigmoid, alpha exp(-softplus))",
-        "config": {"workload": f"gdn_decode_b{B}_h{H}_dk{DK}_dv{DV}_w{W}", "batch": B, "heads": H,
-                   "d_k": DK, "d_v": DV, "window": W, "input_pool_slots": S},
+        "config": {"workload": f"gdn_decode_b{B}_h{H}_dk{DK}_dv{DV}_w{W}" + ("_graph" if args.graph else ""),
+                   "batch": B, "heads": H, "d_k": DK, "d_v": DV, "window": W, "input_pool_slots": S,
+                   "launch": "hip graph of 2 W steps, replayed" if args.graph else "eager"},
         "pct_hbm_peak": round(100 * alg / replay_s / 1e9 / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(B * K / replay_s, 1),
         "rmw_ms_per_step": round(rmw_s * 1e3 / K, 5),
@@ -790,6 +841,8 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
     ap.add_argument("--groups", type=int, default=0,
                     help="Mamba-2 B/C groups (default: one per head)")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode legs: time replays of a captured HIP graph of 2 W steps (both paths)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rmw", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -809,6 +862,8 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy(torch)
+    if args.graph and args.steps:
+        args.steps = (args.steps + 31) // 32 * 32     # whole captured windows of 32 steps
     if args.workload == "m2_spec":
         line, (sh, prm) = run_m2_spec(args, torch, rb, wl)
         if not args.no_cpu_baseline:
