@@ -569,7 +569,7 @@ def normwise_err(got, ref, head_floor=None) -> float:
 
     With head_floor (arrays [..., H, P]: the heads of one sequence-token in the last two axes),
     each head vector's denominator is at least head_floor times the largest |ref| over all heads of
-    the same sequence-token: a head whose output nearly cancels is judged against the scale of the
+    the same sequence-token: a head whose output nearly cancels is measured against the scale of the
     layer output it belongs to rather than against its own near-zero magnitude."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

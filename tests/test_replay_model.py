@@ -258,7 +258,7 @@ def test_replay_model_follows_golden_trace(oracle_lib):
 
 def test_normwise_head_floor():
     """The head floor changes only heads whose output is small next to the sequence-token's
-    largest head: a near-cancelled head is judged against the layer scale."""
+    largest head: a near-cancelled head is measured against the layer scale."""
     from oracle import normwise_err
     ref = np.array([[[1.0, -2.0], [1e-4, 2e-4]]])          # [token, H=2, P=2]
     got = ref.copy()
