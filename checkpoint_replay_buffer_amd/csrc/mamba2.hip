@@ -65,10 +65,22 @@ struct Tile {
     float Ah, Dh;
 };
 
-__device__ __forceinline__ Tile make_tile(const M2Dims &d, const float *A, const float *D)
+// Tile of workgroup w out of n that keeps each XCD on a contiguous range of tiles: workgroups are
+// dispatched round-robin over the 8 XCDs (w runs on XCD w % 8), so XCD k takes tiles
+// [k n/8, (k+1) n/8); the last n % 8 workgroups keep their own index. A bijection.
+__device__ __forceinline__ int xcd_tile(int w, int n)
+{
+    const int per = n / 8;
+    return w < 8 * per ? (w % 8) * per + w / 8 : w;
+}
+
+// xcd: contiguous tile ranges per XCD, for the launches that fold (their read-and-write streams
+// ran 4-7 % faster that way; the replay-only launches did not gain)
+__device__ __forceinline__ Tile make_tile(const M2Dims &d, const float *A, const float *D,
+                                          bool xcd = false)
 {
     Tile c;
-    const int tile = blockIdx.x;
+    const int tile = xcd ? xcd_tile(blockIdx.x, d.B * d.H) : (int)blockIdx.x;
     c.b = tile / d.H;
     c.h = tile - c.b * d.H;
     const int hpg = d.H / d.G;
@@ -380,7 +392,7 @@ template <int P, int N, bool BF16, int MODE>
 __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs a)
 {
     extern __shared__ float smem[];
-    const Tile c = make_tile(a.d, a.A, a.D);
+    const Tile c = make_tile(a.d, a.A, a.D, MODE == kMayFold);
     const int B = a.d.B, W = c.W;
     bool fold = false;
     int head, len;
@@ -432,7 +444,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_fold(M2FoldArgs a
     constexpr int TPB = TileShape<P, N>::TPB;
     using M = RowMap<P, N, TPB, 4>;
     extern __shared__ float smem[];
-    const Tile c = make_tile(a.d, a.A, nullptr);
+    const Tile c = make_tile(a.d, a.A, nullptr, true);
     const int B = a.d.B, W = c.W;
     const int head = a.bk.in[c.b];
     const int len = a.bk.in[B + c.b];
