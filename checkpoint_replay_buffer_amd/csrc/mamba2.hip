@@ -65,22 +65,32 @@ struct Tile {
     float Ah, Dh;
 };
 
-// Tile of workgroup w out of n that keeps each XCD on a contiguous range of tiles: workgroups are
-// dispatched round-robin over the 8 XCDs (w runs on XCD w % 8), so XCD k takes tiles
-// [k n/8, (k+1) n/8); the last n % 8 workgroups keep their own index. A bijection.
-__device__ __forceinline__ int xcd_tile(int w, int n)
+// Tile order. Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on XCD
+// w % 8), each with its own L2. Two orders keep an XCD's workgroups on neighbouring tiles; the
+// tiles of a last incomplete round keep their own index, so both are bijections:
+//   kRuns:       XCD x takes runs of kRunTiles consecutive tiles (2 MiB of fp32 checkpoint at
+//                64 x 128), the XCDs interleaved run by run;
+//   kContiguous: XCD x takes one range of n / 8 consecutive tiles.
+// Same-box A/B at the serving shape: kRuns for the launches that only read the checkpoint, and
+// kContiguous for the launches that fold (read and write it), measured fastest.
+enum TileOrder { kRuns = 0, kContiguous = 1 };
+constexpr int kRunTiles = 64;
+
+__device__ __forceinline__ int tile_of(int w, int n, TileOrder order)
 {
-    const int per = n / 8;
-    return w < 8 * per ? (w % 8) * per + w / 8 : w;
+    if (order == kContiguous) {
+        const int per = n / 8;
+        return w < 8 * per ? (w % 8) * per + w / 8 : w;
+    }
+    const int full = n / (8 * kRunTiles) * (8 * kRunTiles), j = w / 8;
+    return w < full ? ((j / kRunTiles) * 8 + w % 8) * kRunTiles + j % kRunTiles : w;
 }
 
-// xcd: contiguous tile ranges per XCD, for the launches that fold (their read-and-write streams
-// ran 4-7 % faster that way; the replay-only launches did not gain)
 __device__ __forceinline__ Tile make_tile(const M2Dims &d, const float *A, const float *D,
-                                          bool xcd = false)
+                                          TileOrder order)
 {
     Tile c;
-    const int tile = xcd ? xcd_tile(blockIdx.x, d.B * d.H) : (int)blockIdx.x;
+    const int tile = tile_of(blockIdx.x, d.B * d.H, order);
     c.b = tile / d.H;
     c.h = tile - c.b * d.H;
     const int hpg = d.H / d.G;
@@ -392,7 +402,7 @@ template <int P, int N, bool BF16, int MODE>
 __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs a)
 {
     extern __shared__ float smem[];
-    const Tile c = make_tile(a.d, a.A, a.D, MODE == kMayFold);
+    const Tile c = make_tile(a.d, a.A, a.D, MODE == kMayFold ? kContiguous : kRuns);
     const int B = a.d.B, W = c.W;
     bool fold = false;
     int head, len;
@@ -444,7 +454,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_fold(M2FoldArgs a
     constexpr int TPB = TileShape<P, N>::TPB;
     using M = RowMap<P, N, TPB, 4>;
     extern __shared__ float smem[];
-    const Tile c = make_tile(a.d, a.A, nullptr, true);
+    const Tile c = make_tile(a.d, a.A, nullptr, kContiguous);
     const int B = a.d.B, W = c.W;
     const int head = a.bk.in[c.b];
     const int len = a.bk.in[B + c.b];
@@ -620,7 +630,7 @@ template <int P, int N, bool BF16>
 __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_verify(M2StepArgs a)
 {
     extern __shared__ float smem[];
-    const Tile c = make_tile(a.d, a.A, a.D);
+    const Tile c = make_tile(a.d, a.A, a.D, kRuns);
     const int B = a.d.B, W = c.W, K = a.ntok;
     const int head = a.bk.in[c.b];
     const int len = a.bk.in[B + c.b];
@@ -656,7 +666,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_rmw(M2RmwArgs a)
     constexpr int TPB = TileShape<P, N>::TPB;
     using M = RowMap<P, N, TPB, 4>;
     constexpr int R = M::R, LPR = M::LPR;
-    const Tile c = make_tile(a.d, a.A, a.D);
+    const Tile c = make_tile(a.d, a.A, a.D, kRuns);
     const int t = c.t;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
     const size_t BH = (size_t)a.d.B * a.d.H, BG = (size_t)a.d.B * a.d.G, PN = (size_t)P * N;
