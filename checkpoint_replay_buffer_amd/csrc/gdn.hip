@@ -22,6 +22,7 @@
 // in which every decay factor is at most 1. S0 K^T, T Z and C^T K run on the matrix cores.
 #include "dev_common.h"
 #include "internal.h"
+#include "tile_order.h"
 #include "mfma_tile.h"
 
 namespace rssm {
@@ -32,10 +33,12 @@ struct GTile {
     size_t bh, rh;
 };
 
-__device__ __forceinline__ GTile make_gtile(const GdnDims &d)
+// The replay launches and the conventional comparator take runs of tiles per XCD; the launches
+// that fold keep the identity order (contiguous ranges per XCD measured no faster there).
+__device__ __forceinline__ GTile make_gtile(const GdnDims &d, TileOrder order)
 {
     GTile c;
-    const int tile = blockIdx.x;
+    const int tile = tile_of(blockIdx.x, d.B * d.H, order, run_tiles(d.DV * d.DK));
     c.b = tile / d.H;
     c.h = tile - c.b * d.H;
     c.t = threadIdx.x;
@@ -496,7 +499,7 @@ k_gdn_decode(GdnStepArgs a)
 {
     using M = Map4<DV, DK>;
     extern __shared__ float smem[];
-    const GTile c = make_gtile(a.d);
+    const GTile c = make_gtile(a.d, MODE == 2 ? kIdentity : kRuns);
     const int B = a.d.B, W = c.W;
     float4 s[M::R];
     int head, len;
@@ -536,7 +539,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_fold(GdnFoldAr
     constexpr int TPB = TileShape<DV, DK>::TPB;
     using M = Map4<DV, DK>;
     extern __shared__ float smem[];
-    const GTile c = make_gtile(a.d);
+    const GTile c = make_gtile(a.d, kIdentity);
     const int B = a.d.B, W = c.W;
     const int head = a.bk.in[c.b];
     const int len = a.bk.in[B + c.b];
@@ -566,7 +569,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
     using M = Map4<DV, DK>;
     constexpr int R = M::R, LPR = M::LPR;
     __shared__ float sh_sk[DV];
-    const GTile c = make_gtile(a.d);
+    const GTile c = make_gtile(a.d, kRuns);
     const int t = c.t;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
     const size_t BH = (size_t)a.d.B * a.d.H;

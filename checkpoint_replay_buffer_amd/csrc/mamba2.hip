@@ -17,6 +17,7 @@
 // reduce-scatter butterfly over the lanes of a row.
 #include "dev_common.h"
 #include "internal.h"
+#include "tile_order.h"
 
 namespace rssm {
 namespace {
@@ -65,32 +66,13 @@ struct Tile {
     float Ah, Dh;
 };
 
-// Tile order. Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on XCD
-// w % 8), each with its own L2. Two orders keep an XCD's workgroups on neighbouring tiles; the
-// tiles of a last incomplete round keep their own index, so both are bijections:
-//   kRuns:       XCD x takes runs of kRunTiles consecutive tiles (2 MiB of fp32 checkpoint at
-//                64 x 128), the XCDs interleaved run by run;
-//   kContiguous: XCD x takes one range of n / 8 consecutive tiles.
-// Same-box A/B at the serving shape: kRuns for the launches that only read the checkpoint, and
-// kContiguous for the launches that fold (read and write it), measured fastest.
-enum TileOrder { kRuns = 0, kContiguous = 1 };
-constexpr int kRunTiles = 64;
-
-__device__ __forceinline__ int tile_of(int w, int n, TileOrder order)
-{
-    if (order == kContiguous) {
-        const int per = n / 8;
-        return w < 8 * per ? (w % 8) * per + w / 8 : w;
-    }
-    const int full = n / (8 * kRunTiles) * (8 * kRunTiles), j = w / 8;
-    return w < full ? ((j / kRunTiles) * 8 + w % 8) * kRunTiles + j % kRunTiles : w;
-}
-
+// The launches that only read the checkpoint take runs of tiles per XCD, the launches that fold
+// (read and write it) one contiguous range per XCD: each measured fastest in same-box A/B runs.
 __device__ __forceinline__ Tile make_tile(const M2Dims &d, const float *A, const float *D,
                                           TileOrder order)
 {
     Tile c;
-    const int tile = tile_of(blockIdx.x, d.B * d.H, order);
+    const int tile = tile_of(blockIdx.x, d.B * d.H, order, run_tiles(d.P * d.N));
     c.b = tile / d.H;
     c.h = tile - c.b * d.H;
     const int hpg = d.H / d.G;
