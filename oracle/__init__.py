@@ -155,6 +155,24 @@ def m2_spec_round(A, D, drafts: dict, state: np.ndarray, accepted) -> np.ndarray
     return np.stack(ys)
 
 
+def gdn_spec_round(drafts: dict, state: np.ndarray, accepted) -> np.ndarray:
+    """Gated DeltaNet counterpart of m2_spec_round: from the committed ``state`` [B,H,dv,dk] run
+    the K drafts (q, k, v, beta, alpha with a leading K axis) conventionally, keep per sequence b
+    the state after ``accepted[b]`` drafts; ``state`` is updated in place; returns o [K,B,H,dv]."""
+    K = drafts["q"].shape[0]
+    acc = np.asarray(accepted)
+    work = state.copy()
+    keep = state.copy()
+    os_ = []
+    for k in range(K):
+        os_.append(gdn_step(drafts["q"][k], drafts["k"][k], drafts["v"][k], drafts["beta"][k],
+                            drafts["alpha"][k], work))
+        sel = acc == k + 1
+        keep[sel] = work[sel]
+    state[...] = keep
+    return np.stack(os_)
+
+
 def token(inputs: dict, t: int) -> dict:
     """Token ``t`` of a dict of arrays with a leading token axis."""
     return {k: v[t] for k, v in inputs.items()}
@@ -459,6 +477,11 @@ def gdn_replay_output(S0, ks, vs, betas, alphas, q):
     and for j = m..1 take c_j = k_j . r, add (prod_{i>j} alpha_i) beta_j c_j v_j to the output and
     replace r by r - beta_j c_j k_j; finally add (prod_i alpha_i) S0 r.
     """
+    # every operand in fp64: a float32 array times a Python float stays float32 under NumPy's
+    # promotion rules
+    S0 = np.asarray(S0, dtype=np.float64)
+    ks = np.asarray(ks, dtype=np.float64)
+    vs = np.asarray(vs, dtype=np.float64)
     r = np.array(q, dtype=np.float64)
     acc = np.zeros(S0.shape[0])
     later = 1.0

@@ -16,7 +16,8 @@ import pytest
 
 import workloads as wl
 from oracle import (Bookkeeping, GDNReplay, M2Replay, StateError, gdn_conventional, gdn_step,
-                    gdn_wy_fold, m2_conventional, m2_spec_round, m2_step, normwise_err, token)
+                    gdn_wy_fold, m2_conventional, m2_spec_round, m2_step, normwise_err, token,
+                    gdn_spec_round, gdn_replay_output)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -170,6 +171,32 @@ def test_gdn_replay_equals_conventional(oracle_lib, W):
     o = np.stack([rp.decode(t) for t in _toks(ins)])
     assert normwise_err(o, o_ref) < 1e-12
     assert normwise_err(rp.materialize(), st_ref) < 1e-12
+
+
+def test_gdn_spec_round_pins(oracle_lib):
+    """Each draft's output of the recomputed round equals the replay formula applied to the
+    committed state with drafts 0..k as the only entries (a different formulation of the same
+    state); all drafts accepted equals K conventional steps; none accepted leaves the state."""
+    sh = wl.GDNShape(batch=3, nheads=2, d_k=8, d_v=6, window=8)
+    s0 = wl.gdn_state0(sh, 3).astype(np.float64)
+    K = 4
+    d = wl.gdn_token_inputs(sh, 3, 0, ntok=K)
+    st = s0.copy()
+    acc = np.array([K, 0, 2])
+    o = gdn_spec_round(d, st, acc)
+    for b in range(sh.batch):
+        for h in range(sh.nheads):
+            for k in range(K):
+                ref = gdn_replay_output(s0[b, h], d["k"][:k + 1, b, h], d["v"][:k + 1, b, h],
+                                        d["beta"][:k + 1, b, h], d["alpha"][:k + 1, b, h],
+                                        d["q"][k, b, h])
+                assert np.abs(o[k, b, h] - ref).max() < 1e-12 * max(1.0, np.abs(ref).max())
+    o_all, st_all = gdn_conventional(_toks(d), s0)
+    assert np.array_equal(o, o_all)
+    assert np.array_equal(st[0], st_all[0])           # all accepted
+    assert np.array_equal(st[1], s0[1])               # none accepted
+    o2, st2 = gdn_conventional(_toks({k: v[:2] for k, v in d.items()}), s0)
+    assert np.array_equal(st[2], st2[2])              # two accepted
 
 
 def test_gdn_wy_fold_equals_sequential(oracle_lib):
