@@ -343,9 +343,10 @@ class Context:
             pass
 
 
-def step_baseline_spec(cfg: rssm_config, pool, slot_of, y, A, D, stream=None, **kw):
+def step_baseline_spec(cfg: rssm_config, pool, slot_of, y, A=None, D=None, stream=None, **kw):
     """Conventional speculative round over the drafts in kw (leading token axis K): snapshots into
-    the slot pool [2K+1, B, H, P, N] from each sequence's committed slot."""
+    the slot pool [2K+1, B, H, dim_v, dim_k] from each sequence's committed slot (A and D: Mamba-2
+    only)."""
     ntok = next(iter(kw.values())).shape[0]
     rssm_step_baseline_spec(cfg, pool, slot_of, make_inputs(ntok, **kw), A, D, y, stream)
 

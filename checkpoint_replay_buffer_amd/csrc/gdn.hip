@@ -572,11 +572,23 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
     const GTile c = make_gtile(a.d, kRuns);
     const int t = c.t;
     const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
-    const size_t BH = (size_t)a.d.B * a.d.H;
-    const size_t off = c.bh * (size_t)(DV * DK) + (size_t)(rg * R) * DK + c0;
+    const size_t BH = (size_t)a.d.B * a.d.H, VK = (size_t)DV * DK;
+    const size_t lo = (size_t)(rg * R) * DK + c0;          // lane block within a tile
+    const size_t off = c.bh * VK + lo;
+    // source tile and the first snapshot tile (snapshot k is k * BH tiles further)
+    const float *src;
+    float *snap0;
+    if (a.slot_of) {
+        const int sl = a.slot_of[c.b];
+        src = a.state + ((size_t)sl * BH + c.bh) * VK + lo;
+        snap0 = a.state + ((size_t)(sl < a.ntok ? a.ntok : 0) * BH + c.bh) * VK + lo;
+    } else {
+        src = a.state + off;
+        snap0 = a.snap ? a.snap + off : nullptr;
+    }
     float4 S[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) S[r] = ld4_nt(a.state + off + (size_t)r * DK);
+    for (int r = 0; r < R; ++r) S[r] = ld4_nt(src + (size_t)r * DK);
     for (int k = 0; k < a.ntok; ++k) {
         const size_t tk = k * BH + c.bh;
         const float be = a.beta[tk], al = a.alpha[tk];
@@ -602,14 +614,229 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
         __syncthreads();
         const float z = row_reduce_scatter<R, LPR, false>(part, cg, rsel);
         if (row_writer<R, LPR>(cg)) a.o[tk * DV + rg * R + rsel] = z;
-        if (a.snap) {
+        if (snap0) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) st4_nt(a.snap + k * BH * (size_t)(DV * DK) + off + (size_t)r * DK, S[r]);
+            for (int r = 0; r < R; ++r) st4_nt(snap0 + k * BH * VK + (size_t)r * DK, S[r]);
         }
     }
-    if (!a.snap) {
+    if (!snap0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) st4_nt(a.state + off + (size_t)r * DK, S[r]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// speculative verify: K drafts per sequence, outputs only, checkpoint streamed once
+// ------------------------------------------------------------------------------------------
+// LDS floats of the verify outputs for NP = 16 NTM entry rows: keys and values [NP][d+4], the
+// drafts' queries and their r vectors [16][dk+4], the Gram [NP][NP+1], u [16][NP+1], and the
+// coefficients beta_j c_{j,k} and d_{j,k} beta_j c_{j,k} [16][NP+4], gamma [16].
+template <int DV, int DK>
+__host__ __device__ constexpr int gdn_verify_lds(int NP)
+{
+    return NP * (DK + 4 + DV + 4) + 2 * 16 * (DK + 4) + NP * (NP + 1) + 16 * (NP + 1)
+           + 2 * 16 * (NP + 4) + 16;
+}
+
+// u_{j,k} = k_j . q_k (j < ne, k < K) and G[l][i] = k_l . k_i (l < i < ne), lane groups of LPD
+// lanes per dot.
+template <int DK, int TPB, int KS>
+__device__ __forceinline__ void verify_dots(const float *sh_k, const float *sh_q, int ne, int K,
+                                            float *sh_G, int GS, float *sh_u, int US, int t)
+{
+    constexpr int LPD = DotMap<DK>::LPD;
+    const int grp = t / LPD, lane = t - grp * LPD;
+    const int nu = K * ne, ndot = nu + ne * (ne - 1) / 2;
+    for (int d = grp; d < ndot; d += TPB / LPD) {
+        float s;
+        int k = -1, l, i;
+        if (d < nu) {
+            k = d / ne;
+            l = d - k * ne;
+            s = lds_dot<DK, TPB>(sh_k + l * KS, sh_q + k * KS, lane);
+        } else {
+            upper_pair(d - nu, l, i);
+            s = lds_dot<DK, TPB>(sh_k + l * KS, sh_k + i * KS, lane);
+        }
+        s = group_sum<LPD>(s);
+        if (lane == 0) {
+            if (k >= 0) sh_u[k * US + l] = s;
+            else sh_G[l * GS + i] = s;
+        }
+    }
+}
+
+// Drafts k = 0..K-1 become entries len_e + k; draft k's output is that of the state after
+// m_k = len_e + k + 1 entries, S_{m_k} q_k (the replay of A11 with q_k and the first m_k entries):
+//     c = back substitution of u_{., k} over the first m_k entries,  r_k = q_k - sum_j beta_j c_j k_j,
+//     o_k = gamma_k S0 r_k + sum_j d_{j,k} beta_j c_j v_j.
+// Both sums over j are products with the 16 x NP coefficient blocks; S0 r_k for all drafts is
+// R S0^T on the matrix cores with the tile in the layout of mfma_tile.h, and sum_j w_{j,k} v_j is
+// W V there too. Sequences whose ring cannot take the drafts (len + K > W) fold their entries
+// first (the fold of the folding decode step, without a token).
+template <int DV, int DK, int NTM>
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_verify(GdnStepArgs a)
+{
+    using F = FoldMap<DV, DK>;
+    constexpr int TPB = F::TPB, IBW = F::IBW, KB = F::KB, KS = F::CS, VS = F::RS;
+    constexpr int NP = 16 * NTM, GS = NP + 1, US = NP + 1, CS = NP + 4;
+    constexpr int KF = DK / 4, VF = DV / 4;
+    extern __shared__ float smem[];
+    const GTile c = make_gtile(a.d, kRuns);
+    const int B = a.d.B, W = c.W, K = a.ntok, t = c.t, lane = t & 63, wv = t >> 6;
+    const int g = lane >> 4, cl = lane & 15;
+    const size_t BH = (size_t)B * a.d.H;
+    const int head = a.bk.in[c.b], len = a.bk.in[B + c.b];
+    const bool prefold = len + K > W;
+    const int head_e = prefold ? (head + len) % W : head, len_e = prefold ? 0 : len;
+    const int ne = len_e + K;
+    float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
+    float4 s[IBW][KB];
+    if (prefold) {
+        gdn_fold_mfma<DV, DK, NTM>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f, S0);
+        fold_store<DV, DK>(s, S0, t);
+        mfma_settle();                      // the tile is read by the chains below
+        __syncthreads();                    // the fold's LDS is reused
+    }
+    float *sh_k = smem;                     // [NP][KS]
+    float *sh_v = sh_k + NP * KS;           // [NP][VS]
+    float *sh_q = sh_v + NP * VS;           // [16][KS]
+    float *sh_r = sh_q + 16 * KS;           // [16][KS]
+    float *sh_G = sh_r + 16 * KS;           // [NP][GS]
+    float *sh_u = sh_G + NP * GS;           // [16][US]
+    float *sh_bc = sh_u + 16 * US;          // [16][CS]  beta_j c_{j,k}
+    float *sh_w = sh_bc + 16 * CS;          // [16][CS]  d_{j,k} beta_j c_{j,k}
+    float *sh_gam = sh_w + 16 * CS;         // [16]
+
+    // 1. entries (ring entries j < len_e, then the drafts), zero rows to NP; the drafts' queries,
+    //    zero rows to 16; beta and alpha of entry j on lane j of every wave; then the checkpoint
+    for (int i = t; i < NP * KF; i += TPB) {
+        const int j = i / KF, o = (i - j * KF) * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < len_e) v = ld4(a.ring.k + (c.rh + (head_e + j) % W) * DK + o);
+        else if (j < ne) v = ld4(a.k + ((j - len_e) * BH + c.bh) * DK + o);
+        st4(sh_k + j * KS + o, v);
+    }
+    for (int i = t; i < NP * VF; i += TPB) {
+        const int j = i / VF, o = (i - j * VF) * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < len_e) v = ld4(a.ring.v + (c.rh + (head_e + j) % W) * DV + o);
+        else if (j < ne) v = ld4(a.v + ((j - len_e) * BH + c.bh) * DV + o);
+        st4(sh_v + j * VS + o, v);
+    }
+    for (int i = t; i < 16 * KF; i += TPB) {
+        const int k = i / KF, o = (i - k * KF) * 4;
+        st4(sh_q + k * KS + o, k < K ? ld4(a.q + (k * BH + c.bh) * DK + o) : make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+    const float bel = lane < len_e ? a.ring.beta[c.rh + (head_e + lane) % W]
+                                   : (lane < ne ? a.beta[(lane - len_e) * BH + c.bh] : 0.f);
+    const float all = lane < len_e ? a.ring.alpha[c.rh + (head_e + lane) % W]
+                                   : (lane < ne ? a.alpha[(lane - len_e) * BH + c.bh] : 1.f);
+    if (!prefold) {
+#pragma unroll
+        for (int ib = 0; ib < IBW; ++ib) {
+            const float *src = S0 + mfma_tile_offset<DV, DK>(t, ib);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
+        }
+    }
+    __syncthreads();
+
+    // 2. the dots
+    verify_dots<DK, TPB, KS>(sh_k, sh_q, ne, K, sh_G, GS, sh_u, US, t);
+    __syncthreads();
+
+    // 3. per draft (one wave each): c by back substitution over its m entries (lane j ends with
+    //    c_j), the decays d_j = prod_{j<i<m} alpha_i and gamma = prod_{i<m} alpha_i; rows K..15 of
+    //    the coefficient blocks are zero
+    constexpr int NW = TPB / 64;
+    for (int k = wv; k < 16; k += NW) {
+        float bc = 0.f, wj = 0.f, gam = 0.f;
+        if (k < K) {
+            const int m = len_e + k + 1;
+            float val = lane < m ? sh_u[k * US + lane] : 0.f;
+            for (int i = m - 1; i >= 0; --i) {
+                const float ci = lane_value(val, i) * lane_value(bel, i);
+                if (lane < i) val -= sh_G[lane * GS + i] * ci;
+            }
+            const float d = wave_suffix_prod(all, m, gam);
+            bc = lane < m ? bel * val : 0.f;
+            wj = d * bc;
+        }
+        if (lane < NP) {
+            sh_bc[k * CS + lane] = bc;
+            sh_w[k * CS + lane] = wj;
+        }
+        if (lane == 0) sh_gam[k] = gam;
+    }
+    __syncthreads();
+
+    // 4. r_k = q_k - sum_j beta_j c_{j,k} k_j (rows K..15 stay zero)
+    for (int i = t; i < 16 * KF; i += TPB) {
+        const int k = i / KF, o = (i - k * KF) * 4;
+        float4 r = ld4(sh_q + k * KS + o);
+        for (int j = 0; j < ne; ++j) {
+            const float b = sh_bc[k * CS + j];
+            const float4 kj = ld4(sh_k + j * KS + o);
+            r.x -= b * kj.x; r.y -= b * kj.y; r.z -= b * kj.z; r.w -= b * kj.w;
+        }
+        st4(sh_r + k * KS + o, r);
+    }
+    __syncthreads();
+
+    // 5. Z = R S0^T and the value sums W V on the matrix cores; o_k = gamma_k Z_k + (W V)_k
+    const float4 gm4 = ld4(sh_gam + 4 * g);
+    const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+#pragma unroll
+    for (int ib = 0; ib < IBW; ++ib) {
+        const int i = 16 * (wv * IBW + ib) + cl;
+        v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const float4 rv = ld4(sh_r + cl * KS + 16 * kb + 4 * g);   // A: R[c][16 kb + 4 g + r]
+            z = mfma4(rv.x, s[ib][kb].x, z);
+            z = mfma4(rv.y, s[ib][kb].y, z);
+            z = mfma4(rv.z, s[ib][kb].z, z);
+            z = mfma4(rv.w, s[ib][kb].w, z);
+        }
+        v4f u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < NTM; ++tb) {
+            const float4 wv4 = ld4(sh_w + cl * CS + 16 * tb + 4 * g);  // A: W[c][16 tb + 4 g + r]
+            const float *vr = sh_v + (16 * tb + 4 * g) * VS + i;        // B: V[16 tb + 4 g + r][i]
+            u = mfma4(wv4.x, vr[0], u);
+            u = mfma4(wv4.y, vr[VS], u);
+            u = mfma4(wv4.z, vr[2 * VS], u);
+            u = mfma4(wv4.w, vr[3 * VS], u);
+        }
+        float ov[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] = gm[r] * z[r] + u[r];   // draft k = 4 g + r, row i
+        // the accumulators are read here, not inside the conditional stores
+        asm volatile("" ::"v"(ov[0]), "v"(ov[1]), "v"(ov[2]), "v"(ov[3]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * g + r < K) a.o[((size_t)(4 * g + r) * BH + c.bh) * DV + i] = ov[r];
+    }
+
+    // 6. append the drafts as entries len_e .. len_e + K - 1 (every ring read is done)
+    for (int i = t; i < K * KF; i += TPB) {
+        const int k = i / KF, o = (i - k * KF) * 4;
+        st4(a.ring.k + (c.rh + (head_e + len_e + k) % W) * DK + o, ld4(sh_k + (len_e + k) * KS + o));
+    }
+    for (int i = t; i < K * VF; i += TPB) {
+        const int k = i / VF, o = (i - k * VF) * 4;
+        st4(a.ring.v + (c.rh + (head_e + len_e + k) % W) * DV + o, ld4(sh_v + (len_e + k) * VS + o));
+    }
+    for (int k = t; k < K; k += TPB) {
+        const size_t slot = c.rh + (head_e + len_e + k) % W;
+        a.ring.beta[slot] = a.beta[k * BH + c.bh];
+        a.ring.alpha[slot] = a.alpha[k * BH + c.bh];
+    }
+    if (c.h == 0 && t == 0) {
+        a.bk.out[c.b] = head_e;
+        a.bk.out[B + c.b] = len_e;
+        a.bk.out[2 * B + c.b] = K;
     }
 }
 
@@ -630,6 +857,24 @@ hipError_t go_decode(const GdnStepArgs &a, int mode, hipStream_t s)
     if (mode == 0) hipLaunchKernelGGL((k_gdn_decode<DV, DK, 0>), grid, block, lds, s, a);
     else if (mode == 1) hipLaunchKernelGGL((k_gdn_decode<DV, DK, 1>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_gdn_decode<DV, DK, 2>), grid, block, lds, s, a);
+    return hipGetLastError();
+}
+
+template <int DV, int DK>
+size_t gdn_verify_lds_bytes(int W)
+{
+    const size_t np = W > 16 ? 32 : 16;
+    const size_t out = gdn_verify_lds<DV, DK>((int)np), fold = gdn_fold_lds<DV, DK>(W);
+    return 4 * (out > fold ? out : fold);
+}
+
+template <int DV, int DK>
+hipError_t go_verify(const GdnStepArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.d.B * a.d.H), block(TileShape<DV, DK>::TPB);
+    const size_t lds = gdn_verify_lds_bytes<DV, DK>(a.d.W);
+    if (a.d.W > 16) hipLaunchKernelGGL((k_gdn_verify<DV, DK, 2>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_gdn_verify<DV, DK, 1>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
@@ -665,7 +910,8 @@ bool gdn_supported(int DV, int DK)
 
 size_t gdn_lds_bytes(int DV, int DK, int W)
 {
-#define RSSM_C(v, k) if (DV == v && DK == k) return gdn_decode_lds<v, k>(W);
+#define RSSM_C(v, k) if (DV == v && DK == k) { const size_t d = gdn_decode_lds<v, k>(W), \
+    e = gdn_verify_lds_bytes<v, k>(W); return d > e ? d : e; }
     RSSM_GDN_SHAPES(RSSM_C)
 #undef RSSM_C
     return 0;
@@ -682,6 +928,14 @@ hipError_t gdn_decode(const GdnStepArgs &a, int mode, hipStream_t s)
 hipError_t gdn_fold(const GdnFoldArgs &a, hipStream_t s)
 {
 #define RSSM_C(v, k) if (a.d.DV == v && a.d.DK == k) return go_fold<v, k>(a, s);
+    RSSM_GDN_SHAPES(RSSM_C)
+#undef RSSM_C
+    return hipErrorInvalidValue;
+}
+
+hipError_t gdn_verify(const GdnStepArgs &a, hipStream_t s)
+{
+#define RSSM_C(v, k) if (a.d.DV == v && a.d.DK == k) return go_verify<v, k>(a, s);
     RSSM_GDN_SHAPES(RSSM_C)
 #undef RSSM_C
     return hipErrorInvalidValue;

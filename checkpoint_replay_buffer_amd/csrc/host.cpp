@@ -376,14 +376,20 @@ rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *st
     rssm_status s = ready(ctx);
     if (s != RSSM_OK) return s;
     const rssm_config &c = ctx->cfg;
-    if (c.kind != RSSM_MAMBA2) return RSSM_E_UNSUPPORTED;
     if ((s = check_inputs(c, in)) != RSSM_OK) return s;
     if (!aligned16(y)) return RSSM_E_ARG;
     if (in->ntok > c.max_draft || in->ntok > c.window) return RSSM_E_ARG;
+    if (c.kind == RSSM_GDN && in->ntok > kGdnMaxDraft) return RSSM_E_ARG;
     if (ctx->pending) return RSSM_E_STATE;
-    M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
-                 in->x, in->B, in->C, in->dt, y, in->ntok};
-    s = launched(ctx, m2_verify(a, ctx->S0b != nullptr, strm(stream)), true);
+    if (c.kind == RSSM_MAMBA2) {
+        M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
+                     in->x, in->B, in->C, in->dt, y, in->ntok};
+        s = launched(ctx, m2_verify(a, ctx->S0b != nullptr, strm(stream)), true);
+    } else {
+        GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
+                      in->alpha, y, 0, 0, in->ntok};
+        s = launched(ctx, gdn_verify(a, strm(stream)), true);
+    }
     if (s == RSSM_OK) {
         ctx->pending = true;
         ctx->pending_k = in->ntok;
@@ -449,9 +455,14 @@ rssm_status rssm_step_baseline_spec(const rssm_config *cfg, float *pool, const i
 {
     rssm_status s = check_config(cfg);
     if (s != RSSM_OK) return s;
-    if (cfg->kind != RSSM_MAMBA2) return RSSM_E_UNSUPPORTED;
     if ((s = check_inputs(*cfg, in)) != RSSM_OK) return s;
-    if (!aligned16(pool) || !aligned16(y) || !slot_of || !A || !D) return RSSM_E_ARG;
+    if (!aligned16(pool) || !aligned16(y) || !slot_of) return RSSM_E_ARG;
+    if (cfg->kind == RSSM_GDN) {
+        GdnRmwArgs a{gdndims(*cfg), pool, nullptr, in->q, in->k, in->v, in->beta, in->alpha, y,
+                     in->ntok, slot_of};
+        return gdn_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+    }
+    if (!A || !D) return RSSM_E_ARG;
     M2RmwArgs a{m2dims(*cfg), pool, nullptr, A, D, in->x, in->B, in->C, in->dt, y, in->ntok, slot_of};
     return m2_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
 }

@@ -8,6 +8,7 @@
 namespace rssm {
 
 constexpr int kMaxWindow = 32;   // largest ring length W (W + 1 entries fit one wave's lanes)
+constexpr int kGdnMaxDraft = 16; // drafts of one Gated DeltaNet verify (one 16-row matrix-core block)
 
 // Bookkeeping is double-buffered: every launch that changes it reads bk_in and writes bk_out
 // (each [3][B] int32: head, len, ndraft). All head-workgroups of a sequence read bk_in while one
@@ -115,6 +116,7 @@ struct GdnStepArgs {
     const float *q, *k, *v, *beta, *alpha;
     float *o;
     int uhead, ulen;    // ring position shared by every sequence (mode 0 only)
+    int ntok;           // verify: drafts per sequence
 };
 
 struct GdnFoldArgs {
@@ -138,11 +140,12 @@ struct GdnPrefillArgs {
 
 struct GdnRmwArgs {
     GdnDims d;
-    float *state;
-    float *snap;
+    float *state;       // [B,H,dv,dk]; with slot_of: the slot pool [2 ntok + 1][B,H,dv,dk]
+    float *snap;        // nullptr = in place (ignored with slot_of)
     const float *q, *k, *v, *beta, *alpha;
     float *o;
     int ntok;
+    const int32_t *slot_of;   // [B] committed slot per sequence, or nullptr
 };
 
 // ---- launchers (return hipSuccess or the launch error) ----
@@ -162,6 +165,7 @@ size_t gdn_lds_bytes(int DV, int DK, int W);
 hipError_t gdn_decode(const GdnStepArgs &a, int mode, hipStream_t s);   // mode as m2_decode
 hipError_t gdn_fold(const GdnFoldArgs &a, hipStream_t s);
 hipError_t gdn_rmw(const GdnRmwArgs &a, hipStream_t s);
+hipError_t gdn_verify(const GdnStepArgs &a, hipStream_t s);
 hipError_t gdn_prefill(const GdnPrefillArgs &a, hipStream_t s);
 
 hipError_t init_checkpoint(float *S0, uint16_t *S0b, const float *state, const int32_t *mask,

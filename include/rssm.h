@@ -152,11 +152,13 @@ rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream);
  * pending verify (RSSM_E_STATE). */
 rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream);
 
-/* Speculative verify of K = in->ntok drafts (1 <= K <= max_draft): sequences whose drafts would
- * not fit (len + K > W) first fold their committed entries; the drafts are then appended as
- * entries len .. len+K-1 (ndraft = K) and y [K,B,H,dim_v] gets every draft's output, draft k
- * seeing the committed entries and drafts 0..k. S0 is streamed once for all K outputs.
- * Requires no pending verify; afterwards exactly one of commit / rollback must follow. */
+/* Speculative verify of K = in->ntok drafts (1 <= K <= max_draft), both layer types (Mamba-2
+ * drafts: x, B, C, dt; Gated DeltaNet drafts: q, k, v, beta, alpha, each with a leading K axis):
+ * sequences whose drafts would not fit (len + K > W) first fold their committed entries; the
+ * drafts are then appended as entries len .. len+K-1 (ndraft = K) and y [K,B,H,dim_v] gets every
+ * draft's output, draft k seeing the committed entries and drafts 0..k. S0 is streamed once for
+ * all K outputs. Gated DeltaNet takes at most 16 drafts per call (RSSM_E_ARG beyond). Requires no
+ * pending verify; afterwards exactly one of commit / rollback must follow. */
 rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream);
 
 /* Accept accepted[b] ([B] int32, device) drafts per sequence: len += accepted[b] when
@@ -178,7 +180,8 @@ rssm_status rssm_step_baseline(const rssm_config *cfg, float *state, const rssm_
                                const float *A, const float *D, float *y, float *snapshots,
                                void *stream);
 
-/* Conventional speculative round, the comparator for rssm_verify + rssm_verify_commit (Mamba-2).
+/* Conventional speculative round, the comparator for rssm_verify + rssm_verify_commit (both layer
+ * types; A and D are required for Mamba-2 and ignored for Gated DeltaNet).
  * Done conventionally, a rollback needs a copy of the state after every step (news.hamidun.com
  * item "NVIDIA présente ReplaySSM...", section "D'où vient le problème de l'état"); this keeps
  * one snapshot per draft and commits by pointer. `pool` holds 2K+1 state slots
