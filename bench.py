@@ -397,6 +397,154 @@ def run_m2_spec(args, torch, rb, wl):
     }, (sh, prm)
 
 
+def gdn_verify_bytes(DV, DK, W, K, length) -> tuple[float, bool]:
+    """HBM bytes of one Gated DeltaNet verify launch for one (b, h) pair with `length` committed
+    entries, and whether it folds them first (length + K > W)."""
+    f = 4
+    drafts = K * (2 * DK + DV + 2) * f
+    ring = length * (DK + DV + 2) * f
+    outs = K * DV * f
+    append = K * (DK + DV + 2) * f
+    fold = length + K > W
+    s0 = (2 if fold else 1) * DV * DK * f
+    return s0 + ring + drafts + outs + append, fold
+
+
+def run_gdn_spec(args, torch, rb, wl):
+    """Gated DeltaNet speculative decoding: K = 6 drafts per round into the W = 16 ring (batch 512,
+    32 heads, 128 x 128), verify then a pointer commit of the seeded accepted prefix, against the
+    conventional round (state read once, one snapshot written per draft, pointer commit)."""
+    sh = wl.GDNShape(batch=args.batch or 512, nheads=32, d_k=128, d_v=128, window=16, max_draft=6)
+    DV, DK, W, H, B, K = sh.d_v, sh.d_k, sh.window, sh.nheads, sh.batch, sh.max_draft
+    rounds, Wm, S = args.steps or 256, args.warmup, 4
+    t0 = time.time()
+    s0 = torch.from_numpy(wl.gdn_state0(sh, 0)).cuda()
+    pool = [{k: torch.from_numpy(v).cuda() for k, v in wl.gdn_token_inputs(sh, 0, s, ntok=K).items()}
+            for s in range(S)]
+    acc_h = wl.spec_accepted(B, rounds + Wm, K, p=0.35, seed=0)
+    acc = torch.from_numpy(acc_h).cuda()
+    gen_s = time.time() - t0
+
+    ctx = rb.Context("gdn", B, H, DV, DK, W, max_draft=K)
+    ok = torch.empty(K, B, H, DV, device="cuda")
+    ctx.init_checkpoint(s0)
+    for r in range(Wm):
+        ctx.verify(ok, **pool[r % S])
+        ctx.commit(acc[rounds + r])
+    ctx.init_checkpoint(s0)
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for r in range(rounds):
+        ctx.verify(ok, **pool[r % S])
+        ctx.commit(acc[r])
+    ev[1].record()
+    torch.cuda.synchronize()
+    replay_s = ev[0].elapsed_time(ev[1]) / 1e3
+    h, l, n, e = ctx.bookkeeping()
+    assert e == 0
+    ctx.init_checkpoint(s0)
+    torch.cuda.synchronize()
+    evl = _events(torch, 2 * rounds)
+    for r in range(rounds):
+        evl[2 * r].record()
+        ctx.verify(ok, **pool[r % S])
+        evl[2 * r + 1].record()
+        ctx.commit(acc[r])
+    torch.cuda.synchronize()
+    verify_ms = [evl[2 * r].elapsed_time(evl[2 * r + 1]) for r in range(rounds)]
+    del ctx
+
+    L = np.zeros(B, dtype=np.int64)
+    vbytes, folds = 0.0, 0
+    for r in range(rounds):
+        vbytes += sum(gdn_verify_bytes(DV, DK, W, K, int(x))[0] for x in L) * H
+        fold = L + K > W
+        folds += int(fold.sum())
+        L = np.where(fold, 0, L) + acc_h[r]
+    cbytes = 3 * 4 * B * 2 * rounds + B * 4 * rounds          # commits
+    alg_bytes = vbytes + cbytes
+
+    cfg = rb.make_config(rb.RSSM_GDN, B, H, H, DV, DK, W, K)
+    spool = torch.empty((2 * K + 1, B, H, DV, DK), device="cuda")
+    slot_of = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def conv_round(r, a_row):
+        rb.step_baseline_spec(cfg, spool, slot_of, ok, **pool[r % S])
+        rb.rssm_baseline_commit(cfg, slot_of, a_row, K)
+
+    spool[2 * K].copy_(s0)
+    slot_of.fill_(2 * K)
+    for r in range(Wm):
+        conv_round(r, acc[rounds + r])
+    spool[2 * K].copy_(s0)
+    slot_of.fill_(2 * K)
+    torch.cuda.synchronize()
+    ev2 = _events(torch, 2)
+    ev2[0].record()
+    for r in range(rounds):
+        conv_round(r, acc[r])
+    ev2[1].record()
+    torch.cuda.synchronize()
+    conv_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+    del spool
+    conv_bytes = (DV * DK * 4 * (1 + K) + K * (2 * DK + DV + 2) * 4 + K * DV * 4) * B * H * rounds
+
+    vk_s = sum(verify_ms) / 1e3
+    achieved = vbytes / vk_s / 1e9
+    accepted = int(acc_h[:rounds].sum())
+    return {
+        "metric": "speculative verify+commit state GB/s (% of HBM peak) + accepted tokens/s vs "
+                  "conventional per-draft snapshots, Gated DeltaNet batch 512 K=6 W=16",
+        "value": round(alg_bytes / replay_s / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": rounds, "warmup": Wm,
+        "ms_per_step": round(replay_s * 1e3 / rounds, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded drafts; accepted ~ min(Geometric(0.35) failures, 6))",
+        "config": {"workload": f"gdn_spec_b{B}_h{H}_dk{DK}_dv{DV}_w{W}_k{K}", "batch": B,
+                   "heads": H, "d_k": DK, "d_v": DV, "window": W, "drafts": K,
+                   "rounds": rounds, "draft_pool_slots": S},
+        "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
+        "accepted_tokens_per_s": round(accepted / replay_s, 1),
+        "mean_accepted": round(accepted / (rounds * B), 3),
+        "fold_fraction": round(folds / (rounds * B), 4),
+        "conv_ms_per_round": round(conv_s * 1e3 / rounds, 5),
+        "conv_gbs": round(conv_bytes / conv_s / 1e9, 1),
+        "speedup_vs_conventional": round(conv_s / replay_s, 3),
+        "roofline": {"bound": "hbm", "kernel": "k_gdn_verify<128,128,1>",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic("gdn_verify"),
+                     "alg_bytes_per_launch": round(vbytes / rounds),
+                     "avg_launch_us": round(1e6 * vk_s / rounds, 2), "launches": rounds},
+        "input_gen_s": round(gen_s, 1),
+    }, sh
+
+
+def cpu_baseline_gdn_spec(sh, wl, budget_s=8.0):
+    import oracle
+    cores = oracle.set_threads(0)
+    nseq = 64
+    K = sh.max_draft
+    state = wl.gdn_state0(sh, 0)[:nseq].astype(np.float64)
+    drafts = [{k: np.ascontiguousarray(v[:, :nseq]) for k, v in wl.gdn_token_inputs(sh, 0, s, ntok=K).items()}
+              for s in range(2)]
+    acc = wl.spec_accepted(sh.batch, 512, K, seed=0)[:, :nseq]
+    t0 = time.perf_counter()
+    oracle.gdn_spec_round(drafts[0], state, acc[0])
+    one = time.perf_counter() - t0
+    rounds = max(2, min(256, int(budget_s / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    for r in range(rounds):
+        oracle.gdn_spec_round(drafts[r % 2], state, acc[r])
+    el = time.perf_counter() - t0
+    return {"value": round(int(acc[:rounds].sum()) / el, 1), "unit": "accepted tokens/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"first {rounds} rounds of sequences 0..{nseq - 1} (all heads), conventional fp64 "
+                      f"recurrence with a state copy per draft, {el:.1f} s"}
+
+
 def gdn_bytes(DV, DK, W, length) -> float:
     f = 4
     token = (2 * DK + DV + 2) * f
@@ -835,8 +983,8 @@ def main():
                     help="timed steps (decode tokens; verify rounds for m2_spec); default 512 / 256")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="m2_serve",
-                    choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve", "m2_prefill",
-                             "gdn_prefill", "m2_fork"])
+                    choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve", "gdn_spec",
+                             "m2_prefill", "gdn_prefill", "m2_fork"])
     ap.add_argument("--prompt", type=int, default=512, help="prompt tokens (m2_prefill, gdn_prefill)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
     ap.add_argument("--groups", type=int, default=0,
@@ -868,6 +1016,10 @@ def main():
         line, (sh, prm) = run_m2_spec(args, torch, rb, wl)
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_m2_spec(sh, prm, wl)
+    elif args.workload == "gdn_spec":
+        line, sh = run_gdn_spec(args, torch, rb, wl)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_gdn_spec(sh, wl)
     elif args.workload == "m2_prefill":
         args.steps = args.steps or 8
         args.warmup = min(args.warmup, 2)
