@@ -24,6 +24,7 @@
 #include "internal.h"
 #include "tile_order.h"
 #include "mfma_tile.h"
+#include "gdn_chunk.h"
 
 namespace rssm {
 namespace {
@@ -628,59 +629,46 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
 // ------------------------------------------------------------------------------------------
 // speculative verify: K drafts per sequence, outputs only, checkpoint streamed once
 // ------------------------------------------------------------------------------------------
-// LDS floats of the verify outputs for NP = 16 NTM entry rows: keys and values [NP][d+4], the
-// drafts' queries and their r vectors [16][dk+4], the Gram [NP][NP+1], u [16][NP+1], and the
-// coefficients beta_j c_{j,k} and d_{j,k} beta_j c_{j,k} [16][NP+4], gamma [16].
+// LDS floats of the verify with NP = 16 NTM entry rows: keys [NP][d_k+4] and values [NP][d_v+4] by
+// entry position, the drafts' queries (then their r rows) [16][d_k+4], beta and alpha [NP], the
+// Gram and T [NP][NP+4], A and the decay rows [16][NP+4], Gam [16].
 template <int DV, int DK>
 __host__ __device__ constexpr int gdn_verify_lds(int NP)
 {
-    return NP * (DK + 4 + DV + 4) + 2 * 16 * (DK + 4) + NP * (NP + 1) + 16 * (NP + 1)
-           + 2 * 16 * (NP + 4) + 16;
+    return NP * (DK + 4 + DV + 4) + kChunk * (DK + 4) + 2 * NP + 2 * NP * (NP + 4)
+           + 2 * kChunk * (NP + 4) + kChunk;
 }
 
-// u_{j,k} = k_j . q_k (j < ne, k < K) and G[l][i] = k_l . k_i (l < i < ne), lane groups of LPD
-// lanes per dot.
-template <int DK, int TPB, int KS>
-__device__ __forceinline__ void verify_dots(const float *sh_k, const float *sh_q, int ne, int K,
-                                            float *sh_G, int GS, float *sh_u, int US, int t)
-{
-    constexpr int LPD = DotMap<DK>::LPD;
-    const int grp = t / LPD, lane = t - grp * LPD;
-    const int nu = K * ne, ndot = nu + ne * (ne - 1) / 2;
-    for (int d = grp; d < ndot; d += TPB / LPD) {
-        float s;
-        int k = -1, l, i;
-        if (d < nu) {
-            k = d / ne;
-            l = d - k * ne;
-            s = lds_dot<DK, TPB>(sh_k + l * KS, sh_q + k * KS, lane);
-        } else {
-            upper_pair(d - nu, l, i);
-            s = lds_dot<DK, TPB>(sh_k + l * KS, sh_k + i * KS, lane);
-        }
-        s = group_sum<LPD>(s);
-        if (lane == 0) {
-            if (k >= 0) sh_u[k * US + l] = s;
-            else sh_G[l * GS + i] = s;
-        }
-    }
-}
-
-// Drafts k = 0..K-1 become entries len_e + k; draft k's output is that of the state after
-// m_k = len_e + k + 1 entries, S_{m_k} q_k (the replay of A11 with q_k and the first m_k entries):
-//     c = back substitution of u_{., k} over the first m_k entries,  r_k = q_k - sum_j beta_j c_j k_j,
-//     o_k = gamma_k S0 r_k + sum_j d_{j,k} beta_j c_j v_j.
-// Both sums over j are products with the 16 x NP coefficient blocks; S0 r_k for all drafts is
-// R S0^T on the matrix cores with the tile in the layout of mfma_tile.h, and sum_j w_{j,k} v_j is
-// W V there too. Sequences whose ring cannot take the drafts (len + K > W) fold their entries
-// first (the fold of the folding decode step, without a token).
+// Waves per SIMD the verify is compiled for: three 8-wave workgroups per compute unit at 128 x 128
+// (at most 80 VGPRs), the compiler's choice otherwise.
 template <int DV, int DK, int NTM>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_verify(GdnStepArgs a)
+struct VerifyOcc {
+    static constexpr int WPE = TileShape<DV, DK>::TPB == 512 && NTM == 1 ? 6 : 1;
+};
+
+// Drafts k = 0..K-1 become entries len_e + k, and draft k's output is the replay (top of this
+// file) for q_k over the first m_k = len_e + k + 1 entries. Back substitution over a prefix is the leading block
+// of the substitution that T solves (gdn_chunk.h), so with A[k][i] = q_k . k_i for i < m_k (else 0)
+// and U = A T,
+//     beta_j c_{k,j} = U[k][j],     r_k = q_k - sum_j U[k][j] k_j,
+//     o_k = Gam_k S0 r_k + sum_j D[k][j] U[k][j] v_j,
+// with D[k][j] = prod_{j<i<m_k} alpha_i and Gam_k = prod_{i<m_k} alpha_i. While the checkpoint
+// streams in, one wave forms the Gram blocks and T, another A, a third the decays; then U, W = D o U
+// and the rows r_k are 16-wide products on the matrix cores, and the outputs of all drafts are
+// R S0^T + W V on the tile held in the layout of mfma_tile.h. The checkpoint is read once and never
+// written. Sequences whose ring cannot take the drafts (len + K > W) fold their entries first (the
+// fold of the folding decode step, without a token).
+template <int DV, int DK, int NTM>
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, NTM>::WPE)) k_gdn_verify(GdnStepArgs a)
 {
     using F = FoldMap<DV, DK>;
-    constexpr int TPB = F::TPB, IBW = F::IBW, KB = F::KB, KS = F::CS, VS = F::RS;
-    constexpr int NP = 16 * NTM, GS = NP + 1, US = NP + 1, CS = NP + 4;
+    constexpr int TPB = F::TPB, NW = F::NW, IBW = F::IBW, KB = F::KB, KS = F::CS, VS = F::RS;
+    constexpr int NP = kChunk * NTM, PS = NP + 4;
     constexpr int KF = DK / 4, VF = DV / 4;
+    constexpr int KQ = (NP * KF + TPB - 1) / TPB, VQ = (NP * VF + TPB - 1) / TPB;
+    constexpr int QQ = (kChunk * KF + TPB - 1) / TPB;
+    constexpr int NA = KB >= 2 ? 2 : 1;
+    static_assert(KB % NW == 0, "k-blocks of the r rows split evenly over the waves");
     extern __shared__ float smem[];
     const GTile c = make_gtile(a.d, kRuns);
     const int B = a.d.B, W = c.W, K = a.ntok, t = c.t, lane = t & 63, wv = t >> 6;
@@ -700,38 +688,55 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_verify(GdnStep
     }
     float *sh_k = smem;                     // [NP][KS]
     float *sh_v = sh_k + NP * KS;           // [NP][VS]
-    float *sh_q = sh_v + NP * VS;           // [16][KS]
-    float *sh_r = sh_q + 16 * KS;           // [16][KS]
-    float *sh_G = sh_r + 16 * KS;           // [NP][GS]
-    float *sh_u = sh_G + NP * GS;           // [16][US]
-    float *sh_bc = sh_u + 16 * US;          // [16][CS]  beta_j c_{j,k}
-    float *sh_w = sh_bc + 16 * CS;          // [16][CS]  d_{j,k} beta_j c_{j,k}
-    float *sh_gam = sh_w + 16 * CS;         // [16]
+    float *sh_q = sh_v + NP * VS;           // [16][KS]  q_k, then r_k
+    float *sh_be = sh_q + kChunk * KS;      // [NP]
+    float *sh_al = sh_be + NP;              // [NP]
+    float *sh_G = sh_al + NP;               // [NP][PS]  G[t][i] = k_t . k_i, i <= t
+    float *sh_T = sh_G + NP * PS;           // [NP][PS]
+    float *sh_A = sh_T + NP * PS;           // [16][PS]
+    float *sh_D = sh_A + kChunk * PS;       // [16][PS]
+    float *sh_gam = sh_D + kChunk * PS;     // [16]
 
-    // 1. entries (ring entries j < len_e, then the drafts), zero rows to NP; the drafts' queries,
-    //    zero rows to 16; beta and alpha of entry j on lane j of every wave; then the checkpoint
-    for (int i = t; i < NP * KF; i += TPB) {
-        const int j = i / KF, o = (i - j * KF) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j < len_e) v = ld4(a.ring.k + (c.rh + (head_e + j) % W) * DK + o);
-        else if (j < ne) v = ld4(a.k + ((j - len_e) * BH + c.bh) * DK + o);
-        st4(sh_k + j * KS + o, v);
+    // 1. into registers: key and value of entry j (ring entry j < len_e, draft j - len_e below ne,
+    //    zero past ne), the query of draft k (zero from K), beta and alpha of entry t (0 and 1 past
+    //    ne); then the checkpoint goes out; then the rows go to LDS
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 kr[KQ], vr[VQ], qr[QQ];
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) {
+        const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
+        kr[i] = z4;
+        if (u < NP * KF) {
+            if (j < len_e) kr[i] = ld4(a.ring.k + (c.rh + (head_e + j) % W) * DK + o);
+            else if (j < ne) kr[i] = ld4(a.k + ((j - len_e) * BH + c.bh) * DK + o);
+        }
     }
-    for (int i = t; i < NP * VF; i += TPB) {
-        const int j = i / VF, o = (i - j * VF) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j < len_e) v = ld4(a.ring.v + (c.rh + (head_e + j) % W) * DV + o);
-        else if (j < ne) v = ld4(a.v + ((j - len_e) * BH + c.bh) * DV + o);
-        st4(sh_v + j * VS + o, v);
+#pragma unroll
+    for (int i = 0; i < VQ; ++i) {
+        const int u = t + i * TPB, j = u / VF, o = (u - j * VF) * 4;
+        vr[i] = z4;
+        if (u < NP * VF) {
+            if (j < len_e) vr[i] = ld4(a.ring.v + (c.rh + (head_e + j) % W) * DV + o);
+            else if (j < ne) vr[i] = ld4(a.v + ((j - len_e) * BH + c.bh) * DV + o);
+        }
     }
-    for (int i = t; i < 16 * KF; i += TPB) {
-        const int k = i / KF, o = (i - k * KF) * 4;
-        st4(sh_q + k * KS + o, k < K ? ld4(a.q + (k * BH + c.bh) * DK + o) : make_float4(0.f, 0.f, 0.f, 0.f));
+#pragma unroll
+    for (int i = 0; i < QQ; ++i) {
+        const int u = t + i * TPB, k = u / KF, o = (u - k * KF) * 4;
+        qr[i] = u < kChunk * KF && k < K ? ld4(a.q + (k * BH + c.bh) * DK + o) : z4;
     }
-    const float bel = lane < len_e ? a.ring.beta[c.rh + (head_e + lane) % W]
-                                   : (lane < ne ? a.beta[(lane - len_e) * BH + c.bh] : 0.f);
-    const float all = lane < len_e ? a.ring.alpha[c.rh + (head_e + lane) % W]
-                                   : (lane < ne ? a.alpha[(lane - len_e) * BH + c.bh] : 1.f);
+    float be = 0.f, al = 1.f;
+    if (t < NP) {
+        if (t < len_e) {
+            const size_t sl = c.rh + (head_e + t) % W;
+            be = a.ring.beta[sl];
+            al = a.ring.alpha[sl];
+        } else if (t < ne) {
+            const size_t d = (t - len_e) * BH + c.bh;
+            be = a.beta[d];
+            al = a.alpha[d];
+        }
+    }
     if (!prefold) {
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
@@ -740,51 +745,100 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_verify(GdnStep
             for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
         }
     }
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) {
+        const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
+        if (u < NP * KF) st4(sh_k + j * KS + o, kr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VQ; ++i) {
+        const int u = t + i * TPB, j = u / VF, o = (u - j * VF) * 4;
+        if (u < NP * VF) st4(sh_v + j * VS + o, vr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < QQ; ++i) {
+        const int u = t + i * TPB, k = u / KF, o = (u - k * KF) * 4;
+        if (u < kChunk * KF) st4(sh_q + k * KS + o, qr[i]);
+    }
+    if (t < NP) {
+        sh_be[t] = be;
+        sh_al[t] = al;
+    }
     __syncthreads();
 
-    // 2. the dots
-    verify_dots<DK, TPB, KS>(sh_k, sh_q, ne, K, sh_G, GS, sh_u, US, t);
-    __syncthreads();
-
-    // 3. per draft (one wave each): c by back substitution over its m entries (lane j ends with
-    //    c_j), the decays d_j = prod_{j<i<m} alpha_i and gamma = prod_{i<m} alpha_i; rows K..15 of
-    //    the coefficient blocks are zero
-    constexpr int NW = TPB / 64;
-    for (int k = wv; k < 16; k += NW) {
-        float bc = 0.f, wj = 0.f, gam = 0.f;
-        if (k < K) {
-            const int m = len_e + k + 1;
-            float val = lane < m ? sh_u[k * US + lane] : 0.f;
-            for (int i = m - 1; i >= 0; --i) {
-                const float ci = lane_value(val, i) * lane_value(bel, i);
-                if (lane < i) val -= sh_G[lane * GS + i] * ci;
+    // 2. the blocks that do not need the checkpoint: wave 0 the Gram blocks and T, wave 1 the
+    //    masked A, the last wave the decays (one wave does all three when it is alone)
+    if (wv == 0) {
+#pragma unroll
+        for (int ib = 0; ib < NTM; ++ib) {
+#pragma unroll
+            for (int jb = 0; jb <= ib; ++jb) {
+                const v4f gk = ib == jb
+                    ? row_dots16<KB, KS, NA, true>(sh_k + 16 * ib * KS, sh_k + 16 * ib * KS)
+                    : row_dots16<KB, KS, NA, false>(sh_k + 16 * ib * KS, sh_k + 16 * jb * KS);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sh_G[(16 * ib + 4 * g + r) * PS + 16 * jb + cl] = gk[r];
             }
-            const float d = wave_suffix_prod(all, m, gam);
-            bc = lane < m ? bel * val : 0.f;
-            wj = d * bc;
         }
-        if (lane < NP) {
-            sh_bc[k * CS + lane] = bc;
-            sh_w[k * CS + lane] = wj;
-        }
-        if (lane == 0) sh_gam[k] = gam;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        t_solve_regs<NP, PS, PS>(sh_G, sh_be, sh_T);
     }
+    if (wv == (NW > 1 ? 1 : 0)) {
+#pragma unroll
+        for (int jb = 0; jb < NTM; ++jb) {
+            const v4f qk = row_dots16<KB, KS, NA, false>(sh_q, sh_k + 16 * jb * KS);   // q_{4g+r} . k_{16jb+c}
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sh_A[(4 * g + r) * PS + 16 * jb + cl] = 16 * jb + cl <= len_e + 4 * g + r ? qk[r] : 0.f;
+        }
+    }
+    if (wv == NW - 1) decay_row<NP, PS>(sh_al, len_e + lane, sh_D, sh_gam);
     __syncthreads();
 
-    // 4. r_k = q_k - sum_j beta_j c_{j,k} k_j (rows K..15 stay zero)
-    for (int i = t; i < 16 * KF; i += TPB) {
-        const int k = i / KF, o = (i - k * KF) * 4;
-        float4 r = ld4(sh_q + k * KS + o);
-        for (int j = 0; j < ne; ++j) {
-            const float b = sh_bc[k * CS + j];
-            const float4 kj = ld4(sh_k + j * KS + o);
-            r.x -= b * kj.x; r.y -= b * kj.y; r.z -= b * kj.z; r.w -= b * kj.w;
+    // 3. U = A T as U^T = T^T A^T, so that lane (g, c) ends with U[k = c][j = 16 jb + 4 g + r], the
+    //    A operand of the products below (T[i][j] = 0 for i < j); W = D o U; then the rows
+    //    r_k = q_k - sum_j U[k][j] k_j of the wave's k-blocks, written over the queries
+    float ua[NTM][4], wa[NTM][4];
+#pragma unroll
+    for (int jb = 0; jb < NTM; ++jb) {
+        v4f ut = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ib = jb; ib < NTM; ++ib) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ut = mfma4(sh_T[(16 * ib + 4 * g + r) * PS + 16 * jb + cl], sh_A[cl * PS + 16 * ib + 4 * g + r], ut);
         }
-        st4(sh_r + k * KS + o, r);
+        const float4 dv = ld4(sh_D + cl * PS + 16 * jb + 4 * g);
+        const float dr[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            ua[jb][r] = ut[r];
+            wa[jb][r] = ut[r] * dr[r];
+        }
     }
+#pragma unroll
+    for (int n = 0; n < KB / NW; ++n) {
+        const int kb = wv + n * NW;
+        v4f rk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rk[r] = sh_q[(4 * g + r) * KS + 16 * kb + cl];   // Q[4g+r][16kb+c]
+#pragma unroll
+        for (int jb = 0; jb < NTM; ++jb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                rk = mfma4(-ua[jb][r], sh_k[(16 * jb + 4 * g + r) * KS + 16 * kb + cl], rk);
+        }
+        const float rv[4] = {rk[0], rk[1], rk[2], rk[3]};
+        asm volatile("" ::"v"(rv[0]), "v"(rv[1]), "v"(rv[2]), "v"(rv[3]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sh_q[(4 * g + r) * KS + 16 * kb + cl] = rv[r];
+    }
+    mfma_settle();
     __syncthreads();
 
-    // 5. Z = R S0^T and the value sums W V on the matrix cores; o_k = gamma_k Z_k + (W V)_k
+    // 4. Z = R S0^T and the value sums W V on the matrix cores; o_k = Gam_k Z_k + (W V)_k
     const float4 gm4 = ld4(sh_gam + 4 * g);
     const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
 #pragma unroll
@@ -793,7 +847,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_verify(GdnStep
         v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const float4 rv = ld4(sh_r + cl * KS + 16 * kb + 4 * g);   // A: R[c][16 kb + 4 g + r]
+            const float4 rv = ld4(sh_q + cl * KS + 16 * kb + 4 * g);   // A: R[c][16 kb + 4 g + r]
             z = mfma4(rv.x, s[ib][kb].x, z);
             z = mfma4(rv.y, s[ib][kb].y, z);
             z = mfma4(rv.z, s[ib][kb].z, z);
@@ -801,13 +855,10 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_verify(GdnStep
         }
         v4f u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tb = 0; tb < NTM; ++tb) {
-            const float4 wv4 = ld4(sh_w + cl * CS + 16 * tb + 4 * g);  // A: W[c][16 tb + 4 g + r]
-            const float *vr = sh_v + (16 * tb + 4 * g) * VS + i;        // B: V[16 tb + 4 g + r][i]
-            u = mfma4(wv4.x, vr[0], u);
-            u = mfma4(wv4.y, vr[VS], u);
-            u = mfma4(wv4.z, vr[2 * VS], u);
-            u = mfma4(wv4.w, vr[3 * VS], u);
+        for (int jb = 0; jb < NTM; ++jb) {
+            const float *vc = sh_v + (16 * jb + 4 * g) * VS + i;            // B: V[16 jb + 4 g + r][i]
+#pragma unroll
+            for (int r = 0; r < 4; ++r) u = mfma4(wa[jb][r], vc[r * VS], u);
         }
         float ov[4];
 #pragma unroll
@@ -819,7 +870,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_verify(GdnStep
             if (4 * g + r < K) a.o[((size_t)(4 * g + r) * BH + c.bh) * DV + i] = ov[r];
     }
 
-    // 6. append the drafts as entries len_e .. len_e + K - 1 (every ring read is done)
+    // 5. append the drafts as entries len_e .. ne - 1 (every ring read is done)
     for (int i = t; i < K * KF; i += TPB) {
         const int k = i / KF, o = (i - k * KF) * 4;
         st4(a.ring.k + (c.rh + (head_e + len_e + k) % W) * DK + o, ld4(sh_k + (len_e + k) * KS + o));
@@ -830,8 +881,8 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_verify(GdnStep
     }
     for (int k = t; k < K; k += TPB) {
         const size_t slot = c.rh + (head_e + len_e + k) % W;
-        a.ring.beta[slot] = a.beta[k * BH + c.bh];
-        a.ring.alpha[slot] = a.alpha[k * BH + c.bh];
+        a.ring.beta[slot] = sh_be[len_e + k];
+        a.ring.alpha[slot] = sh_al[len_e + k];
     }
     if (c.h == 0 && t == 0) {
         a.bk.out[c.b] = head_e;

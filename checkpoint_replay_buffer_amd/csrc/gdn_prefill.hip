@@ -17,13 +17,11 @@
 // rank-16 update are v_mfma_f32_16x16x4_f32 chains on the register-resident tile of mfma_tile.h.
 #include "dev_common.h"
 #include "internal.h"
+#include "gdn_chunk.h"
 #include "mfma_tile.h"
 
 namespace rssm {
 namespace {
-
-constexpr int kChunk = 16;
-constexpr int kTS = kChunk + 4;   // row stride of the 16 x 16 blocks in LDS
 
 // LDS floats: two staging buffers (q and k [16][d_k+4], v [16][d_v+4], beta and alpha [16]),
 // then the Gram, T, A and R blocks [16][20] and Gam [16] of the current chunk
@@ -36,51 +34,6 @@ template <int DV, int DK>
 __host__ __device__ constexpr int gp_lds_floats()
 {
     return 2 * gp_buf_floats<DV, DK>() + 4 * kChunk * kTS + kChunk;
-}
-
-// T of the chunk by forward substitution, T[t][q] = beta_t ([t == q] - sum_{i<t} G_it T[i][q]),
-// one column per lane (q = lane % 16) held in registers; the Gram rows and the betas are read
-// from LDS at addresses common to the wave. Padding rows have k = 0 and beta = 0, so their rows of
-// T are zero.
-__device__ __forceinline__ void chunk_t_solve(const float *sh_G, const float *sh_be, float *sh_T)
-{
-    const int lane = threadIdx.x & 63, q = lane & 15;
-    float tq[kChunk];
-#pragma unroll
-    for (int t = 0; t < kChunk; ++t) {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < t; ++i) acc = fmaf(sh_G[t * kTS + i], tq[i], acc);
-        tq[t] = sh_be[t] * ((t == q ? 1.f : 0.f) - acc);
-    }
-    if (lane < kChunk) {
-#pragma unroll
-        for (int t = 0; t < kChunk; ++t) sh_T[t * kTS + q] = tq[t];
-    }
-}
-
-// Decays of the chunk, lane t < 16: R[t][q] = prod_{q<i<=t} alpha_i (1 for q >= t), taken as a
-// running product from q = t down, and Gam_t = prod_{i<=t} alpha_i.
-__device__ __forceinline__ void chunk_decays(const float *sh_al, float *sh_R, float *sh_gam)
-{
-    const int t = threadIdx.x & 63;
-    float al[kChunk];
-#pragma unroll
-    for (int i = 0; i < kChunk; i += 4) {
-        const float4 x = ld4(sh_al + i);
-        al[i] = x.x; al[i + 1] = x.y; al[i + 2] = x.z; al[i + 3] = x.w;
-    }
-    float p = 1.f, row[kChunk];
-#pragma unroll
-    for (int q = kChunk - 1; q >= 0; --q) {
-        if (q < kChunk - 1 && q + 1 <= t) p *= al[q + 1];
-        row[q] = p;
-    }
-    if (t < kChunk) {
-#pragma unroll
-        for (int q = 0; q < kChunk; q += 4) st4(sh_R + t * kTS + q, make_float4(row[q], row[q + 1], row[q + 2], row[q + 3]));
-        sh_gam[t] = p * al[0];
-    }
 }
 
 // Waves per (b, h) workgroup: 4 for 128 x 128 (two i-blocks per wave, so that two workgroups share
@@ -212,45 +165,20 @@ __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPr
         //    waves' matrix work: wave 0 the Gram block and T, wave 1 the masked Q K^T, the last
         //    wave the decays (one wave does all three when it is alone)
         if (wv == 0) {
-            v4f gp[NA];
-#pragma unroll
-            for (int p = 0; p < NA; ++p) gp[p] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);   // A: K[c][k], B: K[c][k]
-                v4f &p = gp[kb % NA];
-                p = mfma4(kv.x, kv.x, p);
-                p = mfma4(kv.y, kv.y, p);
-                p = mfma4(kv.z, kv.z, p);
-                p = mfma4(kv.w, kv.w, p);
-            }
-            const v4f gk = tree_sum<NA>(gp);   // k_{4g+r} . k_c
+            const v4f gk = row_dots16<KB, KS, NA, true>(sh_k, sh_k);      // k_{4g+r} . k_c
 #pragma unroll
             for (int r = 0; r < 4; ++r) sh_G[(4 * g + r) * kTS + cl] = gk[r];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            chunk_t_solve(sh_G, sh_be, sh_T);
+            t_solve_regs<kChunk, kTS, kTS>(sh_G, sh_be, sh_T);
         }
         if (wv == (NW > 1 ? 1 : 0)) {
-            v4f ap[NA];
-#pragma unroll
-            for (int p = 0; p < NA; ++p) ap[p] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float4 qv = ld4(sh_q + cl * KS + 16 * kb + 4 * g);   // A: Q[c][k]
-                const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);   // B: K[c][k]
-                v4f &p = ap[kb % NA];
-                p = mfma4(qv.x, kv.x, p);
-                p = mfma4(qv.y, kv.y, p);
-                p = mfma4(qv.z, kv.z, p);
-                p = mfma4(qv.w, kv.w, p);
-            }
-            const v4f qk = tree_sum<NA>(ap);   // q_{4g+r} . k_c
+            const v4f qk = row_dots16<KB, KS, NA, false>(sh_q, sh_k);     // q_{4g+r} . k_c
 #pragma unroll
             for (int r = 0; r < 4; ++r) sh_A[(4 * g + r) * kTS + cl] = cl <= 4 * g + r ? qk[r] : 0.f;
         }
-        if (wv == NW - 1) chunk_decays(sh_al, sh_R, sh_gam);
+        if (wv == NW - 1) decay_row<kChunk, kTS>(sh_al, lane, sh_R, sh_gam);
         //    every wave: F = K S^T and Qs = Q S^T for its i-blocks (S at the chunk start)
         v4f fz[IBW], qs[IBW];
 #pragma unroll
