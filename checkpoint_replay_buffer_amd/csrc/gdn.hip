@@ -629,14 +629,26 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
 // ------------------------------------------------------------------------------------------
 // speculative verify: K drafts per sequence, outputs only, checkpoint streamed once
 // ------------------------------------------------------------------------------------------
-// LDS floats of the verify with NP = 16 NTM entry rows: keys [NP][d_k+4] and values [NP][d_v+4] by
-// entry position, the drafts' queries (then their r rows) [16][d_k+4], beta and alpha [NP], the
-// Gram and T [NP][NP+4], A and the decay rows [16][NP+4], Gam [16].
-template <int DV, int DK>
-__host__ __device__ constexpr int gdn_verify_lds(int NP)
+// One block of 16 entries (W <= 16): sequences that fold stage their ring entries and their drafts
+// in two separate blocks and fold the first inside the verify's own phases. Two blocks (W > 16):
+// they fold first with the decode fold, then verify.
+template <int NTM>
+struct VerifySplit {
+    static constexpr bool value = NTM == 1;
+};
+
+// LDS floats of the verify with NP = 16 NTM entry rows (two blocks of them when split): keys
+// [.][d_k+4] and values [.][d_v+4] by entry position, the drafts' queries (then their r rows)
+// [16][d_k+4], beta and alpha [.], the Gram and T [NP][NP+4] of the verified entries, A and the
+// decay rows [16][NP+4], Gam [16]; when split also the Gram, T and decay rows of the folded block
+// and its Gam.
+template <int DV, int DK, int NTM>
+__host__ __device__ constexpr int gdn_verify_lds()
 {
-    return NP * (DK + 4 + DV + 4) + kChunk * (DK + 4) + 2 * NP + 2 * NP * (NP + 4)
-           + 2 * kChunk * (NP + 4) + kChunk;
+    constexpr int NP = kChunk * NTM, PS = NP + 4, NR = VerifySplit<NTM>::value ? 2 * NP : NP;
+    constexpr int base = NR * (DK + 4 + DV + 4) + kChunk * (DK + 4) + 2 * NR + 2 * NP * PS
+                         + 2 * kChunk * PS + kChunk;
+    return VerifySplit<NTM>::value ? base + 2 * NP * PS + kChunk * PS + kChunk : base;
 }
 
 // Waves per SIMD the verify is compiled for: three 8-wave workgroups per compute unit at 128 x 128
@@ -647,25 +659,29 @@ struct VerifyOcc {
 };
 
 // Drafts k = 0..K-1 become entries len_e + k, and draft k's output is the replay (top of this
-// file) for q_k over the first m_k = len_e + k + 1 entries. Back substitution over a prefix is the leading block
-// of the substitution that T solves (gdn_chunk.h), so with A[k][i] = q_k . k_i for i < m_k (else 0)
-// and U = A T,
+// file) for q_k over the first m_k = len_e + k + 1 entries. Back substitution over a prefix is the
+// leading block of the substitution that T solves (gdn_chunk.h), so with A[k][i] = q_k . k_i for
+// i < m_k (else 0) and U = A T,
 //     beta_j c_{k,j} = U[k][j],     r_k = q_k - sum_j U[k][j] k_j,
 //     o_k = Gam_k S0 r_k + sum_j D[k][j] U[k][j] v_j,
 // with D[k][j] = prod_{j<i<m_k} alpha_i and Gam_k = prod_{i<m_k} alpha_i. While the checkpoint
 // streams in, one wave forms the Gram blocks and T, another A, a third the decays; then U, W = D o U
 // and the rows r_k are 16-wide products on the matrix cores, and the outputs of all drafts are
-// R S0^T + W V on the tile held in the layout of mfma_tile.h. The checkpoint is read once and never
-// written. Sequences whose ring cannot take the drafts (len + K > W) fold their entries first (the
-// fold of the folding decode step, without a token).
+// R S0^T + W V on the tile held in the layout of mfma_tile.h. The checkpoint is read once.
+//
+// Sequences whose ring cannot take the drafts (len + K > W) first fold their len entries into the
+// checkpoint. Split (one block): the ring entries are a block of their own, folded in the same
+// phases by the chunk fold of the prefill (F = K S0^T, C = T Z with Z_q = R[q] v_q - gam F_q,
+// S0 <- gam S0 + C^T K) while the drafts' blocks are formed, and the new checkpoint is written.
 template <int DV, int DK, int NTM>
 __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, NTM>::WPE)) k_gdn_verify(GdnStepArgs a)
 {
     using F = FoldMap<DV, DK>;
     constexpr int TPB = F::TPB, NW = F::NW, IBW = F::IBW, KB = F::KB, KS = F::CS, VS = F::RS;
-    constexpr int NP = kChunk * NTM, PS = NP + 4;
+    constexpr bool SPLIT = VerifySplit<NTM>::value;
+    constexpr int NP = kChunk * NTM, PS = NP + 4, NR = SPLIT ? 2 * NP : NP;
     constexpr int KF = DK / 4, VF = DV / 4;
-    constexpr int KQ = (NP * KF + TPB - 1) / TPB, VQ = (NP * VF + TPB - 1) / TPB;
+    constexpr int KQ = (NR * KF + TPB - 1) / TPB, VQ = (NR * VF + TPB - 1) / TPB;
     constexpr int QQ = (kChunk * KF + TPB - 1) / TPB;
     constexpr int NA = KB >= 2 ? 2 : 1;
     static_assert(KB % NW == 0, "k-blocks of the r rows split evenly over the waves");
@@ -676,48 +692,58 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, N
     const size_t BH = (size_t)B * a.d.H;
     const int head = a.bk.in[c.b], len = a.bk.in[B + c.b];
     const bool prefold = len + K > W;
+    const bool fold_here = SPLIT && prefold;             // the ring block is folded below
     const int head_e = prefold ? (head + len) % W : head, len_e = prefold ? 0 : len;
     const int ne = len_e + K;
+    const int nring = prefold && !SPLIT ? 0 : len;        // ring entries staged from slot `head`
+    const int d0 = fold_here ? NP : nring;                // row of draft 0
+    const int vb = fold_here ? NP : 0;                    // first row of the verified entries
     float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
     float4 s[IBW][KB];
-    if (prefold) {
-        gdn_fold_mfma<DV, DK, NTM>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f, S0);
-        fold_store<DV, DK>(s, S0, t);
-        mfma_settle();                      // the tile is read by the chains below
-        __syncthreads();                    // the fold's LDS is reused
+    if constexpr (!SPLIT) {
+        if (prefold) {
+            gdn_fold_mfma<DV, DK, NTM>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f, S0);
+            fold_store<DV, DK>(s, S0, t);
+            mfma_settle();                  // the tile is read by the chains below
+            __syncthreads();                // the fold's LDS is reused
+        }
     }
-    float *sh_k = smem;                     // [NP][KS]
-    float *sh_v = sh_k + NP * KS;           // [NP][VS]
-    float *sh_q = sh_v + NP * VS;           // [16][KS]  q_k, then r_k
-    float *sh_be = sh_q + kChunk * KS;      // [NP]
-    float *sh_al = sh_be + NP;              // [NP]
-    float *sh_G = sh_al + NP;               // [NP][PS]  G[t][i] = k_t . k_i, i <= t
+    float *sh_k = smem;                     // [NR][KS]  entries by row
+    float *sh_v = sh_k + NR * KS;           // [NR][VS]
+    float *sh_q = sh_v + NR * VS;           // [16][KS]  q_k, then r_k
+    float *sh_be = sh_q + kChunk * KS;      // [NR]
+    float *sh_al = sh_be + NR;              // [NR]
+    float *sh_G = sh_al + NR;               // [NP][PS]  G[t][i] = k_t . k_i, i <= t
     float *sh_T = sh_G + NP * PS;           // [NP][PS]
     float *sh_A = sh_T + NP * PS;           // [16][PS]
     float *sh_D = sh_A + kChunk * PS;       // [16][PS]
     float *sh_gam = sh_D + kChunk * PS;     // [16]
+    float *sh_Gf = sh_gam + kChunk;         // [NP][PS]  the folded block (split only)
+    float *sh_Tf = sh_Gf + NP * PS;         // [NP][PS]
+    float *sh_Df = sh_Tf + NP * PS;         // [16][PS]
+    float *sh_gf = sh_Df + kChunk * PS;     // [16]
 
-    // 1. into registers: key and value of entry j (ring entry j < len_e, draft j - len_e below ne,
-    //    zero past ne), the query of draft k (zero from K), beta and alpha of entry t (0 and 1 past
-    //    ne); then the checkpoint goes out; then the rows go to LDS
+    // 1. into registers: key and value of row j (ring entry j < nring, then the drafts from row
+    //    d0, zero elsewhere), the query of draft k (zero from K), beta and alpha of row t (0 and 1
+    //    on zero rows); then the checkpoint goes out; then the rows go to LDS
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 kr[KQ], vr[VQ], qr[QQ];
 #pragma unroll
     for (int i = 0; i < KQ; ++i) {
         const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
         kr[i] = z4;
-        if (u < NP * KF) {
-            if (j < len_e) kr[i] = ld4(a.ring.k + (c.rh + (head_e + j) % W) * DK + o);
-            else if (j < ne) kr[i] = ld4(a.k + ((j - len_e) * BH + c.bh) * DK + o);
+        if (u < NR * KF) {
+            if (j < nring) kr[i] = ld4(a.ring.k + (c.rh + (head + j) % W) * DK + o);
+            else if (j >= d0 && j < d0 + K) kr[i] = ld4(a.k + ((j - d0) * BH + c.bh) * DK + o);
         }
     }
 #pragma unroll
     for (int i = 0; i < VQ; ++i) {
         const int u = t + i * TPB, j = u / VF, o = (u - j * VF) * 4;
         vr[i] = z4;
-        if (u < NP * VF) {
-            if (j < len_e) vr[i] = ld4(a.ring.v + (c.rh + (head_e + j) % W) * DV + o);
-            else if (j < ne) vr[i] = ld4(a.v + ((j - len_e) * BH + c.bh) * DV + o);
+        if (u < NR * VF) {
+            if (j < nring) vr[i] = ld4(a.ring.v + (c.rh + (head + j) % W) * DV + o);
+            else if (j >= d0 && j < d0 + K) vr[i] = ld4(a.v + ((j - d0) * BH + c.bh) * DV + o);
         }
     }
 #pragma unroll
@@ -726,18 +752,18 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, N
         qr[i] = u < kChunk * KF && k < K ? ld4(a.q + (k * BH + c.bh) * DK + o) : z4;
     }
     float be = 0.f, al = 1.f;
-    if (t < NP) {
-        if (t < len_e) {
-            const size_t sl = c.rh + (head_e + t) % W;
+    if (t < NR) {
+        if (t < nring) {
+            const size_t sl = c.rh + (head + t) % W;
             be = a.ring.beta[sl];
             al = a.ring.alpha[sl];
-        } else if (t < ne) {
-            const size_t d = (t - len_e) * BH + c.bh;
+        } else if (t >= d0 && t < d0 + K) {
+            const size_t d = (t - d0) * BH + c.bh;
             be = a.beta[d];
             al = a.alpha[d];
         }
     }
-    if (!prefold) {
+    if (SPLIT || !prefold) {
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
             const float *src = S0 + mfma_tile_offset<DV, DK>(t, ib);
@@ -748,34 +774,37 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, N
 #pragma unroll
     for (int i = 0; i < KQ; ++i) {
         const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
-        if (u < NP * KF) st4(sh_k + j * KS + o, kr[i]);
+        if (u < NR * KF) st4(sh_k + j * KS + o, kr[i]);
     }
 #pragma unroll
     for (int i = 0; i < VQ; ++i) {
         const int u = t + i * TPB, j = u / VF, o = (u - j * VF) * 4;
-        if (u < NP * VF) st4(sh_v + j * VS + o, vr[i]);
+        if (u < NR * VF) st4(sh_v + j * VS + o, vr[i]);
     }
 #pragma unroll
     for (int i = 0; i < QQ; ++i) {
         const int u = t + i * TPB, k = u / KF, o = (u - k * KF) * 4;
         if (u < kChunk * KF) st4(sh_q + k * KS + o, qr[i]);
     }
-    if (t < NP) {
+    if (t < NR) {
         sh_be[t] = be;
         sh_al[t] = al;
     }
     __syncthreads();
 
-    // 2. the blocks that do not need the checkpoint: wave 0 the Gram blocks and T, wave 1 the
-    //    masked A, the last wave the decays (one wave does all three when it is alone)
+    // 2. the blocks that do not need the checkpoint, one role per wave (roles share a wave when
+    //    there are fewer than four): the verified entries' Gram blocks and T; A; the decays (and
+    //    those of the folded block); the folded block's Gram and T. Then, when folding, every wave
+    //    forms F = K S0^T of the folded block for its i-blocks.
+    const float *vk = sh_k + vb * KS;
     if (wv == 0) {
 #pragma unroll
         for (int ib = 0; ib < NTM; ++ib) {
 #pragma unroll
             for (int jb = 0; jb <= ib; ++jb) {
                 const v4f gk = ib == jb
-                    ? row_dots16<KB, KS, NA, true>(sh_k + 16 * ib * KS, sh_k + 16 * ib * KS)
-                    : row_dots16<KB, KS, NA, false>(sh_k + 16 * ib * KS, sh_k + 16 * jb * KS);
+                    ? row_dots16<KB, KS, NA, true>(vk + 16 * ib * KS, vk + 16 * ib * KS)
+                    : row_dots16<KB, KS, NA, false>(vk + 16 * ib * KS, vk + 16 * jb * KS);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sh_G[(16 * ib + 4 * g + r) * PS + 16 * jb + cl] = gk[r];
             }
@@ -783,23 +812,95 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, N
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        t_solve_regs<NP, PS, PS>(sh_G, sh_be, sh_T);
+        t_solve_regs<NP, PS, PS>(sh_G, sh_be + vb, sh_T);
     }
-    if (wv == (NW > 1 ? 1 : 0)) {
+    if (wv == 1 % NW) {
 #pragma unroll
         for (int jb = 0; jb < NTM; ++jb) {
-            const v4f qk = row_dots16<KB, KS, NA, false>(sh_q, sh_k + 16 * jb * KS);   // q_{4g+r} . k_{16jb+c}
+            const v4f qk = row_dots16<KB, KS, NA, false>(sh_q, vk + 16 * jb * KS);   // q_{4g+r} . k_{16jb+c}
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 sh_A[(4 * g + r) * PS + 16 * jb + cl] = 16 * jb + cl <= len_e + 4 * g + r ? qk[r] : 0.f;
         }
     }
-    if (wv == NW - 1) decay_row<NP, PS>(sh_al, len_e + lane, sh_D, sh_gam);
+    if (wv == 3 % NW) {
+        decay_row<NP, PS>(sh_al + vb, len_e + lane, sh_D, sh_gam);
+        if (fold_here) decay_row<NP, PS>(sh_al, NP - 1, sh_Df, sh_gf);   // R[q] of the whole block
+    }
+    if constexpr (SPLIT) {
+        if (fold_here) {
+            if (wv == 2 % NW) {
+                const v4f gk = row_dots16<KB, KS, NA, true>(sh_k, sh_k);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sh_Gf[(4 * g + r) * PS + cl] = gk[r];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                t_solve_regs<NP, PS, PS>(sh_Gf, sh_be, sh_Tf);
+            }
+        }
+    }
+    v4f fz[IBW];                            // F[q = 4 g + r][i = 16 ib' + c] of the folded block
+    if constexpr (SPLIT) {
+        if (fold_here) {
+#pragma unroll
+            for (int ib = 0; ib < IBW; ++ib) {
+                v4f fp[NA];
+#pragma unroll
+                for (int n = 0; n < NA; ++n) fp[n] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);   // A: K[c][16 kb + 4 g + r]
+                    v4f &f = fp[kb % NA];
+                    f = mfma4(kv.x, s[ib][kb].x, f);
+                    f = mfma4(kv.y, s[ib][kb].y, f);
+                    f = mfma4(kv.z, s[ib][kb].z, f);
+                    f = mfma4(kv.w, s[ib][kb].w, f);
+                }
+                fz[ib] = tree_sum<NA>(fp);
+            }
+            mfma_settle();
+        }
+    }
     __syncthreads();
 
-    // 3. U = A T as U^T = T^T A^T, so that lane (g, c) ends with U[k = c][j = 16 jb + 4 g + r], the
-    //    A operand of the products below (T[i][j] = 0 for i < j); W = D o U; then the rows
-    //    r_k = q_k - sum_j U[k][j] k_j of the wave's k-blocks, written over the queries
+    // 3. when folding: Z = R o V - gam F, C = T Z, S0 <- gam S0 + C^T K, and the new checkpoint
+    //    goes out. Then U = A T as U^T = T^T A^T, so that lane (g, c) ends with
+    //    U[k = c][j = 16 jb + 4 g + r], the A operand of the products below (T[i][j] = 0 for
+    //    i < j); W = D o U; and the rows r_k = q_k - sum_j U[k][j] k_j of the wave's k-blocks,
+    //    written over the queries
+    if constexpr (SPLIT) {
+        if (fold_here) {
+            const float4 rf4 = ld4(sh_Df + 4 * g);                  // R[q = 4 g + r]
+            const float rf[4] = {rf4.x, rf4.y, rf4.z, rf4.w};
+            const float gf = sh_gf[0];
+            const float4 tv = ld4(sh_Tf + cl * PS + 4 * g);         // T[t = c][4 g + r]
+#pragma unroll
+            for (int ib = 0; ib < IBW; ++ib) {
+                const int i = 16 * (wv * IBW + ib) + cl;
+                float zf[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zf[r] = rf[r] * sh_v[(4 * g + r) * VS + i] - gf * fz[ib][r];
+                v4f cz = {0.f, 0.f, 0.f, 0.f};
+                cz = mfma4(tv.x, zf[0], cz);
+                cz = mfma4(tv.y, zf[1], cz);
+                cz = mfma4(tv.z, zf[2], cz);
+                cz = mfma4(tv.w, zf[3], cz);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    v4f u = {gf * s[ib][kb].x, gf * s[ib][kb].y, gf * s[ib][kb].z, gf * s[ib][kb].w};
+                    const float *kc = sh_k + (4 * g) * KS + 16 * kb + cl;   // K[t = 4 g + r][16 kb + c]
+                    u = mfma4(kc[0], cz[0], u);
+                    u = mfma4(kc[KS], cz[1], u);
+                    u = mfma4(kc[2 * KS], cz[2], u);
+                    u = mfma4(kc[3 * KS], cz[3], u);
+                    s[ib][kb] = make_float4(u[0], u[1], u[2], u[3]);
+                }
+            }
+            mfma_settle();
+            fold_store<DV, DK>(s, S0, t);
+        }
+    }
     float ua[NTM][4], wa[NTM][4];
 #pragma unroll
     for (int jb = 0; jb < NTM; ++jb) {
@@ -828,7 +929,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, N
         for (int jb = 0; jb < NTM; ++jb) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                rk = mfma4(-ua[jb][r], sh_k[(16 * jb + 4 * g + r) * KS + 16 * kb + cl], rk);
+                rk = mfma4(-ua[jb][r], vk[(16 * jb + 4 * g + r) * KS + 16 * kb + cl], rk);
         }
         const float rv[4] = {rk[0], rk[1], rk[2], rk[3]};
         asm volatile("" ::"v"(rv[0]), "v"(rv[1]), "v"(rv[2]), "v"(rv[3]));
@@ -856,7 +957,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, N
         v4f u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int jb = 0; jb < NTM; ++jb) {
-            const float *vc = sh_v + (16 * jb + 4 * g) * VS + i;            // B: V[16 jb + 4 g + r][i]
+            const float *vc = sh_v + (vb + 16 * jb + 4 * g) * VS + i;       // B: V[16 jb + 4 g + r][i]
 #pragma unroll
             for (int r = 0; r < 4; ++r) u = mfma4(wa[jb][r], vc[r * VS], u);
         }
@@ -871,18 +972,19 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, N
     }
 
     // 5. append the drafts as entries len_e .. ne - 1 (every ring read is done)
+    const int dr0 = vb + len_e;             // row of draft 0
     for (int i = t; i < K * KF; i += TPB) {
         const int k = i / KF, o = (i - k * KF) * 4;
-        st4(a.ring.k + (c.rh + (head_e + len_e + k) % W) * DK + o, ld4(sh_k + (len_e + k) * KS + o));
+        st4(a.ring.k + (c.rh + (head_e + len_e + k) % W) * DK + o, ld4(sh_k + (dr0 + k) * KS + o));
     }
     for (int i = t; i < K * VF; i += TPB) {
         const int k = i / VF, o = (i - k * VF) * 4;
-        st4(a.ring.v + (c.rh + (head_e + len_e + k) % W) * DV + o, ld4(sh_v + (len_e + k) * VS + o));
+        st4(a.ring.v + (c.rh + (head_e + len_e + k) % W) * DV + o, ld4(sh_v + (dr0 + k) * VS + o));
     }
     for (int k = t; k < K; k += TPB) {
         const size_t slot = c.rh + (head_e + len_e + k) % W;
-        a.ring.beta[slot] = sh_be[len_e + k];
-        a.ring.alpha[slot] = sh_al[len_e + k];
+        a.ring.beta[slot] = sh_be[dr0 + k];
+        a.ring.alpha[slot] = sh_al[dr0 + k];
     }
     if (c.h == 0 && t == 0) {
         a.bk.out[c.b] = head_e;
@@ -914,8 +1016,8 @@ hipError_t go_decode(const GdnStepArgs &a, int mode, hipStream_t s)
 template <int DV, int DK>
 size_t gdn_verify_lds_bytes(int W)
 {
-    const size_t np = W > 16 ? 32 : 16;
-    const size_t out = gdn_verify_lds<DV, DK>((int)np), fold = gdn_fold_lds<DV, DK>(W);
+    if (W <= 16) return 4 * (size_t)gdn_verify_lds<DV, DK, 1>();
+    const size_t out = gdn_verify_lds<DV, DK, 2>(), fold = gdn_fold_lds<DV, DK>(W);
     return 4 * (out > fold ? out : fold);
 }
 
