@@ -279,25 +279,36 @@ __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c,
 template <int DV, int DK>
 using FoldMap = MfmaTile<DV, DK>;
 
-// LDS rows of the fold: the window rounded up to whole 16-entry blocks.
-__host__ __device__ constexpr int fold_rows(int W) { return (W + 15) / 16 * 16; }
+// Waves per SIMD the kernels that fold (and the verify) are compiled for: three 8-wave workgroups
+// per compute unit at 128 x 128 with one entry block (at most 80 VGPRs), the compiler's choice
+// otherwise.
+template <int DV, int DK, int NTM>
+struct FoldOcc {
+    static constexpr int WPE = TileShape<DV, DK>::TPB == 512 && NTM == 1 ? 6 : 1;
+};
+
+// Entry blocks of the fold: one for W <= 16, two up to 32.
+__host__ __device__ constexpr int fold_blocks(int W) { return W > 16 ? 2 : 1; }
 
 template <int DV, int DK>
 __host__ __device__ constexpr int gdn_fold_lds(int W)
 {
-    // K [WP][DK+4], V [WP][DV+4], T [WP][WP+4], Gram [W][W+1], d [WP], gamma
-    return fold_rows(W) * (DK + 4 + DV + 4 + fold_rows(W) + 4 + 1) + W * (W + 1) + 1;
+    // K [NP][DK+4], V [NP][DV+4], beta [NP], decays d [NP], gamma [4], Gram and T [NP][NP+4]
+    const int NP = 16 * fold_blocks(W);
+    return NP * (DK + 4 + DV + 4) + 2 * NP + 4 + 2 * NP * (NP + 4);
 }
 
 // Fold n = nring (+1 with the token) entries, 1 <= n <= 16 NTM, (ring entries [0, nring) from
 // slot `head`, then the token (kt, vt, bet, alt) if tok) into the tile, which is read from S0t
-// (fold layout) after the entries' loads went out. All threads call it; three barriers.
+// (fold layout) after the entries' loads went out. All threads call it; two barriers. Wave 0
+// forms the Gram blocks on the matrix cores and solves T in registers (gdn_chunk.h) while every
+// wave forms Z = d o V - gamma K S0^T for its i-blocks; then C = T Z and S0 <- gamma S0 + C^T K.
 //
 // Every MFMA chain runs a compile-time number of steps (NTM blocks of 16 entries; rows past n are
 // zero), and its accumulator is first read in the same straight-line code that issued the chain:
 // a conditional chain followed by a read on the other side of a branch was given too few wait
 // states by the compiler (the read saw a stale accumulator register), so no chain sits in a
-// branch and no chain result is read across one.
+// branch and no chain result is read across one (the Gram chains of wave 0 are read inside it).
 template <int DV, int DK, int NTM, int IBW, int KB>
 __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem, const GdnRing &ring,
                                               const GTile &c, int head, int nring, bool tok,
@@ -308,33 +319,34 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
     static_assert(IBW == F::IBW && KB == F::KB, "fold block");
     static_assert(NTM == 1 || NTM == 2, "one or two 16-entry blocks");
     constexpr int TPB = F::TPB, KS = F::CS, VS = F::RS, KF = DK / 4, VF = DV / 4;
-    constexpr int XQ = (kMaxWindow * (KF + VF) + TPB - 1) / TPB;
-    constexpr int NP = 16 * NTM;        // entry rows, zero past n
+    constexpr int NP = 16 * NTM, PS = NP + 4;          // entry rows, zero past n
+    constexpr int KQ = (NP * KF + TPB - 1) / TPB, VQ = (NP * VF + TPB - 1) / TPB;
+    constexpr int NA = KB >= 2 ? 2 : 1;
     const int W = c.W, t = c.t, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
     const int n = nring + (tok ? 1 : 0);
-    const int WP = fold_rows(W), TS = WP + 4, W1 = W + 1;
-    float *sh_k = smem;                 // [WP][KS]
-    float *sh_v = sh_k + WP * KS;       // [WP][VS]
-    float *sh_T = sh_v + WP * VS;       // [WP][TS]
-    float *sh_G = sh_T + WP * TS;       // [W][W1]
-    float *sh_d = sh_G + W * W1;        // [WP]
-    float *sh_g = sh_d + WP;            // gamma
+    float *sh_k = smem;                 // [NP][KS]
+    float *sh_v = sh_k + NP * KS;       // [NP][VS]
+    float *sh_be = sh_v + NP * VS;      // [NP]
+    float *sh_d = sh_be + NP;           // [NP]
+    float *sh_g = sh_d + NP;            // gamma
+    float *sh_G = sh_g + 4;             // [NP][PS]
+    float *sh_T = sh_G + NP * PS;       // [NP][PS]
 
-    // 1. the entries' loads, then the tile's; stage the entries (zero rows up to NP), decay
-    //    ratios d_q and gamma (wave 0)
-    float4 xs[XQ];
+    // 1. the entries' loads, then the tile's; stage the entries (zero rows up to NP), beta, the
+    //    decay ratios d_q and gamma (wave 0)
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 kr[KQ], vr[VQ];
 #pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-        const int i = t + q * TPB;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < n * KF) {
-            const int j = i / KF, o = (i - j * KF) * 4;
-            v = j < nring ? ld4(ring.k + (c.rh + (head + j) % W) * DK + o) : ld4(kt + o);
-        } else if (i < n * (KF + VF)) {
-            const int i2 = i - n * KF, j = i2 / VF, o = (i2 - j * VF) * 4;
-            v = j < nring ? ld4(ring.v + (c.rh + (head + j) % W) * DV + o) : ld4(vt + o);
-        }
-        xs[q] = v;
+    for (int i = 0; i < KQ; ++i) {
+        const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
+        kr[i] = z4;
+        if (u < NP * KF && j < n) kr[i] = j < nring ? ld4(ring.k + (c.rh + (head + j) % W) * DK + o) : ld4(kt + o);
+    }
+#pragma unroll
+    for (int i = 0; i < VQ; ++i) {
+        const int u = t + i * TPB, j = u / VF, o = (u - j * VF) * 4;
+        vr[i] = z4;
+        if (u < NP * VF && j < n) vr[i] = j < nring ? ld4(ring.v + (c.rh + (head + j) % W) * DV + o) : ld4(vt + o);
     }
     float bel = 0.f, all = 1.f;
     if (wv == 0) {
@@ -348,37 +360,45 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
         for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
     }
 #pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-        const int i = t + q * TPB;
-        if (i < n * KF) {
-            const int j = i / KF, o = (i - j * KF) * 4;
-            st4(sh_k + j * KS + o, xs[q]);
-        } else if (i < n * (KF + VF)) {
-            const int i2 = i - n * KF, j = i2 / VF, o = (i2 - j * VF) * 4;
-            st4(sh_v + j * VS + o, xs[q]);
-        }
+    for (int i = 0; i < KQ; ++i) {
+        const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
+        if (u < NP * KF) st4(sh_k + j * KS + o, kr[i]);
     }
-    for (int i = t; i < (NP - n) * (KF + VF); i += TPB) {
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < (NP - n) * KF) {
-            const int j = i / KF;
-            st4(sh_k + (n + j) * KS + (i - j * KF) * 4, z);
-        } else {
-            const int i2 = i - (NP - n) * KF, j = i2 / VF;
-            st4(sh_v + (n + j) * VS + (i2 - j * VF) * 4, z);
-        }
+#pragma unroll
+    for (int i = 0; i < VQ; ++i) {
+        const int u = t + i * TPB, j = u / VF, o = (u - j * VF) * 4;
+        if (u < NP * VF) st4(sh_v + j * VS + o, vr[i]);
     }
     if (wv == 0) {
         float gam;
         const float d = wave_suffix_prod(all, n, gam);
-        if (lane < NP) sh_d[lane] = lane < n ? d : 0.f;
+        if (lane < NP) {
+            sh_be[lane] = bel;
+            sh_d[lane] = lane < n ? d : 0.f;
+        }
         if (lane == 0) sh_g[0] = gam;
     }
     __syncthreads();
 
-    // 2. Gram entries (every wave); Z = d_q v_q - gamma S0 k_q for the wave's i-blocks, with
-    //    S0 k_q from K S0^T on the matrix cores
-    gram_dots<DK, TPB, KS>(sh_k, nullptr, n, W1, sh_G, nullptr, t);
+    // 2. wave 0: the Gram blocks on the matrix cores, then T in registers; every wave:
+    //    Z = d_q v_q - gamma S0 k_q for its i-blocks, with S0 k_q from K S0^T
+    if (wv == 0) {
+#pragma unroll
+        for (int ib = 0; ib < NTM; ++ib) {
+#pragma unroll
+            for (int jb = 0; jb <= ib; ++jb) {
+                const v4f gk = ib == jb
+                    ? row_dots16<KB, KS, NA, true>(sh_k + 16 * ib * KS, sh_k + 16 * ib * KS)
+                    : row_dots16<KB, KS, NA, false>(sh_k + 16 * ib * KS, sh_k + 16 * jb * KS);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sh_G[(16 * ib + 4 * g + r) * PS + 16 * jb + cl] = gk[r];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        t_solve_regs<NP, PS, PS>(sh_G, sh_be, sh_T);
+    }
     const float gam = sh_g[0];
     v4f fz[IBW][NTM];
 #pragma unroll
@@ -386,15 +406,19 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
         const int i = 16 * (wv * IBW + ib) + cl;
 #pragma unroll
         for (int tb = 0; tb < NTM; ++tb) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            v4f fp[NA];
+#pragma unroll
+            for (int a = 0; a < NA; ++a) fp[a] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const float4 kv = ld4(sh_k + (16 * tb + cl) * KS + 16 * kb + 4 * g);
-                acc = mfma4(kv.x, s[ib][kb].x, acc);
-                acc = mfma4(kv.y, s[ib][kb].y, acc);
-                acc = mfma4(kv.z, s[ib][kb].z, acc);
-                acc = mfma4(kv.w, s[ib][kb].w, acc);
+                v4f &f = fp[kb % NA];
+                f = mfma4(kv.x, s[ib][kb].x, f);
+                f = mfma4(kv.y, s[ib][kb].y, f);
+                f = mfma4(kv.z, s[ib][kb].z, f);
+                f = mfma4(kv.w, s[ib][kb].w, f);
             }
+            const v4f acc = tree_sum<NA>(fp);
             // acc[r] = (S0 k_q)[i] for q = 16 tb + 4 g + r
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -405,11 +429,7 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
     }
     __syncthreads();
 
-    // 3. T (wave 0)
-    if (wv == 0) t_solve<64 / NP>(sh_G, W1, bel, n, NP, sh_T, TS);
-    __syncthreads();
-
-    // 4. C = T Z, then S0 <- gamma S0 + C^T K
+    // 3. C = T Z, then S0 <- gamma S0 + C^T K
 #pragma unroll
     for (int ib = 0; ib < IBW; ++ib) {
         v4f cz[NTM];
@@ -418,7 +438,7 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
             v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int tb = 0; tb <= tt; ++tb) {
-                const float4 tv = ld4(sh_T + (16 * tt + cl) * TS + 16 * tb + 4 * g);
+                const float4 tv = ld4(sh_T + (16 * tt + cl) * PS + 16 * tb + 4 * g);
                 acc = mfma4(tv.x, fz[ib][tb][0], acc);
                 acc = mfma4(tv.y, fz[ib][tb][1], acc);
                 acc = mfma4(tv.z, fz[ib][tb][2], acc);
@@ -493,9 +513,10 @@ __device__ __forceinline__ void gdn_fold_tile(const GdnFoldArgs &a, const GTile 
 
 // Decode variants, chosen on the host as for Mamba-2: 0 = every sequence at the ring position
 // (a.uhead, a.ulen) with no fold (ring loads before the checkpoint read), 1 = no sequence folds
-// (positions read from the device), 2 = any sequence may fold.
-template <int DV, int DK, int MODE>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB))
+// (positions read from the device), 2 = any sequence may fold (NTM entry blocks: one kernel per
+// block count, so that the one-block fold keeps its register budget).
+template <int DV, int DK, int MODE, int NTM = 1>
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (MODE == 2 ? FoldOcc<DV, DK, NTM>::WPE : 1))
 k_gdn_decode(GdnStepArgs a)
 {
     using M = Map4<DV, DK>;
@@ -524,8 +545,7 @@ k_gdn_decode(GdnStepArgs a)
         len = a.bk.in[B + c.b];
         fold = len + 1 >= W;
         if (!fold) gdn_replay<DV, DK, M::R, true>(a, c, head, len, s, smem);
-        else if (W > 16) gdn_fold_decode<DV, DK, 2>(a, c, head, len, smem);
-        else gdn_fold_decode<DV, DK, 1>(a, c, head, len, smem);
+        else gdn_fold_decode<DV, DK, NTM>(a, c, head, len, smem);
     }
     if (c.h == 0 && c.t == 0) {
         a.bk.out[c.b] = fold ? (head + len + 1) % W : head;
@@ -534,8 +554,8 @@ k_gdn_decode(GdnStepArgs a)
     }
 }
 
-template <int DV, int DK>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_fold(GdnFoldArgs a)
+template <int DV, int DK, int NTM>
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (FoldOcc<DV, DK, NTM>::WPE)) k_gdn_fold(GdnFoldArgs a)
 {
     constexpr int TPB = TileShape<DV, DK>::TPB;
     using M = Map4<DV, DK>;
@@ -559,8 +579,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_fold(GdnFoldAr
         }
         return;
     }
-    if (W > 16) gdn_fold_tile<DV, DK, 2>(a, c, head, len, smem);
-    else gdn_fold_tile<DV, DK, 1>(a, c, head, len, smem);
+    gdn_fold_tile<DV, DK, NTM>(a, c, head, len, smem);
 }
 
 // conventional read-modify-write comparator
@@ -651,13 +670,6 @@ __host__ __device__ constexpr int gdn_verify_lds()
     return VerifySplit<NTM>::value ? base + 2 * NP * PS + kChunk * PS + kChunk : base;
 }
 
-// Waves per SIMD the verify is compiled for: three 8-wave workgroups per compute unit at 128 x 128
-// (at most 80 VGPRs), the compiler's choice otherwise.
-template <int DV, int DK, int NTM>
-struct VerifyOcc {
-    static constexpr int WPE = TileShape<DV, DK>::TPB == 512 && NTM == 1 ? 6 : 1;
-};
-
 // Drafts k = 0..K-1 become entries len_e + k, and draft k's output is the replay (top of this
 // file) for q_k over the first m_k = len_e + k + 1 entries. Back substitution over a prefix is the
 // leading block of the substitution that T solves (gdn_chunk.h), so with A[k][i] = q_k . k_i for
@@ -674,7 +686,7 @@ struct VerifyOcc {
 // phases by the chunk fold of the prefill (F = K S0^T, C = T Z with Z_q = R[q] v_q - gam F_q,
 // S0 <- gam S0 + C^T K) while the drafts' blocks are formed, and the new checkpoint is written.
 template <int DV, int DK, int NTM>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (VerifyOcc<DV, DK, NTM>::WPE)) k_gdn_verify(GdnStepArgs a)
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (FoldOcc<DV, DK, NTM>::WPE)) k_gdn_verify(GdnStepArgs a)
 {
     using F = FoldMap<DV, DK>;
     constexpr int TPB = F::TPB, NW = F::NW, IBW = F::IBW, KB = F::KB, KS = F::CS, VS = F::RS;
@@ -1009,7 +1021,8 @@ hipError_t go_decode(const GdnStepArgs &a, int mode, hipStream_t s)
     const size_t lds = gdn_decode_lds<DV, DK>(a.d.W);
     if (mode == 0) hipLaunchKernelGGL((k_gdn_decode<DV, DK, 0>), grid, block, lds, s, a);
     else if (mode == 1) hipLaunchKernelGGL((k_gdn_decode<DV, DK, 1>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((k_gdn_decode<DV, DK, 2>), grid, block, lds, s, a);
+    else if (a.d.W > 16) hipLaunchKernelGGL((k_gdn_decode<DV, DK, 2, 2>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_gdn_decode<DV, DK, 2, 1>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
@@ -1036,7 +1049,8 @@ hipError_t go_fold(const GdnFoldArgs &a, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(TileShape<DV, DK>::TPB);
     const size_t lds = 4 * (size_t)gdn_fold_lds<DV, DK>(a.d.W);
-    hipLaunchKernelGGL((k_gdn_fold<DV, DK>), grid, block, lds, s, a);
+    if (a.d.W > 16) hipLaunchKernelGGL((k_gdn_fold<DV, DK, 2>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_gdn_fold<DV, DK, 1>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
