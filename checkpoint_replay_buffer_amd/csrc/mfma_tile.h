@@ -66,27 +66,4 @@ __device__ __forceinline__ float readlane_f(float v, int lane)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// T by forward substitution, in one wave: T[t][q] = beta_t ([t == q] - sum_{i<t} G_it T[i][q])
-// with G_it = sh_G[i W1 + t] (i < t). Column q is lane group q / LPC (LPC = 64 / np lanes, each
-// summing every LPC-th i); rows n..np-1 are zero. beta_t is on lane t (`bel`).
-template <int LPC>
-__device__ __forceinline__ void t_solve(const float *sh_G, int W1, float bel, int n, int np,
-                                        float *sh_T, int TS)
-{
-    const int lane = threadIdx.x & 63, q = lane / LPC, part = lane - q * LPC;
-    for (int t = 0; t < n; ++t) {
-        float acc = 0.f;
-        for (int i = part; i < t; i += LPC) acc += sh_G[i * W1 + t] * sh_T[i * TS + q];
-        acc = group_sum<LPC>(acc);
-        const float b = readlane_f(bel, t);
-        if (part == 0) sh_T[t * TS + q] = b * ((t == q ? 1.f : 0.f) - acc);
-        // row t is read by every lane of the wave in the next steps
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    for (int t = n; t < np; ++t)
-        if (part == 0) sh_T[t * TS + q] = 0.f;
-}
-
 }  // namespace rssm
