@@ -6,6 +6,7 @@
 // ndraft), read from bk.in and written to bk.out.
 #include "dev_common.h"
 #include "internal.h"
+#include "gdn_layout.h"
 
 namespace rssm {
 namespace {
@@ -14,10 +15,11 @@ constexpr uint32_t kCommitRange = 1u;
 constexpr uint32_t kRollbackRange = 2u;
 
 // One workgroup per (b, h) tile: copy the initial state of selected sequences into S0 (and its
-// bf16 copy) and reset their bookkeeping.
+// bf16 copy) and reset their bookkeeping. ckpt_dv > 0: S0 in the layout of gdn_layout.h (tiles
+// of ckpt_dv rows).
 __global__ void __launch_bounds__(256) k_init(float *S0, uint16_t *S0b, const float *state,
                                               const int32_t *mask, Bk bk, uint32_t *err, int B,
-                                              int H, long tile_elems)
+                                              int H, long tile_elems, int ckpt_dv)
 {
     const int tile = blockIdx.x;
     const int b = tile / H, h = tile - b * H;
@@ -32,7 +34,13 @@ __global__ void __launch_bounds__(256) k_init(float *S0, uint16_t *S0b, const fl
     const size_t base = (size_t)tile * tile_elems;
     for (long i = threadIdx.x; i < tile_elems / 4; i += blockDim.x) {
         const float4 v = ld4_nt(state + base + 4 * i);
-        st4(S0 + base + 4 * i, v);
+        if (ckpt_dv > 0) {
+            const long cols = tile_elems / ckpt_dv;
+            const int row = (int)(4 * i / cols), col = (int)(4 * i - row * cols);
+            st4(S0 + base + ckpt_offset(row, col, ckpt_dv), v);
+        } else {
+            st4(S0 + base + 4 * i, v);
+        }
         if (S0b) {
             uint2 w;
             w.x = pack_bf16x2(v.x, v.y);
@@ -81,10 +89,11 @@ __global__ void k_clear(uint32_t *w) { *w = 0u; }
 }  // namespace
 
 hipError_t init_checkpoint(float *S0, uint16_t *S0b, const float *state, const int32_t *mask,
-                           Bk bk, uint32_t *err, int B, int H, long tile_elems, hipStream_t s)
+                           Bk bk, uint32_t *err, int B, int H, long tile_elems, int ckpt_dv,
+                           hipStream_t s)
 {
     hipLaunchKernelGGL(k_init, dim3(B * H), dim3(256), 0, s, S0, S0b, state, mask, bk, err, B, H,
-                       tile_elems);
+                       tile_elems, ckpt_dv);
     return hipGetLastError();
 }
 

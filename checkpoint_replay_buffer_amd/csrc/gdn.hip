@@ -25,6 +25,7 @@
 #include "tile_order.h"
 #include "mfma_tile.h"
 #include "gdn_chunk.h"
+#include "gdn_layout.h"
 
 namespace rssm {
 namespace {
@@ -157,30 +158,41 @@ __device__ __forceinline__ float lane_value(float v, int lane)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// LOAD = true: the checkpoint tile s is read here, after the ring loads went out (the ring position
-// is known without a device read); LOAD = false: the caller already issued it.
-template <int DV, int DK, int R, bool LOAD>
-__device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c, int head, int len,
-                                           float4 (&s)[R], float *smem)
+// LDS floats of the replay: k and v rows of the W entries, q, the Gram entries [W][W+1], u [W],
+// and per wave r [DK] and the value-sum coefficients [32].
+template <int DV, int DK>
+__host__ __device__ constexpr int gdn_replay_lds(int W)
 {
-    constexpr int TPB = TileShape<DV, DK>::TPB;
-    using M = Map4<DV, DK>;
-    static_assert(R == M::R, "tile block");
-    constexpr int LPR = M::LPR, DUP = LPR / R;
+    return W * (DK + DV) + DK + W * (W + 1) + W + (TileShape<DV, DK>::TPB / 64) * (DK + 32);
+}
+
+// The tile is held as in the fold (lane (g, c) of wave w keeps S[16 (w IBW + ib) + c][16 kb + 4 g
+// .. +3]), which the checkpoint layout makes 1 KB per load instruction. LOAD = true: the tile is
+// read here, after the ring loads went out (the ring position is known without a device read);
+// LOAD = false: the caller already issued it.
+template <int DV, int DK, bool LOAD>
+__device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c, int head, int len,
+                                           float4 (&s)[MfmaTile<DV, DK>::IBW][MfmaTile<DV, DK>::KB],
+                                           float *smem)
+{
+    using F = MfmaTile<DV, DK>;
+    constexpr int TPB = F::TPB, IBW = F::IBW, KB = F::KB;
     constexpr int KF = DK / 4, VF = DV / 4;
     constexpr int XQ = (16 * (KF + VF) + TPB - 1) / TPB;   // float4 staged in registers (W <= 16)
-    const int W = c.W, t = c.t, m = len + 1, W1 = W + 1, lane = t & 63;
-    const int rg = t / LPR, cg = t - rg * LPR, c0 = cg * 4;
+    const int W = c.W, t = c.t, m = len + 1, W1 = W + 1, lane = t & 63, wv = t >> 6;
+    const int g = lane >> 4, cl = lane & 15;
     float *sh_k = smem;                 // [m][DK]
     float *sh_v = sh_k + W * DK;        // [m][DV]
     float *sh_q = sh_v + W * DV;        // [DK]
     float *sh_G = sh_q + DK;            // [m][W1]  k_l . k_i, l < i
     float *sh_u = sh_G + W * W1;        // [m]      k_j . q
+    float *sh_r = sh_u + W + wv * (DK + 32);   // [DK]  this wave's copy of r
+    float *sh_cv = sh_r + DK;                  // [32]  d_j beta_j c_j, 0 past m
 
     const float *qt = a.q + c.bh * DK, *kt = a.k + c.bh * DK, *vt = a.v + c.bh * DV;
     const float bet = a.beta[c.bh], alt = a.alpha[c.bh];
     const int slot = (head + len) % W;
-    // ring-side loads: beta / alpha of entry `lane` (every wave), k and v rows of all entries
+    // ring-side loads: beta / alpha of entry `lane` (every wave), k and v rows of all entries, q
     const float bel = lane < len ? a.ring.beta[c.rh + (head + lane) % W] : bet;
     const float all = lane < len ? a.ring.alpha[c.rh + (head + lane) % W] : alt;
     float4 xs[XQ];
@@ -197,12 +209,8 @@ __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c,
         }
         xs[q] = v;
     }
-    const float4 qv = ld4(qt + c0);
-    if constexpr (LOAD) {
-        const size_t off = c.bh * (size_t)(DV * DK) + (size_t)(rg * R) * DK + c0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) s[r] = ld4_nt(a.S0 + off + (size_t)r * DK);
-    }
+    const float4 qv = t < KF ? ld4(qt + 4 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (LOAD) ckpt_load<DV>(s, a.S0 + c.bh * (size_t)(DV * DK), t);
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
         const int i = t + q * TPB;
@@ -223,7 +231,7 @@ __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c,
             st4(sh_v + j * DV + o, j < len ? ld4(a.ring.v + (c.rh + (head + j) % W) * DV + o) : ld4(vt + o));
         }
     }
-    if (rg == 0) st4(sh_q + c0, qv);
+    if (t < KF) st4(sh_q + 4 * t, qv);
     __syncthreads();
     gram_dots<DK, TPB>(sh_k, sh_q, m, W1, sh_G, sh_u, t);
     __syncthreads();
@@ -240,26 +248,62 @@ __device__ __forceinline__ void gdn_replay(const GdnStepArgs &a, const GTile &c,
     const float bc = bel * val;                           // beta_j c_j
     const float cv = d * bc;
 
-    // r = q - sum_j beta_j c_j k_j on the lane's columns, then S0 r
-    float4 rv = qv;
-    for (int j = 0; j < m; ++j) {
-        const float b = lane_value(bc, j);
-        const float4 kj = ld4(sh_k + j * DK + c0);
-        rv.x -= b * kj.x; rv.y -= b * kj.y; rv.z -= b * kj.z; rv.w -= b * kj.w;
-    }
-    float part[R];
+    // r = q - sum_j beta_j c_j k_j into this wave's copy (CPL consecutive columns per lane) and
+    // d_j beta_j c_j into the wave's coefficient row, both before the checkpoint is needed. The
+    // loops run whole groups of eight entries without branches (coefficient 0 and a valid row past
+    // m), so their LDS loads are in flight together.
+    constexpr int CPL = DK >= 64 ? DK / 64 : 1;
+    static_assert(CPL == 1 || CPL == 2, "r columns per lane");
+    if (lane < 32) sh_cv[lane] = lane < m ? cv : 0.f;
+    if (lane * CPL < DK) {
+        const int col = lane * CPL;
+        float r0 = sh_q[col], r1 = CPL == 2 ? sh_q[col + 1] : 0.f;
+        for (int j0 = 0; j0 < m; j0 += 8) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) part[r] = s[r].x * rv.x + s[r].y * rv.y + s[r].z * rv.z + s[r].w * rv.w;
-    int rsel;
-    const float z = row_reduce_scatter<R, LPR>(part, cg, rsel);
-    const int row = rg * R + rsel, k = cg & (DUP - 1);
-    float acc = 0.f;
-    for (int j = 0; j < m; ++j) {                         // split over the DUP lanes of the row
-        const float w = lane_value(cv, j);
-        if ((j & (DUP - 1)) == k) acc += w * sh_v[j * DV + row];
+            for (int jj = 0; jj < 8; ++jj) {
+                const int j = j0 + jj, jr = j < m ? j : m - 1;
+                const float b = j < m ? lane_value(bc, j & 63) : 0.f;
+                if constexpr (CPL == 2) {
+                    const float2 kv = *reinterpret_cast<const float2 *>(sh_k + jr * DK + col);
+                    r0 -= b * kv.x;
+                    r1 -= b * kv.y;
+                } else {
+                    r0 -= b * sh_k[jr * DK + col];
+                }
+            }
+        }
+        if constexpr (CPL == 2) *reinterpret_cast<float2 *>(sh_r + col) = make_float2(r0, r1);
+        else sh_r[col] = r0;
     }
-    acc = group_sum<DUP>(acc);
-    if (k == 0) a.o[c.bh * DV + row] = gam * z + acc;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // o = gamma S0 r + sum_j d_j beta_j c_j v_j for the wave's rows: lane (g, c) takes its four
+    // columns of each k-block and the entries j = g mod 4; the four lanes of a row are added by two
+    // exchanges
+#pragma unroll
+    for (int ib = 0; ib < IBW; ++ib) {
+        const int row = 16 * (wv * IBW + ib) + cl;
+        float u = 0.f;
+        for (int j0 = 0; j0 < m; j0 += 16) {
+#pragma unroll
+            for (int jj = 0; jj < 16; jj += 4) {
+                const int j = j0 + jj + g, jr = j < m ? j : m - 1;
+                u += sh_cv[j & 31] * sh_v[jr * DV + row];
+            }
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const float4 rq = ld4(sh_r + 16 * kb + 4 * g);
+            p += s[ib][kb].x * rq.x + s[ib][kb].y * rq.y + s[ib][kb].z * rq.z + s[ib][kb].w * rq.w;
+        }
+        p = gam * p + u;
+        p += __shfl_xor(p, 16);
+        p += __shfl_xor(p, 32);
+        if (g == 0) a.o[c.bh * DV + row] = p;
+    }
 
     // Append the token as entry len (its slot is none of the entries read above); after the last
     // barrier, so no barrier waits for these stores.
@@ -353,12 +397,7 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
         bel = lane < nring ? ring.beta[c.rh + (head + lane) % W] : (lane < n ? bet : 0.f);
         all = lane < nring ? ring.alpha[c.rh + (head + lane) % W] : (lane < n ? alt : 1.f);
     }
-#pragma unroll
-    for (int ib = 0; ib < IBW; ++ib) {
-        const float *src = S0t + mfma_tile_offset<DV, DK>(t, ib);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
-    }
+    ckpt_load<DV>(s, S0t, t);
 #pragma unroll
     for (int i = 0; i < KQ; ++i) {
         const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
@@ -460,8 +499,9 @@ __device__ __forceinline__ void gdn_fold_mfma(float4 (&s)[IBW][KB], float *smem,
     }
 }
 
+// The tile, held in the operand layout, written row-major (materialisation).
 template <int DV, int DK, int IBW, int KB>
-__device__ __forceinline__ void fold_store(const float4 (&s)[IBW][KB], float *dst, int t)
+__device__ __forceinline__ void store_rows(const float4 (&s)[IBW][KB], float *dst, int t)
 {
 #pragma unroll
     for (int ib = 0; ib < IBW; ++ib) {
@@ -484,7 +524,7 @@ __device__ __forceinline__ void gdn_fold_decode(const GdnStepArgs &a, const GTil
     float4 s[F::IBW][F::KB];
     gdn_fold_mfma<DV, DK, NTM>(s, smem, a.ring, c, head, len, true, a.k + c.bh * DK,
                                a.v + c.bh * DV, a.beta[c.bh], a.alpha[c.bh], S0);
-    fold_store<DV, DK>(s, S0, t);
+    ckpt_store<DV>(s, S0, t);
 #pragma unroll
     for (int ib = 0; ib < F::IBW; ++ib) {
         float p = 0.f;
@@ -508,7 +548,9 @@ __device__ __forceinline__ void gdn_fold_tile(const GdnFoldArgs &a, const GTile 
     float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
     float4 s[F::IBW][F::KB];
     gdn_fold_mfma<DV, DK, NTM>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f, S0);
-    fold_store<DV, DK>(s, a.out ? a.out + c.bh * (size_t)(DV * DK) : S0, c.t);
+    mfma_settle();                      // the tile is read on either side of the branch below
+    if (a.out) store_rows<DV, DK>(s, a.out + c.bh * (size_t)(DV * DK), c.t);
+    else ckpt_store<DV>(s, S0, c.t);
 }
 
 // Decode variants, chosen on the host as for Mamba-2: 0 = every sequence at the ring position
@@ -519,32 +561,29 @@ template <int DV, int DK, int MODE, int NTM = 1>
 __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (MODE == 2 ? FoldOcc<DV, DK, NTM>::WPE : 1))
 k_gdn_decode(GdnStepArgs a)
 {
-    using M = Map4<DV, DK>;
+    using F = MfmaTile<DV, DK>;
     extern __shared__ float smem[];
     const GTile c = make_gtile(a.d, MODE == 2 ? kIdentity : kRuns);
     const int B = a.d.B, W = c.W;
-    float4 s[M::R];
+    float4 s[F::IBW][F::KB];
     int head, len;
     bool fold = false;
     if constexpr (MODE == 0) {
         head = a.uhead;
         len = a.ulen;
-        gdn_replay<DV, DK, M::R, true>(a, c, head, len, s, smem);
+        gdn_replay<DV, DK, true>(a, c, head, len, s, smem);
     } else if constexpr (MODE == 1) {
         // the checkpoint tile first, then the ring position
-        const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
-        const size_t off = c.bh * (size_t)(DV * DK) + (size_t)(rg * M::R) * DK + c0;
-#pragma unroll
-        for (int r = 0; r < M::R; ++r) s[r] = ld4_nt(a.S0 + off + (size_t)r * DK);
+        ckpt_load<DV>(s, a.S0 + c.bh * (size_t)(DV * DK), c.t);
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
-        gdn_replay<DV, DK, M::R, false>(a, c, head, len, s, smem);
+        gdn_replay<DV, DK, false>(a, c, head, len, s, smem);
     } else {
-        // the ring position first: the fold and the replay read the tile with different maps
+        // the ring position first: the fold issues the entries' loads before the tile's
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
         fold = len + 1 >= W;
-        if (!fold) gdn_replay<DV, DK, M::R, true>(a, c, head, len, s, smem);
+        if (!fold) gdn_replay<DV, DK, true>(a, c, head, len, s, smem);
         else gdn_fold_decode<DV, DK, NTM>(a, c, head, len, smem);
     }
     if (c.h == 0 && c.t == 0) {
@@ -558,7 +597,6 @@ template <int DV, int DK, int NTM>
 __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (FoldOcc<DV, DK, NTM>::WPE)) k_gdn_fold(GdnFoldArgs a)
 {
     constexpr int TPB = TileShape<DV, DK>::TPB;
-    using M = Map4<DV, DK>;
     extern __shared__ float smem[];
     const GTile c = make_gtile(a.d, kIdentity);
     const int B = a.d.B, W = c.W;
@@ -575,7 +613,10 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (FoldOcc<DV, DK, NTM
     if (!fold) {
         if (a.out) {
             float *dst = a.out + c.bh * (size_t)(DV * DK);
-            for (int i = c.t; i < DV * DK / 4; i += TPB) st4(dst + 4 * i, ld4(S0 + 4 * i));
+            for (int i = c.t; i < DV * DK / 4; i += TPB) {     // row-major from the checkpoint layout
+                const int row = 4 * i / DK, col = 4 * i - row * DK;
+                st4(dst + 4 * i, ld4(S0 + ckpt_offset(row, col, DV)));
+            }
         }
         return;
     }
@@ -715,7 +756,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (FoldOcc<DV, DK, NTM
     if constexpr (!SPLIT) {
         if (prefold) {
             gdn_fold_mfma<DV, DK, NTM>(s, smem, a.ring, c, head, len, false, nullptr, nullptr, 0.f, 0.f, S0);
-            fold_store<DV, DK>(s, S0, t);
+            ckpt_store<DV>(s, S0, t);
             mfma_settle();                  // the tile is read by the chains below
             __syncthreads();                // the fold's LDS is reused
         }
@@ -775,14 +816,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (FoldOcc<DV, DK, NTM
             al = a.alpha[d];
         }
     }
-    if (SPLIT || !prefold) {
-#pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            const float *src = S0 + mfma_tile_offset<DV, DK>(t, ib);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
-        }
-    }
+    if (SPLIT || !prefold) ckpt_load<DV>(s, S0, t);
 #pragma unroll
     for (int i = 0; i < KQ; ++i) {
         const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
@@ -910,7 +944,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (FoldOcc<DV, DK, NTM
                 }
             }
             mfma_settle();
-            fold_store<DV, DK>(s, S0, t);
+            ckpt_store<DV>(s, S0, t);
         }
     }
     float ua[NTM][4], wa[NTM][4];
@@ -1008,8 +1042,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (FoldOcc<DV, DK, NTM
 template <int DV, int DK>
 size_t gdn_decode_lds(int W)
 {
-    const size_t W1 = W + 1;
-    const size_t replay = (size_t)W * (DK + DV) + DK + W * W1 + W;
+    const size_t replay = gdn_replay_lds<DV, DK>(W);
     const size_t fold = gdn_fold_lds<DV, DK>(W);
     return 4 * (replay > fold ? replay : fold);
 }

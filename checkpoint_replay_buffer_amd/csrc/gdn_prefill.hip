@@ -18,6 +18,7 @@
 #include "dev_common.h"
 #include "internal.h"
 #include "gdn_chunk.h"
+#include "gdn_layout.h"
 #include "mfma_tile.h"
 
 namespace rssm {
@@ -138,12 +139,7 @@ __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPr
     rows.load(q0, k0, v0, b0, a0, BH, T < kChunk ? T : kChunk, t);
     float4 s[IBW][KB];
     float *S0 = a.S0 + bh * (size_t)(DV * DK);
-#pragma unroll
-    for (int ib = 0; ib < IBW; ++ib) {
-        const float *src = S0 + mfma_tile_offset<DV, DK, F::NW>(t, ib);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(src + 16 * kb);
-    }
+    ckpt_load<DV>(s, S0, t);
 
     int buf = 0;
     for (int t0 = 0; t0 < T; t0 += kChunk, buf ^= 1) {
@@ -269,12 +265,7 @@ __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPr
     }
 
     // the final state is the new checkpoint; the ring is empty
-#pragma unroll
-    for (int ib = 0; ib < IBW; ++ib) {
-        float *dst = S0 + mfma_tile_offset<DV, DK, F::NW>(t, ib);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) st4_nt(dst + 16 * kb, s[ib][kb]);
-    }
+    ckpt_store<DV>(s, S0, t);
     if (h == 0 && t == 0) {
         a.bk.out[b] = a.bk.in[b];
         a.bk.out[B + b] = 0;

@@ -269,7 +269,8 @@ rssm_status rssm_init_checkpoint(rssm_ctx *ctx, const float *state, const int32_
     if (seq_mask && !ctx->initialized) return RSSM_E_STATE;   // the first load must cover all
     const rssm_config &c = ctx->cfg;
     const hipError_t e = init_checkpoint(ctx->S0, ctx->S0b, state, seq_mask, flip(ctx), ctx->err,
-                                         c.batch, c.nheads, (long)c.dim_v * c.dim_k, strm(stream));
+                                         c.batch, c.nheads, (long)c.dim_v * c.dim_k,
+                                         c.kind == RSSM_GDN ? c.dim_v : 0, strm(stream));
     const rssm_status s = launched(ctx, e, true);
     if (s == RSSM_OK) {
         ctx->initialized = true;

@@ -168,8 +168,11 @@ hipError_t gdn_rmw(const GdnRmwArgs &a, hipStream_t s);
 hipError_t gdn_verify(const GdnStepArgs &a, hipStream_t s);
 hipError_t gdn_prefill(const GdnPrefillArgs &a, hipStream_t s);
 
+// ckpt_dv > 0: the tiles are Gated DeltaNet checkpoints with ckpt_dv rows, stored in the layout
+// of gdn_layout.h; 0: row-major (Mamba-2).
 hipError_t init_checkpoint(float *S0, uint16_t *S0b, const float *state, const int32_t *mask,
-                           Bk bk, uint32_t *err, int B, int H, long tile_elems, hipStream_t s);
+                           Bk bk, uint32_t *err, int B, int H, long tile_elems, int ckpt_dv,
+                           hipStream_t s);
 hipError_t bk_commit(Bk bk, const int32_t *accepted, uint32_t *err, int B, hipStream_t s);
 hipError_t bk_rollback(Bk bk, const int32_t *new_len, uint32_t *err, int B, hipStream_t s);
 hipError_t slot_commit(int32_t *slot_of, const int32_t *accepted, int B, int K, hipStream_t s);
