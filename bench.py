@@ -65,6 +65,56 @@ def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
+def _repeat_ms(torch, first_ms, reps, restart, step, K):
+    """The timed region repeated: `first_ms` is the first run; each further run restarts the
+    context (`restart`, untimed) and times the same K steps. Returns median, min and max of the
+    runs in ms per step."""
+    runs = [first_ms]
+    for _ in range(reps - 1):
+        restart()
+        torch.cuda.synchronize()
+        ev = _events(torch, 2)
+        ev[0].record()
+        for t in range(K):
+            step(t)
+        ev[1].record()
+        torch.cuda.synchronize()
+        runs.append(ev[0].elapsed_time(ev[1]))
+    per = sorted(r / K for r in runs)
+    return {"n": len(runs), "median": round(per[len(per) // 2], 5), "min": round(per[0], 5),
+            "max": round(per[-1], 5)}
+
+
+def measure_copy_gbs(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate on this machine ((read + write) bytes / time): the practical ceiling
+    the HBM-bound legs are also quoted against."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms / 1e3) / 1e9
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _src_hash(files) -> str:
     h = hashlib.sha256()
     for f in files:
@@ -140,6 +190,7 @@ def run_m2(args, torch, rb, wl):
     torch.cuda.synchronize()
 
     # timed region: K steps bracketed by events only (wall time of the whole job)
+    reps = None
     if not args.graph:
         ev = _events(torch, 2)
         ev[0].record()
@@ -150,6 +201,8 @@ def run_m2(args, torch, rb, wl):
         total_ms = ev[0].elapsed_time(ev[1])
         h, l, n, e = ctx.bookkeeping()
         assert e == 0 and l[0] == K % W, "unexpected bookkeeping after the timed steps"
+        reps = _repeat_ms(torch, total_ms, args.reps, lambda: ctx.init_checkpoint(s0),
+                          lambda t: ctx.decode_step(y, **pool[t % pool_n]), K)
 
     # the same K steps again with an event pair around every launch (per-kernel durations on the
     # stream the kernels run on)
@@ -230,6 +283,7 @@ def run_m2(args, torch, rb, wl):
                    "groups": sh.ngroups, "input_pool_slots": pool_n,
                    "launch": "hip graph of 2 W steps, replayed" if args.graph else "eager"},
         "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
+        "ms_per_step_reps": reps,
         "state_gbs": round(state_bytes / replay_s / 1e9, 1),
         "tokens_per_s": round(B * K / replay_s, 1),
         "rmw_ms_per_step": round(rmw_s * 1e3 / K, 5) if rmw_s else None,
@@ -809,6 +863,7 @@ def run_gdn(args, torch, rb, wl):
         ctx.decode_step(o, **pool[t % S])
     ctx.init_checkpoint(s0)
     torch.cuda.synchronize()
+    reps = None
     if not args.graph:
         ev = _events(torch, 2)
         ev[0].record()
@@ -817,6 +872,8 @@ def run_gdn(args, torch, rb, wl):
         ev[1].record()
         torch.cuda.synchronize()
         total_ms = ev[0].elapsed_time(ev[1])
+        reps = _repeat_ms(torch, total_ms, args.reps, lambda: ctx.init_checkpoint(s0),
+                          lambda t: ctx.decode_step(o, **pool[t % S]), K)
     ctx.init_checkpoint(s0)
     torch.cuda.synchronize()
     evl = _events(torch, 2 * K)
@@ -868,6 +925,7 @@ def run_gdn(args, torch, rb, wl):
                    "batch": B, "heads": H, "d_k": DK, "d_v": DV, "window": W, "input_pool_slots": S,
                    "launch": "hip graph of 2 W steps, replayed" if args.graph else "eager"},
         "pct_hbm_peak": round(100 * alg / replay_s / 1e9 / HBM_PEAK_GBS, 2),
+        "ms_per_step_reps": reps,
         "tokens_per_s": round(B * K / replay_s, 1),
         "rmw_ms_per_step": round(rmw_s * 1e3 / K, 5),
         "rmw_gbs": round(rmw_bytes / rmw_s / 1e9, 1),
@@ -904,9 +962,13 @@ def cpu_baseline_gdn(sh, wl, budget_s=8.0):
         oracle.gdn_step(*(toks[t % 4][k] for k in ("q", "k", "v", "beta", "alpha")), state)
     el = time.perf_counter() - t0
     tok_s = sh.batch * steps / el
+    one_core = _single_core(lambda k, st: oracle.gdn_step(*(k[n] for n in ("q", "k", "v", "beta",
+                                                                            "alpha")), st),
+                            toks, state, sh.batch, cores)
     return {"value": round(2 * sh.d_v * sh.d_k * 8 * sh.nheads * tok_s / 1e9, 3),
             "unit": "GB/s (fp64 state read+write)", "cores": cores, "kind": "oracle",
-            "tokens_per_s": round(tok_s, 1),
+            "tokens_per_s": round(tok_s, 1), "cpu_model": _cpu_model(),
+            "single_core_tokens_per_s": one_core,
             "sample": f"first {steps} decode steps of all {sh.batch} sequences, conventional fp64 "
                       f"recurrence, {el:.1f} s"}
 
@@ -959,10 +1021,30 @@ def cpu_baseline_m2(sh, prm, wl, budget_s=12.0):
     tok_s = nseq * steps / el
     # the oracle reads and rewrites the fp64 state once per token
     gbs = 2 * sh.head_dim * sh.d_state * 8 * sh.nheads * tok_s / 1e9
+    one_core = _single_core(lambda k, st: oracle.m2_step(prm["A"], prm["D"], k["x"], k["B"], k["C"],
+                                                         k["dt"], st),
+                            toks, state, nseq, cores)
     return {"value": round(gbs, 3), "unit": "GB/s (fp64 state read+write)", "cores": cores,
-            "kind": "oracle", "tokens_per_s": round(tok_s, 1),
+            "kind": "oracle", "tokens_per_s": round(tok_s, 1), "cpu_model": _cpu_model(),
+            "single_core_tokens_per_s": one_core,
             "sample": f"first {steps} decode steps of sequences 0..{nseq - 1} (all {sh.nheads} heads) "
                       f"of the same seeded schedule, conventional fp64 recurrence, {el:.1f} s"}
+
+
+def _single_core(step, toks, state, nseq, cores, budget_s=2.0):
+    """The same oracle step on one thread (about `budget_s` of work), tokens/s; the thread count is
+    restored afterwards."""
+    import oracle
+    oracle.set_threads(1)
+    try:
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            step(toks[n % len(toks)], state)
+            n += 1
+        el = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(cores)
+    return round(nseq * n / el, 1)
 
 
 def calibrate_copy(torch, nbytes=1 << 30, reps=3):
@@ -994,6 +1076,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rmw", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="serving legs: runs of the timed region (the first gives value)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -1052,6 +1136,10 @@ def main():
         line, (sh, prm) = run_m2(args, torch, rb, wl)
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_m2(sh, prm, wl)
+    if args.workload in ("m2_serve", "m2_serve_bf16", "gdn_serve", "m2_spec", "gdn_spec", "m2_fork"):
+        cg = measure_copy_gbs(torch)
+        line["copy_gbs"] = round(cg, 1)
+        line["pct_of_copy"] = round(100 * line["value"] / cg, 1)
     print(json.dumps(line), flush=True)
 
 
