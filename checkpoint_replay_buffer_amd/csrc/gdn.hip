@@ -81,30 +81,6 @@ __device__ __forceinline__ float lds_dot(const float *a, const float *b, int lan
     return s;
 }
 
-// Stage n entries (ring entries [0, nring) from slot `head`, then the token `tok` if given) of
-// k, v, beta, alpha into LDS.
-template <int DV, int DK, int TPB>
-__device__ __forceinline__ void stage_entries(const GdnRing &ring, const GTile &c, int head, int nring,
-                                              bool tok, const float *kt, const float *vt, float bet,
-                                              float alt, float *sh_k, float *sh_v, float *sh_be,
-                                              float *sh_al)
-{
-    const int W = c.W, t = c.t, n = nring + (tok ? 1 : 0);
-    for (int j = t; j < n; j += TPB) {
-        sh_be[j] = j < nring ? ring.beta[c.rh + (head + j) % W] : bet;
-        sh_al[j] = j < nring ? ring.alpha[c.rh + (head + j) % W] : alt;
-    }
-    constexpr int KF = DK / 4, VF = DV / 4;
-    for (int i = t; i < n * KF; i += TPB) {
-        const int j = i / KF, q = (i - j * KF) * 4;
-        st4(sh_k + j * DK + q, j < nring ? ld4(ring.k + (c.rh + (head + j) % W) * DK + q) : ld4(kt + q));
-    }
-    for (int i = t; i < n * VF; i += TPB) {
-        const int j = i / VF, q = (i - j * VF) * 4;
-        st4(sh_v + j * DV + q, j < nring ? ld4(ring.v + (c.rh + (head + j) % W) * DV + q) : ld4(vt + q));
-    }
-}
-
 // Gram entries G[l][i] = k_l . k_i (l < i < n), row stride W1; with q != nullptr also
 // u_j = k_j . q into sh_u. Lane groups of LPD lanes take one dot each.
 template <int DK, int TPB, int KSTR = DK>
