@@ -164,9 +164,4 @@ __device__ __forceinline__ uint2 ldu2_nt(const void *p)
     return make_uint2(v.x, v.y);
 }
 
-__device__ __forceinline__ float f4get(const float4 &v, int e)
-{
-    return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
-}
-
 }  // namespace rssm

@@ -61,9 +61,4 @@ __device__ __forceinline__ void mfma_settle()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ float readlane_f(float v, int lane)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
 }  // namespace rssm
