@@ -46,11 +46,23 @@ __device__ __forceinline__ void load_cols(float (&cc)[EPL], const float *src)
     }
 }
 
+// Threads per workgroup of the Mamba-2 kernels for a P x N tile. WIDE gives each thread about
+// 4 float4 of the fp32 checkpoint (512 threads at 64 x 128), NARROW about 8 (256). The fp32
+// decode, the fold and the conventional kernels take WIDE; verify and the decode that reads the
+// bf16 copy take NARROW. Each choice measured fastest in same-box comparisons.
+template <int P, int N>
+struct M2Threads {
+    static constexpr int NF4 = P * N / 4;
+    static constexpr int WIDE = NF4 / 4 < 64 ? 64 : (NF4 / 4 > 512 ? 512 : NF4 / 4);
+    static constexpr int NARROW = TileShape<P, N>::TPB;
+    static constexpr int decode(bool bf16) { return bf16 ? NARROW : WIDE; }
+};
+
 // bf16 read-copy layout: 16-byte loads (8 values) when the tile has enough of them for every
 // lane, else 8-byte loads.
-template <int P, int N>
+template <int P, int N, int TPB>
 struct Bf16Epl {
-    static constexpr int value = (P * N / 8 >= TileShape<P, N>::TPB) ? 8 : 4;
+    static constexpr int value = (P * N / 8 >= TPB) ? 8 : 4;
 };
 
 template <int EPL> struct RawBf16;
@@ -123,13 +135,12 @@ __device__ __forceinline__ float lane_value(float v, int lane)
 // slot `head`; the current token (xt, Bt, dtt), if xt != nullptr, is the newest entry.
 // n <= W + 1 <= 33 entries, so each wave holds every step size in its lanes. All threads of the
 // workgroup must call it; it synchronises once.
-template <int P, int N, int R>
+template <int P, int N, int TPB, int R>
 __device__ __forceinline__ void m2_fold_core(float4 (&acc)[R], float *smem, const M2Ring &ring,
                                              const Tile &c, int head, int nring, const float *xt,
                                              const float *Bt, float dtt)
 {
-    constexpr int TPB = TileShape<P, N>::TPB;
-    using M = Map4<P, N>;
+    using M = RowMap<P, N, TPB, 4>;
     static_assert(R == M::R, "fold block");
     const int W = c.W, t = c.t, lane = t & 63;
     const int rg = t / M::LPR, c0 = (t - rg * M::LPR) * 4;
@@ -169,10 +180,10 @@ __device__ __forceinline__ void m2_fold_core(float4 (&acc)[R], float *smem, cons
 }
 
 // Store the lane's block of a folded checkpoint (and its bf16 read copy).
-template <int P, int N, int R>
+template <int P, int N, int TPB, int R>
 __device__ __forceinline__ void store_tile(const float4 (&acc)[R], float *dst, uint16_t *dstb, int t)
 {
-    using M = Map4<P, N>;
+    using M = RowMap<P, N, TPB, 4>;
     static_assert(R == M::R, "fold block");
     const int rg = t / M::LPR, c0 = (t - rg * M::LPR) * 4;
     const size_t off = (size_t)(rg * M::R) * N + c0;
@@ -190,10 +201,10 @@ __device__ __forceinline__ void store_tile(const float4 (&acc)[R], float *dst, u
 }
 
 // The lane's R rows x EPL columns of the checkpoint read: fp32 S0 or its bf16 copy.
-template <int P, int N, bool BF16>
+template <int P, int N, int TPB, bool BF16>
 struct ReadTile {
-    static constexpr int EPL = BF16 ? Bf16Epl<P, N>::value : 4;
-    using M = RowMap<P, N, TileShape<P, N>::TPB, EPL>;
+    static constexpr int EPL = BF16 ? Bf16Epl<P, N, TPB>::value : 4;
+    using M = RowMap<P, N, TPB, EPL>;
     using RawT = typename std::conditional<BF16, typename RawBf16<EPL>::type, float4>::type;
     RawT v[M::R];
 
@@ -210,10 +221,10 @@ struct ReadTile {
     }
 };
 
-template <int P, int N, int R>
+template <int P, int N, int TPB, int R>
 __device__ __forceinline__ void load_fp32_tile(float4 (&acc)[R], const float *S0, const Tile &c)
 {
-    using M = Map4<P, N>;
+    using M = RowMap<P, N, TPB, 4>;
     const int rg = c.t / M::LPR, c0 = (c.t - rg * M::LPR) * 4;
     const size_t off = c.bh * (size_t)(P * N) + (size_t)(rg * M::R) * N + c0;
 #pragma unroll
@@ -229,12 +240,11 @@ __device__ __forceinline__ void load_fp32_tile(float4 (&acc)[R], const float *S0
 // B_j . C) then overlaps the checkpoint stream. EARLY = true means the caller already issued the
 // checkpoint read (needed when the ring position must first be read from device memory).
 // ------------------------------------------------------------------------------------------
-template <int P, int N, bool BF16, bool EARLY>
+template <int P, int N, int TPB, bool BF16, bool EARLY>
 __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile &c, int head,
-                                                 int len, ReadTile<P, N, BF16> &tile, float *smem)
+                                                 int len, ReadTile<P, N, TPB, BF16> &tile, float *smem)
 {
-    constexpr int TPB = TileShape<P, N>::TPB;
-    using RT = ReadTile<P, N, BF16>;
+    using RT = ReadTile<P, N, TPB, BF16>;
     constexpr int EPL = RT::EPL;
     using M = typename RT::M;
     constexpr int R = M::R, LPR = M::LPR, RG = M::RG;
@@ -292,7 +302,7 @@ __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile
             part += bq[q][e].x * cc[4 * e] + bq[q][e].y * cc[4 * e + 1] + bq[q][e].z * cc[4 * e + 2]
                   + bq[q][e].w * cc[4 * e + 3];
         const float sj = group_sum<LPR>(part);
-        const float wj = __shfl(w, j);                   // all lanes active: j < 2 RG <= 32
+        const float wj = __shfl(w, j);                   // all lanes active: j < 2 RG <= 64
         if (cg == 0 && j < m) sh_cf[j] = wj * sj;
     }
     for (int q = 2; q * RG < m; ++q) {                   // rings longer than 2 RG (trip count is
@@ -327,17 +337,18 @@ __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile
 
     // 5. Append the token as entry len. Its slot is none of the entries read above. The stores
     //    come after the barrier: a workgroup barrier waits for the workgroup's outstanding
-    //    stores, so stores issued before it would put their latency on every tile.
-    for (int i = t; i < PF; i += TPB) st4(a.ring.x + (c.rh + slot) * P + 4 * i, ld4(sh_x + len * P + 4 * i));
+    //    stores, so stores issued before it would put their latency on every tile. They are
+    //    non-temporal, which measured faster than write-back stores here and in verify.
+    for (int i = t; i < PF; i += TPB) st4_nt(a.ring.x + (c.rh + slot) * P + 4 * i, ld4(sh_x + len * P + 4 * i));
     if (c.own_group) {
         if (rg == len % RG) {        // the token's B row (in cache from the loads above)
 #pragma unroll
-            for (int e = 0; e < EPL / 4; ++e) st4(a.ring.B + (c.rg_ + slot) * N + c0 + 4 * e, ld4(Bt + c0 + 4 * e));
+            for (int e = 0; e < EPL / 4; ++e) st4_nt(a.ring.B + (c.rg_ + slot) * N + c0 + 4 * e, ld4(Bt + c0 + 4 * e));
         }
         if (a.ring.C && rg == 0) {
 #pragma unroll
             for (int e = 0; e < EPL; e += 4)
-                st4(a.ring.C + (c.rg_ + slot) * N + c0 + e, make_float4(cc[e], cc[e + 1], cc[e + 2], cc[e + 3]));
+                st4_nt(a.ring.C + (c.rg_ + slot) * N + c0 + e, make_float4(cc[e], cc[e + 1], cc[e + 2], cc[e + 3]));
         }
     }
     if (t == 0) a.ring.dt[c.rh + slot] = dtt;
@@ -347,11 +358,11 @@ __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile
 // decode: fold path (the token fills the ring; with len == W after a full commit the ring is
 // already full and the token is the (W+1)-th entry)
 // ------------------------------------------------------------------------------------------
-template <int P, int N, bool BF16, int R>
+template <int P, int N, int TPB, bool BF16, int R>
 __device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &c, int head, int len,
                                                float4 (&acc)[R], float *smem)
 {
-    using M = Map4<P, N>;
+    using M = RowMap<P, N, TPB, 4>;
     static_assert(R == M::R, "fold block");
     constexpr int LPR = M::LPR;
     const int t = c.t;
@@ -359,8 +370,8 @@ __device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &
     const float *xt = a.x + c.bh * P;
     float cc[4];
     load_cols<4>(cc, a.C + c.bg * N + c0);
-    m2_fold_core<P, N>(acc, smem, a.ring, c, head, len, xt, a.Bm + c.bg * N, a.dt[c.bh]);
-    store_tile<P, N>(acc, a.S0 + c.bh * (size_t)(P * N), BF16 ? a.S0b + c.bh * (size_t)(P * N) : nullptr, t);
+    m2_fold_core<P, N, TPB>(acc, smem, a.ring, c, head, len, xt, a.Bm + c.bg * N, a.dt[c.bh]);
+    store_tile<P, N, TPB>(acc, a.S0 + c.bh * (size_t)(P * N), BF16 ? a.S0b + c.bh * (size_t)(P * N) : nullptr, t);
     float part[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) part[r] = dot_row(acc[r], cc);
@@ -381,43 +392,44 @@ __device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &
 enum DecodeMode { kUniform = 0, kReplay = 1, kMayFold = 2 };
 
 template <int P, int N, bool BF16, int MODE>
-__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs a)
+__global__ void __launch_bounds__((M2Threads<P, N>::decode(BF16))) k_m2_decode(M2StepArgs a)
 {
+    constexpr int TPB = M2Threads<P, N>::decode(BF16);
     extern __shared__ float smem[];
     const Tile c = make_tile(a.d, a.A, a.D, MODE == kMayFold ? kContiguous : kRuns);
     const int B = a.d.B, W = c.W;
     bool fold = false;
     int head, len;
     if constexpr (MODE == kUniform) {
-        ReadTile<P, N, BF16> tile;
+        ReadTile<P, N, TPB, BF16> tile;
         head = a.uhead;
         len = a.ulen;
-        m2_replay_decode<P, N, BF16, false>(a, c, head, len, tile, smem);
+        m2_replay_decode<P, N, TPB, BF16, false>(a, c, head, len, tile, smem);
     } else if constexpr (MODE == kReplay) {
-        ReadTile<P, N, BF16> tile;
+        ReadTile<P, N, TPB, BF16> tile;
         tile.load(a, c);
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
-        m2_replay_decode<P, N, BF16, true>(a, c, head, len, tile, smem);
+        m2_replay_decode<P, N, TPB, BF16, true>(a, c, head, len, tile, smem);
     } else if constexpr (!BF16) {
-        ReadTile<P, N, false> tile;
+        ReadTile<P, N, TPB, false> tile;
         tile.load(a, c);
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
         fold = len + 1 >= W;
-        if (fold) m2_fold_decode<P, N, false>(a, c, head, len, tile.v, smem);
-        else m2_replay_decode<P, N, false, true>(a, c, head, len, tile, smem);
+        if (fold) m2_fold_decode<P, N, TPB, false>(a, c, head, len, tile.v, smem);
+        else m2_replay_decode<P, N, TPB, false, true>(a, c, head, len, tile, smem);
     } else {
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
         fold = len + 1 >= W;
         if (fold) {
-            float4 acc[Map4<P, N>::R];
-            load_fp32_tile<P, N>(acc, a.S0, c);
-            m2_fold_decode<P, N, true>(a, c, head, len, acc, smem);
+            float4 acc[RowMap<P, N, TPB, 4>::R];
+            load_fp32_tile<P, N, TPB>(acc, a.S0, c);
+            m2_fold_decode<P, N, TPB, true>(a, c, head, len, acc, smem);
         } else {
-            ReadTile<P, N, true> tile;
-            m2_replay_decode<P, N, true, false>(a, c, head, len, tile, smem);
+            ReadTile<P, N, TPB, true> tile;
+            m2_replay_decode<P, N, TPB, true, false>(a, c, head, len, tile, smem);
         }
     }
     if (c.h == 0 && c.t == 0) {
@@ -431,9 +443,9 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_decode(M2StepArgs
 // consolidation / materialisation
 // ------------------------------------------------------------------------------------------
 template <int P, int N, bool BF16>
-__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_fold(M2FoldArgs a)
+__global__ void __launch_bounds__((M2Threads<P, N>::WIDE)) k_m2_fold(M2FoldArgs a)
 {
-    constexpr int TPB = TileShape<P, N>::TPB;
+    constexpr int TPB = M2Threads<P, N>::WIDE;
     using M = RowMap<P, N, TPB, 4>;
     extern __shared__ float smem[];
     const Tile c = make_tile(a.d, a.A, nullptr, kContiguous);
@@ -460,9 +472,9 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_fold(M2FoldArgs a
     const size_t off = (size_t)(rg * M::R) * N + c0;
 #pragma unroll
     for (int r = 0; r < M::R; ++r) acc[r] = ld4_nt(S0 + off + (size_t)r * N);
-    m2_fold_core<P, N>(acc, smem, a.ring, c, head, len, nullptr, nullptr, 0.f);
-    if (a.out) store_tile<P, N>(acc, a.out + c.bh * (size_t)(P * N), nullptr, c.t);
-    else store_tile<P, N>(acc, S0, BF16 ? a.S0b + c.bh * (size_t)(P * N) : nullptr, c.t);
+    m2_fold_core<P, N, TPB>(acc, smem, a.ring, c, head, len, nullptr, nullptr, 0.f);
+    if (a.out) store_tile<P, N, TPB>(acc, a.out + c.bh * (size_t)(P * N), nullptr, c.t);
+    else store_tile<P, N, TPB>(acc, S0, BF16 ? a.S0b + c.bh * (size_t)(P * N) : nullptr, c.t);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -485,12 +497,11 @@ __host__ __device__ constexpr int verify_lds_floats(int W, int P, int N)
 
 // LOADED = true: the tile already holds the checkpoint (folded just before); otherwise it is read
 // here after the ring and draft loads went out.
-template <int P, int N, bool BF16, bool LOADED>
+template <int P, int N, int TPB, bool BF16, bool LOADED>
 __device__ __forceinline__ void m2_verify_outputs(const M2StepArgs &a, const Tile &c, int head_e,
-                                                  int len_e, ReadTile<P, N, BF16> &tile, float *smem)
+                                                  int len_e, ReadTile<P, N, TPB, BF16> &tile, float *smem)
 {
-    constexpr int TPB = TileShape<P, N>::TPB;
-    using RT = ReadTile<P, N, BF16>;
+    using RT = ReadTile<P, N, TPB, BF16>;
     constexpr int EPL = RT::EPL;
     using M = typename RT::M;
     constexpr int R = M::R, LPR = M::LPR;
@@ -595,22 +606,23 @@ __device__ __forceinline__ void m2_verify_outputs(const M2StepArgs &a, const Til
     // 5. append the drafts as entries len_e .. len_e + K - 1 (every ring read is done)
     for (int i = t; i < K * PF; i += TPB) {
         const int k = i / PF, q = (i - k * PF) * 4;
-        st4(a.ring.x + (c.rh + (head_e + len_e + k) % W) * P + q, ld4(sh_x + (len_e + k) * P + q));
+        st4_nt(a.ring.x + (c.rh + (head_e + len_e + k) % W) * P + q, ld4(sh_x + (len_e + k) * P + q));
     }
     if (c.own_group) {
         for (int i = t; i < K * NF; i += TPB) {
             const int k = i / NF, q = (i - k * NF) * 4;
             const size_t row = (c.rg_ + (head_e + len_e + k) % W) * N + q;
-            st4(a.ring.B + row, ld4(sh_B + (len_e + k) * N + q));
-            if (a.ring.C) st4(a.ring.C + row, ld4(sh_C + k * N + q));
+            st4_nt(a.ring.B + row, ld4(sh_B + (len_e + k) * N + q));
+            if (a.ring.C) st4_nt(a.ring.C + row, ld4(sh_C + k * N + q));
         }
     }
     for (int k = t; k < K; k += TPB) a.ring.dt[c.rh + (head_e + len_e + k) % W] = a.dt[k * BH + c.bh];
 }
 
 template <int P, int N, bool BF16>
-__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_verify(M2StepArgs a)
+__global__ void __launch_bounds__((M2Threads<P, N>::NARROW)) k_m2_verify(M2StepArgs a)
 {
+    constexpr int TPB = M2Threads<P, N>::NARROW;
     extern __shared__ float smem[];
     const Tile c = make_tile(a.d, a.A, a.D, kRuns);
     const int B = a.d.B, W = c.W, K = a.ntok;
@@ -621,16 +633,16 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_verify(M2StepArgs
     const int len_e = prefold ? 0 : len;
     if (prefold) {
         // fold the committed entries first; the drafts then read the folded fp32 tile
-        ReadTile<P, N, false> tile;
-        load_fp32_tile<P, N>(tile.v, a.S0, c);
-        m2_fold_core<P, N>(tile.v, smem, a.ring, c, head, len, nullptr, nullptr, 0.f);
+        ReadTile<P, N, TPB, false> tile;
+        load_fp32_tile<P, N, TPB>(tile.v, a.S0, c);
+        m2_fold_core<P, N, TPB>(tile.v, smem, a.ring, c, head, len, nullptr, nullptr, 0.f);
         const size_t off0 = c.bh * (size_t)(P * N);
-        store_tile<P, N>(tile.v, a.S0 + off0, BF16 ? a.S0b + off0 : nullptr, c.t);
+        store_tile<P, N, TPB>(tile.v, a.S0 + off0, BF16 ? a.S0b + off0 : nullptr, c.t);
         __syncthreads();
-        m2_verify_outputs<P, N, false, true>(a, c, head_e, len_e, tile, smem);
+        m2_verify_outputs<P, N, TPB, false, true>(a, c, head_e, len_e, tile, smem);
     } else {
-        ReadTile<P, N, BF16> tile;
-        m2_verify_outputs<P, N, BF16, false>(a, c, head_e, len_e, tile, smem);
+        ReadTile<P, N, TPB, BF16> tile;
+        m2_verify_outputs<P, N, TPB, BF16, false>(a, c, head_e, len_e, tile, smem);
     }
     if (c.h == 0 && c.t == 0) {
         a.bk.out[c.b] = head_e;
@@ -643,9 +655,9 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_verify(M2StepArgs
 // conventional read-modify-write comparator
 // ------------------------------------------------------------------------------------------
 template <int P, int N>
-__global__ void __launch_bounds__((TileShape<P, N>::TPB)) k_m2_rmw(M2RmwArgs a)
+__global__ void __launch_bounds__((M2Threads<P, N>::WIDE)) k_m2_rmw(M2RmwArgs a)
 {
-    constexpr int TPB = TileShape<P, N>::TPB;
+    constexpr int TPB = M2Threads<P, N>::WIDE;
     using M = RowMap<P, N, TPB, 4>;
     constexpr int R = M::R, LPR = M::LPR;
     const Tile c = make_tile(a.d, a.A, a.D, kRuns);
@@ -723,7 +735,7 @@ size_t verify_lds(int W)
 template <int P, int N>
 hipError_t go_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::decode(bf16));
     const size_t lds = decode_lds<P, N>(a.d.W);
 #define RSSM_GO(b, md) hipLaunchKernelGGL((k_m2_decode<P, N, b, md>), grid, block, lds, s, a)
     if (bf16) {
@@ -742,7 +754,7 @@ hipError_t go_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s)
 template <int P, int N>
 hipError_t go_verify(const M2StepArgs &a, bool bf16, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::NARROW);
     const size_t lds = verify_lds<P, N>(a.d.W);
     if (bf16) hipLaunchKernelGGL((k_m2_verify<P, N, true>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_m2_verify<P, N, false>), grid, block, lds, s, a);
@@ -752,7 +764,7 @@ hipError_t go_verify(const M2StepArgs &a, bool bf16, hipStream_t s)
 template <int P, int N>
 hipError_t go_fold(const M2FoldArgs &a, bool bf16, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::WIDE);
     const size_t lds = 4 * (size_t)fold_lds_floats(a.d.W, P, N);
     if (bf16) hipLaunchKernelGGL((k_m2_fold<P, N, true>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_m2_fold<P, N, false>), grid, block, lds, s, a);
@@ -762,7 +774,7 @@ hipError_t go_fold(const M2FoldArgs &a, bool bf16, hipStream_t s)
 template <int P, int N>
 hipError_t go_rmw(const M2RmwArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::WIDE);
     hipLaunchKernelGGL((k_m2_rmw<P, N>), grid, block, 0, s, a);
     return hipGetLastError();
 }
