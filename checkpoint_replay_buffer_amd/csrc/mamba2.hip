@@ -48,8 +48,9 @@ __device__ __forceinline__ void load_cols(float (&cc)[EPL], const float *src)
 
 // Threads per workgroup of the Mamba-2 kernels for a P x N tile. WIDE gives each thread about
 // 4 float4 of the fp32 checkpoint (512 threads at 64 x 128), NARROW about 8 (256). The fp32
-// decode, the fold and the conventional kernels take WIDE; verify and the decode that reads the
-// bf16 copy take NARROW. Each choice measured fastest in same-box comparisons.
+// decode and the fold take WIDE; verify and the decode that reads the bf16 copy take NARROW; the
+// conventional kernel chooses by token count (go_rmw). Each choice measured fastest in same-box
+// comparisons.
 template <int P, int N>
 struct M2Threads {
     static constexpr int NF4 = P * N / 4;
@@ -341,14 +342,23 @@ __device__ __forceinline__ void m2_replay_decode(const M2StepArgs &a, const Tile
     //    non-temporal, which measured faster than write-back stores here and in verify.
     for (int i = t; i < PF; i += TPB) st4_nt(a.ring.x + (c.rh + slot) * P + 4 * i, ld4(sh_x + len * P + 4 * i));
     if (c.own_group) {
-        if (rg == len % RG) {        // the token's B row (in cache from the loads above)
+        // The B and C rows (in cache from the loads above) go out as LPR consecutive float4 per
+        // instruction, whole 128-byte lines: a non-temporal store of part of a line costs a
+        // write of the whole line.
+        if (rg == len % RG) {
 #pragma unroll
-            for (int e = 0; e < EPL / 4; ++e) st4_nt(a.ring.B + (c.rg_ + slot) * N + c0 + 4 * e, ld4(Bt + c0 + 4 * e));
+            for (int e = 0; e < EPL / 4; ++e) {
+                const int q = 4 * (cg + e * LPR);
+                st4_nt(a.ring.B + (c.rg_ + slot) * N + q, ld4(Bt + q));
+            }
         }
         if (a.ring.C && rg == 0) {
 #pragma unroll
-            for (int e = 0; e < EPL; e += 4)
-                st4_nt(a.ring.C + (c.rg_ + slot) * N + c0 + e, make_float4(cc[e], cc[e + 1], cc[e + 2], cc[e + 3]));
+            for (int e = 0; e < EPL / 4; ++e) {
+                const int q = 4 * (cg + e * LPR);
+                const float4 v = EPL == 4 ? make_float4(cc[0], cc[1], cc[2], cc[3]) : ld4(a.C + c.bg * N + q);
+                st4_nt(a.ring.C + (c.rg_ + slot) * N + q, v);
+            }
         }
     }
     if (t == 0) a.ring.dt[c.rh + slot] = dtt;
@@ -654,10 +664,9 @@ __global__ void __launch_bounds__((M2Threads<P, N>::NARROW)) k_m2_verify(M2StepA
 // ------------------------------------------------------------------------------------------
 // conventional read-modify-write comparator
 // ------------------------------------------------------------------------------------------
-template <int P, int N>
-__global__ void __launch_bounds__((M2Threads<P, N>::WIDE)) k_m2_rmw(M2RmwArgs a)
+template <int P, int N, int TPB>
+__global__ void __launch_bounds__(TPB) k_m2_rmw(M2RmwArgs a)
 {
-    constexpr int TPB = M2Threads<P, N>::WIDE;
     using M = RowMap<P, N, TPB, 4>;
     constexpr int R = M::R, LPR = M::LPR;
     const Tile c = make_tile(a.d, a.A, a.D, kRuns);
@@ -771,11 +780,20 @@ hipError_t go_fold(const M2FoldArgs &a, bool bf16, hipStream_t s)
     return hipGetLastError();
 }
 
+// The conventional kernel over a few tokens is bound by the state stream and takes the wide
+// workgroup; over long runs (a prompt) the per-token work of each lane dominates and the narrow
+// one, with twice the rows per lane, is faster (measured at 1, 6 and 512 tokens).
 template <int P, int N>
 hipError_t go_rmw(const M2RmwArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::WIDE);
-    hipLaunchKernelGGL((k_m2_rmw<P, N>), grid, block, 0, s, a);
+    const dim3 grid(a.d.B * a.d.H);
+    if (a.ntok <= 8) {
+        constexpr int T = M2Threads<P, N>::WIDE;
+        hipLaunchKernelGGL((k_m2_rmw<P, N, T>), grid, dim3(T), 0, s, a);
+    } else {
+        constexpr int T = M2Threads<P, N>::NARROW;
+        hipLaunchKernelGGL((k_m2_rmw<P, N, T>), grid, dim3(T), 0, s, a);
+    }
     return hipGetLastError();
 }
 
