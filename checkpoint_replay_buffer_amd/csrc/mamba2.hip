@@ -48,15 +48,15 @@ __device__ __forceinline__ void load_cols(float (&cc)[EPL], const float *src)
 
 // Threads per workgroup of the Mamba-2 kernels for a P x N tile. WIDE gives each thread about
 // 4 float4 of the fp32 checkpoint (512 threads at 64 x 128), NARROW about 8 (256). The fp32
-// decode and the fold take WIDE; verify and the decode that reads the bf16 copy take NARROW; the
-// conventional kernel chooses by token count (go_rmw). Each choice measured fastest in same-box
-// comparisons.
+// decode, the fold and every decode launch that may fold take WIDE; verify and the replay-only
+// launches that read the bf16 copy take NARROW; the conventional kernel chooses by token count
+// (go_rmw). Each choice measured fastest in same-box comparisons.
 template <int P, int N>
 struct M2Threads {
     static constexpr int NF4 = P * N / 4;
     static constexpr int WIDE = NF4 / 4 < 64 ? 64 : (NF4 / 4 > 512 ? 512 : NF4 / 4);
     static constexpr int NARROW = TileShape<P, N>::TPB;
-    static constexpr int decode(bool bf16) { return bf16 ? NARROW : WIDE; }
+    static constexpr int decode(bool bf16, bool may_fold) { return bf16 && !may_fold ? NARROW : WIDE; }
 };
 
 // bf16 read-copy layout: 16-byte loads (8 values) when the tile has enough of them for every
@@ -402,9 +402,9 @@ __device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &
 enum DecodeMode { kUniform = 0, kReplay = 1, kMayFold = 2 };
 
 template <int P, int N, bool BF16, int MODE>
-__global__ void __launch_bounds__((M2Threads<P, N>::decode(BF16))) k_m2_decode(M2StepArgs a)
+__global__ void __launch_bounds__((M2Threads<P, N>::decode(BF16, MODE == kMayFold))) k_m2_decode(M2StepArgs a)
 {
-    constexpr int TPB = M2Threads<P, N>::decode(BF16);
+    constexpr int TPB = M2Threads<P, N>::decode(BF16, MODE == kMayFold);
     extern __shared__ float smem[];
     const Tile c = make_tile(a.d, a.A, a.D, MODE == kMayFold ? kContiguous : kRuns);
     const int B = a.d.B, W = c.W;
@@ -744,7 +744,7 @@ size_t verify_lds(int W)
 template <int P, int N>
 hipError_t go_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::decode(bf16));
+    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::decode(bf16, mode == kMayFold));
     const size_t lds = decode_lds<P, N>(a.d.W);
 #define RSSM_GO(b, md) hipLaunchKernelGGL((k_m2_decode<P, N, b, md>), grid, block, lds, s, a)
     if (bf16) {
