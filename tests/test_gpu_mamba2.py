@@ -103,6 +103,43 @@ def test_rmw_comparator_tiny():
         assert normwise_err(host(snaps)[k], r2) < TOL
 
 
+@pytest.mark.parametrize("P,N", [(64, 64), (64, 128)])
+def test_rmw_comparator_workgroup_sizes(P, N):
+    """The conventional kernel at the shapes where its workgroup depends on the token count: one
+    token and a 5-draft snapshot launch (wide workgroup), then 12 tokens in one launch (narrow)."""
+    sh = wl.M2Shape(batch=2, nheads=3, ngroups=3, head_dim=P, d_state=N, window=16)
+    prm = wl.m2_params(sh, 7)
+    s0 = wl.m2_state0(sh, 7)
+    ins = wl.m2_token_inputs(sh, 7, 0, ntok=13)
+    d = m2_dev_tokens(sh, ins, 13)
+    cfg = rb.make_config(rb.RSSM_MAMBA2, sh.batch, sh.nheads, sh.ngroups, P, N, 16)
+    A, D = dev(prm["A"]), dev(prm["D"])
+    st = dev(s0)
+    ref = s0.astype(np.float64).copy()
+    y1 = torch.empty(1, sh.batch, sh.nheads, P, device="cuda")
+    rb.step_baseline(cfg, st, y1, A, D, **{k: v[0:1] for k, v in d.items()})
+    y_ref = m2_step(prm["A"], prm["D"], ins["x"][0], ins["B"][0], ins["C"][0], ins["dt"][0], ref)
+    assert normwise_err(host(y1)[0], y_ref) < TOL
+    assert normwise_err(host(st), ref) < TOL
+    K = 5
+    snaps = torch.empty((K,) + s0.shape, device="cuda")
+    yk = torch.empty(K, sh.batch, sh.nheads, P, device="cuda")
+    rb.step_baseline(cfg, st, yk, A, D, snapshots=snaps, **{k: v[1:1 + K] for k, v in d.items()})
+    r2 = ref.copy()
+    for k in range(K):
+        y_ref = m2_step(prm["A"], prm["D"], ins["x"][1 + k], ins["B"][1 + k], ins["C"][1 + k],
+                        ins["dt"][1 + k], r2)
+        assert normwise_err(host(yk)[k], y_ref) < TOL
+        assert normwise_err(host(snaps)[k], r2) < TOL
+    y12 = torch.empty(12, sh.batch, sh.nheads, P, device="cuda")
+    rb.step_baseline(cfg, st, y12, A, D, **{k: v[1:13] for k, v in d.items()})
+    for k in range(12):
+        y_ref = m2_step(prm["A"], prm["D"], ins["x"][1 + k], ins["B"][1 + k], ins["C"][1 + k],
+                        ins["dt"][1 + k], ref)
+        assert normwise_err(host(y12)[k], y_ref) < TOL, k
+    assert normwise_err(host(st), ref) < TOL
+
+
 def test_ragged_lengths_masked_init_consolidate():
     """Sequences at different buffer fills (masked re-init), grouped B/C, partial folds."""
     sh = wl.M2Shape(batch=5, nheads=4, ngroups=2, head_dim=32, d_state=32, window=4)
