@@ -47,7 +47,8 @@ __device__ __forceinline__ void load_cols(float (&cc)[EPL], const float *src)
 }
 
 // Threads per workgroup of the Mamba-2 kernels for a P x N tile. WIDE gives each thread about
-// 4 float4 of the fp32 checkpoint (512 threads at 64 x 128), NARROW about 8 (256). The fp32
+// 4 float4 of the fp32 checkpoint (512 threads at 64 x 128), NARROW about 8 (256), SINGLE about
+// 2 (1024, for the conventional kernel over a single token). The fp32
 // decode, the fold and every decode launch that may fold take WIDE; verify and the replay-only
 // launches that read the bf16 copy take NARROW; the conventional kernel chooses by token count
 // (go_rmw). Each choice measured fastest in same-box comparisons.
@@ -56,6 +57,7 @@ struct M2Threads {
     static constexpr int NF4 = P * N / 4;
     static constexpr int WIDE = NF4 / 4 < 64 ? 64 : (NF4 / 4 > 512 ? 512 : NF4 / 4);
     static constexpr int NARROW = TileShape<P, N>::TPB;
+    static constexpr int SINGLE = NF4 / 2 < 64 ? 64 : (NF4 / 2 > 1024 ? 1024 : NF4 / 2);
     static constexpr int decode(bool bf16, bool may_fold) { return bf16 && !may_fold ? NARROW : WIDE; }
 };
 
@@ -780,14 +782,18 @@ hipError_t go_fold(const M2FoldArgs &a, bool bf16, hipStream_t s)
     return hipGetLastError();
 }
 
-// The conventional kernel over a few tokens is bound by the state stream and takes the wide
-// workgroup; over long runs (a prompt) the per-token work of each lane dominates and the narrow
-// one, with twice the rows per lane, is faster (measured at 1, 6 and 512 tokens).
+// The conventional kernel over a few tokens is bound by the state stream and takes a wide
+// workgroup (the widest for a single token); over long runs (a prompt) the per-token work of each
+// lane dominates and the narrow one, with more rows per lane, is faster (measured at 1, 6 and 512
+// tokens).
 template <int P, int N>
 hipError_t go_rmw(const M2RmwArgs &a, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H);
-    if (a.ntok <= 8) {
+    if (a.ntok == 1) {
+        constexpr int T = M2Threads<P, N>::SINGLE;
+        hipLaunchKernelGGL((k_m2_rmw<P, N, T>), grid, dim3(T), 0, s, a);
+    } else if (a.ntok <= 8) {
         constexpr int T = M2Threads<P, N>::WIDE;
         hipLaunchKernelGGL((k_m2_rmw<P, N, T>), grid, dim3(T), 0, s, a);
     } else {

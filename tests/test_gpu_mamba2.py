@@ -103,10 +103,10 @@ def test_rmw_comparator_tiny():
         assert normwise_err(host(snaps)[k], r2) < TOL
 
 
-@pytest.mark.parametrize("P,N", [(64, 64), (64, 128)])
+@pytest.mark.parametrize("P,N", [(16, 16), (32, 32), (64, 64), (64, 128), (128, 128)])
 def test_rmw_comparator_workgroup_sizes(P, N):
-    """The conventional kernel at the shapes where its workgroup depends on the token count: one
-    token and a 5-draft snapshot launch (wide workgroup), then 12 tokens in one launch (narrow)."""
+    """The conventional kernel on each of its workgroup sizes, which depend on the token count: one
+    token, a 5-draft snapshot launch, then 12 tokens in one launch."""
     sh = wl.M2Shape(batch=2, nheads=3, ngroups=3, head_dim=P, d_state=N, window=16)
     prm = wl.m2_params(sh, 7)
     s0 = wl.m2_state0(sh, 7)
