@@ -783,14 +783,15 @@ hipError_t go_fold(const M2FoldArgs &a, bool bf16, hipStream_t s)
 }
 
 // The conventional kernel over a few tokens is bound by the state stream and takes a wide
-// workgroup (the widest for a single token); over long runs (a prompt) the per-token work of each
-// lane dominates and the narrow one, with more rows per lane, is faster (measured at 1, 6 and 512
-// tokens).
+// workgroup, the widest for a single token over at least 16k tiles (with fewer tiles, as at
+// batch 1 or 32 with 128 heads, the 512-thread one is faster); over long runs (a prompt) the
+// per-token work of each lane dominates and the narrow one, with more rows per lane, is faster
+// (measured at 1, 6 and 512 tokens and batch 1 to 512).
 template <int P, int N>
 hipError_t go_rmw(const M2RmwArgs &a, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H);
-    if (a.ntok == 1) {
+    if (a.ntok == 1 && (long)a.d.B * a.d.H >= 16384) {
         constexpr int T = M2Threads<P, N>::SINGLE;
         hipLaunchKernelGGL((k_m2_rmw<P, N, T>), grid, dim3(T), 0, s, a);
     } else if (a.ntok <= 8) {

@@ -140,6 +140,24 @@ def test_rmw_comparator_workgroup_sizes(P, N):
     assert normwise_err(host(st), ref) < TOL
 
 
+def test_rmw_comparator_single_token_large_grid():
+    """One token over 16k tiles at 64 x 128, where the conventional kernel takes its widest
+    workgroup (1024 threads)."""
+    sh = wl.M2Shape(batch=64, nheads=256, ngroups=16, head_dim=64, d_state=128, window=16)
+    prm = wl.m2_params(sh, 8)
+    s0 = wl.m2_state0(sh, 8)
+    ins = wl.m2_token_inputs(sh, 8, 0, ntok=1)
+    d = m2_dev_tokens(sh, ins, 1)
+    cfg = rb.make_config(rb.RSSM_MAMBA2, sh.batch, sh.nheads, sh.ngroups, 64, 128, 16)
+    st = dev(s0)
+    ref = s0.astype(np.float64)
+    y = torch.empty(1, sh.batch, sh.nheads, 64, device="cuda")
+    rb.step_baseline(cfg, st, y, dev(prm["A"]), dev(prm["D"]), **d)
+    y_ref = m2_step(prm["A"], prm["D"], ins["x"][0], ins["B"][0], ins["C"][0], ins["dt"][0], ref)
+    assert normwise_err(host(y)[0], y_ref) < TOL
+    assert normwise_err(host(st), ref) < TOL
+
+
 def test_ragged_lengths_masked_init_consolidate():
     """Sequences at different buffer fills (masked re-init), grouped B/C, partial folds."""
     sh = wl.M2Shape(batch=5, nheads=4, ngroups=2, head_dim=32, d_state=32, window=4)
