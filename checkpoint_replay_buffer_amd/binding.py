@@ -21,6 +21,8 @@ STATUS = {0: "RSSM_OK", -1: "RSSM_E_ARG", -2: "RSSM_E_SHAPE", -3: "RSSM_E_SPACE"
           -4: "RSSM_E_STATE", -5: "RSSM_E_DEVICE", -6: "RSSM_E_UNSUPPORTED"}
 RSSM_DEV_COMMIT_RANGE = 1
 RSSM_DEV_ROLLBACK_RANGE = 2
+RSSM_DEV_INDEX_RANGE = 8
+RSSM_DEV_IMPORT_HEADER = 16
 RSSM_MAMBA2 = 1
 RSSM_GDN = 2
 RSSM_F_BF16_READ = 1

@@ -158,6 +158,7 @@ SeqCopyArgs seq_args(const rssm_ctx *c, int mode, int n, const int32_t *src, con
     a.mode = mode;
     a.n = n;
     a.B = g.batch;
+    a.W = g.window;
     a.src = src;
     a.dst = dst;
     a.buf = buf;
@@ -383,6 +384,23 @@ rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *st
     if (c.kind == RSSM_GDN && in->ntok > kGdnMaxDraft) return RSSM_E_ARG;
     if (ctx->pending) return RSSM_E_STATE;
     if (c.kind == RSSM_MAMBA2) {
+        // With B / C shared by a group of heads (G < H), a sequence whose drafts do not fit
+        // (len + K > W) cannot fold inside the verify launch: the group's first head appends the
+        // drafts' B rows to slots that wrap onto committed slots, which the group's other heads,
+        // in other workgroups of the same launch, still read for their own fold. Those sequences
+        // are folded by a consolidation launch first, so the verify launch folds nothing and
+        // every slot it writes is disjoint from every slot it reads.
+        const int min_fold = c.window - in->ntok + 1;
+        if (c.ngroups < c.nheads && ctx->hi >= min_fold) {
+            M2FoldArgs f{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, min_fold, nullptr};
+            if ((s = launched(ctx, m2_fold(f, ctx->S0b != nullptr, strm(stream)), true)) != RSSM_OK)
+                return s;
+            bounds_after_fold(ctx, min_fold);
+            if (ctx->ulen >= min_fold) {
+                ctx->uhead = (ctx->uhead + ctx->ulen) % c.window;
+                ctx->ulen = 0;
+            }
+        }
         M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
                      in->x, in->B, in->C, in->dt, y, in->ntok};
         s = launched(ctx, m2_verify(a, ctx->S0b != nullptr, strm(stream)), true);

@@ -48,9 +48,10 @@ enum SeqMode { kSeqFork = 0, kSeqExport = 1, kSeqImport = 2 };
 constexpr int kSeqMaxSeg = 6;              // checkpoint, read copy and up to four ring arrays
 constexpr size_t kSeqHeader = 16;          // packed slot: head, len, ndraft, 0, then the segments
 constexpr uint32_t kDevIndexRange = 8u;    // device error bit: a sequence index out of range
+constexpr uint32_t kDevImportHeader = 16u; // device error bit: an imported slot header out of range
 
 struct SeqCopyArgs {
-    int mode, n, B, nseg;
+    int mode, n, B, W, nseg;
     const int32_t *src, *dst;              // fork: src[n], dst[n]; export: src = sequences; import: dst
     char *base[kSeqMaxSeg];                // array bases in the workspace
     uint64_t seg_bytes[kSeqMaxSeg];        // bytes of one sequence in each array

@@ -27,7 +27,17 @@ __device__ __forceinline__ void copy16_nt(char *dst, const char *src)
     __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(dst));
 }
 
+// A packed slot's header may come from anywhere: it is accepted only as an export writes it
+// (ring head in [0, W), committed length in [0, W], no pending drafts), so that every later kernel
+// sees ring indices in range.
+__device__ __forceinline__ bool header_ok(const SeqCopyArgs &a, int slot)
+{
+    const int32_t *h = reinterpret_cast<const int32_t *>(a.buf + (size_t)slot * a.pack_bytes);
+    return h[0] >= 0 && h[0] < a.W && h[1] >= 0 && h[1] <= a.W && h[2] == 0;
+}
+
 // source and destination (sequence or buffer slot) of pair p; false when an index is out of range
+// or an imported header is invalid (the pair is then skipped whole: state and bookkeeping)
 __device__ __forceinline__ bool pair_of(const SeqCopyArgs &a, int p, int &s, int &d)
 {
     if (a.mode == kSeqFork) {
@@ -42,7 +52,7 @@ __device__ __forceinline__ bool pair_of(const SeqCopyArgs &a, int p, int &s, int
     }
     s = p;
     d = a.dst[p];
-    return in_range(d, a.B);
+    return in_range(d, a.B) && header_ok(a, p);
 }
 
 __global__ void __launch_bounds__(256) k_seq_copy(SeqCopyArgs a)
@@ -81,7 +91,10 @@ __global__ void __launch_bounds__(256) k_seq_bk(SeqCopyArgs a, Bk bk)
     for (int p = t; p < a.n; p += 256) {
         int s, d;
         if (!pair_of(a, p, s, d)) {
-            atomicOr(a.err, kDevIndexRange);
+            const bool index_ok = a.mode == kSeqImport ? in_range(a.dst[p], B)
+                                : a.mode == kSeqExport ? in_range(a.src[p], B)
+                                : in_range(a.src[p], B) && in_range(a.dst[p], B);
+            atomicOr(a.err, index_ok ? kDevImportHeader : kDevIndexRange);
             continue;
         }
         if (a.mode == kSeqFork) {

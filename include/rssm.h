@@ -75,8 +75,11 @@ enum {
 enum {
     RSSM_DEV_COMMIT_RANGE = 1u,    /* accepted[b] outside [0, ndraft[b]]; len left unchanged */
     RSSM_DEV_ROLLBACK_RANGE = 2u,  /* new_len[b] outside [0, len[b]]; len left unchanged */
-    RSSM_DEV_INDEX_RANGE = 8u      /* a fork / export / import sequence index outside [0, B); that
+    RSSM_DEV_INDEX_RANGE = 8u,     /* a fork / export / import sequence index outside [0, B); that
                                       pair is skipped */
+    RSSM_DEV_IMPORT_HEADER = 16u   /* an imported slot's header is not one an export writes (head
+                                      outside [0, W), len outside [0, W] or pending drafts); that
+                                      pair is skipped: the sequence keeps its state */
 };
 
 enum { RSSM_MAMBA2 = 1, RSSM_GDN = 2 };
@@ -222,7 +225,9 @@ rssm_status rssm_fork(rssm_ctx *ctx, const int32_t *src, const int32_t *dst, int
 rssm_status rssm_export(rssm_ctx *ctx, const int32_t *seq, int32_t n, void *buf, void *stream);
 
 /* Replace the state of sequence seq[i] by packed slot i of buf (as written by rssm_export of a
- * context with the same configuration). seq indices must be distinct. */
+ * context with the same configuration). seq indices must be distinct. A slot whose header an
+ * export could not have written (head outside [0, W), len outside [0, W], ndraft != 0) is not
+ * imported and sets RSSM_DEV_IMPORT_HEADER. */
 rssm_status rssm_import(rssm_ctx *ctx, const int32_t *seq, int32_t n, const void *buf, void *stream);
 
 /* Write the current state of every sequence (S0 with its committed entries folded in) to

@@ -71,6 +71,10 @@ def _load():
         lib.orc_m2_step.restype = None
         lib.orc_gdn_step.argtypes = [i, i, i, i, fp, fp, fp, fp, fp, fp, fp]
         lib.orc_gdn_step.restype = None
+        lib.orc_m2_step_f32.argtypes = [i, i, i, i, i, fp, fp, fp, fp, fp, fp, fp, fp]
+        lib.orc_m2_step_f32.restype = None
+        lib.orc_gdn_kappa_step.argtypes = [i, i, i, i, fp, fp, fp, fp, fp, fp, fp]
+        lib.orc_gdn_kappa_step.restype = None
         lib.orc_set_threads.argtypes = [i]
         lib.orc_set_threads.restype = i
         _lib = lib
@@ -109,6 +113,45 @@ def m2_step(A, D, x, Bm, C, dt, state: np.ndarray) -> np.ndarray:
     y = np.empty((nb, nh, P), dtype=np.float64)
     _load().orc_m2_step(nb, nh, ng, P, N, *[k[1] for k in keep], _chk64(state), _chk64(y))
     return y
+
+
+def m2_step_f32(A, D, x, Bm, C, dt, state32: np.ndarray) -> np.ndarray:
+    """One conventional Mamba-2 token in fp32 arithmetic (``oracle.c``: orc_m2_step_f32).
+    ``state32`` [B,H,P,N] float32 is updated in place; returns y [B,H,P] float32. It measures how
+    far fp32 conventional decoding itself lands from the fp64 definition on given inputs."""
+    nb, nh, P, N = state32.shape
+    ng = Bm.shape[1]
+    assert nh % ng == 0 and x.shape == (nb, nh, P) and Bm.shape == (nb, ng, N)
+    assert C.shape == (nb, ng, N) and dt.shape == (nb, nh)
+    assert state32.dtype == np.float32 and state32.flags["C_CONTIGUOUS"]
+    keep = [_f32(v) for v in (A, D, x, Bm, C, dt)]
+    y = np.empty((nb, nh, P), dtype=np.float32)
+    _load().orc_m2_step_f32(nb, nh, ng, P, N, *[k[1] for k in keep], state32.ctypes.data,
+                            y.ctypes.data)
+    return y
+
+
+def m2_kappa_step(A, D, x, Bm, C, dt, M: np.ndarray) -> np.ndarray:
+    """Conditioning of one Mamba-2 token: the recurrence on absolute values. ``M`` [B,H,P,N]
+    float64 (start it at |S_0|) is updated in place to
+        M <- exp(dt A) M + dt |x| |B|^T
+    (dt > 0, so every coefficient is non-negative and M bounds entry by entry the absolute value
+    of every partial sum of the state's terms, in any evaluation order), and the return value
+        kappa[p] = sum_n M[p,n] |C_n| + |D x_p|
+    bounds the terms of the output y = S C + D x. A relative perturbation e of every term moves
+    y_p by at most e kappa_p. It is the conventional step run on |x|, |B|, |C|, |D|."""
+    ab = lambda a: np.abs(np.asarray(a, dtype=np.float32))
+    return m2_step(A, ab(D), ab(x), ab(Bm), ab(C), dt, M)
+
+
+def gdn_kappa_step(q, k, v, beta, alpha, M: np.ndarray) -> np.ndarray:
+    """Conditioning of one Gated DeltaNet token (``oracle.c``: orc_gdn_kappa_step). ``M``
+    [B,H,dv,dk] float64, start at |S_0|, updated in place; returns kappa [B,H,dv]."""
+    nb, nh, dv, dk = M.shape
+    keep = [_f32(a) for a in (q, k, v, beta, alpha)]
+    kap = np.empty((nb, nh, dv), dtype=np.float64)
+    _load().orc_gdn_kappa_step(nb, nh, dk, dv, *[kk[1] for kk in keep], _chk64(M), _chk64(kap))
+    return kap
 
 
 def gdn_step(q, k, v, beta, alpha, state: np.ndarray) -> np.ndarray:
@@ -153,6 +196,24 @@ def m2_spec_round(A, D, drafts: dict, state: np.ndarray, accepted) -> np.ndarray
         keep[sel] = work[sel]
     state[...] = keep
     return np.stack(ys)
+
+
+def m2_spec_kappa(A, D, drafts: dict, M: np.ndarray, accepted) -> np.ndarray:
+    """Conditioning (m2_kappa_step) of the K draft outputs of a speculative round, with ``M``
+    [B,H,P,N] kept, per sequence, after ``accepted[b]`` drafts, as m2_spec_round keeps the state.
+    Returns kappa [K,B,H,P]."""
+    K = drafts["x"].shape[0]
+    acc = np.asarray(accepted)
+    work = M.copy()
+    keep = M.copy()
+    ks = []
+    for k in range(K):
+        ks.append(m2_kappa_step(A, D, drafts["x"][k], drafts["B"][k], drafts["C"][k],
+                                drafts["dt"][k], work))
+        sel = acc == k + 1
+        keep[sel] = work[sel]
+    M[...] = keep
+    return np.stack(ks)
 
 
 def gdn_spec_round(drafts: dict, state: np.ndarray, accepted) -> np.ndarray:
@@ -587,18 +648,65 @@ class GDNReplay:
 # Comparison metric
 # ----------------------------------------------------------------------------------------------
 
-def normwise_err(got, ref, head_floor=None) -> float:
-    """max over output vectors (last axis) of max|got - ref| / max|ref|.
-
-    With head_floor (arrays [..., H, P]: the heads of one sequence-token in the last two axes),
-    each head vector's denominator is at least head_floor times the largest |ref| over all heads of
-    the same sequence-token: a head whose output nearly cancels is measured against the scale of the
-    layer output it belongs to rather than against its own near-zero magnitude."""
+def normwise_err(got, ref) -> float:
+    """max over output vectors (last axis) of max|got - ref| / max|ref| (0 for an empty array)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     num = np.max(np.abs(got - ref), axis=-1)
     den = np.max(np.abs(ref), axis=-1)
-    if head_floor is not None:
-        den = np.maximum(den, head_floor * np.max(den, axis=-1, keepdims=True))
     den = np.where(den == 0, 1.0, den)
     return float(np.max(num / den)) if num.size else 0.0
+
+
+# Unit roundoff of fp32 and of bf16 (round to nearest).
+U32 = 2.0 ** -24
+U16 = 2.0 ** -8
+# Rounding-error constant of the fp32 paths. A term of an output passes through at most about
+# N + 2W + 8 roundings that the decay does not damp (the d_state products and their sum, the W
+# buffered entries of the newest window and one fold's scale and sum; 168 at d_state 128, W 16);
+# the worst-case bound of a sum evaluated in any order is then that many unit roundoffs of the
+# sum of the absolute values of its terms (kappa). 256 covers it with room for the errors carried
+# in the checkpoint from earlier windows, which each window's decay shrinks.
+C_FP32 = 256
+
+
+class Cond:
+    """Result of ``cond_check``: the worst unfloored normwise error over the output vectors, how
+    many vectors exceed the tolerance, the worst ratio |got - ref| / bound over the elements of
+    those vectors (0 if there are none) and over all elements."""
+
+    def __init__(self, worst, n_over, ratio_over, ratio_all, where):
+        self.worst, self.n_over = worst, n_over
+        self.ratio_over, self.ratio_all, self.where = ratio_over, ratio_all, where
+
+    @property
+    def ok(self) -> bool:
+        """Every vector within the tolerance or, element by element, within its bound."""
+        return self.ratio_over <= 1.0
+
+    def __repr__(self):
+        return (f"normwise {self.worst:.3e} ({self.n_over} vectors over tolerance, worst "
+                f"|d|/bound there {self.ratio_over:.3f} at {self.where}); "
+                f"worst |d|/bound over all elements {self.ratio_all:.3f}")
+
+
+def cond_check(got, ref, bound, tol) -> Cond:
+    """Per output vector (last axis): it passes when its normwise error max|d| / max|ref| is within
+    ``tol``, or else when every element satisfies |d| <= ``bound`` (broadcast to ref's shape: the
+    rounding-error bound of that element, e.g. C_FP32 * U32 * kappa)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = np.broadcast_to(np.asarray(bound, dtype=np.float64), ref.shape)
+    d = np.abs(got - ref)
+    den = np.max(np.abs(ref), axis=-1)
+    nw = np.max(d, axis=-1) / np.where(den == 0, 1.0, den)
+    over = nw > tol
+    r = np.max(d / np.where(bound > 0, bound, np.inf), axis=-1) if d.size else np.zeros(nw.shape)
+    ratio_all = float(np.max(r)) if r.size else 0.0
+    ratio_over, where = 0.0, None
+    if over.any():
+        ro = np.where(over, r, 0.0)
+        idx = np.unravel_index(int(np.argmax(ro)), ro.shape)
+        ratio_over, where = float(ro[idx]), tuple(int(v) for v in idx)
+    worst = float(np.max(nw)) if nw.size else 0.0
+    return Cond(worst, int(over.sum()), ratio_over, ratio_all, where)

@@ -113,3 +113,84 @@ void orc_gdn_step(int nb, int nh, int dk, int dv,
         }
     }
 }
+
+/*
+ * The same conventional Mamba-2 token evaluated in fp32: the state is fp32, every operation is
+ * rounded to fp32 in the order of the definition above (exp by the C library's expf, the output
+ * sum accumulated over n in increasing order, no contraction). This is conventional decoding as
+ * an fp32 implementation runs it; the pages fix the state precision at FP32 (fagnersouza.tech
+ * post, section "O que muda para quem desenvolve"), and the outputs of the method are to equal
+ * conventional decoding up to floating-point differences (same post, "Cuidados e limites"). It
+ * gives the size of those differences on given inputs; it is not what the GPU path is checked
+ * against. Layouts as orc_m2_step; state [nb,nh,P,N] fp32 in place, y [nb,nh,P] fp32.
+ */
+void orc_m2_step_f32(int nb, int nh, int ng, int P, int N,
+                     const float *A, const float *D,
+                     const float *x, const float *Bm, const float *C, const float *dt,
+                     float *state, float *y)
+{
+    const int hpg = nh / ng;
+    const long pairs = (long)nb * nh;
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < pairs; ++bh) {
+        const long b = bh / nh;
+        const int h = (int)(bh % nh);
+        const int g = h / hpg;
+        const float dtv = dt[bh];
+        const float a = expf(dtv * A[h]);
+        const float *xv = x + bh * P;
+        const float *Bv = Bm + (b * ng + g) * N;
+        const float *Cv = C + (b * ng + g) * N;
+        float *S = state + bh * (long)P * N;
+        for (int p = 0; p < P; ++p) {
+            const float coef = dtv * xv[p];
+            float acc = 0.0f;
+            for (int n = 0; n < N; ++n) {
+                const float s = a * S[(long)p * N + n] + coef * Bv[n];
+                S[(long)p * N + n] = s;
+                acc += s * Cv[n];
+            }
+            y[bh * P + p] = acc + D[h] * xv[p];
+        }
+    }
+}
+
+/*
+ * Conditioning of one Gated DeltaNet token, for rounding-error bounds. M [nb,nh,dv,dk] (fp64, in
+ * place) bounds, entry by entry, the absolute values of the terms the update sums: with
+ * s_i = sum_l M[i][l] |k_l|,
+ *     M[i][j] <- alpha (M[i][j] + beta s_i |k_j|) + beta |v_i| |k_j|
+ * (the three terms of alpha (S - beta (S k) k^T) + beta v k^T), starting from |S_0|; and
+ *     kappa[i] = sum_j M[i][j] |q_j|
+ * bounds the terms of the output o = S q. A rounding error of relative size e on any term moves
+ * o_i by at most e kappa_i. Layouts as orc_gdn_step; kappa [nb,nh,dv].
+ */
+void orc_gdn_kappa_step(int nb, int nh, int dk, int dv,
+                        const float *q, const float *k, const float *v,
+                        const float *beta, const float *alpha,
+                        double *M, double *kappa)
+{
+    const long pairs = (long)nb * nh;
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < pairs; ++bh) {
+        const double be = (double)beta[bh];
+        const double al = (double)alpha[bh];
+        const float *qv = q + bh * dk;
+        const float *kv = k + bh * dk;
+        const float *vv = v + bh * dv;
+        double *Mt = M + bh * (long)dv * dk;
+        for (int i = 0; i < dv; ++i) {
+            double *row = Mt + (long)i * dk;
+            double s = 0.0;
+            for (int j = 0; j < dk; ++j) s += row[j] * fabs((double)kv[j]);
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) {
+                const double kj = fabs((double)kv[j]);
+                const double m = al * (row[j] + be * s * kj) + be * fabs((double)vv[i]) * kj;
+                row[j] = m;
+                acc += m * fabs((double)qv[j]);
+            }
+            kappa[bh * dv + i] = acc;
+        }
+    }
+}

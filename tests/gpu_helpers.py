@@ -46,3 +46,29 @@ def host(t) -> np.ndarray:
 
 def say(msg: str):
     print(msg, flush=True)
+
+
+# Conditioning of every sequence of a full batch, for rounding bounds between two GPU results
+# (plain PyTorch on the device; the oracle's m2_kappa_step / gdn_kappa_step give the same scale
+# for the sampled sequences compared against the oracle).
+
+def m2_kappa_torch(M, A, D, x, Bm, C, dt):
+    """M [B,H,P,N] fp32 (start at |S_0|) <- exp(dt A) M + dt |x| |B|^T in place; returns
+    kappa [B,H,P] = sum_n M |C| + |D x| (the absolute-value recurrence, all terms >= 0)."""
+    H, G = M.shape[1], Bm.shape[1]
+    hmap = torch.arange(H, device=M.device) // (H // G)
+    a = torch.exp(dt * A[None, :])
+    Bh, Ch = Bm.abs()[:, hmap], C.abs()[:, hmap]
+    M.mul_(a[..., None, None]).add_((dt[..., None] * x.abs())[..., None] * Bh[:, :, None, :])
+    return (M * Ch[:, :, None, :]).sum(-1) + (D.abs()[None, :, None] * x.abs())
+
+
+def gdn_kappa_torch(M, q, k, v, beta, alpha):
+    """M [B,H,dv,dk] fp32 (start at |S_0|) <- alpha (M + beta s |k|^T) + beta |v| |k|^T with
+    s = M |k|, in place; returns kappa [B,H,dv] = M |q|."""
+    ka = k.abs()
+    s = (M * ka[:, :, None, :]).sum(-1)
+    be, al = beta[..., None, None], alpha[..., None, None]
+    M.add_(be * s[..., None] * ka[:, :, None, :]).mul_(al)
+    M.add_(be * v.abs()[..., None] * ka[:, :, None, :])
+    return (M * q.abs()[:, :, None, :]).sum(-1)

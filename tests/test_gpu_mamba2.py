@@ -2,7 +2,10 @@
 
 Tolerances: normwise relative error (max over output vectors of max|d| / max|ref|) 1e-5 for the
 fp32 paths and 2e-2 for the bf16 read copy; bookkeeping (head, len, ndraft, error bits)
-bit-exact.
+bit-exact. At the serving shape an output vector that misses its tolerance must instead be within
+its rounding bound element by element: C_FP32 u32 kappa for fp32 (kappa the sum of the absolute
+values of the output's terms, oracle.m2_kappa_step), plus Lam u16 sum_n |S0[p,n]| |C_n| for the
+bf16 read copy.
 """
 import json
 import os
@@ -13,14 +16,14 @@ import torch
 
 import workloads as wl
 from checkpoint_replay_buffer_amd import binding as rb
-from oracle import Bookkeeping, m2_spec_round, m2_step, normwise_err
-from tests.gpu_helpers import dev, host, m2_dev_tokens, say, tok0
+from oracle import (C_FP32, U16, U32, Bookkeeping, cond_check, m2_kappa_step, m2_spec_kappa,
+                    m2_spec_round, m2_step, normwise_err)
+from tests.gpu_helpers import dev, host, m2_dev_tokens, m2_kappa_torch, say, tok0
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
 TOL_BF16 = 2e-2
-HEAD_FLOOR = 0.01   # full-batch serving checks: a head's denominator >= 1 % of the token's largest head
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -105,8 +108,9 @@ def test_rmw_comparator_tiny():
 
 @pytest.mark.parametrize("P,N", [(16, 16), (32, 32), (64, 64), (64, 128), (128, 128)])
 def test_rmw_comparator_workgroup_sizes(P, N):
-    """The conventional kernel on each of its workgroup sizes, which depend on the token count: one
-    token, a 5-draft snapshot launch, then 12 tokens in one launch."""
+    """The conventional kernel on the workgroup sizes of few tiles, which depend on the token
+    count: one token, a 5-draft snapshot launch, then 12 tokens in one launch (the single-token
+    workgroup of large grids is covered by the next test)."""
     sh = wl.M2Shape(batch=2, nheads=3, ngroups=3, head_dim=P, d_state=N, window=16)
     prm = wl.m2_params(sh, 7)
     s0 = wl.m2_state0(sh, 7)
@@ -140,18 +144,21 @@ def test_rmw_comparator_workgroup_sizes(P, N):
     assert normwise_err(host(st), ref) < TOL
 
 
-def test_rmw_comparator_single_token_large_grid():
-    """One token over 16k tiles at 64 x 128, where the conventional kernel takes its widest
-    workgroup (1024 threads)."""
-    sh = wl.M2Shape(batch=64, nheads=256, ngroups=16, head_dim=64, d_state=128, window=16)
+@pytest.mark.parametrize("P,N", [(64, 128), (128, 128), (64, 64), (32, 32)])
+def test_rmw_comparator_single_token_large_grid(P, N):
+    """One token over 16k tiles, where the conventional kernel takes its single-token workgroup
+    (clamp(P N / 8, 64, 1024) threads: 1024 at 64 x 128 and 128 x 128, 512 at 64 x 64, 128 at
+    32 x 32), at each of those shapes."""
+    sh = wl.M2Shape(batch=64, nheads=256, ngroups=16, head_dim=P, d_state=N, window=16)
+    say(f"conventional kernel, one token, 16k tiles of {P}x{N}")
     prm = wl.m2_params(sh, 8)
     s0 = wl.m2_state0(sh, 8)
     ins = wl.m2_token_inputs(sh, 8, 0, ntok=1)
     d = m2_dev_tokens(sh, ins, 1)
-    cfg = rb.make_config(rb.RSSM_MAMBA2, sh.batch, sh.nheads, sh.ngroups, 64, 128, 16)
+    cfg = rb.make_config(rb.RSSM_MAMBA2, sh.batch, sh.nheads, sh.ngroups, P, N, 16)
     st = dev(s0)
     ref = s0.astype(np.float64)
-    y = torch.empty(1, sh.batch, sh.nheads, 64, device="cuda")
+    y = torch.empty(1, sh.batch, sh.nheads, P, device="cuda")
     rb.step_baseline(cfg, st, y, dev(prm["A"]), dev(prm["D"]), **d)
     y_ref = m2_step(prm["A"], prm["D"], ins["x"][0], ins["B"][0], ins["C"][0], ins["dt"][0], ref)
     assert normwise_err(host(y)[0], y_ref) < TOL
@@ -393,12 +400,14 @@ def test_determinism_and_head_permutation():
 SUBSET = np.array([0, 1, 37, 101, 128, 190, 254, 255])
 
 
-@pytest.mark.parametrize("bf16,steps,G", [(False, 512, 128), (True, 160, 128), (False, 128, 8),
+@pytest.mark.parametrize("bf16,steps,G", [(False, 512, 128), (True, 512, 128), (False, 128, 8),
                                           (False, 128, 1)])
 def test_serving_shape_sampled(bf16, steps, G):
     """Serving shape (batch 256, 128 heads, 64x128, W = 16): sampled sequences against the oracle
     at every step, all sequences against the read-modify-write kernel; also with B/C shared by
-    groups of heads (G = 8, G = 1)."""
+    groups of heads (G = 8, G = 1). With the bf16 read copy: every replayed element within the
+    bf16 rounding bound of the checkpoint term, and no drift (the worst error of the last 64 steps
+    no larger than that of the first 64: every fold restarts the copy from the fp32 checkpoint)."""
     sh = wl.M2_SERVE if G == 128 else wl.M2Shape(batch=256, nheads=128, ngroups=G, head_dim=64,
                                                    d_state=128, window=16)
     say(f"serving shape bf16={bf16} steps={steps} G={G}: generating inputs")
@@ -412,11 +421,12 @@ def test_serving_shape_sampled(bf16, steps, G):
     cfg = rb.make_config(rb.RSSM_MAMBA2, sh.batch, sh.nheads, sh.ngroups, sh.head_dim, sh.d_state,
                          sh.window)
     st_rmw = dev(s0)
+    kap_state = dev(np.abs(s0)) if not bf16 else None
     y = torch.empty(sh.batch, sh.nheads, sh.head_dim, device="cuda")
     y2 = torch.empty(1, sh.batch, sh.nheads, sh.head_dim, device="cuda")
     sub = torch.from_numpy(SUBSET).cuda()
     ys = torch.empty(steps, len(SUBSET), sh.nheads, sh.head_dim, device="cuda")
-    worst_pair = 0.0
+    pair = []
     say("  running GPU steps")
     for t in range(steps):
         tok = dslots[t % pool]
@@ -424,47 +434,63 @@ def test_serving_shape_sampled(bf16, steps, G):
         ys[t] = y.index_select(0, sub)
         if not bf16:
             rb.step_baseline(cfg, st_rmw, y2, A, D, **{k: v.unsqueeze(0) for k, v in tok.items()})
+            kap = m2_kappa_torch(kap_state, A, D, tok["x"], tok["B"], tok["C"], tok["dt"])
             if t % 64 == 63:     # replay vs read-modify-write at every sequence
-                worst_pair = max(worst_pair, normwise_err(host(y), host(y2)[0], HEAD_FLOOR))
+                pair.append(cond_check(host(y), host(y2)[0], 2 * C_FP32 * U32 * host(kap), 2 * TOL))
     mat = torch.empty(s0.shape, device="cuda")
     ctx.materialize(mat)
     h, l, n, e = ctx.bookkeeping()
     assert l == [steps % sh.window] * sh.batch and h == [0] * sh.batch and e == 0
     say("  oracle on the sampled sequences")
     ref = s0[SUBSET].astype(np.float64)
+    M = np.abs(ref)        # absolute-value recurrence: kappa of every output
     ck = ref.copy()        # the checkpoint the kernel reads: the state at the last fold
     win_dt = []            # dt of the entries buffered since that fold
+    tol = TOL_BF16 if bf16 else TOL
+    worst_ratio = worst_ratio_all = 0.0
     worst = worst_tok = 0.0
+    n_over = 0
+    per_step = []
     ys_h = host(ys)
     W = sh.window
     for t in range(steps):
         s = {k: v[0][SUBSET] for k, v in slots[t % pool].items()}
-        y_ref = m2_step(prm["A"], prm["D"], s["x"], s["B"], s["C"], s["dt"], ref)
-        worst = max(worst, normwise_err(ys_h[t], y_ref, HEAD_FLOOR))
-        worst_tok = max(worst_tok, normwise_err(ys_h[t].reshape(len(SUBSET), -1),
-                                                y_ref.reshape(len(SUBSET), -1)))
+        args = (s["x"], s["B"], s["C"], s["dt"])
+        y_ref = m2_step(prm["A"], prm["D"], *args, ref)
+        kap = m2_kappa_step(prm["A"], prm["D"], *args, M)
+        bound = C_FP32 * U32 * kap
         win_dt.append(s["dt"].astype(np.float64))
         if bf16 and t % W + 1 < W:
-            # bf16 rounding of the checkpoint read: |dy| <= Lam * 2^-8 * sum_n |S0[p,n]| |C_n|
+            # bf16 rounding of the checkpoint read: |dy| <= Lam * u16 * sum_n |S0[p,n]| |C_n|
             lam = np.exp(prm["A"].astype(np.float64)[None, :] * np.sum(win_dt, axis=0))
-            bound = lam[..., None] * 2.0 ** -8 * np.einsum("bhpn,bhn->bhp", np.abs(ck),
-                                                           np.abs(s["C"].astype(np.float64)))
-            slack = TOL * np.max(np.abs(y_ref), axis=-1, keepdims=True)
-            assert np.all(np.abs(ys_h[t] - y_ref) <= bound + slack), t
+            hh = np.arange(sh.nheads) // (sh.nheads // sh.ngroups)
+            Cg = np.abs(s["C"].astype(np.float64))[:, hh]
+            bound = bound + lam[..., None] * U16 * np.einsum("bhpn,bhn->bhp", np.abs(ck), Cg)
+        c = cond_check(ys_h[t], y_ref, bound, tol)
+        assert c.ok, (t, c)
+        worst_ratio = max(worst_ratio, c.ratio_over)
+        worst_ratio_all = max(worst_ratio_all, c.ratio_all)
+        worst = max(worst, c.worst)
+        n_over += c.n_over
+        per_step.append(normwise_err(ys_h[t].reshape(len(SUBSET), -1), y_ref.reshape(len(SUBSET), -1)))
+        worst_tok = max(worst_tok, per_step[-1])
         if t % W + 1 == W:
             ck = ref.copy()
             win_dt = []
-    say(f"  worst normwise per head {worst:.3e}, per sequence-token {worst_tok:.3e} "
-        f"(replay vs rmw {worst_pair:.3e})")
+    say(f"  per head: worst normwise {worst:.3e}, {n_over} head vectors over {tol:g}, worst "
+        f"|d|/bound over them {worst_ratio:.3f}, over all elements {worst_ratio_all:.3f}; per "
+        f"sequence-token {worst_tok:.3e}")
+    for c in pair:
+        say(f"  replay vs read-modify-write, all sequences: {c}")
+        assert c.ok
+    assert worst_ratio_all <= 1.0
     if bf16:
-        # tolerance on the layer output of one token of one sequence (all heads); single heads
-        # whose output is small next to the checkpoint term can exceed it within the bound above
-        assert worst_tok < TOL_BF16
-    else:
-        assert worst < TOL
+        first, last = max(per_step[:64]), max(per_step[-64:])
+        say(f"  bf16 drift: worst per sequence-token error, first 64 steps {first:.3e}, last 64 "
+            f"{last:.3e}")
+        assert last <= first
     assert normwise_err(host(mat)[SUBSET], ref) < TOL
     if not bf16:
-        assert worst_pair < 2 * TOL
         assert normwise_err(host(st_rmw)[SUBSET], ref) < TOL
 
 
@@ -485,10 +511,15 @@ def test_bf16_small_batches(batch):
         assert normwise_err(host(y), y_ref) < TOL_BF16
 
 
-def test_speculative_serving_shape_sampled():
+@pytest.mark.parametrize("G", [128, 8])
+def test_speculative_serving_shape_sampled(G):
     """batch 512, K = 6 drafts per round into the W = 16 ring, censored-geometric acceptance:
-    bookkeeping of all 512 sequences bit-exact after every call, outputs of sampled sequences."""
-    sh = wl.M2_SPEC
+    bookkeeping of all 512 sequences bit-exact after every call, outputs of sampled sequences.
+    With B / C shared by groups of 16 heads (G = 8), sequences whose drafts do not fit are folded
+    by a consolidation launch before the verify, whose draft appends then never overwrite a ring
+    slot another head of the group still reads."""
+    sh = wl.M2_SPEC if G == 128 else wl.M2Shape(batch=512, nheads=128, ngroups=G, head_dim=64,
+                                                  d_state=128, window=16, max_draft=6)
     K, rounds = 6, 24
     prm = wl.m2_params(sh, 0)
     s0 = wl.m2_state0(sh, 0)
@@ -498,8 +529,9 @@ def test_speculative_serving_shape_sampled():
     model = Bookkeeping(sh.batch, sh.window, K)
     sub = np.array([0, 5, 300, 511])
     ref = s0[sub].astype(np.float64)
+    M = np.abs(ref)
     yk = torch.empty(K, sh.batch, sh.nheads, sh.head_dim, device="cuda")
-    worst = 0.0
+    worst, worst_ratio, n_over = 0.0, 0.0, 0
     pool = [wl.m2_token_inputs(sh, 0, s, ntok=K) for s in range(3)]
     dpool = [m2_dev_tokens(sh, p, K) for p in pool]
     for r in range(rounds):
@@ -512,9 +544,13 @@ def test_speculative_serving_shape_sampled():
         _check_bk(ctx, model, 0)
         sub_ins = {k: v[:, sub] for k, v in ins.items()}
         y_ref = m2_spec_round(prm["A"], prm["D"], sub_ins, ref, acc[r][sub])
-        worst = max(worst, normwise_err(host(yk)[:, sub], y_ref))
-    say(f"  spec worst normwise {worst:.3e}")
-    assert worst < TOL
+        kap = m2_spec_kappa(prm["A"], prm["D"], sub_ins, M, acc[r][sub])
+        c = cond_check(host(yk)[:, sub], y_ref, C_FP32 * U32 * kap, TOL)
+        assert c.ok and c.ratio_all <= 1.0, (r, c)
+        worst, n_over = max(worst, c.worst), n_over + c.n_over
+        worst_ratio = max(worst_ratio, c.ratio_all)
+    say(f"  spec G={G}: worst normwise {worst:.3e}, {n_over} head vectors over {TOL:g}, worst "
+        f"|d|/bound {worst_ratio:.3f}")
 
 
 def test_snapshot_comparator_rounds():

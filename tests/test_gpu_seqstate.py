@@ -146,6 +146,43 @@ def test_bad_indices_set_error_bit():
     assert e == 0 and (h[2], l[2]) == (h[0], l[0])
 
 
+def test_import_rejects_bad_headers():
+    """A packed slot whose header an export could not have written (head outside [0, W), len
+    outside [0, W], pending drafts) is not imported: the device error bit is set and the sequence
+    keeps its state and bookkeeping; the valid slots of the same call are imported."""
+    sh = wl.M2Shape(batch=4, nheads=2, ngroups=2, head_dim=16, d_state=16, window=4)
+    prm = wl.m2_params(sh, 8)
+    s0 = wl.m2_state0(sh, 8)
+    ins = wl.m2_token_inputs(sh, 8, 0, ntok=3)
+    d = m2_dev_tokens(sh, ins, 3)
+    ctx = _m2_ctx(sh, prm)
+    ctx.init_checkpoint(dev(s0))
+    y = torch.empty(sh.batch, sh.nheads, 16, device="cuda")
+    for t in range(3):
+        ctx.decode_step(y, **_tok(d, t))
+    nbytes = ctx.seq_state_bytes()
+    buf = torch.zeros(4 * nbytes // 4, dtype=torch.float32, device="cuda")
+    ctx.export(_i32([0, 0, 0, 0]), buf)      # four copies of sequence 0 (len 3)
+    hdr = buf.view(torch.int32).view(4, nbytes // 4)
+    hdr[0, 0] = sh.window                    # head out of range
+    hdr[1, 1] = sh.window + 1                # len out of range
+    hdr[2, 2] = 1                            # pending drafts
+    ctx2 = _m2_ctx(sh, prm)
+    ctx2.init_checkpoint(dev(wl.m2_state0(sh, 9)))
+    m = torch.empty(s0.shape, device="cuda")
+    ctx2.materialize(m)
+    before = host(m).copy()
+    ctx2.import_(_i32([0, 1, 2, 3]), buf)
+    h, l, n, e = ctx2.bookkeeping()
+    assert e == rb.RSSM_DEV_IMPORT_HEADER
+    assert (h[:3], l[:3], n[:3]) == ([0, 0, 0], [0, 0, 0], [0, 0, 0]) and l[3] == 3
+    ctx2.materialize(m)
+    after = host(m)
+    assert np.array_equal(after[:3], before[:3])
+    ctx.materialize(m)
+    assert np.array_equal(after[3], host(m)[0])
+
+
 @pytest.mark.parametrize("dd,W", [(16, 4), (128, 16)])
 def test_gdn_fork(dd, W):
     sh = wl.GDNShape(batch=3, nheads=2, d_k=dd, d_v=dd, window=W)

@@ -283,15 +283,47 @@ def test_replay_model_follows_golden_trace(oracle_lib):
         assert list(h) == op["head"] and list(l) == op["len"] and list(nd) == op["ndraft"], op
 
 
-def test_normwise_head_floor():
-    """The head floor changes only heads whose output is small next to the sequence-token's
-    largest head: a near-cancelled head is measured against the layer scale."""
-    from oracle import normwise_err
+def test_cond_check_semantics():
+    """A vector within the normwise tolerance passes whatever its bound; one over it passes only
+    if every element is within its bound; the ratios say which element decided."""
+    from oracle import cond_check
     ref = np.array([[[1.0, -2.0], [1e-4, 2e-4]]])          # [token, H=2, P=2]
     got = ref.copy()
-    got[0, 1, 0] += 1e-6                                   # absolute error 1e-6 on the small head
-    assert abs(normwise_err(got, ref) - 1e-6 / 2e-4) < 1e-12
-    assert abs(normwise_err(got, ref, head_floor=0.01) - 1e-6 / 0.02) < 1e-12
+    got[0, 1, 0] += 1e-6                                   # 5e-3 normwise on the small head
+    bound = np.full(ref.shape, 2e-6)
+    c = cond_check(got, ref, bound, 1e-5)
+    assert c.n_over == 1 and abs(c.worst - 1e-6 / 2e-4) < 1e-12
+    assert abs(c.ratio_over - 0.5) < 1e-12 and c.where == (0, 1) and c.ok
+    c = cond_check(got, ref, bound / 4, 1e-5)              # same error, bound too small: fails
+    assert not c.ok and abs(c.ratio_over - 2.0) < 1e-12
     got2 = ref.copy()
-    got2[0, 0, 1] += 1e-6                                  # a large head is unaffected
-    assert normwise_err(got2, ref, head_floor=0.01) == normwise_err(got2, ref)
+    got2[0, 0, 1] += 1e-6                                  # within 1e-5 of a large head: passes
+    c = cond_check(got2, ref, bound / 100, 1e-5)
+    assert c.ok and c.n_over == 0 and c.ratio_over == 0.0 and abs(c.ratio_all - 50.0) < 1e-6
+
+
+def test_verify_launch_ring_slots_disjoint():
+    """Ring slots touched by one speculative-verify launch, for every (W, K, head, len).
+
+    The verify launch appends the K drafts at logical entries len_e .. len_e + K - 1 and, with B / C
+    shared by a group of heads, only the group's first head writes the group's B rows, while every
+    head of the group reads the committed entries 0 .. len_e - 1 in other workgroups of the same
+    launch. With G < H the library folds sequences whose drafts do not fit (len + K > W) in a
+    consolidation launch before the verify, so the verify launch sees len_e + K <= W; with G = H
+    each workgroup reads and writes only its own head's rows, ordered by its own barrier. Under
+    that plan the written slots never meet a slot read by another workgroup."""
+    for W in range(1, 33):
+        for K in range(1, W + 1):
+            for head in range(W):
+                for ln in range(W + 1):
+                    # G < H: the consolidation launch folds first when the drafts do not fit
+                    h_e, l_e = ((head + ln) % W, 0) if ln + K > W else (head, ln)
+                    assert l_e + K <= W
+                    reads = {(h_e + j) % W for j in range(l_e)}
+                    writes = {(h_e + l_e + k) % W for k in range(K)}
+                    assert len(writes) == K and not (reads & writes), (W, K, head, ln)
+                    # the bookkeeping model lands on the same ring position
+                    bk = Bookkeeping(1, W, K)
+                    bk.head[0], bk.len[0] = head, ln
+                    bk.verify(K)
+                    assert (int(bk.head[0]), int(bk.len[0])) == (h_e, l_e)
