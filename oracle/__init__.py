@@ -10,7 +10,9 @@ Contents
 * ``m2_conventional`` / ``gdn_conventional``: those steps run over a token schedule.
 * ``Bookkeeping``: the integer model of the ring pointers (head, len, ndraft) and of the
   commit / rollback rules, which the device bookkeeping must match bit for bit.
-* ``M2Replay`` / ``GDNReplay``: fp64 numpy models of the checkpoint + ring-buffer form itself
+* ``kda_step`` and friends: the Kimi Delta Attention counterparts (a per key channel gate; the
+  pages name the layer type without a formula, so the step is the reading stated in ``oracle.c``).
+* ``M2Replay`` / ``GDNReplay`` / ``KDAReplay``: fp64 numpy models of the checkpoint + ring-buffer form itself
   (append, replay output, consolidation, speculative verify, commit, rollback). They exist so that
   the invariants the pages fix -- replayed outputs equal conventional decoding, consolidation equals
   the sequential steps, rollback equals recomputation from the accepted prefix -- can be checked on
@@ -45,14 +47,19 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# RSSM_ORACLE_SANITIZE=1 selects a build with AddressSanitizer and UndefinedBehaviorSanitizer
+# (the process must then preload libasan, e.g. LD_PRELOAD=$(gcc -print-file-name=libasan.so)).
+_SANITIZE = os.environ.get("RSSM_ORACLE_SANITIZE") == "1"
+_SO = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile ``oracle.c`` into ``liboracle.so`` with gcc (fp64, no contraction, OpenMP)."""
     if force or not os.path.exists(_SO):
-        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-fno-omit-frame-pointer", "-g"] if _SANITIZE else []
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", *san,
                "-shared", os.path.join(_HERE, "oracle.c"), "-o", _SO + ".tmp", "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(_SO + ".tmp", _SO)
@@ -75,6 +82,10 @@ def _load():
         lib.orc_m2_step_f32.restype = None
         lib.orc_gdn_kappa_step.argtypes = [i, i, i, i, fp, fp, fp, fp, fp, fp, fp]
         lib.orc_gdn_kappa_step.restype = None
+        lib.orc_kda_step.argtypes = [i, i, i, i, fp, fp, fp, fp, fp, fp, fp]
+        lib.orc_kda_step.restype = None
+        lib.orc_kda_kappa_step.argtypes = [i, i, i, i, fp, fp, fp, fp, fp, fp, fp]
+        lib.orc_kda_kappa_step.restype = None
         lib.orc_set_threads.argtypes = [i]
         lib.orc_set_threads.restype = i
         _lib = lib
@@ -165,6 +176,28 @@ def gdn_step(q, k, v, beta, alpha, state: np.ndarray) -> np.ndarray:
     return o
 
 
+def kda_step(q, k, v, beta, a, state: np.ndarray) -> np.ndarray:
+    """One conventional Kimi Delta Attention token (``oracle.c``: orc_kda_step): per key channel
+    gate a [B,H,dk]; ``state`` [B,H,dv,dk] float64, updated in place; returns o [B,H,dv]."""
+    nb, nh, dv, dk = state.shape
+    assert q.shape == (nb, nh, dk) and k.shape == (nb, nh, dk) and v.shape == (nb, nh, dv)
+    assert beta.shape == (nb, nh) and a.shape == (nb, nh, dk)
+    keep = [_f32(x) for x in (q, k, v, beta, a)]
+    o = np.empty((nb, nh, dv), dtype=np.float64)
+    _load().orc_kda_step(nb, nh, dk, dv, *[kk[1] for kk in keep], _chk64(state), _chk64(o))
+    return o
+
+
+def kda_kappa_step(q, k, v, beta, a, M: np.ndarray) -> np.ndarray:
+    """Conditioning of one Kimi Delta Attention token (``oracle.c``: orc_kda_kappa_step). ``M``
+    [B,H,dv,dk] float64, start at |S_0|, updated in place; returns kappa [B,H,dv]."""
+    nb, nh, dv, dk = M.shape
+    keep = [_f32(x) for x in (q, k, v, beta, a)]
+    kap = np.empty((nb, nh, dv), dtype=np.float64)
+    _load().orc_kda_kappa_step(nb, nh, dk, dv, *[kk[1] for kk in keep], _chk64(M), _chk64(kap))
+    return kap
+
+
 def m2_conventional(A, D, tokens, state0) -> tuple[np.ndarray, np.ndarray]:
     """Run conventional decoding over ``tokens`` (an iterable of dicts with x, B, C, dt, one token
     each). Returns (y [T,B,H,P] float64, final state float64)."""
@@ -232,6 +265,46 @@ def gdn_spec_round(drafts: dict, state: np.ndarray, accepted) -> np.ndarray:
         keep[sel] = work[sel]
     state[...] = keep
     return np.stack(os_)
+
+
+def kda_conventional(tokens, state0) -> tuple[np.ndarray, np.ndarray]:
+    state = np.array(state0, dtype=np.float64, order="C", copy=True)
+    os_ = [kda_step(t["q"], t["k"], t["v"], t["beta"], t["alpha"], state) for t in tokens]
+    return np.stack(os_), state
+
+
+def kda_spec_round(drafts: dict, state: np.ndarray, accepted) -> np.ndarray:
+    """Kimi Delta Attention counterpart of m2_spec_round (drafts q, k, v, beta, alpha with a
+    leading K axis; alpha [K,B,H,dk]); ``state`` is updated in place; returns o [K,B,H,dv]."""
+    K = drafts["q"].shape[0]
+    acc = np.asarray(accepted)
+    work = state.copy()
+    keep = state.copy()
+    os_ = []
+    for k in range(K):
+        os_.append(kda_step(drafts["q"][k], drafts["k"][k], drafts["v"][k], drafts["beta"][k],
+                            drafts["alpha"][k], work))
+        sel = acc == k + 1
+        keep[sel] = work[sel]
+    state[...] = keep
+    return np.stack(os_)
+
+
+def kda_spec_kappa(drafts: dict, M: np.ndarray, accepted) -> np.ndarray:
+    """Conditioning (kda_kappa_step) of the K draft outputs of a speculative round, ``M`` kept per
+    sequence after ``accepted[b]`` drafts. Returns kappa [K,B,H,dv]."""
+    K = drafts["q"].shape[0]
+    acc = np.asarray(accepted)
+    work = M.copy()
+    keep = M.copy()
+    ks = []
+    for k in range(K):
+        ks.append(kda_kappa_step(drafts["q"][k], drafts["k"][k], drafts["v"][k],
+                                 drafts["beta"][k], drafts["alpha"][k], work))
+        sel = acc == k + 1
+        keep[sel] = work[sel]
+    M[...] = keep
+    return np.stack(ks)
 
 
 def token(inputs: dict, t: int) -> dict:
@@ -641,6 +714,143 @@ class GDNReplay:
                 for h in range(self.nh):
                     ks, vs, be, al = self._entries(b, h, n)
                     out[b, h] = gdn_wy_fold(self.S0[b, h], ks, vs, be, al)
+        return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Kimi Delta Attention checkpoint + ring replay model (fp64)
+# ----------------------------------------------------------------------------------------------
+
+def kda_replay_output(S0, ks, vs, betas, alphas, q):
+    """Output of the newest of m buffered entries from checkpoint S0 (d_v x d_k), entry j with key
+    k_j, value v_j, beta_j and per-channel gate a_j (oldest first).
+
+    The state after the entries is S0 M_1 ... M_m + sum_j beta_j v_j k_j^T M_{j+1} ... M_m with
+    M_i = diag(a_i) (I - beta_i k_i k_i^T). Applying it to q right to left: keep r (initially q);
+    for j = m..1 take c_j = k_j . r, add beta_j c_j v_j to the output and replace r by
+    a_j o (r - beta_j c_j k_j); finally add S0 r. The gates act on r channel by channel, so no
+    decay factor multiplies the checkpoint term or the value sum.
+    """
+    S0 = np.asarray(S0, dtype=np.float64)
+    r = np.array(q, dtype=np.float64)
+    acc = np.zeros(S0.shape[0])
+    for j in range(len(betas) - 1, -1, -1):
+        kj = np.asarray(ks[j], dtype=np.float64)
+        c = float(np.dot(kj, r))
+        acc += float(betas[j]) * c * np.asarray(vs[j], dtype=np.float64)
+        r = np.asarray(alphas[j], dtype=np.float64) * (r - float(betas[j]) * c * kj)
+    return S0 @ r + acc
+
+
+def kda_fold(S0, ks, vs, betas, alphas):
+    """Fold m entries into S0: the entries' updates applied in order (the consolidation)."""
+    S = np.array(S0, dtype=np.float64)
+    for j in range(len(betas)):
+        kj = np.asarray(ks[j], dtype=np.float64)
+        S = S * np.asarray(alphas[j], dtype=np.float64)[None, :]
+        S = S + float(betas[j]) * np.outer(np.asarray(vs[j], dtype=np.float64) - S @ kj, kj)
+    return S
+
+
+class KDAReplay:
+    """Kimi Delta Attention checkpoint + ring of the last W tokens' (k, v, beta, gate vector)."""
+
+    def __init__(self, state0, window: int, max_draft: int = 0):
+        nb, nh, dv, dk = state0.shape
+        self.nb, self.nh, self.dv, self.dk, self.W = nb, nh, dv, dk, int(window)
+        self.bk = Bookkeeping(nb, window, max_draft)
+        self.S0 = np.array(state0, dtype=np.float64, copy=True)
+        self.rk = np.zeros((nb, nh, window, dk))
+        self.rv = np.zeros((nb, nh, window, dv))
+        self.rbeta = np.zeros((nb, nh, window), dtype=np.float32)
+        self.ralpha = np.zeros((nb, nh, window, dk), dtype=np.float32)
+
+    def _entries(self, b, h, n, extra=()):
+        W, hd = self.W, int(self.bk.head[b])
+        sl = [(hd + j) % W for j in range(n)]
+        ks = [self.rk[b, h, s] for s in sl]
+        vs = [self.rv[b, h, s] for s in sl]
+        be = [self.rbeta[b, h, s] for s in sl]
+        al = [self.ralpha[b, h, s] for s in sl]
+        for e in extra:
+            ks.append(e["k"][b, h].astype(np.float64))
+            vs.append(e["v"][b, h].astype(np.float64))
+            be.append(e["beta"][b, h])
+            al.append(e["alpha"][b, h])
+        return ks, vs, be, al
+
+    def _append(self, b, pos, tok):
+        s = (int(self.bk.head[b]) + pos) % self.W
+        self.rk[b, :, s] = tok["k"][b]
+        self.rv[b, :, s] = tok["v"][b]
+        self.rbeta[b, :, s] = tok["beta"][b]
+        self.ralpha[b, :, s] = tok["alpha"][b]
+
+    def decode(self, tok) -> np.ndarray:
+        if self.bk.pending:
+            raise StateError("decode with pending drafts")
+        o = np.empty((self.nb, self.nh, self.dv))
+        for b in range(self.nb):
+            n = int(self.bk.len[b])
+            for h in range(self.nh):
+                ks, vs, be, al = self._entries(b, h, n, [tok])
+                q = tok["q"][b, h].astype(np.float64)
+                if n + 1 >= self.W:
+                    self.S0[b, h] = kda_fold(self.S0[b, h], ks, vs, be, al)
+                    o[b, h] = self.S0[b, h] @ q
+                else:
+                    o[b, h] = kda_replay_output(self.S0[b, h], ks, vs, be, al, q)
+            if n + 1 < self.W:
+                self._append(b, n, tok)
+        self.bk.decode()
+        return o
+
+    def consolidate(self, min_len: int):
+        if self.bk.pending:
+            raise StateError("consolidate with pending drafts")
+        for b in range(self.nb):
+            n = int(self.bk.len[b])
+            if n >= max(int(min_len), 1):
+                for h in range(self.nh):
+                    self.S0[b, h] = kda_fold(self.S0[b, h], *self._entries(b, h, n))
+        self.bk.consolidate(min_len)
+
+    def verify(self, drafts: dict) -> np.ndarray:
+        K = drafts["q"].shape[0]
+        if self.bk.pending:
+            raise StateError("verify with pending drafts")
+        toks = [token(drafts, k) for k in range(K)]
+        for b in range(self.nb):
+            n = int(self.bk.len[b])
+            if n + K > self.W:
+                for h in range(self.nh):
+                    self.S0[b, h] = kda_fold(self.S0[b, h], *self._entries(b, h, n))
+        self.bk.verify(K)
+        o = np.empty((K, self.nb, self.nh, self.dv))
+        for b in range(self.nb):
+            n = int(self.bk.len[b])
+            for k in range(K):
+                for h in range(self.nh):
+                    ks, vs, be, al = self._entries(b, h, n, toks[:k + 1])
+                    o[k, b, h] = kda_replay_output(self.S0[b, h], ks, vs, be, al,
+                                                   toks[k]["q"][b, h])
+            for k in range(K):
+                self._append(b, n + k, toks[k])
+        return o
+
+    def commit(self, accepted):
+        self.bk.commit(accepted)
+
+    def rollback(self, new_len):
+        self.bk.rollback(new_len)
+
+    def materialize(self) -> np.ndarray:
+        out = self.S0.copy()
+        for b in range(self.nb):
+            n = int(self.bk.len[b])
+            if n:
+                for h in range(self.nh):
+                    out[b, h] = kda_fold(self.S0[b, h], *self._entries(b, h, n))
         return out
 
 

@@ -194,3 +194,84 @@ void orc_gdn_kappa_step(int nb, int nh, int dk, int dv,
         }
     }
 }
+
+/*
+ * One conventional Kimi Delta Attention decode token for every (b, h) pair. The pages name Kimi
+ * Delta Attention as the third SSM layer type of the hybrids ReplaySSM targets (news.hamidun.com
+ * item "NVIDIA présente ReplaySSM : accélérer le décodage des modèles hybrides Mamba et GDN",
+ * section "Pourquoi les hybrides sont devenus la norme") but give no formula. Read here as the
+ * delta rule of Gated DeltaNet with the scalar forget gate replaced by one gate per key channel
+ * (a vector a in (0, 1]^dk applied before the rank-1 correction); with S d_v x d_k as for Gated
+ * DeltaNet (row i is an output channel):
+ *     S   <- S diag(a) (I - beta k k^T) + beta v k^T
+ *          = S' - beta (S' k) k^T + beta v k^T,       S' = S diag(a)  (column j scaled by a_j)
+ *     o    = S q                                                     (post-update state)
+ * With a_j = alpha for every j this is the Gated DeltaNet step above.
+ * Layouts: q, k, a [nb,nh,dk], v [nb,nh,dv], beta [nb,nh], state [nb,nh,dv,dk] fp64 in place,
+ * o [nb,nh,dv] fp64.
+ */
+void orc_kda_step(int nb, int nh, int dk, int dv,
+                  const float *q, const float *k, const float *v,
+                  const float *beta, const float *a,
+                  double *state, double *o)
+{
+    const long pairs = (long)nb * nh;
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < pairs; ++bh) {
+        const double be = (double)beta[bh];
+        const float *qv = q + bh * dk;
+        const float *kv = k + bh * dk;
+        const float *av = a + bh * dk;
+        const float *vv = v + bh * dv;
+        double *S = state + bh * (long)dv * dk;
+        for (int i = 0; i < dv; ++i) {
+            double *row = S + (long)i * dk;
+            for (int j = 0; j < dk; ++j) row[j] = row[j] * (double)av[j];
+            double sk = 0.0;
+            for (int j = 0; j < dk; ++j) sk += row[j] * (double)kv[j];
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) {
+                const double s = row[j] - be * sk * (double)kv[j] + be * (double)vv[i] * (double)kv[j];
+                row[j] = s;
+                acc += s * (double)qv[j];
+            }
+            o[bh * dv + i] = acc;
+        }
+    }
+}
+
+/*
+ * Conditioning of one Kimi Delta Attention token (as orc_gdn_kappa_step): M bounds the absolute
+ * values of the terms the update sums, with s_i = sum_l a_l M[i][l] |k_l|,
+ *     M[i][j] <- a_j M[i][j] + beta s_i |k_j| + beta |v_i| |k_j|,
+ * starting from |S_0|, and kappa[i] = sum_j M[i][j] |q_j|. Layouts as orc_kda_step.
+ */
+void orc_kda_kappa_step(int nb, int nh, int dk, int dv,
+                        const float *q, const float *k, const float *v,
+                        const float *beta, const float *a,
+                        double *M, double *kappa)
+{
+    const long pairs = (long)nb * nh;
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < pairs; ++bh) {
+        const double be = (double)beta[bh];
+        const float *qv = q + bh * dk;
+        const float *kv = k + bh * dk;
+        const float *av = a + bh * dk;
+        const float *vv = v + bh * dv;
+        double *Mt = M + bh * (long)dv * dk;
+        for (int i = 0; i < dv; ++i) {
+            double *row = Mt + (long)i * dk;
+            double s = 0.0;
+            for (int j = 0; j < dk; ++j) s += (double)av[j] * row[j] * fabs((double)kv[j]);
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j) {
+                const double kj = fabs((double)kv[j]);
+                const double m = (double)av[j] * row[j] + be * s * kj + be * fabs((double)vv[i]) * kj;
+                row[j] = m;
+                acc += m * fabs((double)qv[j]);
+            }
+            kappa[bh * dv + i] = acc;
+        }
+    }
+}

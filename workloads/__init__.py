@@ -24,6 +24,12 @@ Gated DeltaNet (per decode token)
     beta = sigmoid(N(0, 1))             [B, H]
     alpha = exp(-softplus(N(0, 1)))     [B, H]
     initial state ~ N(0, 0.1)           [B, H, d_v, d_k]
+Kimi Delta Attention (per decode token; Gated DeltaNet with one forget gate per key channel)
+    q, k ~ N(0, 1), then L2-normalised  [B, H, d_k]
+    v ~ N(0, 1)                         [B, H, d_v]
+    beta = sigmoid(N(0, 1))             [B, H]
+    alpha = exp(-softplus(N(0, 1)))     [B, H, d_k]   (each key channel drawn on its own)
+    initial state ~ N(0, 0.1)           [B, H, d_v, d_k]
 Speculative decoding
     accepted = min(Geometric(0.35) failures before the first success, K)   [rounds, B] int32
 
@@ -42,6 +48,7 @@ _TID = {
     "m2_x": 10, "m2_B": 11, "m2_C": 12, "m2_dt": 13,
     "gdn_state0": 20, "gdn_q": 21, "gdn_k": 22, "gdn_v": 23, "gdn_beta": 24, "gdn_alpha": 25,
     "accepted": 30,
+    "kda_state0": 40, "kda_q": 41, "kda_k": 42, "kda_v": 43, "kda_beta": 44, "kda_alpha": 45,
 }
 
 
@@ -139,6 +146,25 @@ def gdn_token_inputs(shape: GDNShape, seed: int, slot: int, ntok: int = 1) -> di
     return {"q": q, "k": k, "v": v, "beta": beta, "alpha": alpha}
 
 
+def kda_state0(shape: GDNShape, seed: int = 0) -> np.ndarray:
+    s = shape
+    return _normal(seed, "kda_state0", 0, (s.batch, s.nheads, s.d_v, s.d_k),
+                   scale=0.1).astype(np.float32)
+
+
+def kda_token_inputs(shape: GDNShape, seed: int, slot: int, ntok: int = 1) -> dict:
+    """Inputs of `ntok` Kimi Delta Attention tokens: q, k [T,B,H,d_k], v [T,B,H,d_v],
+    beta [T,B,H], alpha [T,B,H,d_k] (one gate per key channel)."""
+    s = shape
+    T, Bt, H = ntok, s.batch, s.nheads
+    q = _l2n(_normal(seed, "kda_q", slot, (T, Bt, H, s.d_k))).astype(np.float32)
+    k = _l2n(_normal(seed, "kda_k", slot, (T, Bt, H, s.d_k))).astype(np.float32)
+    v = _normal(seed, "kda_v", slot, (T, Bt, H, s.d_v)).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-_normal(seed, "kda_beta", slot, (T, Bt, H))))).astype(np.float32)
+    alpha = np.exp(-_softplus(_normal(seed, "kda_alpha", slot, (T, Bt, H, s.d_k)))).astype(np.float32)
+    return {"q": q, "k": k, "v": v, "beta": beta, "alpha": alpha}
+
+
 def spec_accepted(batch: int, rounds: int, max_accept: int, p: float = 0.35,
                   seed: int = 0) -> np.ndarray:
     """Accepted draft counts [rounds, batch]: failures before the first success, capped at K."""
@@ -152,3 +178,4 @@ M2_SERVE = M2Shape(batch=256, nheads=128, ngroups=128, head_dim=64, d_state=128,
 M2_SPEC = M2Shape(batch=512, nheads=128, ngroups=128, head_dim=64, d_state=128, window=16,
                   max_draft=6)
 GDN_SERVE = GDNShape(batch=256, nheads=32, d_k=128, d_v=128, window=16)
+KDA_SERVE = GDNShape(batch=256, nheads=32, d_k=128, d_v=128, window=16)
