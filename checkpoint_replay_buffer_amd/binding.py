@@ -25,6 +25,7 @@ RSSM_DEV_INDEX_RANGE = 8
 RSSM_DEV_IMPORT_HEADER = 16
 RSSM_MAMBA2 = 1
 RSSM_GDN = 2
+RSSM_KDA = 3
 RSSM_F_BF16_READ = 1
 RSSM_F_STORE_C = 2
 
@@ -255,14 +256,15 @@ def _f32(t, name):
 class Context:
     """A ReplaySSM context and its device workspace (a torch uint8 tensor it owns).
 
-    kind 'mamba2' or 'gdn'; dim_v / dim_k are (head_dim, d_state) for Mamba-2 and (d_v, d_k) for
-    Gated DeltaNet.
+    kind 'mamba2', 'gdn' or 'kda'; dim_v / dim_k are (head_dim, d_state) for Mamba-2 and
+    (d_v, d_k) for Gated DeltaNet and Kimi Delta Attention (whose alpha inputs carry one gate per
+    key channel, [..., d_k]).
     """
 
     def __init__(self, kind: str, batch: int, nheads: int, dim_v: int, dim_k: int, window: int,
                  ngroups: int | None = None, max_draft: int = 0, bf16_read: bool = False,
                  store_c: bool = True, device="cuda"):
-        k = {"mamba2": RSSM_MAMBA2, "gdn": RSSM_GDN}[kind]
+        k = {"mamba2": RSSM_MAMBA2, "gdn": RSSM_GDN, "kda": RSSM_KDA}[kind]
         flags = (RSSM_F_BF16_READ if bf16_read else 0) | \
                 (RSSM_F_STORE_C if (store_c and k == RSSM_MAMBA2) else 0)
         self.kind = kind

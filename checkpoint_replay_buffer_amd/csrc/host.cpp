@@ -50,7 +50,7 @@ struct Layout {
 rssm_status check_config(const rssm_config *c)
 {
     if (!c) return RSSM_E_ARG;
-    if (c->kind != RSSM_MAMBA2 && c->kind != RSSM_GDN) return RSSM_E_ARG;
+    if (c->kind != RSSM_MAMBA2 && c->kind != RSSM_GDN && c->kind != RSSM_KDA) return RSSM_E_ARG;
     if (c->batch < 1 || c->nheads < 1 || c->ngroups < 1 || c->dim_v < 1 || c->dim_k < 1)
         return RSSM_E_SHAPE;
     if (c->window < 1 || c->window > kMaxWindow) return RSSM_E_SHAPE;
@@ -63,6 +63,11 @@ rssm_status check_config(const rssm_config *c)
         if (c->flags != 0) return RSSM_E_UNSUPPORTED;
         if (!gdn_supported(c->dim_v, c->dim_k)) return RSSM_E_UNSUPPORTED;
         if (gdn_lds_bytes(c->dim_v, c->dim_k, c->window) > 65536) return RSSM_E_UNSUPPORTED;
+    } else if (c->kind == RSSM_KDA) {
+        if (c->ngroups != c->nheads) return RSSM_E_SHAPE;
+        if (c->flags != 0) return RSSM_E_UNSUPPORTED;
+        if (!kda_supported(c->dim_v, c->dim_k)) return RSSM_E_UNSUPPORTED;
+        if (kda_lds_bytes(c->dim_v, c->dim_k, c->window, c->max_draft) > 65536) return RSSM_E_UNSUPPORTED;
     } else {
         if (!m2_supported(c->dim_v, c->dim_k)) return RSSM_E_UNSUPPORTED;
         // ring entries staged in LDS by the fold and verify kernels: within 64 KiB per workgroup
@@ -87,10 +92,11 @@ Layout layout(const rssm_config *c)
         L.r2 = o; o += (c->flags & RSSM_F_STORE_C) ? up(B * G * W * N * sizeof(float)) : 0;  // C
         L.r3 = o; o += up(B * H * W * sizeof(float));                                   // dt
     } else {
+        const size_t A = c->kind == RSSM_KDA ? N : 1;   // gate: one per key channel (KDA) or scalar
         L.r0 = o; o += up(B * H * W * N * sizeof(float));                               // k
         L.r1 = o; o += up(B * H * W * P * sizeof(float));                               // v
         L.r2 = o; o += up(B * H * W * sizeof(float));                                   // beta
-        L.r3 = o; o += up(B * H * W * sizeof(float));                                   // alpha
+        L.r3 = o; o += up(B * H * W * A * sizeof(float));                               // alpha
     }
     L.total = o;
     return L;
@@ -181,7 +187,7 @@ SeqCopyArgs seq_args(const rssm_ctx *c, int mode, int n, const int32_t *src, con
         add(c->gdn.k, H * W * N * sizeof(float));
         add(c->gdn.v, H * W * P * sizeof(float));
         add(c->gdn.beta, H * W * sizeof(float));
-        add(c->gdn.alpha, H * W * sizeof(float));
+        add(c->gdn.alpha, H * W * (g.kind == RSSM_KDA ? N : 1) * sizeof(float));
     }
     uint64_t off = 0, units = 0;
     for (int k = 0; k < a.nseg; ++k) {
@@ -271,7 +277,7 @@ rssm_status rssm_init_checkpoint(rssm_ctx *ctx, const float *state, const int32_
     const rssm_config &c = ctx->cfg;
     const hipError_t e = init_checkpoint(ctx->S0, ctx->S0b, state, seq_mask, flip(ctx), ctx->err,
                                          c.batch, c.nheads, (long)c.dim_v * c.dim_k,
-                                         c.kind == RSSM_GDN ? c.dim_v : 0, strm(stream));
+                                         c.kind == RSSM_MAMBA2 ? 0 : c.dim_v, strm(stream));
     const rssm_status s = launched(ctx, e, true);
     if (s == RSSM_OK) {
         ctx->initialized = true;
@@ -302,7 +308,8 @@ rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, voi
         GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
                       in->alpha, y, ctx->uhead, ctx->ulen};
         const int mode = (ctx->uni && ctx->ulen + 1 < c.window) ? 0 : (mayfold ? 2 : 1);
-        s = launched(ctx, gdn_decode(a, mode, strm(stream)), true);
+        s = launched(ctx, c.kind == RSSM_KDA ? kda_decode(a, mode, strm(stream))
+                                             : gdn_decode(a, mode, strm(stream)), true);
     }
     if (s == RSSM_OK) {
         if (ctx->ulen + 1 >= c.window) {
@@ -335,7 +342,7 @@ rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream)
         s = launched(ctx, m2_fold(a, ctx->S0b != nullptr, strm(stream)), true);
     } else {
         GdnFoldArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, min_len, nullptr};
-        s = launched(ctx, gdn_fold(a, strm(stream)), true);
+        s = launched(ctx, c.kind == RSSM_KDA ? kda_fold(a, strm(stream)) : gdn_fold(a, strm(stream)), true);
     }
     if (s == RSSM_OK) {
         const int m = min_len > 1 ? min_len : 1;
@@ -355,6 +362,7 @@ rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *s
     const rssm_config &c = ctx->cfg;
     if ((s = check_inputs(c, in)) != RSSM_OK) return s;
     if (!aligned16(y)) return RSSM_E_ARG;
+    if (c.kind == RSSM_KDA) return RSSM_E_UNSUPPORTED;
     if (ctx->pending) return RSSM_E_STATE;
     if (ctx->hi > 0 && (s = rssm_consolidate(ctx, 1, stream)) != RSSM_OK) return s;
     if (c.kind == RSSM_MAMBA2) {
@@ -407,7 +415,8 @@ rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *st
     } else {
         GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
                       in->alpha, y, 0, 0, in->ntok};
-        s = launched(ctx, gdn_verify(a, strm(stream)), true);
+        s = launched(ctx, c.kind == RSSM_KDA ? kda_verify(a, strm(stream)) : gdn_verify(a, strm(stream)),
+                     true);
     }
     if (s == RSSM_OK) {
         ctx->pending = true;
@@ -465,7 +474,8 @@ rssm_status rssm_step_baseline(const rssm_config *cfg, float *state, const rssm_
     }
     GdnRmwArgs a{gdndims(*cfg), state, snapshots, in->q, in->k, in->v, in->beta, in->alpha, y,
                  in->ntok};
-    return gdn_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+    const hipError_t e = cfg->kind == RSSM_KDA ? kda_rmw(a, strm(stream)) : gdn_rmw(a, strm(stream));
+    return e == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
 }
 
 rssm_status rssm_step_baseline_spec(const rssm_config *cfg, float *pool, const int32_t *slot_of,
@@ -476,10 +486,11 @@ rssm_status rssm_step_baseline_spec(const rssm_config *cfg, float *pool, const i
     if (s != RSSM_OK) return s;
     if ((s = check_inputs(*cfg, in)) != RSSM_OK) return s;
     if (!aligned16(pool) || !aligned16(y) || !slot_of) return RSSM_E_ARG;
-    if (cfg->kind == RSSM_GDN) {
+    if (cfg->kind != RSSM_MAMBA2) {
         GdnRmwArgs a{gdndims(*cfg), pool, nullptr, in->q, in->k, in->v, in->beta, in->alpha, y,
                      in->ntok, slot_of};
-        return gdn_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+        const hipError_t e = cfg->kind == RSSM_KDA ? kda_rmw(a, strm(stream)) : gdn_rmw(a, strm(stream));
+        return e == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
     }
     if (!A || !D) return RSSM_E_ARG;
     M2RmwArgs a{m2dims(*cfg), pool, nullptr, A, D, in->x, in->B, in->C, in->dt, y, in->ntok, slot_of};
@@ -508,7 +519,7 @@ rssm_status rssm_materialize(rssm_ctx *ctx, float *state_out, void *stream)
         return launched(ctx, m2_fold(a, false, strm(stream)), false);
     }
     GdnFoldArgs a{gdndims(c), bk, ctx->S0, ctx->gdn, 1, state_out};
-    return launched(ctx, gdn_fold(a, strm(stream)), false);
+    return launched(ctx, c.kind == RSSM_KDA ? kda_fold(a, strm(stream)) : gdn_fold(a, strm(stream)), false);
 }
 
 rssm_status rssm_seq_state_bytes(const rssm_config *cfg, size_t *bytes)

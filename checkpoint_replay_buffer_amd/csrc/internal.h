@@ -98,11 +98,14 @@ struct M2RmwArgs {
     const int32_t *slot_of;   // [B] committed slot per sequence, or nullptr
 };
 
+// Rings of the delta-rule layers (Gated DeltaNet; Kimi Delta Attention with a gate per key
+// channel, alpha [B,H,W,dk]). The step arguments of both use the structs below, with alpha
+// [ntok,B,H] for Gated DeltaNet and [ntok,B,H,dk] for Kimi Delta Attention.
 struct GdnRing {
     float *k;      // [B,H,W,dk]
     float *v;      // [B,H,W,dv]
     float *beta;   // [B,H,W]
-    float *alpha;  // [B,H,W]
+    float *alpha;  // [B,H,W] (Gated DeltaNet) or [B,H,W,dk] (Kimi Delta Attention)
 };
 
 struct GdnDims {
@@ -168,6 +171,13 @@ hipError_t gdn_fold(const GdnFoldArgs &a, hipStream_t s);
 hipError_t gdn_rmw(const GdnRmwArgs &a, hipStream_t s);
 hipError_t gdn_verify(const GdnStepArgs &a, hipStream_t s);
 hipError_t gdn_prefill(const GdnPrefillArgs &a, hipStream_t s);
+
+bool kda_supported(int DV, int DK);
+size_t kda_lds_bytes(int DV, int DK, int W, int K);   // dynamic LDS of the largest KDA kernel
+hipError_t kda_decode(const GdnStepArgs &a, int mode, hipStream_t s);   // mode as m2_decode
+hipError_t kda_fold(const GdnFoldArgs &a, hipStream_t s);
+hipError_t kda_rmw(const GdnRmwArgs &a, hipStream_t s);
+hipError_t kda_verify(const GdnStepArgs &a, hipStream_t s);
 
 // ckpt_dv > 0: the tiles are Gated DeltaNet checkpoints with ckpt_dv rows, stored in the layout
 // of gdn_layout.h; 0: row-major (Mamba-2).

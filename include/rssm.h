@@ -18,12 +18,15 @@
  *  - an optional lower-precision copy of the checkpoint may serve the reads while the recurrence
  *    stays in full precision (ia.goatify.app, paragraph "La precisión separa lectura y
  *    recurrencia"); here that copy is bf16;
- *  - the layer types are Mamba-2 and Gated DeltaNet (news.hamidun.com item "NVIDIA présente
- *    ReplaySSM...", section "Pourquoi les hybrides sont devenus la norme").
+ *  - the layer types are Mamba-2, Gated DeltaNet and Kimi Delta Attention (news.hamidun.com item
+ *    "NVIDIA présente ReplaySSM...", section "Pourquoi les hybrides sont devenus la norme"; the
+ *    pages give no formula for Kimi Delta Attention, read here as Gated DeltaNet with one forget
+ *    gate per key channel).
  *
  * Recurrences (per sequence b and head h; the plain reading, since the pages print no formulas):
  *   Mamba-2, state S [P x N]:   S <- exp(dt A_h) S + dt x B^T,   y = S C + D_h x
  *   Gated DeltaNet, S [dv x dk]: S <- alpha S (I - beta k k^T) + beta v k^T,   o = S q
+ *   Kimi Delta Attention, S [dv x dk]: S <- S diag(a) (I - beta k k^T) + beta v k^T,   o = S q
  * Outputs use the post-update state. ReplaySSM produces the same outputs up to rounding
  * (fagnersouza.tech post, section "Cuidados e limites").
  *
@@ -82,7 +85,7 @@ enum {
                                       pair is skipped: the sequence keeps its state */
 };
 
-enum { RSSM_MAMBA2 = 1, RSSM_GDN = 2 };
+enum { RSSM_MAMBA2 = 1, RSSM_GDN = 2, RSSM_KDA = 3 };
 
 enum {
     RSSM_F_BF16_READ = 1u,   /* keep a bf16 copy of S0 and read it for replayed outputs */
@@ -90,12 +93,12 @@ enum {
 };
 
 typedef struct {
-    int32_t kind;        /* RSSM_MAMBA2 or RSSM_GDN */
+    int32_t kind;        /* RSSM_MAMBA2, RSSM_GDN or RSSM_KDA */
     int32_t batch;       /* B */
     int32_t nheads;      /* H */
-    int32_t ngroups;     /* G (Mamba-2 B/C groups; must be H for GDN) */
-    int32_t dim_v;       /* P (Mamba-2 head_dim) or d_v (GDN) */
-    int32_t dim_k;       /* N (Mamba-2 d_state) or d_k (GDN) */
+    int32_t ngroups;     /* G (Mamba-2 B/C groups; must be H for GDN and KDA) */
+    int32_t dim_v;       /* P (Mamba-2 head_dim) or d_v (GDN, KDA) */
+    int32_t dim_k;       /* N (Mamba-2 d_state) or d_k (GDN, KDA) */
     int32_t window;      /* W, ring length, 1..32 */
     int32_t max_draft;   /* largest K accepted by rssm_verify, 0..W (0 = no speculative use) */
     uint32_t flags;      /* RSSM_F_* */
@@ -104,6 +107,7 @@ typedef struct {
 /* Inputs of ntok consecutive tokens, token-major (leading axis ntok).
  * Mamba-2: x [ntok,B,H,P], B and C [ntok,B,G,N], dt [ntok,B,H] (dt > 0, already discretised).
  * GDN:     q and k [ntok,B,H,dk], v [ntok,B,H,dv], beta and alpha [ntok,B,H].
+ * KDA:     as GDN, but alpha [ntok,B,H,dk] (one forget gate per key channel).
  * Fields of the other kind are ignored and may be NULL. */
 typedef struct {
     int32_t ntok;
@@ -125,21 +129,28 @@ void rssm_destroy(rssm_ctx *ctx);
  * pointers kept by reference: they must stay valid while the context is used. */
 rssm_status rssm_set_params(rssm_ctx *ctx, const float *A, const float *D);
 
-/* Load checkpoints: S0[b] <- state[b] ([B,H,dim_v,dim_k]) for every sequence b with
+/* The state of a sequence is a checkpoint plus a short buffer of its recent inputs (ia.goatify.app
+ * article, paragraph "ReplaySSM cambia qué se almacena").
+ * Load checkpoints: S0[b] <- state[b] ([B,H,dim_v,dim_k]) for every sequence b with
  * seq_mask[b] != 0 (seq_mask [B] int32, or NULL for all), refresh the bf16 copy, and reset those
  * sequences' bookkeeping to head = len = ndraft = 0. With seq_mask NULL the error word is cleared
  * too. Clears a pending verify. */
 rssm_status rssm_init_checkpoint(rssm_ctx *ctx, const float *state, const int32_t *seq_mask,
                                  void *stream);
 
-/* One decode token (inputs->ntok must be 1) for every sequence; writes y [B,H,dim_v].
+/* A normal step appends its inputs to the buffer and computes the output from the checkpoint;
+ * only a full buffer is consolidated (ia.goatify.app article, paragraph "El checkpoint reduce
+ * escrituras de estado").
+ * One decode token (inputs->ntok must be 1) for every sequence; writes y [B,H,dim_v].
  * The token becomes logical entry len and its output is computed from the read-only checkpoint
  * and the buffered entries ("replay"). When the token fills the buffer (len + 1 >= W) the same
  * launch folds all buffered entries and the token into S0 and the output is read from the new
  * checkpoint; then len = 0. Requires no pending verify (RSSM_E_STATE). */
 rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream);
 
-/* Fold the buffered entries of every sequence with len >= max(min_len, 1) into its checkpoint.
+/* Consolidation, the update of the persistent state from the buffered entries (ia.goatify.app
+ * article, paragraph "El checkpoint reduce escrituras de estado").
+ * Fold the buffered entries of every sequence with len >= max(min_len, 1) into its checkpoint.
  * Requires no pending verify. */
 rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream);
 
@@ -152,29 +163,41 @@ rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream);
  * decode steps would give. Buffered entries are folded first (one consolidation launch when any
  * sequence may hold some); afterwards len = ndraft = 0 for every sequence and the bf16 read copy,
  * if any, is refreshed. The checkpoint is read and written once for the whole prompt. Requires no
- * pending verify (RSSM_E_STATE). */
+ * pending verify (RSSM_E_STATE). Not compiled for Kimi Delta Attention (RSSM_E_UNSUPPORTED). */
 rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream);
 
-/* Speculative verify of K = in->ntok drafts (1 <= K <= max_draft), both layer types (Mamba-2
- * drafts: x, B, C, dt; Gated DeltaNet drafts: q, k, v, beta, alpha, each with a leading K axis):
+/* Speculative decoding stores the drafts' inputs and evaluates outputs only (ia.goatify.app
+ * article, paragraph "El retroceso usa un puntero del búfer").
+ * Speculative verify of K = in->ntok drafts (1 <= K <= max_draft), every layer type (Mamba-2
+ * drafts: x, B, C, dt; Gated DeltaNet and Kimi Delta Attention drafts: q, k, v, beta, alpha, each
+ * with a leading K axis):
  * sequences whose drafts would not fit (len + K > W) first fold their committed entries; the
  * drafts are then appended as entries len .. len+K-1 (ndraft = K) and y [K,B,H,dim_v] gets every
  * draft's output, draft k seeing the committed entries and drafts 0..k. S0 is streamed once for
- * all K outputs. Gated DeltaNet takes at most 16 drafts per call (RSSM_E_ARG beyond). Requires no
- * pending verify; afterwards exactly one of commit / rollback must follow. */
+ * all K outputs. Gated DeltaNet takes at most 16 drafts per call (RSSM_E_ARG beyond). With B / C
+ * shared by groups of heads (G < H), sequences whose drafts do not fit are folded by a
+ * consolidation launch queued before the verify launch. Requires no pending verify; afterwards
+ * exactly one of commit / rollback must follow. */
 rssm_status rssm_verify(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream);
 
-/* Accept accepted[b] ([B] int32, device) drafts per sequence: len += accepted[b] when
+/* The accepted prefix is confirmed by moving a pointer to the last accepted token, with no state
+ * copy per draft (ia.goatify.app article, paragraph "El retroceso usa un puntero del búfer";
+ * fagnersouza.tech post, section "O que muda para quem desenvolve").
+ * Accept accepted[b] ([B] int32, device) drafts per sequence: len += accepted[b] when
  * 0 <= accepted[b] <= ndraft[b], else RSSM_DEV_COMMIT_RANGE and len unchanged; ndraft = 0.
  * A pointer move only: no state or ring data is copied. Requires a pending verify. */
 rssm_status rssm_verify_commit(rssm_ctx *ctx, const int32_t *accepted, void *stream);
 
-/* Roll back to new_len[b] ([B] int32, device) committed entries: len = new_len[b] when
+/* Rollback by the same pointer (ia.goatify.app article, paragraph "El retroceso usa un puntero
+ * del búfer").
+ * Roll back to new_len[b] ([B] int32, device) committed entries: len = new_len[b] when
  * 0 <= new_len[b] <= len[b], else RSSM_DEV_ROLLBACK_RANGE and len unchanged; pending drafts are
  * discarded (ndraft = 0). The checkpoint is never rolled back. */
 rssm_status rssm_rollback(rssm_ctx *ctx, const int32_t *new_len, void *stream);
 
-/* Conventional read-modify-write decode, the comparator: for each token of `in` in order,
+/* Conventional decoding reads and rewrites the whole state matrix on every token
+ * (fagnersouza.tech post "ReplaySSM: o ganho aparece na carga concorrente...", lede).
+ * Conventional read-modify-write decode, the comparator: for each token of `in` in order,
  * state <- update(state) and y[t] <- output, per the recurrences above. state [B,H,dim_v,dim_k]
  * is updated in place when snapshots is NULL. Otherwise state is only read and the state after
  * token t is written to snapshots [ntok,B,H,dim_v,dim_k] (per-draft snapshots, the conventional
@@ -230,11 +253,15 @@ rssm_status rssm_export(rssm_ctx *ctx, const int32_t *seq, int32_t n, void *buf,
  * imported and sets RSSM_DEV_IMPORT_HEADER. */
 rssm_status rssm_import(rssm_ctx *ctx, const int32_t *seq, int32_t n, const void *buf, void *stream);
 
-/* Write the current state of every sequence (S0 with its committed entries folded in) to
+/* The state a sequence represents is its checkpoint with its buffered entries applied
+ * (ia.goatify.app article, paragraph "ReplaySSM cambia qué se almacena").
+ * Write the current state of every sequence (S0 with its committed entries folded in) to
  * state_out [B,H,dim_v,dim_k] without changing the context. */
 rssm_status rssm_materialize(rssm_ctx *ctx, float *state_out, void *stream);
 
-/* Copy head, len, ndraft ([B] int32 each, HOST, any may be NULL) and the device error word
+/* The buffer pointers of every sequence (ia.goatify.app article, paragraph "El retroceso usa un
+ * puntero del búfer").
+ * Copy head, len, ndraft ([B] int32 each, HOST, any may be NULL) and the device error word
  * (HOST, may be NULL) to the host; synchronises `stream`. When dev_err is given, the error bits
  * it returns are cleared on the device; with dev_err NULL the word is left as it is. */
 rssm_status rssm_read_bookkeeping(rssm_ctx *ctx, int32_t *head, int32_t *len, int32_t *ndraft,

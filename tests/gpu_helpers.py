@@ -34,6 +34,28 @@ def gdn_dev_tokens(sh: wl.GDNShape, ins: dict, ntok: int):
     return {k: dev(v) for k, v in ins.items()}
 
 
+def kda_dev_tokens(sh: wl.GDNShape, ins: dict, ntok: int):
+    """Device copies of token-major Kimi Delta Attention inputs (gate alpha [T,B,H,d_k])."""
+    assert ins["q"].shape == (ntok, sh.batch, sh.nheads, sh.d_k)
+    assert ins["k"].shape == (ntok, sh.batch, sh.nheads, sh.d_k)
+    assert ins["v"].shape == (ntok, sh.batch, sh.nheads, sh.d_v)
+    assert ins["beta"].shape == (ntok, sh.batch, sh.nheads)
+    assert ins["alpha"].shape == (ntok, sh.batch, sh.nheads, sh.d_k)
+    return {k: dev(v) for k, v in ins.items()}
+
+
+def kda_kappa_torch(M, q, k, v, beta, alpha):
+    """Kimi Delta Attention counterpart of gdn_kappa_torch (gate alpha [B,H,dk]):
+    M <- alpha o M + beta s |k|^T + beta |v| |k|^T with s = (alpha o M) |k|; kappa = M |q|."""
+    ka = k.abs()
+    M.mul_(alpha[:, :, None, :])
+    s = (M * ka[:, :, None, :]).sum(-1)
+    be = beta[..., None, None]
+    M.add_(be * s[..., None] * ka[:, :, None, :])
+    M.add_(be * v.abs()[..., None] * ka[:, :, None, :])
+    return (M * q.abs()[:, :, None, :]).sum(-1)
+
+
 def tok0(d: dict) -> dict:
     """Single-token view (drop the leading token axis) of device inputs."""
     return {k: v[0] for k, v in d.items()}

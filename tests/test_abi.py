@@ -61,7 +61,7 @@ def test_workspace_layout(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(kind=3), -1),
+    (dict(kind=4), -1),
     (dict(window=0), -2),
     (dict(window=33), -2),
     (dict(max_draft=17), -2),
@@ -73,6 +73,10 @@ def test_workspace_layout(lib):
     (dict(dim_k=96), -6),
     (dict(kind=rb.RSSM_GDN, dim_v=128, dim_k=128, ngroups=64), -2),
     (dict(kind=rb.RSSM_GDN, dim_v=128, dim_k=128, flags=rb.RSSM_F_BF16_READ), -6),
+    (dict(kind=rb.RSSM_KDA, dim_v=128, dim_k=128, ngroups=64), -2),
+    (dict(kind=rb.RSSM_KDA, dim_v=128, dim_k=128, flags=rb.RSSM_F_BF16_READ), -6),
+    (dict(kind=rb.RSSM_KDA, dim_v=64, dim_k=128), -6),
+    (dict(kind=rb.RSSM_KDA, dim_v=128, dim_k=128, window=32, max_draft=32), -6),   # LDS
 ])
 def test_config_errors(lib, kw, status):
     with pytest.raises(rb.RssmError) as e:
@@ -148,6 +152,7 @@ def test_baseline_argument_checks(lib):
     (rb.RSSM_MAMBA2, 0, (3, 4, 2, 16, 16, 5)),
     (rb.RSSM_MAMBA2, rb.RSSM_F_BF16_READ | rb.RSSM_F_STORE_C, (2, 128, 128, 64, 128, 16)),
     (rb.RSSM_GDN, 0, (2, 3, 3, 64, 64, 7)),
+    (rb.RSSM_KDA, 0, (2, 3, 3, 64, 64, 7)),
 ])
 def test_seq_state_bytes(lib, kind, flags, dims):
     """A packed sequence slot: a 16-byte header (head, len, ndraft) and each state array's share of
@@ -164,5 +169,25 @@ def test_seq_state_bytes(lib, kind, flags, dims):
             segs.append(G * W * K * 4)
         segs.append(H * W * 4)
     else:
-        segs += [H * W * K * 4, H * W * V * 4, H * W * 4, H * W * 4]
+        gate = K if kind == rb.RSSM_KDA else 1          # Kimi Delta Attention: a gate per key channel
+        segs += [H * W * K * 4, H * W * V * 4, H * W * 4, H * W * gate * 4]
     assert rb.rssm_seq_state_bytes(cfg) == 16 + sum(pad(n) for n in segs)
+
+
+def test_kda_workspace_and_prefill(lib):
+    """Kimi Delta Attention rings: k, v, beta and a gate row of d_k per entry; prefill is not
+    compiled for it."""
+    B, H, V, K, W = 4, 3, 64, 64, 8
+    cfg = rb.make_config(rb.RSSM_KDA, B, H, H, V, K, W, 4, 0)
+    want = _up(2 * 3 * B * 4) + _up(4) + _up(B * H * V * K * 4) + _up(B * H * W * K * 4) \
+        + _up(B * H * W * V * 4) + _up(B * H * W * 4) + _up(B * H * W * K * 4)
+    n = rb.rssm_workspace_bytes(cfg)
+    assert n == want
+    h = rb.rssm_create(cfg, FAKE_WS, n)
+    try:
+        tok = rb.make_inputs(3, q=FAKE_WS, k=FAKE_WS, v=FAKE_WS, beta=FAKE_WS, alpha=FAKE_WS)
+        with pytest.raises(rb.RssmError) as e:
+            rb.rssm_prefill(h, tok, FAKE_WS, stream=0)
+        assert e.value.status == -4             # nothing loaded yet
+    finally:
+        rb.rssm_destroy(h)

@@ -239,3 +239,19 @@ def test_torch_kappa_helpers_match_the_oracle(oracle_lib):
         k64 = gdn_kappa_step(*a, M)
         k32 = gdn_kappa_torch(Mt, *[torch.from_numpy(v) for v in a]).numpy()
         assert np.max(np.abs(k32 - k64) / k64) < 1e-5, t
+
+
+def test_torch_kda_kappa_helper_matches_the_oracle(oracle_lib):
+    import torch
+    from oracle import kda_kappa_step
+    from tests.gpu_helpers import kda_kappa_torch
+    gs = wl.GDNShape(batch=2, nheads=3, d_k=16, d_v=8, window=4)
+    g0 = wl.kda_state0(gs, 6)
+    gin = wl.kda_token_inputs(gs, 6, 0, ntok=12)
+    M = np.abs(g0).astype(np.float64)
+    Mt = torch.from_numpy(np.abs(g0))
+    for t in range(12):
+        a = [gin[k][t] for k in ("q", "k", "v", "beta", "alpha")]
+        k64 = kda_kappa_step(*a, M)
+        k32 = kda_kappa_torch(Mt, *[torch.from_numpy(v) for v in a]).numpy()
+        assert np.max(np.abs(k32 - k64) / k64) < 1e-5, t
