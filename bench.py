@@ -122,17 +122,24 @@ def _src_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel_key: str):
-    """HBM bytes per launch measured with rocprofv3 counters for this kernel, if the counters were
-    taken on the current kernel source (the hash of the files it was built from); else None."""
+def _traffic_fields(kernel_key: str) -> dict:
+    """The measured HBM bytes per launch of a kernel (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+    plain copy's counters) beside the byte model of the same profiled launches and their ratio.
+    The profiled launches follow their own schedule, so `traffic` is compared with
+    `traffic_alg_bytes_per_launch`, not with this run's `alg_bytes_per_launch`. None when the
+    counters were taken on other kernel sources."""
     try:
         t = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
-        return None
+        t = {}
     e = t.get(kernel_key)
     if not e or e.get("src_hash") != _src_hash(e.get("files", ())):
-        return None
-    return e.get("bytes_per_launch")
+        return {"traffic": None}
+    out = {"traffic": e.get("bytes_per_launch"),
+           "traffic_alg_bytes_per_launch": e.get("alg_bytes_per_launch")}
+    if out["traffic"] and out["traffic_alg_bytes_per_launch"]:
+        out["traffic_ratio"] = round(out["traffic"] / out["traffic_alg_bytes_per_launch"], 4)
+    return out
 
 
 def _graph_time(torch, nsteps, step, reps_warm, reps):
@@ -159,6 +166,11 @@ def _graph_time(torch, nsteps, step, reps_warm, reps):
 
 
 def run_m2(args, torch, rb, wl):
+    """Mamba-2 decode at the serving shape. Lock-step (default): every sequence starts from an
+    empty ring, so all of them fold in the same launch, one launch in W. --stagger: W - 1 tokens and
+    a rollback of sequence b to b mod W entries before every timed pass (untimed), so every
+    sequence sits at its own ring position and every timed launch mixes tiles that fold (1 / W of
+    them) with tiles that replay, the state continuous batching and speculative commits leave."""
     bf16 = args.workload == "m2_serve_bf16"
     batch = args.batch or 256
     sh = wl.M2Shape(batch=batch, nheads=128, ngroups=args.groups or 128, head_dim=64, d_state=128,
@@ -169,9 +181,10 @@ def run_m2(args, torch, rb, wl):
     t0 = time.time()
     prm = wl.m2_params(sh, 0)
     s0 = torch.from_numpy(wl.m2_state0(sh, 0)).cuda()
-    pool = []
+    host_pool, pool = [], []
     for s in range(pool_n):
         ins = wl.m2_token_inputs(sh, 0, s)
+        host_pool.append({k: v[0] for k, v in ins.items()})
         pool.append({k: torch.from_numpy(v[0]).cuda() for k, v in ins.items()})
     A = torch.from_numpy(prm["A"]).cuda()
     D = torch.from_numpy(prm["D"]).cuda()
@@ -181,12 +194,22 @@ def run_m2(args, torch, rb, wl):
     ctx.set_params(A, D)
     y = torch.empty(B, H, P, device="cuda")
     K, Wm = args.steps, args.warmup
+    start_len = np.arange(B) % W if args.stagger else np.zeros(B, dtype=np.int64)
+    new_len = torch.from_numpy(start_len.astype(np.int32)).cuda()
 
-    # warm-up, then restart from the checkpoint so the timed steps see lengths 0, 1, ..., W-1, ...
-    ctx.init_checkpoint(s0)
+    def restart():
+        """Back to the checkpoint; with --stagger, then to ring fill b mod W (untimed)."""
+        ctx.init_checkpoint(s0)
+        if args.stagger:
+            for t in range(W - 1):
+                ctx.decode_step(y, **pool[(pool_n - 1 - t) % pool_n])
+            ctx.rollback(new_len)
+
+    # warm-up, then restart so the timed steps see the schedule from its start
+    restart()
     for t in range(Wm):
         ctx.decode_step(y, **pool[t % pool_n])
-    ctx.init_checkpoint(s0)
+    restart()
     torch.cuda.synchronize()
 
     # timed region: K steps bracketed by events only (wall time of the whole job)
@@ -200,13 +223,14 @@ def run_m2(args, torch, rb, wl):
         torch.cuda.synchronize()
         total_ms = ev[0].elapsed_time(ev[1])
         h, l, n, e = ctx.bookkeeping()
-        assert e == 0 and l[0] == K % W, "unexpected bookkeeping after the timed steps"
-        reps = _repeat_ms(torch, total_ms, args.reps, lambda: ctx.init_checkpoint(s0),
+        assert e == 0 and list(l) == [int(v) for v in (start_len + K) % W], \
+            "unexpected bookkeeping after the timed steps"
+        reps = _repeat_ms(torch, total_ms, args.reps, restart,
                           lambda t: ctx.decode_step(y, **pool[t % pool_n]), K)
 
     # the same K steps again with an event pair around every launch (per-kernel durations on the
     # stream the kernels run on)
-    ctx.init_checkpoint(s0)
+    restart()
     torch.cuda.synchronize()
     evl = _events(torch, 2 * K)
     for t in range(K):
@@ -225,9 +249,18 @@ def run_m2(args, torch, rb, wl):
         h, l, n, e = ctx.bookkeeping()
         assert e == 0 and l[0] == 0, "unexpected bookkeeping after the graph replays"
 
-    alg_bytes = sum(m2_replay_bytes(P, N, W, gr, t % W, True, bf16) for t in range(K)) * B * H
-    state_bytes = sum((2 * P * N * 4 if t % W == W - 1 else P * N * (2 if bf16 else 4))
-                      for t in range(K)) * B * H
+    # algorithmic bytes of every launch: sequence b holds (start_len[b] + t) mod W entries at
+    # step t; the state-only part is the checkpoint read (and, when folding, its write)
+    def launch_bytes(t):
+        ls = (start_len + t) % W
+        counts = np.bincount(ls, minlength=W)
+        alg = sum(int(c) * m2_replay_bytes(P, N, W, gr, l, True, bf16) for l, c in enumerate(counts))
+        st = sum(int(c) * (2 * P * N * 4 + (P * N * 2 if bf16 else 0) if l == W - 1
+                           else P * N * (2 if bf16 else 4)) for l, c in enumerate(counts))
+        return alg * H, st * H
+    per = [launch_bytes(t) for t in range(K)]
+    alg_bytes = sum(p[0] for p in per)
+    state_bytes = sum(p[1] for p in per)
     replay_s = total_ms / 1e3
 
     # conventional read-modify-write on the same schedule
@@ -254,15 +287,35 @@ def run_m2(args, torch, rb, wl):
             rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
         del st
 
-    # dominant kernel: the replay-only decode launches (no sequence folds); the launches whose
-    # token fills the ring run the folding variant and are reported beside it
-    rep = [t for t in range(K) if t % W != W - 1]
-    fol = [t for t in range(K) if t % W == W - 1]
-    rep_bytes = sum(m2_replay_bytes(P, N, W, gr, t % W, True, bf16) for t in rep) * B * H
-    fol_bytes = sum(m2_replay_bytes(P, N, W, gr, t % W, True, bf16) for t in fol) * B * H
+    # dominant kernel. Lock-step: the replay-only launches (no sequence folds); the launches whose
+    # token fills every ring run the folding variant and are reported beside it. Staggered: every
+    # launch is the variant that may fold, with a mix of folding and replaying tiles.
+    if args.stagger:
+        rep, fol = list(range(K)), []
+        kname = f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kMayFold> (mixed: 1/{W} of the tiles fold)"
+        tkey = "decode_stagger_bf16" if bf16 else "decode_stagger"
+    else:
+        rep = [t for t in range(K) if t % W != W - 1]
+        fol = [t for t in range(K) if t % W == W - 1]
+        kname = f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kUniform> (steps that replay)"
+        tkey = "decode_replay_bf16" if bf16 else "decode_replay"
+    rep_bytes = sum(per[t][0] for t in rep)
+    fol_bytes = sum(per[t][0] for t in fol)
     rep_s = sum(launch_ms[t] for t in rep) / 1e3
     fol_s = sum(launch_ms[t] for t in fol) / 1e3
     achieved = rep_bytes / rep_s / 1e9
+    roof = {
+        "bound": "hbm",
+        "kernel": kname,
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "alg_bytes_per_launch": round(rep_bytes / len(rep)),
+        "avg_launch_us": round(1e6 * rep_s / len(rep), 2),
+        "launches": len(rep),
+    }
+    roof.update(_traffic_fields(tkey))
     line = {
         "metric": METRIC,
         "value": round(alg_bytes / replay_s / 1e9, 1),
@@ -278,53 +331,50 @@ def run_m2(args, torch, rb, wl):
         "data": "synthetic (seeded N(0,1) x, N(0,1)/sqrt(N) B and C, softplus(N(-2,0.5)) dt)",
         "config": {"workload": f"mamba2_decode_b{B}_h{H}_p{P}_n{N}_w{W}"
                                + (f"_g{sh.ngroups}" if sh.ngroups != H else "") + ("_bf16read" if bf16 else "")
-                               + ("_graph" if args.graph else ""),
+                               + ("_stagger" if args.stagger else "") + ("_graph" if args.graph else ""),
                    "batch": B, "heads": H, "head_dim": P, "d_state": N, "window": W,
                    "groups": sh.ngroups, "input_pool_slots": pool_n,
+                   "ring_fill": "staggered: sequence b starts at b mod W entries" if args.stagger
+                   else "lock-step: every sequence starts from an empty ring",
                    "launch": "hip graph of 2 W steps, replayed" if args.graph else "eager"},
+        "value_is": "alg_gbs: every byte the method moves per step (checkpoint reads, the fold's "
+                    "read + write, ring reads and appends, inputs, outputs) / wall time",
+        "alg_gbs": round(alg_bytes / replay_s / 1e9, 1),
+        "state_gbs": round(state_bytes / replay_s / 1e9, 1),
+        "state_gbs_is": "checkpoint bytes only (its reads, and the fold's write) / wall time",
         "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
         "ms_per_step_reps": reps,
-        "state_gbs": round(state_bytes / replay_s / 1e9, 1),
         "tokens_per_s": round(B * K / replay_s, 1),
         "rmw_ms_per_step": round(rmw_s * 1e3 / K, 5) if rmw_s else None,
         "rmw_gbs": round(m2_rmw_bytes(P, N, gr) * B * H * K / rmw_s / 1e9, 1) if rmw_s else None,
         "speedup_vs_rmw": round(rmw_s / replay_s, 3) if rmw_s else None,
-        "roofline": {
-            "bound": "hbm",
-            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kUniform> (steps that replay)",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": _traffic("decode_replay_bf16" if bf16 else "decode_replay"),
-            "alg_bytes_per_launch": round(rep_bytes / len(rep)),
-            "avg_launch_us": round(1e6 * rep_s / len(rep), 2),
-            "launches": len(rep),
-        },
-        "fold_steps": {
-            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kMayFold> (the step that fills the ring)",
-            "achieved_gbs": round(fol_bytes / fol_s / 1e9, 1) if fol else None,
-            "traffic": _traffic("decode_fold_bf16" if bf16 else "decode_fold"),
-            "alg_bytes_per_launch": round(fol_bytes / len(fol)) if fol else None,
-            "avg_launch_us": round(1e6 * fol_s / len(fol), 2) if fol else None,
-            "launches": len(fol),
-        },
+        "roofline": roof,
         "decode_all_launches_gbs": round(alg_bytes / (sum(launch_ms) / 1e3) / 1e9, 1),
         "input_gen_s": round(gen_s, 1),
     }
-    return line, (sh, prm)
+    if fol:
+        line["fold_steps"] = {
+            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kMayFold> (the step that fills every ring)",
+            "achieved_gbs": round(fol_bytes / fol_s / 1e9, 1),
+            "alg_bytes_per_launch": round(fol_bytes / len(fol)),
+            "avg_launch_us": round(1e6 * fol_s / len(fol), 2),
+            "launches": len(fol),
+            **_traffic_fields("decode_fold_bf16" if bf16 else "decode_fold"),
+        }
+    return line, (sh, prm, host_pool)
 
 
 def m2_verify_bytes(P, N, W, gr, K, length, store_c=True) -> tuple[float, bool]:
-    """HBM bytes of one verify launch for one (b, h) pair with `length` committed entries, and
-    whether it folds them first (length + K > W)."""
+    """HBM bytes of one verify for one (b, h) pair with `length` committed entries, and whether it
+    folds them first (length + K > W). With B / C shared by groups (gr < 1) that fold is a
+    consolidation launch of its own, after which the verify reads the new checkpoint again."""
     f = 4
     drafts = K * ((P + 1) * f + 2 * N * f * gr)
     ring = length * ((P + 1) * f + N * f * gr)
     outs = K * P * f
     append = K * ((P + 1) * f + N * f * gr * (2 if store_c else 1))
     fold = length + K > W
-    s0 = (2 if fold else 1) * P * N * f
+    s0 = ((3 if gr < 1 else 2) if fold else 1) * P * N * f
     return s0 + ring + drafts + outs + append, fold
 
 
@@ -332,7 +382,8 @@ def run_m2_spec(args, torch, rb, wl):
     """Speculative decoding: K = 6 drafts per round into the W = 16 ring, verify (outputs of all
     drafts, checkpoint streamed once) then a pointer commit of the seeded accepted prefix, against
     the conventional round (state read once, one snapshot written per draft, pointer commit)."""
-    sh = wl.M2_SPEC
+    sh = wl.M2_SPEC if not args.groups else wl.M2Shape(batch=512, nheads=128, ngroups=args.groups,
+                                                       head_dim=64, d_state=128, window=16, max_draft=6)
     P, N, W, H, B, K = sh.head_dim, sh.d_state, sh.window, sh.nheads, sh.batch, sh.max_draft
     gr = sh.ngroups / sh.nheads
     rounds, Wm, S = args.steps or 256, args.warmup, 4
@@ -349,7 +400,7 @@ def run_m2_spec(args, torch, rb, wl):
     D = torch.from_numpy(prm["D"]).cuda()
     gen_s = time.time() - t0
 
-    ctx = rb.Context("mamba2", B, H, P, N, W, max_draft=K, store_c=True)
+    ctx = rb.Context("mamba2", B, H, P, N, W, ngroups=sh.ngroups, max_draft=K, store_c=True)
     ctx.set_params(A, D)
     yk = torch.empty(K, B, H, P, device="cuda")
     ctx.init_checkpoint(s0)
@@ -431,7 +482,9 @@ def run_m2_spec(args, torch, rb, wl):
         "ms_per_step": round(replay_s * 1e3 / rounds, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
         "data": "synthetic (seeded drafts; accepted ~ min(Geometric(0.35) failures, 6))",
-        "config": {"workload": f"mamba2_spec_b{B}_h{H}_p{P}_n{N}_w{W}_k{K}", "batch": B,
+        "config": {"workload": f"mamba2_spec_b{B}_h{H}_p{P}_n{N}_w{W}_k{K}"
+                               + (f"_g{sh.ngroups}" if sh.ngroups != H else ""), "batch": B,
+                   "groups": sh.ngroups,
                    "heads": H, "head_dim": P, "d_state": N, "window": W, "drafts": K,
                    "rounds": rounds, "draft_pool_slots": S},
         "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
@@ -441,45 +494,63 @@ def run_m2_spec(args, torch, rb, wl):
         "conv_ms_per_round": round(conv_s * 1e3 / rounds, 5),
         "conv_gbs": round(conv_bytes / conv_s / 1e9, 1),
         "speedup_vs_conventional": round(conv_s / replay_s, 3),
-        "roofline": {"bound": "hbm", "kernel": "k_m2_verify<64,128,false>",
+        "roofline": {"bound": "hbm", "kernel": "k_m2_verify<64,128,false>" + (
+                         "" if sh.ngroups == H else " (with the consolidation launch queued before it "
+                         "in rounds where a sequence's drafts do not fit)"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic("verify"),
+                     **_traffic_fields("verify"),
                      "alg_bytes_per_launch": round(vbytes / rounds),
                      "avg_launch_us": round(1e6 * vk_s / rounds, 2), "launches": rounds},
         "input_gen_s": round(gen_s, 1),
     }, (sh, prm)
 
 
-def gdn_verify_bytes(DV, DK, W, K, length) -> tuple[float, bool]:
-    """HBM bytes of one Gated DeltaNet verify launch for one (b, h) pair with `length` committed
-    entries, and whether it folds them first (length + K > W)."""
+def gdn_verify_bytes(DV, DK, W, K, length, ga=1) -> tuple[float, bool]:
+    """HBM bytes of one delta-rule verify launch for one (b, h) pair with `length` committed
+    entries (ga gate floats per entry), and whether it folds them first (length + K > W)."""
     f = 4
-    drafts = K * (2 * DK + DV + 2) * f
-    ring = length * (DK + DV + 2) * f
+    entry = (DK + DV + 1 + ga) * f
+    drafts = K * (entry + DK * f)
+    ring = length * entry
     outs = K * DV * f
-    append = K * (DK + DV + 2) * f
+    append = K * entry
     fold = length + K > W
     s0 = (2 if fold else 1) * DV * DK * f
     return s0 + ring + drafts + outs + append, fold
 
 
-def run_gdn_spec(args, torch, rb, wl):
-    """Gated DeltaNet speculative decoding: K = 6 drafts per round into the W = 16 ring (batch 512,
-    32 heads, 128 x 128), verify then a pointer commit of the seeded accepted prefix, against the
-    conventional round (state read once, one snapshot written per draft, pointer commit)."""
+DELTA = {
+    "gdn": {"name": "Gated DeltaNet", "tag": "gdn", "state0": "gdn_state0", "inputs": "gdn_token_inputs",
+            "kind": "RSSM_GDN", "step": "gdn_step", "spec": "gdn_spec_round",
+            "data": "synthetic (seeded; q, k L2-normalised N(0,1), v N(0,1), beta sigmoid, alpha exp(-softplus))"},
+    "kda": {"name": "Kimi Delta Attention", "tag": "kda", "state0": "kda_state0",
+            "inputs": "kda_token_inputs", "kind": "RSSM_KDA", "step": "kda_step",
+            "spec": "kda_spec_round",
+            "data": "synthetic (seeded; q, k L2-normalised N(0,1), v N(0,1), beta sigmoid, one gate "
+                    "exp(-softplus(N(0,1))) per key channel)"},
+}
+
+
+def run_gdn_spec(args, torch, rb, wl, layer="gdn"):
+    """Delta-rule speculative decoding (Gated DeltaNet, or Kimi Delta Attention with layer="kda"):
+    K = 6 drafts per round into the W = 16 ring (batch 512, 32 heads, 128 x 128), verify then a
+    pointer commit of the seeded accepted prefix, against the conventional round (state read once,
+    one snapshot written per draft, pointer commit)."""
+    L = DELTA[layer]
     sh = wl.GDNShape(batch=args.batch or 512, nheads=32, d_k=128, d_v=128, window=16, max_draft=6)
     DV, DK, W, H, B, K = sh.d_v, sh.d_k, sh.window, sh.nheads, sh.batch, sh.max_draft
+    ga = DK if layer == "kda" else 1
     rounds, Wm, S = args.steps or 256, args.warmup, 4
     t0 = time.time()
-    s0 = torch.from_numpy(wl.gdn_state0(sh, 0)).cuda()
-    pool = [{k: torch.from_numpy(v).cuda() for k, v in wl.gdn_token_inputs(sh, 0, s, ntok=K).items()}
+    s0 = torch.from_numpy(getattr(wl, L["state0"])(sh, 0)).cuda()
+    pool = [{k: torch.from_numpy(v).cuda() for k, v in getattr(wl, L["inputs"])(sh, 0, s, ntok=K).items()}
             for s in range(S)]
     acc_h = wl.spec_accepted(B, rounds + Wm, K, p=0.35, seed=0)
     acc = torch.from_numpy(acc_h).cuda()
     gen_s = time.time() - t0
 
-    ctx = rb.Context("gdn", B, H, DV, DK, W, max_draft=K)
+    ctx = rb.Context(layer, B, H, DV, DK, W, max_draft=K)
     ok = torch.empty(K, B, H, DV, device="cuda")
     ctx.init_checkpoint(s0)
     for r in range(Wm):
@@ -509,17 +580,17 @@ def run_gdn_spec(args, torch, rb, wl):
     verify_ms = [evl[2 * r].elapsed_time(evl[2 * r + 1]) for r in range(rounds)]
     del ctx
 
-    L = np.zeros(B, dtype=np.int64)
+    lens = np.zeros(B, dtype=np.int64)
     vbytes, folds = 0.0, 0
     for r in range(rounds):
-        vbytes += sum(gdn_verify_bytes(DV, DK, W, K, int(x))[0] for x in L) * H
-        fold = L + K > W
+        vbytes += sum(gdn_verify_bytes(DV, DK, W, K, int(x), ga)[0] for x in lens) * H
+        fold = lens + K > W
         folds += int(fold.sum())
-        L = np.where(fold, 0, L) + acc_h[r]
+        lens = np.where(fold, 0, lens) + acc_h[r]
     cbytes = 3 * 4 * B * 2 * rounds + B * 4 * rounds          # commits
     alg_bytes = vbytes + cbytes
 
-    cfg = rb.make_config(rb.RSSM_GDN, B, H, H, DV, DK, W, K)
+    cfg = rb.make_config(getattr(rb, L["kind"]), B, H, H, DV, DK, W, K)
     spool = torch.empty((2 * K + 1, B, H, DV, DK), device="cuda")
     slot_of = torch.empty(B, dtype=torch.int32, device="cuda")
 
@@ -542,21 +613,21 @@ def run_gdn_spec(args, torch, rb, wl):
     torch.cuda.synchronize()
     conv_s = ev2[0].elapsed_time(ev2[1]) / 1e3
     del spool
-    conv_bytes = (DV * DK * 4 * (1 + K) + K * (2 * DK + DV + 2) * 4 + K * DV * 4) * B * H * rounds
+    conv_bytes = (DV * DK * 4 * (1 + K) + K * (2 * DK + DV + 1 + ga) * 4 + K * DV * 4) * B * H * rounds
 
     vk_s = sum(verify_ms) / 1e3
     achieved = vbytes / vk_s / 1e9
     accepted = int(acc_h[:rounds].sum())
     return {
         "metric": "speculative verify+commit state GB/s (% of HBM peak) + accepted tokens/s vs "
-                  "conventional per-draft snapshots, Gated DeltaNet batch 512 K=6 W=16",
+                  f"conventional per-draft snapshots, {L['name']} batch 512 K=6 W=16",
         "value": round(alg_bytes / replay_s / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1, "steps": rounds, "warmup": Wm,
         "ms_per_step": round(replay_s * 1e3 / rounds, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
         "data": "synthetic (seeded drafts; accepted ~ min(Geometric(0.35) failures, 6))",
-        "config": {"workload": f"gdn_spec_b{B}_h{H}_dk{DK}_dv{DV}_w{W}_k{K}", "batch": B,
+        "config": {"workload": f"{layer}_spec_b{B}_h{H}_dk{DK}_dv{DV}_w{W}_k{K}", "batch": B,
                    "heads": H, "d_k": DK, "d_v": DV, "window": W, "drafts": K,
                    "rounds": rounds, "draft_pool_slots": S},
         "pct_hbm_peak": round(100 * alg_bytes / replay_s / 1e9 / HBM_PEAK_GBS, 2),
@@ -566,32 +637,35 @@ def run_gdn_spec(args, torch, rb, wl):
         "conv_ms_per_round": round(conv_s * 1e3 / rounds, 5),
         "conv_gbs": round(conv_bytes / conv_s / 1e9, 1),
         "speedup_vs_conventional": round(conv_s / replay_s, 3),
-        "roofline": {"bound": "hbm", "kernel": "k_gdn_verify<128,128,1>",
+        "roofline": {"bound": "hbm", "kernel": "k_gdn_verify<128,128,1>" if layer == "gdn" else
+                     "k_kda_verify<128,128>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic("gdn_verify"),
+                     **_traffic_fields(f"{layer}_verify"),
                      "alg_bytes_per_launch": round(vbytes / rounds),
                      "avg_launch_us": round(1e6 * vk_s / rounds, 2), "launches": rounds},
         "input_gen_s": round(gen_s, 1),
     }, sh
 
 
-def cpu_baseline_gdn_spec(sh, wl, budget_s=8.0):
+def cpu_baseline_gdn_spec(sh, wl, budget_s=8.0, layer="gdn"):
     import oracle
+    L = DELTA[layer]
+    spec = getattr(oracle, L["spec"])
     cores = oracle.set_threads(0)
     nseq = 64
     K = sh.max_draft
-    state = wl.gdn_state0(sh, 0)[:nseq].astype(np.float64)
-    drafts = [{k: np.ascontiguousarray(v[:, :nseq]) for k, v in wl.gdn_token_inputs(sh, 0, s, ntok=K).items()}
-              for s in range(2)]
+    state = getattr(wl, L["state0"])(sh, 0)[:nseq].astype(np.float64)
+    drafts = [{k: np.ascontiguousarray(v[:, :nseq])
+               for k, v in getattr(wl, L["inputs"])(sh, 0, s, ntok=K).items()} for s in range(2)]
     acc = wl.spec_accepted(sh.batch, 512, K, seed=0)[:, :nseq]
     t0 = time.perf_counter()
-    oracle.gdn_spec_round(drafts[0], state, acc[0])
+    spec(drafts[0], state, acc[0])
     one = time.perf_counter() - t0
     rounds = max(2, min(256, int(budget_s / max(one, 1e-6))))
     t0 = time.perf_counter()
     for r in range(rounds):
-        oracle.gdn_spec_round(drafts[r % 2], state, acc[r])
+        spec(drafts[r % 2], state, acc[r])
     el = time.perf_counter() - t0
     return {"value": round(int(acc[:rounds].sum()) / el, 1), "unit": "accepted tokens/s",
             "cores": cores, "kind": "oracle",
@@ -599,14 +673,18 @@ def cpu_baseline_gdn_spec(sh, wl, budget_s=8.0):
                       f"recurrence with a state copy per draft, {el:.1f} s"}
 
 
-def gdn_bytes(DV, DK, W, length) -> float:
+def gdn_bytes(DV, DK, W, length, ga=1) -> float:
+    """HBM bytes of one decode launch for one (b, h) pair of a delta-rule layer whose ring holds
+    `length` entries; ga = gate floats per entry (1 for Gated DeltaNet, d_k for Kimi Delta
+    Attention)."""
     f = 4
-    token = (2 * DK + DV + 2) * f
-    ring = length * (DK + DV + 2) * f
+    entry = (DK + DV + 1 + ga) * f                 # k, v, beta, gate of one entry
+    token = entry + DK * f                         # and q
+    ring = length * entry
     o = DV * f
     if length + 1 >= W:
         return 2 * DV * DK * f + token + ring + o
-    return DV * DK * f + token + ring + (DK + DV + 2) * f + o
+    return DV * DK * f + token + ring + entry + o
 
 
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
@@ -699,7 +777,7 @@ def run_m2_prefill(args, torch, rb, wl):
                      "unit": "GB/s" if bound_hbm else "TFLOP/s",
                      "frac": round(hbm_frac if bound_hbm else mfma_frac, 4),
                      "other": {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4)},
-                     "traffic": _traffic("prefill"), "alg_bytes_per_launch": round(bytes_call),
+                     **_traffic_fields("prefill"), "alg_bytes_per_launch": round(bytes_call),
                      "flops_per_launch": round(flops_call),
                      "avg_launch_us": round(1e6 * pre_s / K, 2), "launches": K},
         "input_gen_s": round(gen_s, 1),
@@ -785,7 +863,7 @@ def run_gdn_prefill(args, torch, rb, wl):
                      "unit": "GB/s" if bound_hbm else "TFLOP/s",
                      "frac": round(hbm_frac if bound_hbm else mfma_frac, 4),
                      "other": {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4)},
-                     "traffic": _traffic("gdn_prefill"), "alg_bytes_per_launch": round(bytes_call),
+                     **_traffic_fields("gdn_prefill"), "alg_bytes_per_launch": round(bytes_call),
                      "flops_per_launch": round(flops_call),
                      "avg_launch_us": round(1e6 * pre_s / K, 2), "launches": K},
         "input_gen_s": round(gen_s, 1),
@@ -839,24 +917,27 @@ def run_m2_fork(args, torch, rb, wl):
         "export_gbs": round(moved / t_exp / 1e9, 1), "import_gbs": round(moved / t_imp / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "k_seq_copy (fork)", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic("fork"), "alg_bytes_per_launch": moved,
+                     **_traffic_fields("fork"), "alg_bytes_per_launch": moved,
                      "avg_launch_us": round(1e6 * t_fork, 2), "launches": K},
     }
 
 
-def run_gdn(args, torch, rb, wl):
-    """Gated DeltaNet decode: batch 256, 32 heads, d_k = d_v = 128, W = 16."""
+def run_gdn(args, torch, rb, wl, layer="gdn"):
+    """Delta-rule decode (Gated DeltaNet, or Kimi Delta Attention with layer="kda"): batch 256,
+    32 heads, d_k = d_v = 128, W = 16."""
+    L = DELTA[layer]
     sh = wl.GDNShape(batch=args.batch or 256, nheads=32, d_k=128, d_v=128, window=16)
     DV, DK, W, H, B = sh.d_v, sh.d_k, sh.window, sh.nheads, sh.batch
+    ga = DK if layer == "kda" else 1
     K, Wm, S = args.steps, args.warmup, 32
     t0 = time.time()
-    s0 = torch.from_numpy(wl.gdn_state0(sh, 0)).cuda()
+    s0 = torch.from_numpy(getattr(wl, L["state0"])(sh, 0)).cuda()
     pool = []
     for s in range(S):
-        ins = wl.gdn_token_inputs(sh, 0, s)
+        ins = getattr(wl, L["inputs"])(sh, 0, s)
         pool.append({k: torch.from_numpy(v[0]).cuda() for k, v in ins.items()})
     gen_s = time.time() - t0
-    ctx = rb.Context("gdn", B, H, DV, DK, W)
+    ctx = rb.Context(layer, B, H, DV, DK, W)
     o = torch.empty(B, H, DV, device="cuda")
     ctx.init_checkpoint(s0)
     for t in range(Wm):
@@ -888,8 +969,8 @@ def run_gdn(args, torch, rb, wl):
         total_ms = _graph_time(torch, S, lambda t: ctx.decode_step(o, **pool[t]), 1, K // S)
         h, l, n, e = ctx.bookkeeping()
         assert e == 0 and l[0] == 0, "unexpected bookkeeping after the graph replays"
-    alg = sum(gdn_bytes(DV, DK, W, t % W) for t in range(K)) * B * H
-    cfg = rb.make_config(rb.RSSM_GDN, B, H, H, DV, DK, W)
+    alg = sum(gdn_bytes(DV, DK, W, t % W, ga) for t in range(K)) * B * H
+    cfg = rb.make_config(getattr(rb, L["kind"]), B, H, H, DV, DK, W)
     st = s0.clone()
     o1 = torch.empty(1, B, H, DV, device="cuda")
     pool1 = [{k: v.unsqueeze(0) for k, v in pool[t].items()} for t in range(S)]
@@ -907,21 +988,22 @@ def run_gdn(args, torch, rb, wl):
         ev2[1].record()
         torch.cuda.synchronize()
         rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
-    rmw_bytes = (2 * DV * DK * 4 + (2 * DK + DV + 2) * 4 + DV * 4) * B * H * K
+    rmw_bytes = (2 * DV * DK * 4 + (2 * DK + DV + 1 + ga) * 4 + DV * 4) * B * H * K
     rep = [t for t in range(K) if t % W != W - 1]
     fol = [t for t in range(K) if t % W == W - 1]
-    rep_b = sum(gdn_bytes(DV, DK, W, t % W) for t in rep) * B * H
-    fol_b = sum(gdn_bytes(DV, DK, W, t % W) for t in fol) * B * H
+    rep_b = sum(gdn_bytes(DV, DK, W, t % W, ga) for t in rep) * B * H
+    fol_b = sum(gdn_bytes(DV, DK, W, t % W, ga) for t in fol) * B * H
     rep_s = sum(launch_ms[t] for t in rep) / 1e3
     fol_s = sum(launch_ms[t] for t in fol) / 1e3
     replay_s = total_ms / 1e3
     return {
-        "metric": "GDN decode state GB/s (% of HBM peak) + tokens/s vs conventional, batch 256 W=16",
+        "metric": f"{L['name']} decode state GB/s (% of HBM peak) + tokens/s vs conventional, "
+                  "batch 256 W=16",
         "value": round(alg / replay_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": Wm, "ms_per_step": round(total_ms / K, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
-        "data": "synthetic (seeded; q, k L2-normalised N(0,1), v N(0,1), beta sigmoid, alpha exp(-softplus))",
-        "config": {"workload": f"gdn_decode_b{B}_h{H}_dk{DK}_dv{DV}_w{W}" + ("_graph" if args.graph else ""),
+        "data": L["data"],
+        "config": {"workload": f"{layer}_decode_b{B}_h{H}_dk{DK}_dv{DV}_w{W}" + ("_graph" if args.graph else ""),
                    "batch": B, "heads": H, "d_k": DK, "d_v": DV, "window": W, "input_pool_slots": S,
                    "launch": "hip graph of 2 W steps, replayed" if args.graph else "eager"},
         "pct_hbm_peak": round(100 * alg / replay_s / 1e9 / HBM_PEAK_GBS, 2),
@@ -930,15 +1012,15 @@ def run_gdn(args, torch, rb, wl):
         "rmw_ms_per_step": round(rmw_s * 1e3 / K, 5),
         "rmw_gbs": round(rmw_bytes / rmw_s / 1e9, 1),
         "speedup_vs_rmw": round(rmw_s / replay_s, 3),
-        "roofline": {"bound": "hbm", "kernel": "k_gdn_decode<128,128,kUniform> (steps that replay)",
+        "roofline": {"bound": "hbm", "kernel": f"k_{layer}_decode<128,128,kUniform> (steps that replay)",
                      "achieved": round(rep_b / rep_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(rep_b / rep_s / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic("gdn_replay"),
+                     **_traffic_fields(f"{layer}_replay"),
                      "alg_bytes_per_launch": round(rep_b / len(rep)),
                      "avg_launch_us": round(1e6 * rep_s / len(rep), 2), "launches": len(rep)},
-        "fold_steps": {"kernel": "k_gdn_decode<128,128,kMayFold> (the step that fills the ring)",
+        "fold_steps": {"kernel": f"k_{layer}_decode<128,128,kMayFold> (the step that fills the ring)",
                        "achieved_gbs": round(fol_b / fol_s / 1e9, 1) if fol else None,
-                       "traffic": _traffic("gdn_fold"),
+                       **_traffic_fields(f"{layer}_fold"),
                        "alg_bytes_per_launch": round(fol_b / len(fol)) if fol else None,
                        "avg_launch_us": round(1e6 * fol_s / len(fol), 2) if fol else None,
                        "launches": len(fol)},
@@ -946,24 +1028,25 @@ def run_gdn(args, torch, rb, wl):
     }, sh
 
 
-def cpu_baseline_gdn(sh, wl, budget_s=8.0):
+def cpu_baseline_gdn(sh, wl, budget_s=8.0, layer="gdn"):
     import oracle
+    L = DELTA[layer]
+    step = getattr(oracle, L["step"])
     cores = oracle.set_threads(0)
-    state = wl.gdn_state0(sh, 0).astype(np.float64)
-    toks = [{k: np.ascontiguousarray(v[0]) for k, v in wl.gdn_token_inputs(sh, 0, s).items()}
+    state = getattr(wl, L["state0"])(sh, 0).astype(np.float64)
+    toks = [{k: np.ascontiguousarray(v[0]) for k, v in getattr(wl, L["inputs"])(sh, 0, s).items()}
             for s in range(4)]
     for _ in range(2):
         t0 = time.perf_counter()
-        oracle.gdn_step(*(toks[0][k] for k in ("q", "k", "v", "beta", "alpha")), state)
+        step(*(toks[0][k] for k in ("q", "k", "v", "beta", "alpha")), state)
         one = time.perf_counter() - t0
     steps = max(2, min(512, int(budget_s / max(one, 1e-6))))
     t0 = time.perf_counter()
     for t in range(steps):
-        oracle.gdn_step(*(toks[t % 4][k] for k in ("q", "k", "v", "beta", "alpha")), state)
+        step(*(toks[t % 4][k] for k in ("q", "k", "v", "beta", "alpha")), state)
     el = time.perf_counter() - t0
     tok_s = sh.batch * steps / el
-    one_core = _single_core(lambda k, st: oracle.gdn_step(*(k[n] for n in ("q", "k", "v", "beta",
-                                                                            "alpha")), st),
+    one_core = _single_core(lambda k, st: step(*(k[n] for n in ("q", "k", "v", "beta", "alpha")), st),
                             toks, state, sh.batch, cores)
     return {"value": round(2 * sh.d_v * sh.d_k * 8 * sh.nheads * tok_s / 1e9, 3),
             "unit": "GB/s (fp64 state read+write)", "cores": cores, "kind": "oracle",
@@ -998,24 +1081,27 @@ def cpu_baseline_m2_spec(sh, prm, wl, budget_s=8.0):
                       f"recurrence with a state copy per draft, {el:.1f} s"}
 
 
-def cpu_baseline_m2(sh, prm, wl, budget_s=12.0):
-    """Time the CPU oracle (conventional fp64 recurrence) on the first steps of a subset of the
-    same seeded schedule, sized to about `budget_s` of CPU time."""
+def cpu_baseline_m2(sh, prm, wl, host_pool=None, budget_s=12.0):
+    """Time the CPU oracle (conventional fp64 recurrence) on the first steps of the same seeded
+    schedule (step t takes token slot t mod 32, as the GPU legs), sized to about `budget_s` of CPU
+    time."""
     import oracle
     cores = oracle.set_threads(0)
     nseq = sh.batch
-    sub = slice(0, nseq)
     state = wl.m2_state0(sh, 0).astype(np.float64)
-    toks = [wl.m2_token_inputs(sh, 0, s) for s in range(4)]
-    toks = [{k: np.ascontiguousarray(v[0][sub]) for k, v in t.items()} for t in toks]
+    if host_pool is None:
+        host_pool = [{k: v[0] for k, v in wl.m2_token_inputs(sh, 0, s).items()} for s in range(32)]
+    toks = [{k: np.ascontiguousarray(v) for k, v in t.items()} for t in host_pool]
+    S = len(toks)
     for _ in range(2):   # first calls pay for thread start-up and page faults
         t0 = time.perf_counter()
         oracle.m2_step(prm["A"], prm["D"], toks[0]["x"], toks[0]["B"], toks[0]["C"], toks[0]["dt"], state)
         one = time.perf_counter() - t0
+    state = wl.m2_state0(sh, 0).astype(np.float64)
     steps = max(2, min(512, int(budget_s / max(one, 1e-6))))
     t0 = time.perf_counter()
     for t in range(steps):
-        k = toks[t % 4]
+        k = toks[t % S]
         oracle.m2_step(prm["A"], prm["D"], k["x"], k["B"], k["C"], k["dt"], state)
     el = time.perf_counter() - t0
     tok_s = nseq * steps / el
@@ -1027,8 +1113,9 @@ def cpu_baseline_m2(sh, prm, wl, budget_s=12.0):
     return {"value": round(gbs, 3), "unit": "GB/s (fp64 state read+write)", "cores": cores,
             "kind": "oracle", "tokens_per_s": round(tok_s, 1), "cpu_model": _cpu_model(),
             "single_core_tokens_per_s": one_core,
-            "sample": f"first {steps} decode steps of sequences 0..{nseq - 1} (all {sh.nheads} heads) "
-                      f"of the same seeded schedule, conventional fp64 recurrence, {el:.1f} s"}
+            "sample": f"decode steps 0..{steps - 1} of sequences 0..{nseq - 1} (all {sh.nheads} heads), "
+                      f"step t on token slot t mod {S} as on the GPU, from the same initial state; "
+                      f"conventional fp64 recurrence, {el:.1f} s"}
 
 
 def _single_core(step, toks, state, nseq, cores, budget_s=2.0):
@@ -1066,11 +1153,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="m2_serve",
                     choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve", "gdn_spec",
-                             "m2_prefill", "gdn_prefill", "m2_fork"])
+                             "kda_serve", "kda_spec", "m2_prefill", "gdn_prefill", "m2_fork"])
     ap.add_argument("--prompt", type=int, default=512, help="prompt tokens (m2_prefill, gdn_prefill)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
     ap.add_argument("--groups", type=int, default=0,
                     help="Mamba-2 B/C groups (default: one per head)")
+    ap.add_argument("--stagger", action="store_true",
+                    help="m2_serve legs: every sequence at its own ring fill (b mod W), so every "
+                         "launch mixes folding and replaying tiles")
     ap.add_argument("--graph", action="store_true",
                     help="decode legs: time replays of a captured HIP graph of 2 W steps (both paths)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1100,10 +1190,11 @@ def main():
         line, (sh, prm) = run_m2_spec(args, torch, rb, wl)
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_m2_spec(sh, prm, wl)
-    elif args.workload == "gdn_spec":
-        line, sh = run_gdn_spec(args, torch, rb, wl)
+    elif args.workload in ("gdn_spec", "kda_spec"):
+        layer = args.workload[:3]
+        line, sh = run_gdn_spec(args, torch, rb, wl, layer)
         if not args.no_cpu_baseline:
-            line["cpu_baseline"] = cpu_baseline_gdn_spec(sh, wl)
+            line["cpu_baseline"] = cpu_baseline_gdn_spec(sh, wl, layer=layer)
     elif args.workload == "m2_prefill":
         args.steps = args.steps or 8
         args.warmup = min(args.warmup, 2)
@@ -1126,17 +1217,19 @@ def main():
         args.steps = args.steps or 20
         args.warmup = min(args.warmup, 3)
         line = run_m2_fork(args, torch, rb, wl)
-    elif args.workload == "gdn_serve":
+    elif args.workload in ("gdn_serve", "kda_serve"):
+        layer = args.workload[:3]
         args.steps = args.steps or 512
-        line, sh = run_gdn(args, torch, rb, wl)
+        line, sh = run_gdn(args, torch, rb, wl, layer)
         if not args.no_cpu_baseline:
-            line["cpu_baseline"] = cpu_baseline_gdn(sh, wl)
+            line["cpu_baseline"] = cpu_baseline_gdn(sh, wl, layer=layer)
     else:
         args.steps = args.steps or 512
-        line, (sh, prm) = run_m2(args, torch, rb, wl)
+        line, (sh, prm, host_pool) = run_m2(args, torch, rb, wl)
         if not args.no_cpu_baseline:
-            line["cpu_baseline"] = cpu_baseline_m2(sh, prm, wl)
-    if args.workload in ("m2_serve", "m2_serve_bf16", "gdn_serve", "m2_spec", "gdn_spec", "m2_fork"):
+            line["cpu_baseline"] = cpu_baseline_m2(sh, prm, wl, host_pool)
+    if args.workload in ("m2_serve", "m2_serve_bf16", "gdn_serve", "kda_serve", "m2_spec", "gdn_spec",
+                         "kda_spec", "m2_fork"):
         cg = measure_copy_gbs(torch)
         line["copy_gbs"] = round(cg, 1)
         line["pct_of_copy"] = round(100 * line["value"] / cg, 1)

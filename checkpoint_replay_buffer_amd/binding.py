@@ -31,7 +31,8 @@ RSSM_F_STORE_C = 2
 
 EXPORTS = ("rssm_workspace_bytes", "rssm_create", "rssm_destroy", "rssm_set_params",
            "rssm_init_checkpoint", "rssm_decode_step", "rssm_consolidate", "rssm_prefill", "rssm_verify",
-           "rssm_verify_commit", "rssm_rollback", "rssm_step_baseline", "rssm_step_baseline_spec",
+           "rssm_verify_commit", "rssm_rollback", "rssm_step_baseline", "rssm_step_baseline_seqs",
+           "rssm_step_baseline_spec",
            "rssm_baseline_commit", "rssm_seq_state_bytes", "rssm_fork", "rssm_export", "rssm_import",
            "rssm_materialize", "rssm_read_bookkeeping", "rssm_status_str")
 
@@ -85,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "rssm_verify_commit": (I32, [P, P, P]),
         "rssm_rollback": (I32, [P, P, P]),
         "rssm_step_baseline": (I32, [cfgp, P, inp, P, P, P, P, P]),
+        "rssm_step_baseline_seqs": (I32, [cfgp, P, inp, P, P, P, P, P]),
         "rssm_step_baseline_spec": (I32, [cfgp, P, P, inp, P, P, P, P]),
         "rssm_baseline_commit": (I32, [cfgp, P, P, I32, P]),
         "rssm_seq_state_bytes": (I32, [cfgp, ctypes.POINTER(SZ)]),
@@ -197,6 +199,15 @@ def rssm_step_baseline(cfg: rssm_config, state, inputs: rssm_inputs, A, D, y, sn
          load_library().rssm_step_baseline(ctypes.byref(cfg), _ptr(state), ctypes.byref(inputs),
                                            _ptr(A), _ptr(D), _ptr(y), _ptr(snapshots),
                                            _stream(stream)))
+
+
+def rssm_step_baseline_seqs(cfg: rssm_config, seq_ptrs, inputs: rssm_inputs, A, D, y,
+                            snapshots=None, stream=None) -> None:
+    """seq_ptrs: int64 CUDA tensor [B] of device addresses of per-sequence [H,dim_v,dim_k] states."""
+    _chk("rssm_step_baseline_seqs",
+         load_library().rssm_step_baseline_seqs(ctypes.byref(cfg), _ptr(seq_ptrs),
+                                                ctypes.byref(inputs), _ptr(A), _ptr(D), _ptr(y),
+                                                _ptr(snapshots), _stream(stream)))
 
 
 def rssm_step_baseline_spec(cfg: rssm_config, pool, slot_of, inputs: rssm_inputs, A, D, y,
@@ -353,6 +364,13 @@ def step_baseline_spec(cfg: rssm_config, pool, slot_of, y, A=None, D=None, strea
     only)."""
     ntok = next(iter(kw.values())).shape[0]
     rssm_step_baseline_spec(cfg, pool, slot_of, make_inputs(ntok, **kw), A, D, y, stream)
+
+
+def step_baseline_seqs(cfg: rssm_config, seq_ptrs, y, A=None, D=None, snapshots=None, stream=None,
+                       **kw):
+    """Conventional decode over per-sequence state tiles (seq_ptrs: [B] int64 device addresses)."""
+    ntok = next(iter(kw.values())).shape[0]
+    rssm_step_baseline_seqs(cfg, seq_ptrs, make_inputs(ntok, **kw), A, D, y, snapshots, stream)
 
 
 def step_baseline(cfg: rssm_config, state, y, A=None, D=None, snapshots=None, stream=None, **kw):

@@ -613,14 +613,15 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
     const size_t lo = (size_t)(rg * R) * DK + c0;          // lane block within a tile
     const size_t off = c.bh * VK + lo;
     // source tile and the first snapshot tile (snapshot k is k * BH tiles further)
-    const float *src;
+    // source (updated in place when there are no snapshots) and first snapshot
+    float *src;
     float *snap0;
     if (a.slot_of) {
         const int sl = a.slot_of[c.b];
         src = a.state + ((size_t)sl * BH + c.bh) * VK + lo;
         snap0 = a.state + ((size_t)(sl < a.ntok ? a.ntok : 0) * BH + c.bh) * VK + lo;
     } else {
-        src = a.state + off;
+        src = a.seq ? a.seq[c.b] + (size_t)c.h * VK + lo : a.state + off;
         snap0 = a.snap ? a.snap + off : nullptr;
     }
     float4 S[R];
@@ -658,7 +659,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_gdn_rmw(GdnRmwArgs
     }
     if (!snap0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) st4_nt(a.state + off + (size_t)r * DK, S[r]);
+        for (int r = 0; r < R; ++r) st4_nt(src + (size_t)r * DK, S[r]);
     }
 }
 

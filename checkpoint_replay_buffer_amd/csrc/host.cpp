@@ -212,6 +212,28 @@ rssm_status seq_checks(const rssm_ctx *ctx, int32_t n, const void *idx, const vo
     return RSSM_OK;
 }
 
+// The conventional step over a contiguous state (state) or per-sequence tiles (seq, [B] device
+// pointers, each to an [H,dim_v,dim_k] block); exactly one of them is given.
+rssm_status step_baseline_impl(const rssm_config *cfg, float *state, float *const *seq,
+                               const rssm_inputs *in, const float *A, const float *D, float *y,
+                               float *snapshots, void *stream)
+{
+    rssm_status s = check_config(cfg);
+    if (s != RSSM_OK) return s;
+    if ((s = check_inputs(*cfg, in)) != RSSM_OK) return s;
+    if (!aligned16(y) || (snapshots && !aligned16(snapshots))) return RSSM_E_ARG;
+    if (cfg->kind == RSSM_MAMBA2) {
+        if (!A || !D) return RSSM_E_ARG;
+        M2RmwArgs a{m2dims(*cfg), state, snapshots, A, D, in->x, in->B, in->C, in->dt, y, in->ntok,
+                    nullptr, seq};
+        return m2_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+    }
+    GdnRmwArgs a{gdndims(*cfg), state, snapshots, in->q, in->k, in->v, in->beta, in->alpha, y,
+                 in->ntok, nullptr, seq};
+    const hipError_t e = cfg->kind == RSSM_KDA ? kda_rmw(a, strm(stream)) : gdn_rmw(a, strm(stream));
+    return e == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -302,7 +324,8 @@ rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, voi
     if (c.kind == RSSM_MAMBA2) {
         M2StepArgs a{m2dims(c), flip(ctx), ctx->S0, ctx->S0b, ctx->m2, ctx->A, ctx->D,
                      in->x, in->B, in->C, in->dt, y, 1, ctx->uhead, ctx->ulen};
-        const int mode = (ctx->uni && ctx->ulen + 1 < c.window) ? 0 : (mayfold ? 2 : 1);
+        // every sequence at one known position: none folds (0) or all fold (3); else 1 or 2
+        const int mode = ctx->uni ? (ctx->ulen + 1 < c.window ? 0 : 3) : (mayfold ? 2 : 1);
         s = launched(ctx, m2_decode(a, ctx->S0b != nullptr, mode, strm(stream)), true);
     } else {
         GdnStepArgs a{gdndims(c), flip(ctx), ctx->S0, ctx->gdn, in->q, in->k, in->v, in->beta,
@@ -462,20 +485,16 @@ rssm_status rssm_step_baseline(const rssm_config *cfg, float *state, const rssm_
                                const float *A, const float *D, float *y, float *snapshots,
                                void *stream)
 {
-    rssm_status s = check_config(cfg);
-    if (s != RSSM_OK) return s;
-    if ((s = check_inputs(*cfg, in)) != RSSM_OK) return s;
-    if (!aligned16(state) || !aligned16(y) || (snapshots && !aligned16(snapshots))) return RSSM_E_ARG;
-    if (cfg->kind == RSSM_MAMBA2) {
-        if (!A || !D) return RSSM_E_ARG;
-        M2RmwArgs a{m2dims(*cfg), state, snapshots, A, D, in->x, in->B, in->C, in->dt, y, in->ntok,
-                    nullptr};
-        return m2_rmw(a, strm(stream)) == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
-    }
-    GdnRmwArgs a{gdndims(*cfg), state, snapshots, in->q, in->k, in->v, in->beta, in->alpha, y,
-                 in->ntok};
-    const hipError_t e = cfg->kind == RSSM_KDA ? kda_rmw(a, strm(stream)) : gdn_rmw(a, strm(stream));
-    return e == hipSuccess ? RSSM_OK : RSSM_E_DEVICE;
+    if (!aligned16(state)) return RSSM_E_ARG;
+    return step_baseline_impl(cfg, state, nullptr, in, A, D, y, snapshots, stream);
+}
+
+rssm_status rssm_step_baseline_seqs(const rssm_config *cfg, float *const *seq_state,
+                                    const rssm_inputs *in, const float *A, const float *D, float *y,
+                                    float *snapshots, void *stream)
+{
+    if (!seq_state) return RSSM_E_ARG;
+    return step_baseline_impl(cfg, nullptr, seq_state, in, A, D, y, snapshots, stream);
 }
 
 rssm_status rssm_step_baseline_spec(const rssm_config *cfg, float *pool, const int32_t *slot_of,

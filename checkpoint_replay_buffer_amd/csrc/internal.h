@@ -96,6 +96,7 @@ struct M2RmwArgs {
     float *y;
     int ntok;
     const int32_t *slot_of;   // [B] committed slot per sequence, or nullptr
+    float *const *seq;        // [B] per-sequence state tiles [H,P,N] (instead of state), or nullptr
 };
 
 // Rings of the delta-rule layers (Gated DeltaNet; Kimi Delta Attention with a gate per key
@@ -150,12 +151,14 @@ struct GdnRmwArgs {
     float *o;
     int ntok;
     const int32_t *slot_of;   // [B] committed slot per sequence, or nullptr
+    float *const *seq;        // [B] per-sequence state tiles [H,dv,dk] (instead of state), or nullptr
 };
 
 // ---- launchers (return hipSuccess or the launch error) ----
 bool m2_supported(int P, int N);
 // Decode kernel choice. 0: every sequence is at ring position (a.uhead, a.ulen) and none fills
-// its ring; 1: no sequence fills its ring; 2: any sequence may fold.
+// its ring; 1: no sequence fills its ring; 2: any sequence may fold; 3: every sequence is at
+// (a.uhead, a.ulen) and fills its ring (Mamba-2 only).
 hipError_t m2_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s);
 hipError_t m2_verify(const M2StepArgs &a, bool bf16, hipStream_t s);
 size_t m2_lds_bytes(int P, int N, int W);   // dynamic LDS of the largest Mamba-2 kernel

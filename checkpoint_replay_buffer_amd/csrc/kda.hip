@@ -556,14 +556,15 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_rmw(GdnRmwArgs
     const size_t BH = (size_t)a.d.B * a.d.H, VK = (size_t)DV * DK;
     const size_t lo = (size_t)(rg * R) * DK + c0;          // lane block within a tile
     const size_t off = c.bh * VK + lo;
-    const float *src;
+    // source (updated in place when there are no snapshots) and first snapshot
+    float *src;
     float *snap0;
     if (a.slot_of) {
         const int sl = a.slot_of[c.b];
         src = a.state + ((size_t)sl * BH + c.bh) * VK + lo;
         snap0 = a.state + ((size_t)(sl < a.ntok ? a.ntok : 0) * BH + c.bh) * VK + lo;
     } else {
-        src = a.state + off;
+        src = a.seq ? a.seq[c.b] + (size_t)c.h * VK + lo : a.state + off;
         snap0 = a.snap ? a.snap + off : nullptr;
     }
     float4 S[R];
@@ -603,7 +604,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_rmw(GdnRmwArgs
     }
     if (!snap0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) st4_nt(a.state + off + (size_t)r * DK, S[r]);
+        for (int r = 0; r < R; ++r) st4_nt(src + (size_t)r * DK, S[r]);
     }
 }
 

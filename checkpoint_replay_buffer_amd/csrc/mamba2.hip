@@ -46,19 +46,28 @@ __device__ __forceinline__ void load_cols(float (&cc)[EPL], const float *src)
     }
 }
 
+// Decode kernel variants, chosen on the host from what it knows about the ring fill:
+//   kUniform  every sequence has the ring position (a.uhead, a.ulen) and none fills its ring:
+//             no device read is needed before the ring loads, which go out before the checkpoint
+//   kReplay   no sequence fills its ring; positions are read from the device, so the checkpoint
+//             read is issued first and the ring loads after the positions arrive
+//   kMayFold  any mix of replaying and folding sequences (positions read from the device)
+//   kAllFold  every sequence has the position (a.uhead, a.ulen) and fills its ring: all fold
+enum DecodeMode { kUniform = 0, kReplay = 1, kMayFold = 2, kAllFold = 3 };
+
 // Threads per workgroup of the Mamba-2 kernels for a P x N tile. WIDE gives each thread about
 // 4 float4 of the fp32 checkpoint (512 threads at 64 x 128), NARROW about 8 (256), SINGLE about
-// 2 (1024, for the conventional kernel over a single token). The fp32
-// decode, the fold and every decode launch that may fold take WIDE; verify and the replay-only
-// launches that read the bf16 copy take NARROW; the conventional kernel chooses by token count
-// (go_rmw). Each choice measured fastest in same-box comparisons.
+// 2 (1024, for the conventional kernel over a single token). The fp32 decode (every variant), the
+// fold and the bf16 launches in which every tile folds take WIDE; verify and the bf16 launches in
+// which most tiles replay (replay-only, or a mix) take NARROW; the conventional kernel chooses by
+// token count (go_rmw). Each choice measured fastest in same-box comparisons.
 template <int P, int N>
 struct M2Threads {
     static constexpr int NF4 = P * N / 4;
     static constexpr int WIDE = NF4 / 4 < 64 ? 64 : (NF4 / 4 > 512 ? 512 : NF4 / 4);
     static constexpr int NARROW = TileShape<P, N>::TPB;
     static constexpr int SINGLE = NF4 / 2 < 64 ? 64 : (NF4 / 2 > 1024 ? 1024 : NF4 / 2);
-    static constexpr int decode(bool bf16, bool may_fold) { return bf16 && !may_fold ? NARROW : WIDE; }
+    static constexpr int decode(bool bf16, int mode) { return bf16 && mode != kAllFold ? NARROW : WIDE; }
 };
 
 // bf16 read-copy layout: 16-byte loads (8 values) when the tile has enough of them for every
@@ -395,20 +404,14 @@ __device__ __forceinline__ void m2_fold_decode(const M2StepArgs &a, const Tile &
     }
 }
 
-// Decode kernel variants, chosen on the host from what it knows about the ring fill:
-//   kUniform  every sequence has the ring position (a.uhead, a.ulen) and none fills its ring:
-//             no device read is needed before the ring loads, which go out before the checkpoint
-//   kReplay   no sequence fills its ring; positions are read from the device, so the checkpoint
-//             read is issued first and the ring loads after the positions arrive
-//   kMayFold  any mix of replaying and folding sequences
-enum DecodeMode { kUniform = 0, kReplay = 1, kMayFold = 2 };
-
 template <int P, int N, bool BF16, int MODE>
-__global__ void __launch_bounds__((M2Threads<P, N>::decode(BF16, MODE == kMayFold))) k_m2_decode(M2StepArgs a)
+__global__ void __launch_bounds__((M2Threads<P, N>::decode(BF16, MODE))) k_m2_decode(M2StepArgs a)
 {
-    constexpr int TPB = M2Threads<P, N>::decode(BF16, MODE == kMayFold);
+    constexpr int TPB = M2Threads<P, N>::decode(BF16, MODE);
     extern __shared__ float smem[];
-    const Tile c = make_tile(a.d, a.A, a.D, MODE == kMayFold ? kContiguous : kRuns);
+    // the launches that fold take contiguous tile ranges per XCD (mixed launches too), the
+    // replay-only launches runs
+    const Tile c = make_tile(a.d, a.A, a.D, MODE >= kMayFold ? kContiguous : kRuns);
     const int B = a.d.B, W = c.W;
     bool fold = false;
     int head, len;
@@ -423,7 +426,16 @@ __global__ void __launch_bounds__((M2Threads<P, N>::decode(BF16, MODE == kMayFol
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
         m2_replay_decode<P, N, TPB, BF16, true>(a, c, head, len, tile, smem);
+    } else if constexpr (MODE == kAllFold) {
+        head = a.uhead;
+        len = a.ulen;
+        fold = true;
+        float4 acc[RowMap<P, N, TPB, 4>::R];
+        load_fp32_tile<P, N, TPB>(acc, a.S0, c);
+        m2_fold_decode<P, N, TPB, BF16>(a, c, head, len, acc, smem);
     } else if constexpr (!BF16) {
+        // a mix: the checkpoint read goes out before the position read, so the latter hides under
+        // it; the fold and the replay both start from the fp32 tile
         ReadTile<P, N, TPB, false> tile;
         tile.load(a, c);
         head = a.bk.in[c.b];
@@ -432,6 +444,8 @@ __global__ void __launch_bounds__((M2Threads<P, N>::decode(BF16, MODE == kMayFol
         if (fold) m2_fold_decode<P, N, TPB, false>(a, c, head, len, tile.v, smem);
         else m2_replay_decode<P, N, TPB, false, true>(a, c, head, len, tile, smem);
     } else {
+        // a mix read from the bf16 copy: the position first (a folding tile reads the fp32 tile, a
+        // replaying one the copy), then the tile, then the ring (the kReplay order)
         head = a.bk.in[c.b];
         len = a.bk.in[B + c.b];
         fold = len + 1 >= W;
@@ -441,7 +455,8 @@ __global__ void __launch_bounds__((M2Threads<P, N>::decode(BF16, MODE == kMayFol
             m2_fold_decode<P, N, TPB, true>(a, c, head, len, acc, smem);
         } else {
             ReadTile<P, N, TPB, true> tile;
-            m2_replay_decode<P, N, TPB, true, false>(a, c, head, len, tile, smem);
+            tile.load(a, c);
+            m2_replay_decode<P, N, TPB, true, true>(a, c, head, len, tile, smem);
         }
     }
     if (c.h == 0 && c.t == 0) {
@@ -677,14 +692,15 @@ __global__ void __launch_bounds__(TPB) k_m2_rmw(M2RmwArgs a)
     const size_t BH = (size_t)a.d.B * a.d.H, BG = (size_t)a.d.B * a.d.G, PN = (size_t)P * N;
     const size_t off = (size_t)(rg * R) * N + c0;       // lane block within a tile
     // source tile and the first snapshot tile (snapshot k is k * BH tiles further)
-    const float *src;
+    // source tile (updated in place when there are no snapshots), and the first snapshot tile
+    float *src;
     float *snap0;
     if (a.slot_of) {
         const int sl = a.slot_of[c.b];
         src = a.state + ((size_t)sl * BH + c.bh) * PN;
         snap0 = a.state + ((size_t)(sl < a.ntok ? a.ntok : 0) * BH + c.bh) * PN;
     } else {
-        src = a.state + c.bh * PN;
+        src = a.seq ? a.seq[c.b] + (size_t)c.h * PN : a.state + c.bh * PN;
         snap0 = a.snap ? a.snap + c.bh * PN : nullptr;
     }
     float4 S[R];
@@ -720,7 +736,7 @@ __global__ void __launch_bounds__(TPB) k_m2_rmw(M2RmwArgs a)
     }
     if (!snap0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) st4_nt(a.state + c.bh * PN + off + (size_t)r * N, S[r]);
+        for (int r = 0; r < R; ++r) st4_nt(src + off + (size_t)r * N, S[r]);
     }
 }
 
@@ -746,16 +762,18 @@ size_t verify_lds(int W)
 template <int P, int N>
 hipError_t go_decode(const M2StepArgs &a, bool bf16, int mode, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::decode(bf16, mode == kMayFold));
+    const dim3 grid(a.d.B * a.d.H), block(M2Threads<P, N>::decode(bf16, mode));
     const size_t lds = decode_lds<P, N>(a.d.W);
 #define RSSM_GO(b, md) hipLaunchKernelGGL((k_m2_decode<P, N, b, md>), grid, block, lds, s, a)
     if (bf16) {
         if (mode == kUniform) RSSM_GO(true, kUniform);
         else if (mode == kReplay) RSSM_GO(true, kReplay);
+        else if (mode == kAllFold) RSSM_GO(true, kAllFold);
         else RSSM_GO(true, kMayFold);
     } else {
         if (mode == kUniform) RSSM_GO(false, kUniform);
         else if (mode == kReplay) RSSM_GO(false, kReplay);
+        else if (mode == kAllFold) RSSM_GO(false, kAllFold);
         else RSSM_GO(false, kMayFold);
     }
 #undef RSSM_GO

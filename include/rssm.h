@@ -206,6 +206,16 @@ rssm_status rssm_step_baseline(const rssm_config *cfg, float *state, const rssm_
                                const float *A, const float *D, float *y, float *snapshots,
                                void *stream);
 
+/* rssm_step_baseline over per-sequence state tiles: seq_state [B] (a DEVICE array of device
+ * pointers, each 16-byte aligned) gives sequence b's [H,dim_v,dim_k] state, which the launch
+ * updates in place when snapshots is NULL (snapshots, if given, stay one contiguous
+ * [ntok,B,H,dim_v,dim_k] array). This is how a serving engine's conventional kernel reaches
+ * states kept in per-sequence slots of a cache pool. The pointers are read on the device; they
+ * must not alias each other. */
+rssm_status rssm_step_baseline_seqs(const rssm_config *cfg, float *const *seq_state,
+                                    const rssm_inputs *in, const float *A, const float *D,
+                                    float *y, float *snapshots, void *stream);
+
 /* Conventional speculative round, the comparator for rssm_verify + rssm_verify_commit (both layer
  * types; A and D are required for Mamba-2 and ignored for Gated DeltaNet).
  * Done conventionally, a rollback needs a copy of the state after every step (news.hamidun.com

@@ -579,3 +579,56 @@ def test_snapshot_comparator_rounds():
         st = host(pool)
         committed = np.stack([st[sl[b], b] for b in range(sh.batch)])
         assert normwise_err(committed, ref) < TOL, r
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
+def test_conventional_step_over_per_sequence_tiles(kind):
+    """rssm_step_baseline_seqs: the conventional step on states kept in scattered per-sequence
+    blocks (pointer array), in place and with snapshots, equals the contiguous form bit for bit
+    and the oracle within tolerance."""
+    B, H, d, W = 5, 3, 16, 4
+    if kind == "mamba2":
+        sh = wl.M2Shape(batch=B, nheads=H, ngroups=H, head_dim=d, d_state=d, window=W)
+        prm = wl.m2_params(sh, 13)
+        s0 = wl.m2_state0(sh, 13)
+        ins = wl.m2_token_inputs(sh, 13, 0, ntok=4)
+        d_in = m2_dev_tokens(sh, ins, 4)
+        A, D = dev(prm["A"]), dev(prm["D"])
+        cfg = rb.make_config(rb.RSSM_MAMBA2, B, H, H, d, d, W)
+    else:
+        sh = wl.GDNShape(batch=B, nheads=H, d_k=d, d_v=d, window=W)
+        gen = wl.gdn_token_inputs if kind == "gdn" else wl.kda_token_inputs
+        s0 = (wl.gdn_state0 if kind == "gdn" else wl.kda_state0)(sh, 13)
+        ins = gen(sh, 13, 0, ntok=4)
+        d_in = {k: dev(v) for k, v in ins.items()}
+        A = D = None
+        cfg = rb.make_config(rb.RSSM_GDN if kind == "gdn" else rb.RSSM_KDA, B, H, H, d, d, W)
+    # per-sequence blocks scattered in a larger pool, in reverse order with gaps
+    pool = torch.zeros(2 * B + 1, H, d, d, device="cuda")
+    slots = [2 * (B - 1 - b) + 1 for b in range(B)]
+    for b in range(B):
+        pool[slots[b]] = dev(s0[b])
+    ptrs = torch.tensor([pool[sl].data_ptr() for sl in slots], dtype=torch.int64, device="cuda")
+    st = dev(s0)
+    y1 = torch.empty(4, B, H, d, device="cuda")
+    y2 = torch.empty(4, B, H, d, device="cuda")
+    rb.step_baseline(cfg, st, y1, A, D, **d_in)
+    rb.step_baseline_seqs(cfg, ptrs, y2, A, D, **d_in)
+    assert np.array_equal(host(y1), host(y2))
+    got = host(pool)
+    for b in range(B):
+        assert np.array_equal(got[slots[b]], host(st)[b])
+    assert np.count_nonzero(got[[0, 2, 4, 6, 8, 10]]) == 0       # gaps untouched
+    snaps = torch.empty(4, B, H, d, d, device="cuda")
+    before = host(pool).copy()
+    rb.step_baseline_seqs(cfg, ptrs, y2, A, D, snapshots=snaps, **d_in)
+    assert np.array_equal(host(pool), before)                    # read-only with snapshots
+    ref = s0.astype(np.float64).copy()
+    for t in range(4):
+        if kind == "mamba2":
+            y_ref = m2_step(prm["A"], prm["D"], ins["x"][t], ins["B"][t], ins["C"][t], ins["dt"][t], ref)
+        else:
+            from oracle import gdn_step, kda_step
+            step = gdn_step if kind == "gdn" else kda_step
+            y_ref = step(*(ins[k][t] for k in ("q", "k", "v", "beta", "alpha")), ref)
+        assert normwise_err(host(y1)[t], y_ref) < TOL, t
