@@ -140,6 +140,7 @@ __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPr
     float4 s[IBW][KB];
     float *S0 = a.S0 + bh * (size_t)(DV * DK);
     ckpt_load<DV>(s, S0, t);
+    tile_loaded(s);
 
     int buf = 0;
     for (int t0 = 0; t0 < T; t0 += kChunk, buf ^= 1) {

@@ -23,6 +23,8 @@
 // S[16 ib' + c][16 kb + 4 g + r], ib' = w IBW + ib, r = 0..3. That float4 is the B operand of
 // C S^T (inner index 16 kb + 4 g + r in step r of k-block kb) and the accumulator of B^T (w X),
 // the transpose of the rank-16 update.
+#include <type_traits>
+
 #include "dev_common.h"
 #include "internal.h"
 #include "mfma_tile.h"
@@ -33,68 +35,59 @@ namespace {
 constexpr int kChunk = 16;
 constexpr int kMS = kChunk + 4;   // row stride of the 16 x 16 blocks in LDS
 
-// LDS floats: two staging buffers, each x [16][P+4], B and C [16][N+4], dt [16]; then one 16 x 16
-// partial of B C^T per wave, the weights w[t][j] [16][20], w[15][j] [16] and Lam_t [16]
+// LDS floats: two staging buffers of the rows read on both sides of the mid-chunk barrier, x
+// [16][P+4] and B [16][N+4]; one buffer of those read before it only, C [16][N+4] and dt [16];
+// then one 16 x 16 partial of B C^T per wave, the weights w[t][j] [16][20], w[15][j] [16] and
+// Lam_t [16]. At 64 x 128 that is 40,640 bytes: four workgroups fit the 160 KB of a CU.
 template <int P, int N>
 __host__ __device__ constexpr int prefill_buf_floats()
 {
-    return kChunk * (P + 4) + 2 * kChunk * (N + 4) + kChunk;
+    return kChunk * (P + 4) + kChunk * (N + 4);
 }
 template <int P, int N>
 __host__ __device__ constexpr int prefill_lds_floats()
 {
-    return 2 * prefill_buf_floats<P, N>() + (MfmaTile<P, N>::NW + 1) * kChunk * kMS + 2 * kChunk;
+    return 2 * prefill_buf_floats<P, N>() + kChunk * (N + 4) + kChunk
+         + (MfmaTile<P, N>::NW + 1) * kChunk * kMS + 2 * kChunk;
 }
 
-// sum_{lo < i <= hi} d[i] over the 16 step sizes of a chunk, in increasing i. The indices are
-// lane-dependent, so the terms outside the range are added as exact zeros instead of indexing
-// the register array (which would move it to scratch memory).
-__device__ __forceinline__ float range_sum(const float (&d)[kChunk], int lo, int hi)
+// Inclusive prefix sum over the 16 lanes of each row of the wave (lanes 16 g .. 16 g + 15): four
+// shifted adds across the row, the lanes shifted in from outside it reading zero.
+__device__ __forceinline__ float row_scan16(float v)
 {
-    float e = 0.f;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) e += (i > lo && i <= hi) ? d[i] : 0.f;
-    return e;
+#define RSSM_SHR(n) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + (n), 0xF, 0xF, true))
+    v += RSSM_SHR(1);
+    v += RSSM_SHR(2);
+    v += RSSM_SHR(4);
+    v += RSSM_SHR(8);
+#undef RSSM_SHR
+    return v;
 }
 
-// Decay weights of the chunk, one wave; lane (g, c) takes t = c and j = 4 g + r:
+// Decay weights of the chunk, spread over the NW waves of the workgroup; lane (g, c) of wave w
+// takes t = c and j = 4 g + r for r = w, w + NW, ... < 4:
 //     w[t][j] = dt_j exp(A sum_{j<i<=t} dt_i) (0 for j > t)  -> sh_wm[t][j]
-//     w[15][j], Lam_t = exp(A sum_{i<=t} dt_i) for t = 4 g + r   -> sh_wf, sh_lam (lanes c = 0)
+//     w[15][j] = dt_j exp(A sum_{j<i<=15} dt_i)              -> sh_wf (lanes c = 15)
+//     Lam_t = exp(A sum_{i<=t} dt_i)                        -> sh_lam (wave 0, lanes g = 0)
+// Every exponent is a sum of the step sizes between the two tokens, formed as a prefix sum over
+// the row of lanes c of dt_c masked to c > j: no differences of running sums.
+template <int NW>
 __device__ __forceinline__ void chunk_weights(const float *sh_dt, float Ah, float *sh_wm,
-                                              float *sh_wf, float *sh_lam)
+                                              float *sh_wf, float *sh_lam, int wv)
 {
     const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
-    float d[kChunk];
-#pragma unroll
-    for (int q = 0; q < kChunk; q += 4) {
-        const float4 v = ld4(sh_dt + q);
-        d[q] = v.x; d[q + 1] = v.y; d[q + 2] = v.z; d[q + 3] = v.w;
+    const float dc = sh_dt[cl];
+    for (int r = wv; r < 4; r += NW) {
+        const int j = 4 * g + r;
+        const float dj = sh_dt[j];
+        const float e = row_scan16(cl > j ? dc : 0.f);   // sum_{j<i<=c} dt_i
+        const float wm = j <= cl ? dj * expf(Ah * e) : 0.f;
+        sh_wm[cl * kMS + j] = wm;
+        if (cl == kChunk - 1) sh_wf[j] = wm;
     }
-    // this lane's step sizes d[4 g .. 4 g + 3] without indexing d by a lane-dependent value
-    const float4 dq = ld4(sh_dt + 4 * g);
-    const float dg[4] = {dq.x, dq.y, dq.z, dq.w};
-    // sum_{j<i<=t} d_i for j = 4 g + r, by adding d_{j+1} to the sum from j + 1 down
-    float sm[4], su[4];
-    sm[3] = range_sum(d, 4 * g + 3, cl);            // upper end t = c
-    su[3] = range_sum(d, 4 * g + 3, kChunk - 1);    // upper end 15 (fold weights)
-#pragma unroll
-    for (int r = 2; r >= 0; --r) {
-        sm[r] = sm[r + 1] + (4 * g + r + 1 <= cl ? dg[r + 1] : 0.f);
-        su[r] = su[r + 1] + dg[r + 1];
-    }
-    float wm[4], wf[4], lam[4];
-    float pre = range_sum(d, -1, 4 * g - 1);        // sum_{i < 4 g} d_i
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        wm[r] = 4 * g + r <= cl ? dg[r] * expf(Ah * sm[r]) : 0.f;
-        wf[r] = dg[r] * expf(Ah * su[r]);
-        pre += dg[r];
-        lam[r] = expf(Ah * pre);                    // exp(A sum_{i <= 4 g + r} d_i)
-    }
-    st4(sh_wm + cl * kMS + 4 * g, make_float4(wm[0], wm[1], wm[2], wm[3]));
-    if (cl == 0) {
-        st4(sh_wf + 4 * g, make_float4(wf[0], wf[1], wf[2], wf[3]));
-        st4(sh_lam + 4 * g, make_float4(lam[0], lam[1], lam[2], lam[3]));
+    if (wv == 0) {
+        const float lam = expf(Ah * row_scan16(dc));
+        if (g == 0) sh_lam[cl] = lam;
     }
 }
 
@@ -142,10 +135,22 @@ struct ChunkRows {
         }
     }
 
-    // rows of tokens t0 .. t0 + ct - 1; xb, bb, cb, db point at token t0's row of this tile
+    // rows of tokens t0 .. t0 + ct - 1 (zeros past them); xb, bb, cb, db point at token t0's row
+    // of this tile. A full chunk (every chunk but a ragged last one) loads without predicates.
     __device__ __forceinline__ void load(const float *xb, const float *bb, const float *cb,
                                          const float *db, size_t BH, int ct, int t)
     {
+        if (ct == kChunk) {
+#pragma unroll
+            for (int q = 0; q < XQ; ++q) x[q] = ld4(xb + xo[q]);
+#pragma unroll
+            for (int q = 0; q < BQ; ++q) {
+                b[q] = ld4(bb + bo[q]);
+                c[q] = ld4(cb + bo[q]);
+            }
+            dt = db[(size_t)(t & (kChunk - 1)) * BH];   // lanes t < 16 keep theirs
+            return;
+        }
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int q = 0; q < XQ; ++q) x[q] = xj[q] < ct ? ld4(xb + xo[q]) : z;
@@ -163,12 +168,12 @@ struct ChunkRows {
 #pragma unroll
         for (int q = 0; q < XQ; ++q) {
             const int i = t + q * TPB, j = i / PF, o = (i - j * PF) * 4;
-            if (i < kChunk * PF) st4(sh_x + j * XS + o, x[q]);
+            if (XQ * TPB == kChunk * PF || i < kChunk * PF) st4(sh_x + j * XS + o, x[q]);
         }
 #pragma unroll
         for (int q = 0; q < BQ; ++q) {
             const int i = t + q * TPB, j = i / NF, o = (i - j * NF) * 4;
-            if (i < kChunk * NF) {
+            if (BQ * TPB == kChunk * NF || i < kChunk * NF) {
                 st4(sh_B + j * BS + o, b[q]);
                 st4(sh_C + j * BS + o, c[q]);
             }
@@ -192,7 +197,9 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
     static_assert(KBW * NW == KB, "B C^T split");
     constexpr int BUF = prefill_buf_floats<P, N>();
     extern __shared__ float smem[];
-    float *sh_P = smem + 2 * BUF;          // [NW][16][kMS]  partials of B C^T
+    float *sh_C = smem + 2 * BUF;          // [16][BS]       C of the chunk
+    float *sh_dt = sh_C + kChunk * BS;     // [16]           dt of the chunk
+    float *sh_P = sh_dt + kChunk;          // [NW][16][kMS]  partials of B C^T
     float *sh_wm = sh_P + NW * kChunk * kMS;   // [16][kMS]  w[t][j] (0 for j > t)
     float *sh_wf = sh_wm + kChunk * kMS;   // [16]       w[15][j]
     float *sh_lam = sh_wf + kChunk;        // [16]       Lam_t
@@ -219,14 +226,17 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) s[ib][kb] = ld4_nt(S0 + off[ib] + 16 * kb);
     }
+    tile_loaded(s);
 
-    int buf = 0;
-    for (int t0 = 0; t0 < T; t0 += kChunk, buf ^= 1) {
-        const int ct = T - t0 < kChunk ? T - t0 : kChunk;
+    // One chunk of tokens t0 .. t0 + ct - 1. FULL (ct = 16, every chunk but a ragged last one)
+    // stores every output row without predicates, so the chunk is straight-line code.
+    auto chunk = [&](auto full, int t0, int buf) {
+        constexpr bool FULL = decltype(full)::value;
+        const int ct = FULL ? kChunk : T - t0;
         float *sh_x = smem + buf * BUF;
         float *sh_B = sh_x + kChunk * XS;
-        float *sh_C = sh_B + kChunk * BS;
-        float *sh_dt = sh_C + kChunk * BS;
+        // C and dt are read before the mid-chunk barrier only: every wave is past it before any
+        // wave stores the next chunk's, so they need one buffer; x and B are read after it too
         rows.store(sh_x, sh_B, sh_C, sh_dt, t);
         __syncthreads();
         if (t0 + kChunk < T) {             // the next chunk's rows, in flight during this chunk
@@ -236,7 +246,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
         }
 
         // 1. S-independent blocks first: every wave its share of B C^T (k-blocks wv KBW ..
-        //    wv KBW + KBW - 1), the last wave the decay weights of the chunk
+        //    wv KBW + KBW - 1) and of the decay weights of the chunk
         {
             v4f pp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -253,7 +263,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
             // [c][4 g + r], where every wave's lane (g, c) reads it back
             st4(sh_P + wv * kChunk * kMS + cl * kMS + 4 * g, make_float4(pp[0], pp[1], pp[2], pp[3]));
         }
-        if (wv == NW - 1) chunk_weights(sh_dt, Ah, sh_wm, sh_wf, sh_lam);
+        chunk_weights<NW>(sh_dt, Ah, sh_wm, sh_wf, sh_lam, wv);
         //    every wave: Z = C S^T for its i-blocks (S at the chunk start)
         v4f z[IBW];
 #pragma unroll
@@ -309,7 +319,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tt = 4 * g + r;
-                if (tt < ct) yc[(size_t)tt * BH * P] = yv[r];
+                if (FULL || tt < ct) yc[(size_t)tt * BH * P] = yv[r];
             }
             // 4. S <- Lam_15 S + B^T (w X): B operand w[15][j] x_j[i] for j = 4 g + r
             float wx[4];
@@ -328,7 +338,10 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
             }
         }
         mfma_settle();
-    }
+    };
+    int t0 = 0, buf = 0;
+    for (; t0 + kChunk <= T; t0 += kChunk, buf ^= 1) chunk(std::true_type{}, t0, buf);
+    if (t0 < T) chunk(std::false_type{}, t0, buf);
 
     // the final state is the new checkpoint (and its bf16 read copy); the ring is empty
 #pragma unroll

@@ -61,4 +61,18 @@ __device__ __forceinline__ void mfma_settle()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Completes the loads of a register tile before a loop that keeps it: an empty statement that
+// reads every element, so the wait for those loads sits here. Left in flight at the loop entry,
+// they would make each iteration wait for every memory operation issued before its first use of
+// the tile, the prefetch of the next iteration's inputs among them.
+template <int IBW, int KB>
+__device__ __forceinline__ void tile_loaded(const float4 (&s)[IBW][KB])
+{
+#pragma unroll
+    for (int ib = 0; ib < IBW; ++ib)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            asm volatile("" ::"v"(s[ib][kb].x), "v"(s[ib][kb].y), "v"(s[ib][kb].z), "v"(s[ib][kb].w));
+}
+
 }  // namespace rssm
