@@ -108,58 +108,41 @@ __device__ __forceinline__ float4 sum_partials(const float4 (&p)[NW])
 }
 
 // The chunk's rows of x, B, C and dt held in registers between their load and their LDS store.
-// The lane-dependent part of every address is fixed for the whole prompt and computed once; a
-// chunk only moves the (uniform) base pointers.
+// Lane t takes float4 i = t + q TPB of the chunk's rows (row i / PF of x, i / NF of B and C). The
+// addresses are formed at each load from t and the (uniform) row bases, not kept in registers
+// from one chunk to the next.
 template <int P, int N>
 struct ChunkRows {
     static constexpr int TPB = TileShape<P, N>::TPB, PF = P / 4, NF = N / 4;
     static constexpr int XQ = (kChunk * PF + TPB - 1) / TPB, BQ = (kChunk * NF + TPB - 1) / TPB;
     float4 x[XQ], b[BQ], c[BQ];
     float dt;
-    size_t xo[XQ], bo[BQ];   // element offsets from the chunk's first row
-    int xj[XQ], bj[BQ];      // token of the row within the chunk (kChunk: no row)
 
-    __device__ __forceinline__ void init(size_t BH, size_t BG, int t)
+    // rows of tokens t0 .. t0 + ct - 1 (zeros past them); xb, bb, cb, db point at token t0's row
+    // of this tile, rows BH (x, dt) or BG (B, C) apart. A full chunk (every chunk but a ragged
+    // last one) loads without predicates.
+    __device__ __forceinline__ void load(const float *xb, const float *bb, const float *cb,
+                                         const float *db, size_t BH, size_t BG, int ct, int t)
     {
+        asm volatile("" : "+v"(t));
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int q = 0; q < XQ; ++q) {
             const int i = t + q * TPB, j = i / PF, o = (i - j * PF) * 4;
-            xj[q] = i < kChunk * PF ? j : kChunk;
-            xo[q] = (size_t)j * BH * P + o;
+            const bool in = (XQ * TPB == kChunk * PF || i < kChunk * PF) && (ct == kChunk || j < ct);
+            x[q] = in ? ld4(xb + (size_t)j * BH * P + o) : z;
         }
 #pragma unroll
         for (int q = 0; q < BQ; ++q) {
             const int i = t + q * TPB, j = i / NF, o = (i - j * NF) * 4;
-            bj[q] = i < kChunk * NF ? j : kChunk;
-            bo[q] = (size_t)j * BG * N + o;
+            const bool in = (BQ * TPB == kChunk * NF || i < kChunk * NF) && (ct == kChunk || j < ct);
+            const size_t e = (size_t)j * BG * N + o;
+            b[q] = in ? ld4(bb + e) : z;
+            c[q] = in ? ld4(cb + e) : z;
         }
-    }
-
-    // rows of tokens t0 .. t0 + ct - 1 (zeros past them); xb, bb, cb, db point at token t0's row
-    // of this tile. A full chunk (every chunk but a ragged last one) loads without predicates.
-    __device__ __forceinline__ void load(const float *xb, const float *bb, const float *cb,
-                                         const float *db, size_t BH, int ct, int t)
-    {
-        if (ct == kChunk) {
-#pragma unroll
-            for (int q = 0; q < XQ; ++q) x[q] = ld4(xb + xo[q]);
-#pragma unroll
-            for (int q = 0; q < BQ; ++q) {
-                b[q] = ld4(bb + bo[q]);
-                c[q] = ld4(cb + bo[q]);
-            }
-            dt = db[(size_t)(t & (kChunk - 1)) * BH];   // lanes t < 16 keep theirs
-            return;
-        }
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int q = 0; q < XQ; ++q) x[q] = xj[q] < ct ? ld4(xb + xo[q]) : z;
-#pragma unroll
-        for (int q = 0; q < BQ; ++q) {
-            b[q] = bj[q] < ct ? ld4(bb + bo[q]) : z;
-            c[q] = bj[q] < ct ? ld4(cb + bo[q]) : z;
-        }
-        dt = t < ct ? db[(size_t)t * BH] : 0.f;
+        // a full chunk: lanes t >= 16 load a row too, and only lanes t < 16 keep theirs
+        const int jt = ct == kChunk ? (t & (kChunk - 1)) : t;
+        dt = ct == kChunk || t < ct ? db[(size_t)jt * BH] : 0.f;
     }
 
     __device__ __forceinline__ void store(float *sh_x, float *sh_B, float *sh_C, float *sh_dt, int t) const
@@ -188,11 +171,12 @@ struct ChunkRows {
 // after the second barrier every wave has what it needs for its outputs and its part of the
 // update.
 template <int P, int N, bool BF16>
-__global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2PrefillArgs a)
+__global__ void __launch_bounds__((TileShape<P, N>::TPB), 4) k_m2_prefill(M2PrefillArgs a)
 {
     using F = MfmaTile<P, N>;
     constexpr int NW = F::NW, IBW = F::IBW, KB = F::KB, XS = F::RS, BS = F::CS;
-    constexpr int NA = KB >= 4 ? 4 : KB;   // independent accumulators of the d_state products
+    constexpr int NA = KB >= 2 ? 2 : KB;   // independent accumulators of the d_state products
+                                           // (two: the registers of four waves per SIMD)
     constexpr int KBW = KB / NW;           // k-blocks of B C^T per wave
     static_assert(KBW * NW == KB, "B C^T split");
     constexpr int BUF = prefill_buf_floats<P, N>();
@@ -215,8 +199,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
     const float *x0 = a.x + bh * P, *b0 = a.Bm + bg * N, *c0 = a.C + bg * N, *d0 = a.dt + bh;
     float *y0 = a.y + bh * P;
     ChunkRows<P, N> rows;
-    rows.init(BH, BG, t);
-    rows.load(x0, b0, c0, d0, BH, T < kChunk ? T : kChunk, t);
+    rows.load(x0, b0, c0, d0, BH, BG, T < kChunk ? T : kChunk, t);
     float4 s[IBW][KB];
     float *S0 = a.S0 + bh * (size_t)(P * N);
     int off[IBW];
@@ -241,7 +224,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
         __syncthreads();
         if (t0 + kChunk < T) {             // the next chunk's rows, in flight during this chunk
             const size_t t1 = t0 + kChunk;
-            rows.load(x0 + t1 * BH * P, b0 + t1 * BG * N, c0 + t1 * BG * N, d0 + t1 * BH, BH,
+            rows.load(x0 + t1 * BH * P, b0 + t1 * BG * N, c0 + t1 * BG * N, d0 + t1 * BH, BH, BG,
                       T - (int)t1 < kChunk ? T - (int)t1 : kChunk, t);
         }
 
@@ -315,12 +298,12 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 3) k_m2_prefill(M2Pref
             // keep the reads of the accumulators here, next to their chains, rather than sunk into
             // the conditional stores below
             asm volatile("" ::"v"(yv[0]), "v"(yv[1]), "v"(yv[2]), "v"(yv[3]));
-            float *yc = y0 + (size_t)t0 * BH * P + i;
+            int iy = i;                     // the output address is formed here, each chunk
+            asm volatile("" : "+v"(iy));
+            float *yc = y0 + (size_t)(t0 + 4 * g) * BH * P + iy;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tt = 4 * g + r;
-                if (FULL || tt < ct) yc[(size_t)tt * BH * P] = yv[r];
-            }
+            for (int r = 0; r < 4; ++r)
+                if (FULL || 4 * g + r < ct) yc[(size_t)r * BH * P] = yv[r];
             // 4. S <- Lam_15 S + B^T (w X): B operand w[15][j] x_j[i] for j = 4 g + r
             float wx[4];
 #pragma unroll
