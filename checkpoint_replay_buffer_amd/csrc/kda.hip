@@ -440,24 +440,29 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_fold(GdnFoldAr
 // speculative verify: K drafts, outputs only, checkpoint streamed once
 // ------------------------------------------------------------------------------------------
 // Drafts k = 0..K-1 become entries len_e + k; draft k's output is the replay over the first
-// m_k = len_e + k + 1 entries with query q_k: one wave per draft runs the recursion, then every
-// draft's output is S0 r_k + sum_j beta_j c_{k,j} v_j on the register tile. Sequences whose ring
-// cannot take the drafts (len + K > W) first fold their len committed entries.
+// m_k = len_e + k + 1 entries with query q_k: one wave per draft runs the recursion, then the
+// outputs of 16 drafts at a time are O = R S0^T + Cf V on the matrix cores, with R the rows r_k
+// and Cf[k][j] = beta_j c_{k,j} (zero for j >= m_k). Sequences whose ring cannot take the drafts
+// (len + K > W) first fold their len committed entries. NJB = 16-entry blocks of the ring.
 template <int DV, int DK>
 __host__ __device__ constexpr int kda_verify_lds(int W, int K)
 {
-    // rows of up to W entries, the drafts' queries (then their r rows) [K][KS], coefficients
-    // [K][W + 4]; the fold of the committed entries uses the same rows
-    return Rows<DV, DK>::floats(W) + K * (DK + 4) + K * (W + 4);
+    // rows of up to W entries (16 NJB, the value rows past the entries zeroed), the drafts'
+    // queries (then their r rows) [K16][KS] and coefficients [K16][16 NJB + 4]; the fold of the
+    // committed entries uses the same rows
+    const int W16 = (W + 15) / 16 * 16, K16 = (K + 15) / 16 * 16;
+    return Rows<DV, DK>::floats(W16) + K16 * (DK + 4) + K16 * (W16 + 4);
 }
 
-template <int DV, int DK>
+template <int DV, int DK, int NJB>
 __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_verify(GdnStepArgs a)
 {
     using F = MfmaTile<DV, DK>;
     using RW = Rows<DV, DK>;
     constexpr int TPB = F::TPB, IBW = F::IBW, KB = F::KB, NW = F::NW;
     constexpr int KF = DK / 4, VF = DV / 4, QS = DK + 4;
+    constexpr int NE = 16 * NJB, CS = NE + 4;   // entry rows on the matrix cores
+    constexpr int NA = KB >= 2 ? 2 : 1;
     extern __shared__ float smem[];
     const KTile c = make_ktile(a.d, kRuns);
     const int B = a.d.B, W = c.W, K = a.ntok, t = c.t, lane = t & 63;
@@ -467,14 +472,14 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_verify(GdnStep
     const bool prefold = len + K > W;
     const int head_e = prefold ? (head + len) % W : head, len_e = prefold ? 0 : len;
     const int ne = len_e + K;
+    const int K16 = (K + 15) & ~15;
     float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
-    float *sh_k = smem;                      // [W][KS]
-    float *sh_a = sh_k + W * RW::KS;         // [W][KS]
-    float *sh_v = sh_a + W * RW::KS;         // [W][VS]
-    float *sh_be = sh_v + W * RW::VS;        // [W]
-    float *sh_q = sh_be + W;                 // [K][QS]  q_k, then r_k
-    float *sh_cf = sh_q + K * QS;            // [K][W+4] beta_j c_{k,j}
-    const int CS = W + 4;
+    float *sh_k = smem;                      // [NE][KS]
+    float *sh_a = sh_k + NE * RW::KS;        // [NE][KS]
+    float *sh_v = sh_a + NE * RW::KS;        // [NE][VS]
+    float *sh_be = sh_v + NE * RW::VS;       // [NE]
+    float *sh_q = sh_be + NE;                // [K16][QS]  q_k, then r_k
+    float *sh_cf = sh_q + K16 * QS;          // [K16][CS]  beta_j c_{k,j}
     float4 s[IBW][KB];
     if (prefold) {
         for (int j = t; j < len; j += TPB) sh_be[j] = a.ring.beta[c.rh + (head + j) % W];
@@ -486,12 +491,18 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_verify(GdnStep
         __syncthreads();                     // the rows are restaged below
     }
     // committed entries [0, len_e) from the ring, then the K drafts (token-major, BH tiles apart);
-    // the checkpoint is read after their loads went out (unless it was folded above)
+    // the checkpoint is read after their loads went out (unless it was folded above); the value
+    // rows past the entries are zeroed (their coefficients are zero, and 0 times stale LDS
+    // contents could be a NaN)
     for (int j = t; j < ne; j += TPB)
         sh_be[j] = j < len_e ? a.ring.beta[c.rh + (head_e + j) % W] : a.beta[(size_t)(j - len_e) * BH + c.bh];
     const EntryRows<DV, DK> er{a.ring, c, head_e, len_e, a.k + c.bh * DK, a.alpha + c.bh * DK,
                                a.v + c.bh * DV, BH, sh_k, sh_a, sh_v};
     stage_rows<DV, DK, TPB>(er, ne, [&] { if (!prefold) ckpt_load<DV>(s, S0, t); });
+    for (int i = t; i < (NE - ne) * VF; i += TPB) {
+        const int j = i / VF, o = 4 * (i - j * VF);
+        st4(sh_v + (ne + j) * RW::VS + o, make_float4(0.f, 0.f, 0.f, 0.f));
+    }
     for (int i = t; i < K * KF; i += TPB) {
         const int k = i / KF, o = 4 * (i - k * KF);
         st4(sh_q + k * QS + o, ld4(a.q + ((size_t)k * BH + c.bh) * DK + o));
@@ -507,20 +518,43 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_verify(GdnStep
     }
     __syncthreads();
 
-    // o_k = S0 r_k + sum_{j < m_k} beta_j c_{k,j} v_j
-    for (int k = 0; k < K; ++k) {
-        const int mk = len_e + k + 1;
+    // O = R S0^T + Cf V, 16 drafts at a time: lane (g, c) of i-block ib ends with draft
+    // 16 db + 4 g + r, row i = 16 ib' + c (the rows of R and Cf past K only reach outputs past K)
+    for (int db = 0; db < K16; db += 16) {
 #pragma unroll
         for (int ib = 0; ib < IBW; ++ib) {
-            const int row = 16 * (wv * IBW + ib) + cl;
-            float u = 0.f;
-            for (int j = g; j < mk; j += 4) u += sh_cf[k * CS + j] * sh_v[j * RW::VS + row];
-            float p = tile_gemv_row<DV, DK>(s, ib, sh_q + k * QS) + u;
-            p += bfly<16>(p);
-            p += __shfl_xor(p, 32);
-            if (g == 0) a.o[((size_t)k * BH + c.bh) * DV + row] = p;
+            const int i = 16 * (wv * IBW + ib) + cl;
+            v4f zp[NA];
+#pragma unroll
+            for (int n = 0; n < NA; ++n) zp[n] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const float4 rv = ld4(sh_q + (db + cl) * QS + 16 * kb + 4 * g);   // A: R[c][16 kb + 4 g + r]
+                v4f &z = zp[kb % NA];
+                z = mfma4(rv.x, s[ib][kb].x, z);
+                z = mfma4(rv.y, s[ib][kb].y, z);
+                z = mfma4(rv.z, s[ib][kb].z, z);
+                z = mfma4(rv.w, s[ib][kb].w, z);
+            }
+            v4f u = tree_sum<NA>(zp);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const float *cf = sh_cf + (db + cl) * CS + 16 * jb + 4 * g;      // A: Cf[c][16 jb + 4 g + r]
+                const float *vc = sh_v + (16 * jb + 4 * g) * RW::VS + i;       // B: V[16 jb + 4 g + r][i]
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u = mfma4(cf[r], vc[r * RW::VS], u);
+            }
+            const float ov[4] = {u[0], u[1], u[2], u[3]};
+            // the accumulators are read here, not inside the conditional stores
+            asm volatile("" ::"v"(ov[0]), "v"(ov[1]), "v"(ov[2]), "v"(ov[3]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k = db + 4 * g + r;
+                if (k < K) a.o[((size_t)k * BH + c.bh) * DV + i] = ov[r];
+            }
         }
     }
+    mfma_settle();
 
     // append the drafts as entries len_e .. ne - 1 (every ring read is done)
     for (int i = t; i < K * KF; i += TPB) {
@@ -636,7 +670,8 @@ hipError_t go_verify(const GdnStepArgs &a, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(TileShape<DV, DK>::TPB);
     const size_t lds = 4 * (size_t)kda_verify_lds<DV, DK>(a.d.W, a.ntok);
-    hipLaunchKernelGGL((k_kda_verify<DV, DK>), grid, block, lds, s, a);
+    if (a.d.W > 16) hipLaunchKernelGGL((k_kda_verify<DV, DK, 2>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_kda_verify<DV, DK, 1>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 

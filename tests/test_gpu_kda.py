@@ -100,7 +100,7 @@ def test_kda_consolidate_and_masked_init(d, W):
 
 
 @pytest.mark.parametrize("d,W,K", [(16, 8, 3), (16, 4, 4), (64, 16, 6), (128, 16, 6),
-                                   (128, 24, 8), (64, 1, 1)])
+                                   (128, 24, 8), (64, 1, 1), (16, 20, 17), (64, 32, 20)])
 def test_kda_speculative_rounds(d, W, K):
     """Rounds of K drafts committed with seeded, full and empty acceptances or discarded, decode
     steps between some rounds: every draft output, the bookkeeping and the materialised state."""
