@@ -46,12 +46,13 @@ __device__ __forceinline__ v4f row_dots16(const float *x, const float *y)
 
 // T by forward substitution over NP entries (a power of two, at most 64), one column per lane
 // (q = lane % NP) held in registers; the Gram rows (G[t][i] at sh_G[t GS + i], i < t) and the betas
-// are read at addresses common to the wave. Rows with beta = 0 (padding) come out zero.
-template <int NP, int GS, int TS>
-__device__ __forceinline__ void t_solve_regs(const float *sh_G, const float *sh_be, float *sh_T)
+// are read at addresses common to the wave. Rows with beta = 0 (padding) come out zero. The
+// substitution and the store are separate steps, so that a caller can place other work between
+// them in the same straight-line code.
+template <int NP, int GS>
+__device__ __forceinline__ void t_solve_cols(const float *sh_G, const float *sh_be, float (&tq)[NP])
 {
-    const int lane = threadIdx.x & 63, q = lane & (NP - 1);
-    float tq[NP];
+    const int q = threadIdx.x & (NP - 1);
 #pragma unroll
     for (int t = 0; t < NP; ++t) {
         float acc = 0.f;
@@ -59,10 +60,24 @@ __device__ __forceinline__ void t_solve_regs(const float *sh_G, const float *sh_
         for (int i = 0; i < t; ++i) acc = fmaf(sh_G[t * GS + i], tq[i], acc);
         tq[t] = sh_be[t] * ((t == q ? 1.f : 0.f) - acc);
     }
+}
+
+template <int NP, int TS>
+__device__ __forceinline__ void t_store_cols(const float (&tq)[NP], float *sh_T)
+{
+    const int lane = threadIdx.x & 63, q = lane & (NP - 1);
     if (lane < NP) {
 #pragma unroll
         for (int t = 0; t < NP; ++t) sh_T[t * TS + q] = tq[t];
     }
+}
+
+template <int NP, int GS, int TS>
+__device__ __forceinline__ void t_solve_regs(const float *sh_G, const float *sh_be, float *sh_T)
+{
+    float tq[NP];
+    t_solve_cols<NP, GS>(sh_G, sh_be, tq);
+    t_store_cols<NP, TS>(tq, sh_T);
 }
 
 // Decay row of lane l < 16 for entries 0..p applied (p < NP): R[l][q] = prod_{q<i<=p} alpha_i for

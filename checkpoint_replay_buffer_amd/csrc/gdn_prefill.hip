@@ -117,7 +117,8 @@ __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPr
 {
     using F = MfmaTile<DV, DK, GpShape<DV, DK>::NW>;
     constexpr int NW = F::NW, IBW = F::IBW, KB = F::KB, KS = F::CS, VS = F::RS;
-    constexpr int NA = KB >= 4 ? 4 : KB;   // independent accumulators of the d_k products
+    constexpr int NA = KB >= 2 ? 2 : KB;   // independent accumulators of the d_k products
+                                           // (two: wave 0 keeps its T column registers beside them)
     constexpr int BUF = gp_buf_floats<DV, DK>();
     extern __shared__ float smem[];
     float *sh_G = smem + 2 * BUF;          // [16][kTS]  k_i . k_t
@@ -160,45 +161,59 @@ __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPr
 
         // 1. the chunk's S-independent blocks first, so that their latency overlaps the other
         //    waves' matrix work: wave 0 the Gram block and T, wave 1 the masked Q K^T, the last
-        //    wave the decays (one wave does all three when it is alone)
+        //    wave the decays (one wave does all three when it is alone); then every wave
+        //    F = K S^T and Qs = Q S^T for its i-blocks (S at the chunk start). Wave 0's forward
+        //    substitution sits in the same straight-line code as its products, so that its LDS
+        //    waits interleave with the matrix-core chains; its store of T comes after them.
+        v4f fz[IBW], qs[IBW];
+        auto products = [&]() {
+#pragma unroll
+            for (int ib = 0; ib < IBW; ++ib) {
+                v4f fp[NA], qp[NA];
+#pragma unroll
+                for (int p = 0; p < NA; ++p) fp[p] = qp[p] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);
+                    const float4 qv = ld4(sh_q + cl * KS + 16 * kb + 4 * g);
+                    v4f &f = fp[kb % NA], &x = qp[kb % NA];
+                    f = mfma4(kv.x, s[ib][kb].x, f);
+                    f = mfma4(kv.y, s[ib][kb].y, f);
+                    f = mfma4(kv.z, s[ib][kb].z, f);
+                    f = mfma4(kv.w, s[ib][kb].w, f);
+                    x = mfma4(qv.x, s[ib][kb].x, x);
+                    x = mfma4(qv.y, s[ib][kb].y, x);
+                    x = mfma4(qv.z, s[ib][kb].z, x);
+                    x = mfma4(qv.w, s[ib][kb].w, x);
+                }
+                fz[ib] = tree_sum<NA>(fp);     // (S k_q)[i] for q = 4 g + r, i = 16 ib' + c
+                qs[ib] = tree_sum<NA>(qp);     // (S q_t)[i] for t = 4 g + r
+            }
+        };
+        auto q_kt = [&]() {
+            const v4f qk = row_dots16<KB, KS, NA, false>(sh_q, sh_k);     // q_{4g+r} . k_c
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sh_A[(4 * g + r) * kTS + cl] = cl <= 4 * g + r ? qk[r] : 0.f;
+        };
         if (wv == 0) {
+            if constexpr (NW == 1) {
+                q_kt();
+                decay_row<kChunk, kTS>(sh_al, lane, sh_R, sh_gam);
+            }
             const v4f gk = row_dots16<KB, KS, NA, true>(sh_k, sh_k);      // k_{4g+r} . k_c
 #pragma unroll
             for (int r = 0; r < 4; ++r) sh_G[(4 * g + r) * kTS + cl] = gk[r];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            t_solve_regs<kChunk, kTS, kTS>(sh_G, sh_be, sh_T);
-        }
-        if (wv == (NW > 1 ? 1 : 0)) {
-            const v4f qk = row_dots16<KB, KS, NA, false>(sh_q, sh_k);     // q_{4g+r} . k_c
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sh_A[(4 * g + r) * kTS + cl] = cl <= 4 * g + r ? qk[r] : 0.f;
-        }
-        if (wv == NW - 1) decay_row<kChunk, kTS>(sh_al, lane, sh_R, sh_gam);
-        //    every wave: F = K S^T and Qs = Q S^T for its i-blocks (S at the chunk start)
-        v4f fz[IBW], qs[IBW];
-#pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            v4f fp[NA], qp[NA];
-#pragma unroll
-            for (int p = 0; p < NA; ++p) fp[p] = qp[p] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float4 kv = ld4(sh_k + cl * KS + 16 * kb + 4 * g);
-                const float4 qv = ld4(sh_q + cl * KS + 16 * kb + 4 * g);
-                v4f &f = fp[kb % NA], &x = qp[kb % NA];
-                f = mfma4(kv.x, s[ib][kb].x, f);
-                f = mfma4(kv.y, s[ib][kb].y, f);
-                f = mfma4(kv.z, s[ib][kb].z, f);
-                f = mfma4(kv.w, s[ib][kb].w, f);
-                x = mfma4(qv.x, s[ib][kb].x, x);
-                x = mfma4(qv.y, s[ib][kb].y, x);
-                x = mfma4(qv.z, s[ib][kb].z, x);
-                x = mfma4(qv.w, s[ib][kb].w, x);
-            }
-            fz[ib] = tree_sum<NA>(fp);     // (S k_q)[i] for q = 4 g + r, i = 16 ib' + c
-            qs[ib] = tree_sum<NA>(qp);     // (S q_t)[i] for t = 4 g + r
+            float tq[kChunk];
+            t_solve_cols<kChunk, kTS>(sh_G, sh_be, tq);
+            products();
+            t_store_cols<kChunk, kTS>(tq, sh_T);
+        } else {
+            if (wv == 1) q_kt();
+            if (wv == NW - 1) decay_row<kChunk, kTS>(sh_al, lane, sh_R, sh_gam);
+            products();
         }
         mfma_settle();
         __syncthreads();
