@@ -354,7 +354,7 @@ def run_m2(args, torch, rb, wl):
     }
     if fol:
         line["fold_steps"] = {
-            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kMayFold> (the step that fills every ring)",
+            "kernel": f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kAllFold> (the step that fills every ring)",
             "achieved_gbs": round(fol_bytes / fol_s / 1e9, 1),
             "alg_bytes_per_launch": round(fol_bytes / len(fol)),
             "avg_launch_us": round(1e6 * fol_s / len(fol), 2),
