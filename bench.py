@@ -194,16 +194,23 @@ def run_m2(args, torch, rb, wl):
     ctx.set_params(A, D)
     y = torch.empty(B, H, P, device="cuda")
     K, Wm = args.steps, args.warmup
-    start_len = np.arange(B) % W if args.stagger else np.zeros(B, dtype=np.int64)
+    # lock-step: the timed steps start at ring fill `pre`, so that K steps hold ceil(K / W) folds
+    # (never fewer than the steady state's K / W when K is not a multiple of W)
+    pre = 0 if args.stagger or args.graph else (W - K % W) % W
+    start_len = np.arange(B) % W if args.stagger else np.full(B, pre, dtype=np.int64)
     new_len = torch.from_numpy(start_len.astype(np.int32)).cuda()
 
     def restart():
-        """Back to the checkpoint; with --stagger, then to ring fill b mod W (untimed)."""
+        """Back to the checkpoint; then (untimed) to ring fill b mod W with --stagger, or to the
+        common fill `pre`."""
         ctx.init_checkpoint(s0)
         if args.stagger:
             for t in range(W - 1):
                 ctx.decode_step(y, **pool[(pool_n - 1 - t) % pool_n])
             ctx.rollback(new_len)
+        else:
+            for t in range(pre):
+                ctx.decode_step(y, **pool[(pool_n - 1 - t) % pool_n])
 
     # warm-up, then restart so the timed steps see the schedule from its start
     restart()
@@ -295,8 +302,8 @@ def run_m2(args, torch, rb, wl):
         kname = f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kMayFold> (mixed: 1/{W} of the tiles fold)"
         tkey = "decode_stagger_bf16" if bf16 else "decode_stagger"
     else:
-        rep = [t for t in range(K) if t % W != W - 1]
-        fol = [t for t in range(K) if t % W == W - 1]
+        rep = [t for t in range(K) if (pre + t) % W != W - 1]
+        fol = [t for t in range(K) if (pre + t) % W == W - 1]
         kname = f"k_m2_decode<64,128,{'true' if bf16 else 'false'},kUniform> (steps that replay)"
         tkey = "decode_replay_bf16" if bf16 else "decode_replay"
     rep_bytes = sum(per[t][0] for t in rep)
@@ -335,7 +342,8 @@ def run_m2(args, torch, rb, wl):
                    "batch": B, "heads": H, "head_dim": P, "d_state": N, "window": W,
                    "groups": sh.ngroups, "input_pool_slots": pool_n,
                    "ring_fill": "staggered: sequence b starts at b mod W entries" if args.stagger
-                   else "lock-step: every sequence starts from an empty ring",
+                   else f"lock-step: every sequence starts at {pre} entries "
+                        f"({sum(1 for t in range(K) if (pre + t) % W == W - 1)} folding steps in {K})",
                    "launch": "hip graph of 2 W steps, replayed" if args.graph else "eager"},
         "value_is": "alg_gbs: every byte the method moves per step (checkpoint reads, the fold's "
                     "read + write, ring reads and appends, inputs, outputs) / wall time",
@@ -939,10 +947,18 @@ def run_gdn(args, torch, rb, wl, layer="gdn"):
     gen_s = time.time() - t0
     ctx = rb.Context(layer, B, H, DV, DK, W)
     o = torch.empty(B, H, DV, device="cuda")
-    ctx.init_checkpoint(s0)
+    # the timed steps start at ring fill `pre`: K steps hold ceil(K / W) folds
+    pre = 0 if args.graph else (W - K % W) % W
+
+    def restart():
+        ctx.init_checkpoint(s0)
+        for t in range(pre):
+            ctx.decode_step(o, **pool[(S - 1 - t) % S])
+
+    restart()
     for t in range(Wm):
         ctx.decode_step(o, **pool[t % S])
-    ctx.init_checkpoint(s0)
+    restart()
     torch.cuda.synchronize()
     reps = None
     if not args.graph:
@@ -953,9 +969,9 @@ def run_gdn(args, torch, rb, wl, layer="gdn"):
         ev[1].record()
         torch.cuda.synchronize()
         total_ms = ev[0].elapsed_time(ev[1])
-        reps = _repeat_ms(torch, total_ms, args.reps, lambda: ctx.init_checkpoint(s0),
+        reps = _repeat_ms(torch, total_ms, args.reps, restart,
                           lambda t: ctx.decode_step(o, **pool[t % S]), K)
-    ctx.init_checkpoint(s0)
+    restart()
     torch.cuda.synchronize()
     evl = _events(torch, 2 * K)
     for t in range(K):
@@ -969,7 +985,7 @@ def run_gdn(args, torch, rb, wl, layer="gdn"):
         total_ms = _graph_time(torch, S, lambda t: ctx.decode_step(o, **pool[t]), 1, K // S)
         h, l, n, e = ctx.bookkeeping()
         assert e == 0 and l[0] == 0, "unexpected bookkeeping after the graph replays"
-    alg = sum(gdn_bytes(DV, DK, W, t % W, ga) for t in range(K)) * B * H
+    alg = sum(gdn_bytes(DV, DK, W, (pre + t) % W, ga) for t in range(K)) * B * H
     cfg = rb.make_config(getattr(rb, L["kind"]), B, H, H, DV, DK, W)
     st = s0.clone()
     o1 = torch.empty(1, B, H, DV, device="cuda")
@@ -989,10 +1005,10 @@ def run_gdn(args, torch, rb, wl, layer="gdn"):
         torch.cuda.synchronize()
         rmw_s = ev2[0].elapsed_time(ev2[1]) / 1e3
     rmw_bytes = (2 * DV * DK * 4 + (2 * DK + DV + 1 + ga) * 4 + DV * 4) * B * H * K
-    rep = [t for t in range(K) if t % W != W - 1]
-    fol = [t for t in range(K) if t % W == W - 1]
-    rep_b = sum(gdn_bytes(DV, DK, W, t % W, ga) for t in rep) * B * H
-    fol_b = sum(gdn_bytes(DV, DK, W, t % W, ga) for t in fol) * B * H
+    rep = [t for t in range(K) if (pre + t) % W != W - 1]
+    fol = [t for t in range(K) if (pre + t) % W == W - 1]
+    rep_b = sum(gdn_bytes(DV, DK, W, (pre + t) % W, ga) for t in rep) * B * H
+    fol_b = sum(gdn_bytes(DV, DK, W, (pre + t) % W, ga) for t in fol) * B * H
     rep_s = sum(launch_ms[t] for t in rep) / 1e3
     fol_s = sum(launch_ms[t] for t in fol) / 1e3
     replay_s = total_ms / 1e3
@@ -1005,6 +1021,8 @@ def run_gdn(args, torch, rb, wl, layer="gdn"):
         "data": L["data"],
         "config": {"workload": f"{layer}_decode_b{B}_h{H}_dk{DK}_dv{DV}_w{W}" + ("_graph" if args.graph else ""),
                    "batch": B, "heads": H, "d_k": DK, "d_v": DV, "window": W, "input_pool_slots": S,
+                   "ring_fill": f"lock-step: every sequence starts at {pre} entries "
+                                f"({sum(1 for t in range(K) if (pre + t) % W == W - 1)} folding steps in {K})",
                    "launch": "hip graph of 2 W steps, replayed" if args.graph else "eager"},
         "pct_hbm_peak": round(100 * alg / replay_s / 1e9 / HBM_PEAK_GBS, 2),
         "ms_per_step_reps": reps,
