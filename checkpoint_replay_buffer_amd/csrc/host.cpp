@@ -131,6 +131,7 @@ rssm_status check_inputs(const rssm_config &c, const rssm_inputs *in)
     } else {
         if (!aligned16(in->q) || !aligned16(in->k) || !aligned16(in->v) || !in->beta || !in->alpha)
             return RSSM_E_ARG;
+        if (c.kind == RSSM_KDA && !aligned16(in->alpha)) return RSSM_E_ARG;   // gate rows read as float4
     }
     return RSSM_OK;
 }
@@ -385,7 +386,6 @@ rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *s
     const rssm_config &c = ctx->cfg;
     if ((s = check_inputs(c, in)) != RSSM_OK) return s;
     if (!aligned16(y)) return RSSM_E_ARG;
-    if (c.kind == RSSM_KDA) return RSSM_E_UNSUPPORTED;
     if (ctx->pending) return RSSM_E_STATE;
     if (ctx->hi > 0 && (s = rssm_consolidate(ctx, 1, stream)) != RSSM_OK) return s;
     if (c.kind == RSSM_MAMBA2) {
@@ -395,7 +395,8 @@ rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *s
     } else {
         GdnPrefillArgs a{gdndims(c), flip(ctx), ctx->S0, in->q, in->k, in->v, in->beta, in->alpha,
                          y, in->ntok};
-        s = launched(ctx, gdn_prefill(a, strm(stream)), true);
+        s = launched(ctx, c.kind == RSSM_KDA ? kda_prefill(a, strm(stream)) : gdn_prefill(a, strm(stream)),
+                     true);
     }
     if (s == RSSM_OK) {
         ctx->lo = ctx->hi = 0;

@@ -181,6 +181,7 @@ hipError_t kda_decode(const GdnStepArgs &a, int mode, hipStream_t s);   // mode 
 hipError_t kda_fold(const GdnFoldArgs &a, hipStream_t s);
 hipError_t kda_rmw(const GdnRmwArgs &a, hipStream_t s);
 hipError_t kda_verify(const GdnStepArgs &a, hipStream_t s);
+hipError_t kda_prefill(const GdnPrefillArgs &a, hipStream_t s);
 
 // ckpt_dv > 0: the tiles are Gated DeltaNet checkpoints with ckpt_dv rows, stored in the layout
 // of gdn_layout.h; 0: row-major (Mamba-2).

@@ -107,7 +107,7 @@ typedef struct {
 /* Inputs of ntok consecutive tokens, token-major (leading axis ntok).
  * Mamba-2: x [ntok,B,H,P], B and C [ntok,B,G,N], dt [ntok,B,H] (dt > 0, already discretised).
  * GDN:     q and k [ntok,B,H,dk], v [ntok,B,H,dv], beta and alpha [ntok,B,H].
- * KDA:     as GDN, but alpha [ntok,B,H,dk] (one forget gate per key channel).
+ * KDA:     as GDN, but alpha [ntok,B,H,dk] (one forget gate per key channel), 16-byte aligned.
  * Fields of the other kind are ignored and may be NULL. */
 typedef struct {
     int32_t ntok;
@@ -155,7 +155,8 @@ rssm_status rssm_decode_step(rssm_ctx *ctx, const rssm_inputs *in, float *y, voi
 rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream);
 
 /* Prefill: run T = in->ntok prompt tokens (Mamba-2 in: x [T,B,H,P], B and C [T,B,G,N],
- * dt [T,B,H]; Gated DeltaNet in: q and k [T,B,H,dim_k], v [T,B,H,dim_v], beta and alpha [T,B,H])
+ * dt [T,B,H]; Gated DeltaNet in: q and k [T,B,H,dim_k], v [T,B,H,dim_v], beta and alpha [T,B,H];
+ * Kimi Delta Attention in: the same with alpha [T,B,H,dim_k])
  * through the recurrence from each sequence's current state and make the final state
  * the checkpoint (ia.goatify.app article "NVIDIA y Princeton aceleran modelos hibridos...",
  * paragraph "ReplaySSM cambia que se almacena": the decode path starts from a checkpoint plus
@@ -163,7 +164,8 @@ rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream);
  * decode steps would give. Buffered entries are folded first (one consolidation launch when any
  * sequence may hold some); afterwards len = ndraft = 0 for every sequence and the bf16 read copy,
  * if any, is refreshed. The checkpoint is read and written once for the whole prompt. Requires no
- * pending verify (RSSM_E_STATE). Not compiled for Kimi Delta Attention (RSSM_E_UNSUPPORTED). */
+ * pending verify (RSSM_E_STATE). Mamba-2 and Gated DeltaNet run the prompt in 16-token chunks on
+ * the matrix cores; Kimi Delta Attention applies the tokens one by one to the register tile. */
 rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream);
 
 /* Speculative decoding stores the drafts' inputs and evaluates outputs only (ia.goatify.app

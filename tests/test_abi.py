@@ -175,8 +175,8 @@ def test_seq_state_bytes(lib, kind, flags, dims):
 
 
 def test_kda_workspace_and_prefill(lib):
-    """Kimi Delta Attention rings: k, v, beta and a gate row of d_k per entry; prefill is not
-    compiled for it."""
+    """Kimi Delta Attention rings: k, v, beta and a gate row of d_k per entry; prefill before any
+    checkpoint is loaded is a state error."""
     B, H, V, K, W = 4, 3, 64, 64, 8
     cfg = rb.make_config(rb.RSSM_KDA, B, H, H, V, K, W, 4, 0)
     want = _up(2 * 3 * B * 4) + _up(4) + _up(B * H * V * K * 4) + _up(B * H * W * K * 4) \

@@ -263,14 +263,61 @@ def test_kda_fork_export_import():
         assert np.array_equal(host(o)[0], outs[i]), t
 
 
-def test_kda_prefill_unsupported():
-    sh = wl.GDNShape(batch=2, nheads=2, d_k=16, d_v=16, window=4)
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("T", [1, 16, 37])
+def test_kda_prefill(d, T):
+    """Every compiled head shape; prompts of one token, one full 16-token chunk and a ragged
+    three-chunk prompt into the checkpoint; the outputs, the state and the bookkeeping against the
+    oracle, then 5 decode steps from the new checkpoint."""
+    sh = wl.GDNShape(batch=2, nheads=3, d_k=d, d_v=d, window=8)
+    say(f"kda prefill d={d} T={T}")
+    s0 = wl.kda_state0(sh, 4)
+    ins = wl.kda_token_inputs(sh, 4, 0, ntok=T + 5)
+    dd = kda_dev_tokens(sh, ins, T + 5)
     ctx = _ctx(sh)
-    ctx.init_checkpoint(dev(wl.kda_state0(sh, 0)))
-    ins = kda_dev_tokens(sh, wl.kda_token_inputs(sh, 0, 0, ntok=3), 3)
-    with pytest.raises(rb.RssmError) as e:
-        ctx.prefill(torch.empty(3, 2, 2, 16, device="cuda"), **ins)
-    assert e.value.status == -6
+    ctx.init_checkpoint(dev(s0))
+    ref = s0.astype(np.float64).copy()
+    o = torch.empty(T, sh.batch, sh.nheads, d, device="cuda")
+    ctx.prefill(o, **{k: v[:T] for k, v in dd.items()})
+    o_ref = np.stack([_ref_step(ins, t, ref) for t in range(T)])
+    err = normwise_err(host(o), o_ref)
+    assert err < TOL, err
+    h, l, n, e = ctx.bookkeeping()
+    assert l == [0] * sh.batch and n == [0] * sh.batch and e == 0
+    mat = torch.empty(s0.shape, device="cuda")
+    ctx.materialize(mat)
+    assert normwise_err(host(mat), ref) < TOL
+    o1 = torch.empty(sh.batch, sh.nheads, d, device="cuda")
+    for t in range(T, T + 5):
+        ctx.decode_step(o1, **tok0({k: v[t:t + 1] for k, v in dd.items()}))
+        assert normwise_err(host(o1), _ref_step(ins, t, ref)) < TOL, t
+    say(f"  prompt outputs {err:.3e}")
+
+
+def test_kda_prefill_after_buffered_entries():
+    """Buffered entries are folded first: 5 decode steps, then a 20-token prompt, then a second
+    prompt continuing the same state, against the oracle run over the same tokens."""
+    sh = wl.GDNShape(batch=3, nheads=2, d_k=64, d_v=64, window=8)
+    s0 = wl.kda_state0(sh, 5)
+    ins = wl.kda_token_inputs(sh, 5, 0, ntok=45)
+    dd = kda_dev_tokens(sh, ins, 45)
+    ctx = _ctx(sh)
+    ctx.init_checkpoint(dev(s0))
+    ref = s0.astype(np.float64).copy()
+    o1 = torch.empty(sh.batch, sh.nheads, 64, device="cuda")
+    for t in range(5):
+        ctx.decode_step(o1, **tok0({k: v[t:t + 1] for k, v in dd.items()}))
+        _ref_step(ins, t, ref)
+    for lo in (5, 25):
+        o = torch.empty(20, sh.batch, sh.nheads, 64, device="cuda")
+        ctx.prefill(o, **{k: v[lo:lo + 20] for k, v in dd.items()})
+        o_ref = np.stack([_ref_step(ins, t, ref) for t in range(lo, lo + 20)])
+        assert normwise_err(host(o), o_ref) < TOL, lo
+        mat = torch.empty(s0.shape, device="cuda")
+        ctx.materialize(mat)
+        assert normwise_err(host(mat), ref) < TOL, lo
+        h, l, n, e = ctx.bookkeeping()
+        assert l == [0] * sh.batch and e == 0
 
 
 # ---------------------------------------------------------------------------------------------
