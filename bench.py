@@ -807,6 +807,90 @@ def gdn_prefill_flops(DV, DK, T) -> float:
     return chunks * (3 * 2 * 16 * DV * DK + 2 * 2 * 256 * DK + 2 * 4096 + 3 * 2 * 256 * DV)
 
 
+VALU_FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs x 2.4 GHz, its published figure)
+
+
+def kda_prefill_bytes(DV, DK, T) -> float:
+    """HBM bytes of one Kimi Delta Attention prefill of T tokens for one (b, h) pair: the
+    checkpoint read and written once, every token's q, k, gate row, v and beta read, every output
+    written."""
+    f = 4
+    return 2 * DV * DK * f + T * (3 * DK + DV + 1) * f + T * DV * f
+
+
+def kda_prefill_flops(DV, DK, T) -> float:
+    """Vector flops of one Kimi Delta Attention prefill for one (b, h) pair: per token the gate
+    scale of the tile (DV * DK multiplies), the row dots with k, the rank-1 update and the row dots
+    with q (2 * DV * DK each)."""
+    return T * 7 * DV * DK
+
+
+def run_kda_prefill(args, torch, rb, wl):
+    """Kimi Delta Attention prefill: a T-token prompt per sequence into the checkpoint (batch 256,
+    32 heads, 128 x 128), the tokens applied one by one to the register tile, against the
+    conventional sequential scan on the row-major state."""
+    T = args.prompt
+    sh = wl.GDNShape(batch=args.batch or 256, nheads=32, d_k=128, d_v=128, window=16)
+    DV, DK, W, H, B = sh.d_v, sh.d_k, sh.window, sh.nheads, sh.batch
+    K, Wm, S = args.steps, args.warmup, 32
+    t0 = time.time()
+    s0 = torch.from_numpy(wl.kda_state0(sh, 0)).cuda()
+    pool = [{k: torch.from_numpy(v[0]).cuda() for k, v in wl.kda_token_inputs(sh, 0, s).items()}
+            for s in range(S)]
+    prompt = {k: torch.stack([pool[t % S][k] for t in range(T)]) for k in pool[0]}
+    del pool
+    gen_s = time.time() - t0
+    ctx = rb.Context("kda", B, H, DV, DK, W)
+    o = torch.empty(T, B, H, DV, device="cuda")
+    ctx.init_checkpoint(s0)
+    for _ in range(Wm):
+        ctx.prefill(o, **prompt)
+    torch.cuda.synchronize()
+    ev = _events(torch, 2 * K)
+    for k in range(K):
+        ev[2 * k].record()
+        ctx.prefill(o, **prompt)
+        ev[2 * k + 1].record()
+    torch.cuda.synchronize()
+    pre_s = sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(K)) / 1e3
+    cfg = rb.make_config(rb.RSSM_KDA, B, H, H, DV, DK, W)
+    st = s0.clone()
+    for _ in range(Wm):
+        rb.step_baseline(cfg, st, o, **prompt)
+    torch.cuda.synchronize()
+    ev2 = _events(torch, 2)
+    ev2[0].record()
+    for _ in range(K):
+        rb.step_baseline(cfg, st, o, **prompt)
+    ev2[1].record()
+    torch.cuda.synchronize()
+    conv_s = ev2[0].elapsed_time(ev2[1]) / 1e3
+    bytes_call = kda_prefill_bytes(DV, DK, T) * B * H
+    flops_call = kda_prefill_flops(DV, DK, T) * B * H
+    gbs = bytes_call * K / pre_s / 1e9
+    tfl = flops_call * K / pre_s / 1e12
+    return {
+        "metric": "SSM prefill tokens/s (prompt into the checkpoint) vs the conventional sequential scan",
+        "value": round(B * T * K / pre_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(1e3 * pre_s / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded; prompt token t is pool slot t mod 32 of the decode inputs)",
+        "config": {"workload": f"kda_prefill_b{B}_h{H}_dk{DK}_dv{DV}_t{T}",
+                   "batch": B, "heads": H, "d_k": DK, "d_v": DV, "prompt": T},
+        "alg_gbs": round(gbs, 1), "valu_tflops": round(tfl, 2),
+        "conventional_ms": round(1e3 * conv_s / K, 4),
+        "speedup_vs_conventional": round(conv_s / pre_s, 3),
+        "roofline": {"bound": "alu", "kernel": "k_kda_prefill<128,128>",
+                     "achieved": round(tfl, 2), "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tfl / VALU_FP32_PEAK_TFLOPS, 4),
+                     "other": {"hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+                     "traffic": None, "alg_bytes_per_launch": round(bytes_call),
+                     "flops_per_launch": round(flops_call),
+                     "avg_launch_us": round(1e6 * pre_s / K, 2), "launches": K},
+        "input_gen_s": round(gen_s, 1),
+    }, sh
+
+
 def run_gdn_prefill(args, torch, rb, wl):
     """Gated DeltaNet prefill: a T-token prompt per sequence into the checkpoint (batch 256, 32
     heads, 128 x 128), against the conventional sequential scan (state read once, the T updates
@@ -1171,8 +1255,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="m2_serve",
                     choices=["m2_serve", "m2_serve_bf16", "m2_spec", "gdn_serve", "gdn_spec",
-                             "kda_serve", "kda_spec", "m2_prefill", "gdn_prefill", "m2_fork"])
-    ap.add_argument("--prompt", type=int, default=512, help="prompt tokens (m2_prefill, gdn_prefill)")
+                             "kda_serve", "kda_spec", "m2_prefill", "gdn_prefill", "kda_prefill",
+                             "m2_fork"])
+    ap.add_argument("--prompt", type=int, default=512,
+                    help="prompt tokens (m2_prefill, gdn_prefill, kda_prefill)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (sweeps)")
     ap.add_argument("--groups", type=int, default=0,
                     help="Mamba-2 B/C groups (default: one per head)")
@@ -1228,6 +1314,15 @@ def main():
         line, sh = run_gdn_prefill(args, torch, rb, wl)
         if not args.no_cpu_baseline:
             cb = cpu_baseline_gdn(sh, wl)
+            cb["gbs_fp64_state"] = cb["value"]
+            cb["value"], cb["unit"] = cb["tokens_per_s"], "tokens/s"
+            line["cpu_baseline"] = cb
+    elif args.workload == "kda_prefill":
+        args.steps = args.steps or 4
+        args.warmup = min(args.warmup, 1)
+        line, sh = run_kda_prefill(args, torch, rb, wl)
+        if not args.no_cpu_baseline:
+            cb = cpu_baseline_gdn(sh, wl, layer="kda")
             cb["gbs_fp64_state"] = cb["value"]
             cb["value"], cb["unit"] = cb["tokens_per_s"], "tokens/s"
             line["cpu_baseline"] = cb

@@ -320,6 +320,56 @@ def test_kda_prefill_after_buffered_entries():
         assert l == [0] * sh.batch and e == 0
 
 
+def test_kda_prefill_serving_shape_sampled():
+    """Batch 256, 32 heads, 128x128, a 64-token prompt: the outputs of sampled sequences against the
+    oracle, and every sequence against 64 decode steps of the same tokens on the GPU, each within
+    its rounding bound where the normwise criterion does not hold."""
+    sh = wl.KDA_SERVE
+    T = 64
+    say("kda prefill serving shape: generating inputs")
+    s0 = wl.kda_state0(sh, 0)
+    ins = wl.kda_token_inputs(sh, 0, 100, ntok=T)
+    dd = kda_dev_tokens(sh, ins, T)
+    ctx = _ctx(sh)
+    ctx.init_checkpoint(dev(s0))
+    o = torch.empty(T, sh.batch, sh.nheads, sh.d_v, device="cuda")
+    ctx.prefill(o, **dd)
+    mat = torch.empty(s0.shape, device="cuda")
+    ctx.materialize(mat)
+    ctx2 = _ctx(sh)
+    ctx2.init_checkpoint(dev(s0))
+    kap_state = dev(np.abs(s0))
+    o1 = torch.empty(sh.batch, sh.nheads, sh.d_v, device="cuda")
+    sub = np.array([0, 31, 128, 255])
+    pair = []
+    oh = host(o)
+    od = np.empty((T, len(sub), sh.nheads, sh.d_v), np.float32)
+    for t in range(T):
+        tok = tok0({k: v[t:t + 1] for k, v in dd.items()})
+        ctx2.decode_step(o1, **tok)
+        kap = host(kda_kappa_torch(kap_state, tok["q"], tok["k"], tok["v"], tok["beta"], tok["alpha"]))
+        o1h = host(o1)
+        od[t] = o1h[sub]
+        pair.append(cond_check(oh[t], o1h, 2 * C_FP32 * U32 * kap, 2 * TOL))
+    ref = s0[sub].astype(np.float64)
+    M = np.abs(ref)
+    o_ref, kref = [], []
+    for t in range(T):
+        a = [ins[k][t][sub] for k in KEYS]
+        o_ref.append(kda_step(*a, ref))
+        kref.append(kda_kappa_step(*a, M))
+    o_ref, kref = np.stack(o_ref), np.stack(kref)
+    cp = cond_check(oh[:, sub], o_ref, C_FP32 * U32 * kref, TOL)
+    cd = cond_check(od, o_ref, C_FP32 * U32 * kref, TOL)
+    worst_pair = max(pair, key=lambda c: c.ratio_all)
+    say(f"  prefill vs oracle: {cp}")
+    say(f"  decode vs oracle: {cd}")
+    say(f"  prefill vs decode, all sequences (worst token): {worst_pair}")
+    assert cp.ok and cd.ok and cp.ratio_all <= 1 and cd.ratio_all <= 1
+    assert all(c.ok and c.ratio_all <= 1 for c in pair)
+    assert normwise_err(host(mat)[sub], ref) < TOL
+
+
 # ---------------------------------------------------------------------------------------------
 # serving shapes: batch 256 x 32 heads, 128 x 128, W = 16; speculative batch 512, K = 6
 # ---------------------------------------------------------------------------------------------
