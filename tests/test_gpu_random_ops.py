@@ -1,4 +1,5 @@
-"""Seeded random sequences of the library's operations on one context, against the CPU oracle and
+"""Seeded random sequences of the library's operations on one context (Mamba-2 in fp32 and with the
+bf16 read copy, Gated DeltaNet, Kimi Delta Attention), against the CPU oracle and
 the bookkeeping model: decode steps, speculative rounds committed or discarded,
 consolidation, masked re-initialisation, prefills, forks, and exports imported again later into
 other slots. After every operation: every output it wrote and the bookkeeping; every few operations
@@ -9,7 +10,8 @@ import torch
 
 import workloads as wl
 from checkpoint_replay_buffer_amd import binding as rb
-from oracle import Bookkeeping, gdn_spec_round, gdn_step, m2_spec_round, m2_step, normwise_err
+from oracle import (Bookkeeping, gdn_spec_round, gdn_step, kda_spec_round, kda_step, m2_spec_round,
+                    m2_step, normwise_err)
 from tests.gpu_helpers import dev, host, say
 
 pytestmark = pytest.mark.gpu
@@ -38,8 +40,8 @@ class _Layer:
             self.dv = 16
         else:
             self.sh = wl.GDNShape(batch=5, nheads=4, d_k=16, d_v=16, window=6, max_draft=3)
-            s0 = wl.gdn_state0(self.sh, seed)
-            self.ctx = rb.Context("gdn", self.sh.batch, self.sh.nheads, 16, 16, self.sh.window,
+            s0 = (wl.kda_state0 if kind == "kda" else wl.gdn_state0)(self.sh, seed)
+            self.ctx = rb.Context(kind, self.sh.batch, self.sh.nheads, 16, 16, self.sh.window,
                                   max_draft=self.sh.max_draft)
             self.dv = 16
         self.ctx.init_checkpoint(dev(s0))
@@ -49,15 +51,20 @@ class _Layer:
     def inputs(self, slot, ntok):
         if self.kind == "mamba2":
             return wl.m2_token_inputs(self.sh, self.seed, slot, ntok=ntok)
+        if self.kind == "kda":
+            return wl.kda_token_inputs(self.sh, self.seed, slot, ntok=ntok)
         return wl.gdn_token_inputs(self.sh, self.seed, slot, ntok=ntok)
 
     def fresh_states(self, slot):
-        return (wl.m2_state0 if self.kind == "mamba2" else wl.gdn_state0)(self.sh, 500 + slot)
+        gen = {"mamba2": wl.m2_state0, "gdn": wl.gdn_state0, "kda": wl.kda_state0}[self.kind]
+        return gen(self.sh, 500 + slot)
 
     def spec_round(self, ins, accepted):
         """The oracle's conventional speculative round on the reference state."""
         if self.kind == "mamba2":
             return m2_spec_round(self.prm["A"], self.prm["D"], ins, self.ref, accepted)
+        if self.kind == "kda":
+            return kda_spec_round(ins, self.ref, accepted)
         return gdn_spec_round(ins, self.ref, accepted)
 
     def step(self, ins, t):
@@ -66,8 +73,8 @@ class _Layer:
             p = self.prm
             return m2_step(p["A"], p["D"], ins["x"][t], ins["B"][t], ins["C"][t], ins["dt"][t],
                            self.ref)
-        return gdn_step(ins["q"][t], ins["k"][t], ins["v"][t], ins["beta"][t], ins["alpha"][t],
-                        self.ref)
+        step = kda_step if self.kind == "kda" else gdn_step
+        return step(ins["q"][t], ins["k"][t], ins["v"][t], ins["beta"][t], ins["alpha"][t], self.ref)
 
     def out_err(self, got, ref):
         """fp32: per head vector; bf16 read copy: per sequence-token layer output."""
@@ -95,7 +102,7 @@ def _i32(v):
     return torch.tensor(np.asarray(v, dtype=np.int32), device="cuda")
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn", "mamba2_bf16"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda", "mamba2_bf16"])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_random_operation_sequences(kind, seed):
     rng = np.random.default_rng(9000 + seed)       # the schedule of operations, not method data
