@@ -8,7 +8,7 @@ import torch
 
 import workloads as wl
 from checkpoint_replay_buffer_amd import binding as rb
-from oracle import gdn_step, m2_step, normwise_err
+from oracle import gdn_step, kda_step, m2_step, normwise_err
 from tests.gpu_helpers import dev, host, say
 
 pytestmark = pytest.mark.gpu
@@ -38,22 +38,25 @@ def _setup(kind, bf16):
         dv = sh.head_dim
     else:
         sh = wl.GDNShape(batch=2, nheads=4, d_k=64, d_v=64, window=4)
-        s0 = wl.gdn_state0(sh, 0)
+        kda = kind == "kda"
+        s0 = (wl.kda_state0 if kda else wl.gdn_state0)(sh, 0)
 
         def make():
-            return rb.Context("gdn", sh.batch, sh.nheads, sh.d_v, sh.d_k, sh.window)
+            return rb.Context(kind, sh.batch, sh.nheads, sh.d_v, sh.d_k, sh.window)
 
         def toks(seed, n):
-            return wl.gdn_token_inputs(sh, seed, 0, ntok=n)
+            return (wl.kda_token_inputs if kda else wl.gdn_token_inputs)(sh, seed, 0, ntok=n)
 
         def oracle_step(ins, t, ref):
-            return gdn_step(ins["q"][t], ins["k"][t], ins["v"][t], ins["beta"][t], ins["alpha"][t], ref)
+            return (kda_step if kda else gdn_step)(ins["q"][t], ins["k"][t], ins["v"][t],
+                                                   ins["beta"][t], ins["alpha"][t], ref)
 
         dv = sh.d_v
     return sh, s0, make, toks, oracle_step, dv
 
 
-@pytest.mark.parametrize("kind,bf16", [("mamba2", False), ("mamba2", True), ("gdn", False)])
+@pytest.mark.parametrize("kind,bf16", [("mamba2", False), ("mamba2", True), ("gdn", False),
+                                       ("kda", False)])
 def test_graph_window_replays_match_eager(kind, bf16):
     sh, s0, make, toks, oracle_step, dv = _setup(kind, bf16)
     n = 2 * sh.window
