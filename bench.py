@@ -884,7 +884,7 @@ def run_kda_prefill(args, torch, rb, wl):
                      "achieved": round(tfl, 2), "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfl / VALU_FP32_PEAK_TFLOPS, 4),
                      "other": {"hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
-                     "traffic": None, "alg_bytes_per_launch": round(bytes_call),
+                     **_traffic_fields("kda_prefill"), "alg_bytes_per_launch": round(bytes_call),
                      "flops_per_launch": round(flops_call),
                      "avg_launch_us": round(1e6 * pre_s / K, 2), "launches": K},
         "input_gen_s": round(gen_s, 1),
