@@ -35,6 +35,12 @@ namespace {
 constexpr int kChunk = 16;
 constexpr int kMS = kChunk + 4;   // row stride of the 16 x 16 blocks in LDS
 
+// Threads per workgroup (one (b, h) tile) and waves per SIMD the prefill is compiled for.
+template <int P, int N>
+struct PrefillShape {
+    static constexpr int TPB = TileShape<P, N>::TPB, OCC = 4;
+};
+
 // LDS floats: two staging buffers of the rows read on both sides of the mid-chunk barrier, x
 // [16][P+4] and B [16][N+4]; one buffer of those read before it only, C [16][N+4] and dt [16];
 // then one 16 x 16 partial of B C^T per wave, the weights w[t][j] [16][20], w[15][j] [16] and
@@ -48,7 +54,7 @@ template <int P, int N>
 __host__ __device__ constexpr int prefill_lds_floats()
 {
     return 2 * prefill_buf_floats<P, N>() + kChunk * (N + 4) + kChunk
-         + (MfmaTile<P, N>::NW + 1) * kChunk * kMS + 2 * kChunk;
+         + (PrefillShape<P, N>::TPB / 64 + 1) * kChunk * kMS + 2 * kChunk;
 }
 
 // Inclusive prefix sum over the 16 lanes of each row of the wave (lanes 16 g .. 16 g + 15): four
@@ -113,7 +119,7 @@ __device__ __forceinline__ float4 sum_partials(const float4 (&p)[NW])
 // from one chunk to the next.
 template <int P, int N>
 struct ChunkRows {
-    static constexpr int TPB = TileShape<P, N>::TPB, PF = P / 4, NF = N / 4;
+    static constexpr int TPB = PrefillShape<P, N>::TPB, PF = P / 4, NF = N / 4;
     static constexpr int XQ = (kChunk * PF + TPB - 1) / TPB, BQ = (kChunk * NF + TPB - 1) / TPB;
     float4 x[XQ], b[BQ], c[BQ];
     float dt;
@@ -171,9 +177,9 @@ struct ChunkRows {
 // after the second barrier every wave has what it needs for its outputs and its part of the
 // update.
 template <int P, int N, bool BF16>
-__global__ void __launch_bounds__((TileShape<P, N>::TPB), 4) k_m2_prefill(M2PrefillArgs a)
+__global__ void __launch_bounds__((PrefillShape<P, N>::TPB), (PrefillShape<P, N>::OCC)) k_m2_prefill(M2PrefillArgs a)
 {
-    using F = MfmaTile<P, N>;
+    using F = MfmaTile<P, N, PrefillShape<P, N>::TPB / 64>;
     constexpr int NW = F::NW, IBW = F::IBW, KB = F::KB, XS = F::RS, BS = F::CS;
     constexpr int NA = KB >= 2 ? 2 : KB;   // independent accumulators of the d_state products
                                            // (two: the registers of four waves per SIMD)
@@ -350,7 +356,7 @@ __global__ void __launch_bounds__((TileShape<P, N>::TPB), 4) k_m2_prefill(M2Pref
 template <int P, int N>
 hipError_t go_prefill(const M2PrefillArgs &a, bool bf16, hipStream_t s)
 {
-    const dim3 grid(a.d.B * a.d.H), block(TileShape<P, N>::TPB);
+    const dim3 grid(a.d.B * a.d.H), block(PrefillShape<P, N>::TPB);
     const size_t lds = 4 * (size_t)prefill_lds_floats<P, N>();
     if (bf16) hipLaunchKernelGGL((k_m2_prefill<P, N, true>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_m2_prefill<P, N, false>), grid, block, lds, s, a);
