@@ -183,6 +183,13 @@ __device__ __forceinline__ void stage_rows(const EntryRows<DV, DK> &er, int n, F
     for (int i = t + XQ * TPB; i < nu; i += TPB) st4(er.dst(i), ld4(er.src(i)));
 }
 
+// Waves per SIMD the kernels that fold are compiled for: three 8-wave workgroups per compute unit
+// at 128 x 128 (at most 80 VGPRs), the compiler's choice otherwise.
+template <int DV, int DK>
+struct KdaFoldOcc {
+    static constexpr int WPE = TileShape<DV, DK>::TPB == 512 ? 6 : 1;
+};
+
 // Fold entries 0..n-1 (staged in LDS, oldest first) into the register tile: for each entry,
 // scale the columns by its gate, form (S k) per row, add beta (v - S k) k^T. No barrier.
 template <int DV, int DK>
@@ -344,7 +351,7 @@ __device__ __forceinline__ void kda_fold_decode(const GdnStepArgs &a, const KTil
 // Variants as the Gated DeltaNet decode: 0 = every sequence at (a.uhead, a.ulen), none folds;
 // 1 = none folds (positions read from the device); 2 = any sequence may fold.
 template <int DV, int DK, int MODE>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_decode(GdnStepArgs a)
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (MODE == 2 ? KdaFoldOcc<DV, DK>::WPE : 1)) k_kda_decode(GdnStepArgs a)
 {
     using F = MfmaTile<DV, DK>;
     extern __shared__ float smem[];
@@ -386,7 +393,7 @@ __host__ __device__ constexpr int kda_fold_lds(int W)
 }
 
 template <int DV, int DK>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_fold(GdnFoldArgs a)
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (KdaFoldOcc<DV, DK>::WPE)) k_kda_fold(GdnFoldArgs a)
 {
     using F = MfmaTile<DV, DK>;
     using RW = Rows<DV, DK>;
