@@ -807,9 +807,6 @@ def gdn_prefill_flops(DV, DK, T) -> float:
     return chunks * (3 * 2 * 16 * DV * DK + 2 * 2 * 256 * DK + 2 * 4096 + 3 * 2 * 256 * DV)
 
 
-VALU_FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs x 2.4 GHz, its published figure)
-
-
 def kda_prefill_bytes(DV, DK, T) -> float:
     """HBM bytes of one Kimi Delta Attention prefill of T tokens for one (b, h) pair: the
     checkpoint read and written once, every token's q, k, gate row, v and beta read, every output
@@ -819,16 +816,19 @@ def kda_prefill_bytes(DV, DK, T) -> float:
 
 
 def kda_prefill_flops(DV, DK, T) -> float:
-    """Vector flops of one Kimi Delta Attention prefill for one (b, h) pair: per token the gate
-    scale of the tile (DV * DK multiplies), the row dots with k, the rank-1 update and the row dots
-    with q (2 * DV * DK each)."""
-    return T * 7 * DV * DK
+    """Matrix-core flops of one Kimi Delta Attention prefill for one (b, h) pair, per 16-token
+    chunk of the chunk form: Kh S^T, Qh S^T and the rank-16 update (2 * 16 * DV * DK each), the
+    A and M blocks (2 * 16 * 16 * DK each), M T (2 * 16^3), (M T) Z and T Z (2 * 16 * 16 * DV
+    each). Chunks that take the token path (a gate product below 2^-64) do not occur in these
+    inputs."""
+    chunks = (T + 15) // 16
+    return chunks * (3 * 2 * 16 * DV * DK + 2 * 2 * 256 * DK + 2 * 4096 + 2 * 2 * 256 * DV)
 
 
 def run_kda_prefill(args, torch, rb, wl):
     """Kimi Delta Attention prefill: a T-token prompt per sequence into the checkpoint (batch 256,
-    32 heads, 128 x 128), the tokens applied one by one to the register tile, against the
-    conventional sequential scan on the row-major state."""
+    32 heads, 128 x 128) in 16-token chunks on the matrix cores, against the conventional
+    sequential scan on the row-major state."""
     T = args.prompt
     sh = wl.GDNShape(batch=args.batch or 256, nheads=32, d_k=128, d_v=128, window=16)
     DV, DK, W, H, B = sh.d_v, sh.d_k, sh.window, sh.nheads, sh.batch
@@ -869,6 +869,8 @@ def run_kda_prefill(args, torch, rb, wl):
     flops_call = kda_prefill_flops(DV, DK, T) * B * H
     gbs = bytes_call * K / pre_s / 1e9
     tfl = flops_call * K / pre_s / 1e12
+    hbm_frac, mfma_frac = gbs / HBM_PEAK_GBS, tfl / MFMA_FP32_PEAK_TFLOPS
+    bound_hbm = hbm_frac >= mfma_frac
     return {
         "metric": "SSM prefill tokens/s (prompt into the checkpoint) vs the conventional sequential scan",
         "value": round(B * T * K / pre_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -877,13 +879,15 @@ def run_kda_prefill(args, torch, rb, wl):
         "data": "synthetic (seeded; prompt token t is pool slot t mod 32 of the decode inputs)",
         "config": {"workload": f"kda_prefill_b{B}_h{H}_dk{DK}_dv{DV}_t{T}",
                    "batch": B, "heads": H, "d_k": DK, "d_v": DV, "prompt": T},
-        "alg_gbs": round(gbs, 1), "valu_tflops": round(tfl, 2),
+        "alg_gbs": round(gbs, 1), "mfma_tflops": round(tfl, 2),
         "conventional_ms": round(1e3 * conv_s / K, 4),
         "speedup_vs_conventional": round(conv_s / pre_s, 3),
-        "roofline": {"bound": "alu", "kernel": "k_kda_prefill<128,128>",
-                     "achieved": round(tfl, 2), "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tfl / VALU_FP32_PEAK_TFLOPS, 4),
-                     "other": {"hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm" if bound_hbm else "mfma", "kernel": "k_kda_prefill<128,128>",
+                     "achieved": round(gbs if bound_hbm else tfl, 2),
+                     "peak": HBM_PEAK_GBS if bound_hbm else MFMA_FP32_PEAK_TFLOPS,
+                     "unit": "GB/s" if bound_hbm else "TFLOP/s",
+                     "frac": round(hbm_frac if bound_hbm else mfma_frac, 4),
+                     "other": {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4)},
                      **_traffic_fields("kda_prefill"), "alg_bytes_per_launch": round(bytes_call),
                      "flops_per_launch": round(flops_call),
                      "avg_launch_us": round(1e6 * pre_s / K, 2), "launches": K},

@@ -11,8 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "librssm.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["mamba2.hip", "m2_prefill.hip", "gdn.hip", "gdn_prefill.hip", "kda.hip", "bookkeep.hip",
-           "seqstate.hip", "host.cpp"]
+SOURCES = ["mamba2.hip", "m2_prefill.hip", "gdn.hip", "gdn_prefill.hip", "kda.hip", "kda_prefill.hip",
+           "bookkeep.hip", "seqstate.hip", "host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -48,11 +48,13 @@ __device__ __forceinline__ v4f row_dots16(const float *x, const float *y)
 // (q = lane % NP) held in registers; the Gram rows (G[t][i] at sh_G[t GS + i], i < t) and the betas
 // are read at addresses common to the wave. Rows with beta = 0 (padding) come out zero. The
 // substitution and the store are separate steps, so that a caller can place other work between
-// them in the same straight-line code.
+// them in the same straight-line code. A caller inside a loop may pass the lane's column q through
+// an empty asm statement, so that the identity's selectors are formed here and not kept in
+// registers across the loop.
 template <int NP, int GS>
-__device__ __forceinline__ void t_solve_cols(const float *sh_G, const float *sh_be, float (&tq)[NP])
+__device__ __forceinline__ void t_solve_cols(const float *sh_G, const float *sh_be, float (&tq)[NP],
+                                             int q = threadIdx.x & (NP - 1))
 {
-    const int q = threadIdx.x & (NP - 1);
 #pragma unroll
     for (int t = 0; t < NP; ++t) {
         float acc = 0.f;

@@ -583,74 +583,6 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_verify(GdnStep
 }
 
 // ------------------------------------------------------------------------------------------
-// prefill: a prompt run through the recurrence into the checkpoint
-// ------------------------------------------------------------------------------------------
-// The tokens are applied in order to the register tile (the gated delta rule has no chunked form
-// here that avoids ratios of gate products, see the fold above): per token the column scale by
-// its gate, the row dot with k, the rank-1 update beta (v - S k) k^T, and the output o = S q.
-// Sixteen tokens' rows are staged in LDS at a time; the final tile becomes the checkpoint with an
-// empty ring.
-template <int DV, int DK>
-__host__ __device__ constexpr int kda_prefill_lds()
-{
-    // k, gate and q rows [16][KS], value rows [16][VS], betas [16]
-    return 16 * (3 * (DK + 4) + DV + 4) + 16;
-}
-
-template <int DV, int DK>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_prefill(GdnPrefillArgs a)
-{
-    using F = MfmaTile<DV, DK>;
-    using RW = Rows<DV, DK>;
-    constexpr int TPB = F::TPB, IBW = F::IBW, KF = DK / 4, VF = DV / 4, RF = 3 * KF + VF;
-    extern __shared__ float smem[];
-    float *sh_k = smem;                      // [16][KS]
-    float *sh_a = sh_k + 16 * RW::KS;        // [16][KS]
-    float *sh_q = sh_a + 16 * RW::KS;        // [16][KS]
-    float *sh_v = sh_q + 16 * RW::KS;        // [16][VS]
-    float *sh_be = sh_v + 16 * RW::VS;       // [16]
-    const KTile c = make_ktile(a.d, kRuns);
-    const int B = a.d.B, T = a.T, t = c.t, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
-    const size_t BH = (size_t)B * a.d.H;
-    float *S0 = a.S0 + c.bh * (size_t)(DV * DK);
-    TileRegs<DV, DK> s;
-    ckpt_load<DV>(s, S0, t);
-    for (int t0 = 0; t0 < T; t0 += 16) {
-        const int ct = T - t0 < 16 ? T - t0 : 16;
-        // the chunk's rows: per token KF key, KF gate, KF query and VF value units
-        for (int i = t; i < ct * RF; i += TPB) {
-            const int j = i / RF, u = i - j * RF;
-            const size_t tk = (size_t)(t0 + j) * BH + c.bh;
-            if (u < KF) st4(sh_k + j * RW::KS + 4 * u, ld4(a.k + tk * DK + 4 * u));
-            else if (u < 2 * KF) st4(sh_a + j * RW::KS + 4 * (u - KF), ld4(a.alpha + tk * DK + 4 * (u - KF)));
-            else if (u < 3 * KF) st4(sh_q + j * RW::KS + 4 * (u - 2 * KF), ld4(a.q + tk * DK + 4 * (u - 2 * KF)));
-            else st4(sh_v + j * RW::VS + 4 * (u - 3 * KF), ld4(a.v + tk * DV + 4 * (u - 3 * KF)));
-        }
-        if (t < ct) sh_be[t] = a.beta[(size_t)(t0 + t) * BH + c.bh];
-        __syncthreads();
-        for (int j = 0; j < ct; ++j) {
-            kda_fold_tile<DV, DK>(s, sh_k + j * RW::KS, sh_a + j * RW::KS, sh_v + j * RW::VS, sh_be + j, 1);
-            float *oj = a.o + ((size_t)(t0 + j) * BH + c.bh) * DV;
-#pragma unroll
-            for (int ib = 0; ib < IBW; ++ib) {
-                const int row = 16 * (wv * IBW + ib) + cl;
-                float p = tile_gemv_row<DV, DK>(s, ib, sh_q + j * RW::KS);
-                p += bfly<16>(p);
-                p += __shfl_xor(p, 32);
-                if (g == 0) oj[row] = p;
-            }
-        }
-        __syncthreads();                     // every wave is done with the rows before restaging
-    }
-    ckpt_store<DV>(s, S0, t);
-    if (c.h == 0 && t == 0) {
-        a.bk.out[c.b] = a.bk.in[c.b];
-        a.bk.out[B + c.b] = 0;
-        a.bk.out[2 * B + c.b] = 0;
-    }
-}
-
-// ------------------------------------------------------------------------------------------
 // conventional read-modify-write comparator (row-major state)
 // ------------------------------------------------------------------------------------------
 template <int DV, int DK>
@@ -751,15 +683,6 @@ hipError_t go_verify(const GdnStepArgs &a, hipStream_t s)
 }
 
 template <int DV, int DK>
-hipError_t go_prefill(const GdnPrefillArgs &a, hipStream_t s)
-{
-    const dim3 grid(a.d.B * a.d.H), block(TileShape<DV, DK>::TPB);
-    const size_t lds = 4 * (size_t)kda_prefill_lds<DV, DK>();
-    hipLaunchKernelGGL((k_kda_prefill<DV, DK>), grid, block, lds, s, a);
-    return hipGetLastError();
-}
-
-template <int DV, int DK>
 hipError_t go_rmw(const GdnRmwArgs &a, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(TileShape<DV, DK>::TPB);
@@ -808,14 +731,6 @@ hipError_t kda_fold(const GdnFoldArgs &a, hipStream_t s)
 hipError_t kda_verify(const GdnStepArgs &a, hipStream_t s)
 {
 #define RSSM_C(v, k) if (a.d.DV == v && a.d.DK == k) return go_verify<v, k>(a, s);
-    RSSM_KDA_SHAPES(RSSM_C)
-#undef RSSM_C
-    return hipErrorInvalidValue;
-}
-
-hipError_t kda_prefill(const GdnPrefillArgs &a, hipStream_t s)
-{
-#define RSSM_C(v, k) if (a.d.DV == v && a.d.DK == k) return go_prefill<v, k>(a, s);
     RSSM_KDA_SHAPES(RSSM_C)
 #undef RSSM_C
     return hipErrorInvalidValue;

@@ -164,8 +164,9 @@ rssm_status rssm_consolidate(rssm_ctx *ctx, int32_t min_len, void *stream);
  * decode steps would give. Buffered entries are folded first (one consolidation launch when any
  * sequence may hold some); afterwards len = ndraft = 0 for every sequence and the bf16 read copy,
  * if any, is refreshed. The checkpoint is read and written once for the whole prompt. Requires no
- * pending verify (RSSM_E_STATE). Mamba-2 and Gated DeltaNet run the prompt in 16-token chunks on
- * the matrix cores; Kimi Delta Attention applies the tokens one by one to the register tile. */
+ * pending verify (RSSM_E_STATE). Every layer type runs the prompt in 16-token chunks on the
+ * matrix cores; a Kimi Delta Attention chunk in which some key channel's gate product falls below
+ * 2^-64 is applied token by token instead. */
 rssm_status rssm_prefill(rssm_ctx *ctx, const rssm_inputs *in, float *y, void *stream);
 
 /* Speculative decoding stores the drafts' inputs and evaluates outputs only (ia.goatify.app

@@ -320,6 +320,52 @@ def test_kda_prefill_after_buffered_entries():
         assert l == [0] * sh.batch and e == 0
 
 
+def _prefill_against_oracle(sh, s0, ins, T):
+    dd = kda_dev_tokens(sh, ins, T)
+    ctx = _ctx(sh)
+    ctx.init_checkpoint(dev(s0))
+    ref = s0.astype(np.float64).copy()
+    o = torch.empty(T, sh.batch, sh.nheads, sh.d_v, device="cuda")
+    ctx.prefill(o, **dd)
+    o_ref = np.stack([_ref_step(ins, t, ref) for t in range(T)])
+    mat = torch.empty(s0.shape, device="cuda")
+    ctx.materialize(mat)
+    return host(o), o_ref, host(mat), ref
+
+
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_kda_prefill_token_path_chunks(d):
+    """Chunks whose gate product in some channel falls below 2^-64 (a run of gates 1e-5 in a few
+    channels, a single gate of exactly 0) go through the token-by-token path; the other tiles and
+    chunks of the same launch take the matrix-core form. Outputs and state against the oracle."""
+    sh = wl.GDNShape(batch=2, nheads=3, d_k=d, d_v=d, window=8)
+    T = 53
+    say(f"kda prefill token-path chunks d={d}")
+    s0 = wl.kda_state0(sh, 6)
+    ins = wl.kda_token_inputs(sh, 6, 0, ntok=T)
+    ins["alpha"][16:32, 0, 1, :5] = 1e-5        # chunk 1 of tile (0, 1)
+    ins["alpha"][40, 1, 2, d - 1] = 0.0         # chunk 2 of tile (1, 2)
+    ins["alpha"][50, 0, 0, 3] = 0.0             # the ragged last chunk of tile (0, 0)
+    oh, o_ref, mh, ref = _prefill_against_oracle(sh, s0, ins, T)
+    assert normwise_err(oh, o_ref) < TOL
+    assert normwise_err(mh, ref) < TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kda_prefill_strong_gates(d):
+    """Every gate 0.07: the chunk products reach 0.07^16 ~ 2^-61, just inside the matrix-core form
+    (1 / Gam up to 2^61 on one operand); outputs and state against the oracle."""
+    sh = wl.GDNShape(batch=2, nheads=2, d_k=d, d_v=d, window=8)
+    T = 40
+    say(f"kda prefill strong gates d={d}")
+    s0 = wl.kda_state0(sh, 7)
+    ins = wl.kda_token_inputs(sh, 7, 0, ntok=T)
+    ins["alpha"][:] = np.float32(0.07)
+    oh, o_ref, mh, ref = _prefill_against_oracle(sh, s0, ins, T)
+    assert normwise_err(oh, o_ref) < TOL
+    assert normwise_err(mh, ref) < TOL
+
+
 def test_kda_prefill_serving_shape_sampled():
     """Batch 256, 32 heads, 128x128, a 64-token prompt: the outputs of sampled sequences against the
     oracle, and every sequence against 64 decode steps of the same tokens on the GPU, each within
