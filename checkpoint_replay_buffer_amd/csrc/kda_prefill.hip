@@ -1,5 +1,5 @@
-// kda_prefill.hip -- Kimi Delta Attention prefill into the checkpoint, in chunks of 16 tokens on the
-// matrix cores (gfx950).
+// kda_prefill.hip -- Kimi Delta Attention prefill into the checkpoint, in chunks of 16 tokens on
+// the matrix cores (gfx950).
 //
 // Kimi Delta Attention is one of the layer types ReplaySSM targets (news.hamidun.com item "NVIDIA
 // présente ReplaySSM...", section "Pourquoi les hybrides sont devenus la norme"); the pages give no
@@ -15,8 +15,8 @@
 // Put kh_t = k_t o Gam_t, kt_j = k_j / Gam_j, qh_t = q_t o Gam_t and A[t][j] = kh_t . kt_j (which
 // carries the ratio Gam_t / Gam_j channel by channel). Then
 //     u_t = beta_t (v_t - S kh_t - sum_{j<t} A[t][j] u_j),  i.e. U = T Z,  Z = V - Kh S^T,
-// with T the lower-triangular factor of the delta rule's WY form (gdn_chunk.h) taken over A in place
-// of the Gram block;
+// with T the lower-triangular factor of the delta rule's WY form (gdn_chunk.h) taken over A in
+// place of the Gram block;
 //     O = Qh S^T + M U,  M[t][j] = qh_t . kt_j for j <= t (else 0);
 // and the chunk ends in S diag(Gam_15) + U^T Kb, Kb_j = kt_j o Gam_15. Every product is a
 // v_mfma_f32_16x16x4_f32 chain on the register-resident tile of mfma_tile.h, as in the Gated
@@ -43,28 +43,38 @@ struct KpShape {
 // Smallest gate product over a chunk that the chunk form takes (then 1 / Gam_j <= 2^64).
 constexpr float kMinGam = 0x1p-64f;
 
-// LDS layout (floats). The chunk's raw rows q, k, a [16][d_k+4], v [16][d_v+4] and beta [16]; the
-// chunk form's rows qh, kh, kt [16][d_k+4] and Gam_15 [d_k]; the A, T and M blocks [16][20]; two
-// flags (chunk parity) that say a chunk runs token by token.
+// LDS layout (floats). The chunk-form rows qh, kh, kt [16][d_k+4], beta [16] and Gam_15 [d_k] of
+// two chunks (the next chunk's are written while the current one's are still read); the value rows
+// [16][d_v+4]; the A, T and M blocks [16][20]; per chunk parity and wave a flag that sends the
+// chunk to the token path.
 template <int DV, int DK>
 struct KpLds {
     static constexpr int KS = DK + 4, VS = DV + 4, R = kChunk * KS;
-    static constexpr int q = 0, k = q + R, a = k + R, v = a + R, be = v + kChunk * VS;
-    static constexpr int qh = be + kChunk, kh = qh + R, kt = kh + R, gam = kt + R;
-    static constexpr int A = gam + DK, T = A + kChunk * kTS, M = T + kChunk * kTS;
-    static constexpr int flag = M + kChunk * kTS, floats = flag + 2;
-    static_assert(qh % 4 == 0 && gam % 4 == 0 && A % 4 == 0, "16-byte aligned rows");
+    static constexpr int rows(int p, int x) { return (3 * p + x) * R; }   // x: 0 qh, 1 kh, 2 kt
+    static constexpr int v = 6 * R, be = v + kChunk * VS, gam = be + 2 * kChunk;
+    static constexpr int A = gam + 2 * DK, T = A + kChunk * kTS, M = T + kChunk * kTS;
+    static constexpr int flag = M + kChunk * kTS, floats = flag + 8;
+    static_assert(R % 4 == 0 && be % 4 == 0 && gam % 4 == 0 && A % 4 == 0, "16-byte aligned rows");
 };
 
-// The chunk's raw rows in registers between their load and their LDS store: q, k and gate units
-// (KQ float4 per thread), value units (VQ), beta. The addresses are formed again for every chunk
-// rather than kept in registers across it. Padding rows (tokens past the prompt) load as
-// q = k = v = 0, gate 1, beta 0: they change nothing.
+__device__ __forceinline__ float4 mul4(float4 x, float4 y)
+{
+    return make_float4(x.x * y.x, x.y * y.y, x.z * y.z, x.w * y.w);
+}
+
+// The chunk's raw rows in registers between their load and their LDS store. Thread t holds the q,
+// k and gate units of channels 4 cg .. 4 cg + 3 (cg = t / LPC) for TPT consecutive tokens, so
+// that the LPC lanes of a channel group cover the chunk and the gate products are a scan across
+// them; value units as VQ float4 in token-major order; beta of token t. The addresses are formed
+// again for every chunk rather than kept in registers. Padding rows (tokens past the prompt) load
+// as q = k = v = 0, gate 1, beta 0: they change nothing.
 template <int DV, int DK>
 struct KdaRows {
     static constexpr int TPB = KpShape<DV, DK>::TPB, KF = DK / 4, VF = DV / 4;
-    static constexpr int KQ = (kChunk * KF + TPB - 1) / TPB, VQ = (kChunk * VF + TPB - 1) / TPB;
-    float4 q[KQ], k[KQ], a[KQ], v[VQ];
+    static constexpr int TPT = kChunk * KF / TPB, LPC = kChunk / TPT;
+    static constexpr int VQ = (kChunk * VF + TPB - 1) / TPB;
+    static_assert(TPT * TPB == kChunk * KF && (TPT == 1 || TPT == 2) && 64 % LPC == 0, "row map");
+    float4 q[TPT], k[TPT], a[TPT], v[VQ];
     float be;
 
     // tokens t0 .. t0 + ct - 1; the pointers are at token t0's row of this tile
@@ -73,11 +83,11 @@ struct KdaRows {
     {
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f), one = make_float4(1.f, 1.f, 1.f, 1.f);
         asm volatile("" : "+v"(t));        // the offsets are recomputed here
+        const int cg = t / LPC, j0 = TPT * (t - cg * LPC);
 #pragma unroll
-        for (int i = 0; i < KQ; ++i) {
-            const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
-            const bool in = u < kChunk * KF && j < ct;
-            const size_t off = (size_t)j * BH * DK + o;
+        for (int i = 0; i < TPT; ++i) {
+            const bool in = j0 + i < ct;
+            const size_t off = (size_t)(j0 + i) * BH * DK + 4 * cg;
             q[i] = in ? ld4(qb + off) : z;
             k[i] = in ? ld4(kb + off) : z;
             a[i] = in ? ld4(ab + off) : one;
@@ -90,19 +100,45 @@ struct KdaRows {
         be = t < ct ? bb[(size_t)t * BH] : 0.f;
     }
 
-    __device__ __forceinline__ void store_qka(float *sm, int t) const
+    // The chunk-form rows of the held tokens into LDS buffer p: the gate products (over the
+    // thread's tokens, then an exclusive product scan over the lanes of the channel group), qh,
+    // kh and kt, beta; the group's last lane writes Gam_15 of its four channels and returns whether
+    // one of them is below kMinGam or not a number.
+    __device__ __forceinline__ bool derive(float *sm, int p, int t) const
     {
         using L = KpLds<DV, DK>;
+        const int cg = t / LPC, l = t - cg * LPC, j0 = TPT * l;
+        float4 pr[TPT];
+        pr[0] = a[0];
 #pragma unroll
-        for (int i = 0; i < KQ; ++i) {
-            const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
-            if (u < kChunk * KF) {
-                st4(sm + L::q + j * L::KS + o, q[i]);
-                st4(sm + L::k + j * L::KS + o, k[i]);
-                st4(sm + L::a + j * L::KS + o, a[i]);
-            }
+        for (int i = 1; i < TPT; ++i) pr[i] = mul4(pr[i - 1], a[i]);
+        float4 x = pr[TPT - 1];            // inclusive product scan over the group's lanes
+#pragma unroll
+        for (int d = 1; d < LPC; d *= 2) {
+            const float yx = __shfl_up(x.x, d, LPC), yy = __shfl_up(x.y, d, LPC);
+            const float yz = __shfl_up(x.z, d, LPC), yw = __shfl_up(x.w, d, LPC);
+            if (l >= d) x = mul4(x, make_float4(yx, yy, yz, yw));
         }
-        if (t < kChunk) sm[L::be + t] = be;
+        float4 e = make_float4(__shfl_up(x.x, 1, LPC), __shfl_up(x.y, 1, LPC),
+                               __shfl_up(x.z, 1, LPC), __shfl_up(x.w, 1, LPC));
+        if (l == 0) e = make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            const float4 gm = mul4(e, pr[i]);
+            const float4 rg = make_float4(__builtin_amdgcn_rcpf(gm.x), __builtin_amdgcn_rcpf(gm.y),
+                                          __builtin_amdgcn_rcpf(gm.z), __builtin_amdgcn_rcpf(gm.w));
+            const int o = (j0 + i) * L::KS + 4 * cg;
+            st4(sm + L::rows(p, 0) + o, mul4(q[i], gm));
+            st4(sm + L::rows(p, 1) + o, mul4(k[i], gm));
+            st4(sm + L::rows(p, 2) + o, mul4(k[i], rg));
+        }
+        if (t < kChunk) sm[L::be + p * kChunk + t] = be;
+        bool bad = false;
+        if (l == LPC - 1) {
+            st4(sm + L::gam + p * DK + 4 * cg, x);
+            bad = !(x.x >= kMinGam && x.y >= kMinGam && x.z >= kMinGam && x.w >= kMinGam);
+        }
+        return bad;
     }
 
     __device__ __forceinline__ void store_v(float *sm, int t) const
@@ -116,7 +152,7 @@ struct KdaRows {
     }
 };
 
-// One token applied to the register tile by the recurrence itself (gate, key, value rows and beta
+// One token applied to the register tile by the recurrence itself (gate, key, query and value rows
 // in LDS), then its output o = S q: per row the column scale, the dot with k, the rank-1 update and
 // the dot with q; the four lanes that share a row add their parts by two exchanges.
 template <typename F>
@@ -158,12 +194,10 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
 {
     using F = MfmaTile<DV, DK, KpShape<DV, DK>::NW>;
     using L = KpLds<DV, DK>;
-    constexpr int NW = F::NW, IBW = F::IBW, KB = F::KB, KS = L::KS, VS = L::VS;
+    constexpr int NW = F::NW, IBW = F::IBW, KB = F::KB, KS = L::KS, VS = L::VS, KF = DK / 4;
     constexpr int NA = KB >= 2 ? 2 : KB;   // independent accumulators of the d_k products
     extern __shared__ float smem[];
-    float *sh_q = smem + L::q, *sh_k = smem + L::k, *sh_a = smem + L::a, *sh_v = smem + L::v;
-    float *sh_be = smem + L::be, *sh_qh = smem + L::qh, *sh_kh = smem + L::kh, *sh_kt = smem + L::kt;
-    float *sh_gam = smem + L::gam, *sh_A = smem + L::A, *sh_T = smem + L::T, *sh_M = smem + L::M;
+    float *sh_v = smem + L::v, *sh_A = smem + L::A, *sh_T = smem + L::T, *sh_M = smem + L::M;
     int *sh_flag = reinterpret_cast<int *>(smem + L::flag);
 
     const int B = a.d.B, H = a.d.H, T = a.T;
@@ -180,16 +214,18 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
     float *S0 = a.S0 + bh * (size_t)(DV * DK);
     ckpt_load<DV>(s, S0, t);
     tile_loaded(s);
-    rows.store_qka(smem, t);
-    if (t == 0) sh_flag[0] = 0;
+    auto derive = [&](int p) {
+        const unsigned long long bad = __ballot(rows.derive(smem, p, t));
+        if (lane == 0) sh_flag[4 * p + wv] = bad != 0;
+    };
+    derive(0);
 
-    // Barriers per chunk: (1) the raw q, k, a rows and beta are in LDS and every wave is done with
-    // the previous chunk (its value rows, the chunk-form rows and blocks may be rewritten);
-    // (2) the chunk-form rows and the flag are in LDS (the raw q, k, a rows are no longer read on
-    // the matrix-core path); (3) the A, T, M blocks are in LDS (beta is no longer read). The next
-    // chunk's raw q, k, a rows and beta are stored after (2) and (3), its value rows after (1).
+    // Barriers per chunk: (1) the chunk-form rows, beta, Gam_15 and the flags of this chunk are in
+    // LDS (written at the end of the previous one), and every wave is done with the previous chunk
+    // (the value rows and the blocks may be rewritten); (3) the value rows and the A, T, M blocks
+    // are in LDS. The next chunk's chunk-form rows go to the other buffer at the end of the chunk.
     for (int t0 = 0, n = 0; t0 < T; t0 += kChunk, ++n) {
-        const int ct = T - t0 < kChunk ? T - t0 : kChunk;
+        const int ct = T - t0 < kChunk ? T - t0 : kChunk, p = n & 1;
         __syncthreads();                                                             // (1)
         rows.store_v(smem, t);
         const bool more = t0 + kChunk < T;
@@ -198,150 +234,137 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
             rows.load(q0 + t1 * BH * DK, k0 + t1 * BH * DK, a0 + t1 * BH * DK, v0 + t1 * BH * DV,
                       b0 + t1 * BH, BH, T - (int)t1 < kChunk ? T - (int)t1 : kChunk, t);
         }
+        int slow = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) slow |= sh_flag[4 * p + w];
+        const float *sh_qh = smem + L::rows(p, 0), *sh_kh = smem + L::rows(p, 1);
+        const float *sh_kt = smem + L::rows(p, 2), *sh_be = smem + L::be + p * kChunk;
+        const float *sh_gam = smem + L::gam + p * DK;
 
-        // 1. the chunk-form rows, one key channel per thread: thread c < d_k forms kh and kt and
-        //    Gam_15, thread d_k + c forms qh; a channel whose product falls below kMinGam (or is
-        //    not a number) sends the chunk to the token path
-        if (t < 2 * DK) {
-            const int c = t < DK ? t : t - DK;
-            float gm = 1.f;
-            if (t < DK) {
-#pragma unroll
-                for (int j = 0; j < kChunk; ++j) {
-                    gm *= sh_a[j * KS + c];
-                    const float kv = sh_k[j * KS + c];
-                    sh_kh[j * KS + c] = kv * gm;
-                    sh_kt[j * KS + c] = kv / gm;
-                }
-                sh_gam[c] = gm;
-                if (!(gm >= kMinGam)) sh_flag[n & 1] = 1;
-            } else {
-#pragma unroll
-                for (int j = 0; j < kChunk; ++j) {
-                    gm *= sh_a[j * KS + c];
-                    sh_qh[j * KS + c] = sh_q[j * KS + c] * gm;
-                }
+        if (slow) {
+            // token path (some channel's gate product is below kMinGam): the raw q, k and gate rows
+            // of the chunk go to this chunk's buffer in place of the chunk-form rows
+            float *rq = smem + L::rows(p, 0), *rk = smem + L::rows(p, 1);
+            float *ra = smem + L::rows(p, 2);
+            for (int u = t; u < ct * KF; u += F::TPB) {
+                const int j = u / KF, o = 4 * (u - j * KF);
+                const size_t tk = (size_t)(t0 + j) * BH * DK + o;
+                st4(rq + j * KS + o, ld4(q0 + tk));
+                st4(rk + j * KS + o, ld4(k0 + tk));
+                st4(ra + j * KS + o, ld4(a0 + tk));
             }
-        }
-        if (t == 0) sh_flag[(n + 1) & 1] = 0;   // read last in the previous chunk, before (1)
-        __syncthreads();                                                             // (2)
-
-        if (sh_flag[n & 1]) {
-            // token path: the raw rows, token by token
+            __syncthreads();               // those rows and the value rows stored above
             for (int j = 0; j < ct; ++j)
-                token_step<F>(s, sh_k + j * KS, sh_a + j * KS, sh_q + j * KS, sh_v + j * VS,
-                              sh_be[j], o0 + (size_t)(t0 + j) * BH * DV);
-            if (more) {
-                __syncthreads();           // every wave is done with the raw rows
-                rows.store_qka(smem, t);
-            }
-            continue;
-        }
-
-        // 2. the S-independent blocks first, so that their latency overlaps the other waves'
-        //    matrix work: wave 0 A and T, wave 1 the masked M (wave 0 does both when alone); then
-        //    every wave F = Kh S^T and Qs = Qh S^T for its i-blocks. Wave 0's forward substitution
-        //    sits in the same straight-line code as its products; its store of T comes after them.
-        v4f fz[IBW], qs[IBW];
-        auto products = [&]() {
-#pragma unroll
-            for (int ib = 0; ib < IBW; ++ib) {
-                v4f fp[NA], qp[NA];
-#pragma unroll
-                for (int p = 0; p < NA; ++p) fp[p] = qp[p] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const float4 kv = ld4(sh_kh + cl * KS + 16 * kb + 4 * g);
-                    const float4 qv = ld4(sh_qh + cl * KS + 16 * kb + 4 * g);
-                    v4f &f = fp[kb % NA], &x = qp[kb % NA];
-                    f = mfma4(kv.x, s[ib][kb].x, f);
-                    f = mfma4(kv.y, s[ib][kb].y, f);
-                    f = mfma4(kv.z, s[ib][kb].z, f);
-                    f = mfma4(kv.w, s[ib][kb].w, f);
-                    x = mfma4(qv.x, s[ib][kb].x, x);
-                    x = mfma4(qv.y, s[ib][kb].y, x);
-                    x = mfma4(qv.z, s[ib][kb].z, x);
-                    x = mfma4(qv.w, s[ib][kb].w, x);
-                }
-                fz[ib] = tree_sum<NA>(fp);     // (S kh_q)[i] for q = 4 g + r, i = 16 ib' + c
-                qs[ib] = tree_sum<NA>(qp);     // (S qh_t)[i] for t = 4 g + r
-            }
-        };
-        auto m_block = [&]() {
-            const v4f m = row_dots16<KB, KS, NA, false>(sh_qh, sh_kt);   // qh_{4g+r} . kt_c
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sh_M[(4 * g + r) * kTS + cl] = cl <= 4 * g + r ? m[r] : 0.f;
-        };
-        if (wv == 0) {
-            if constexpr (NW == 1) m_block();
-            const v4f ak = row_dots16<KB, KS, NA, false>(sh_kh, sh_kt);  // kh_{4g+r} . kt_c
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sh_A[(4 * g + r) * kTS + cl] = ak[r];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            float tq[kChunk];
-            int q = cl;
-            asm volatile("" : "+v"(q));
-            t_solve_cols<kChunk, kTS>(sh_A, sh_be, tq, q);
-            products();
-            t_store_cols<kChunk, kTS>(tq, sh_T);
+                token_step<F>(s, rk + j * KS, ra + j * KS, rq + j * KS, sh_v + j * VS, sh_be[j],
+                              o0 + (size_t)(t0 + j) * BH * DV);
         } else {
-            if (wv == 1) m_block();
-            products();
-        }
-        mfma_settle();
-        __syncthreads();                                                             // (3)
+            // 2. the S-independent blocks first, so that their latency overlaps the other waves'
+            //    matrix work: wave 0 A and T, wave 1 the masked M (wave 0 does both when alone);
+            //    then every wave F = Kh S^T and Qs = Qh S^T for its i-blocks. Wave 0's forward
+            //    substitution sits in the same straight-line code as its products; its store of T
+            //    comes after them.
+            v4f fz[IBW], qs[IBW];
+            auto products = [&]() {
+#pragma unroll
+                for (int ib = 0; ib < IBW; ++ib) {
+                    v4f fp[NA], qp[NA];
+#pragma unroll
+                    for (int p = 0; p < NA; ++p) fp[p] = qp[p] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const float4 kv = ld4(sh_kh + cl * KS + 16 * kb + 4 * g);
+                        const float4 qv = ld4(sh_qh + cl * KS + 16 * kb + 4 * g);
+                        v4f &f = fp[kb % NA], &x = qp[kb % NA];
+                        f = mfma4(kv.x, s[ib][kb].x, f);
+                        f = mfma4(kv.y, s[ib][kb].y, f);
+                        f = mfma4(kv.z, s[ib][kb].z, f);
+                        f = mfma4(kv.w, s[ib][kb].w, f);
+                        x = mfma4(qv.x, s[ib][kb].x, x);
+                        x = mfma4(qv.y, s[ib][kb].y, x);
+                        x = mfma4(qv.z, s[ib][kb].z, x);
+                        x = mfma4(qv.w, s[ib][kb].w, x);
+                    }
+                    fz[ib] = tree_sum<NA>(fp);     // (S kh_q)[i] for q = 4 g + r, i = 16 ib' + c
+                    qs[ib] = tree_sum<NA>(qp);     // (S qh_t)[i] for t = 4 g + r
+                }
+            };
+            auto m_block = [&]() {
+                const v4f m = row_dots16<KB, KS, NA, false>(sh_qh, sh_kt);   // qh_{4g+r} . kt_c
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sh_M[(4 * g + r) * kTS + cl] = cl <= 4 * g + r ? m[r] : 0.f;
+            };
+            if (wv == 0) {
+                if constexpr (NW == 1) m_block();
+                const v4f ak = row_dots16<KB, KS, NA, false>(sh_kh, sh_kt);  // kh_{4g+r} . kt_c
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sh_A[(4 * g + r) * kTS + cl] = ak[r];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                float tq[kChunk];
+                int q = cl;
+                asm volatile("" : "+v"(q));
+                t_solve_cols<kChunk, kTS>(sh_A, sh_be, tq, q);
+                products();
+                t_store_cols<kChunk, kTS>(tq, sh_T);
+            } else {
+                if (wv == 1) m_block();
+                products();
+            }
+            mfma_settle();
+            __syncthreads();                                                             // (3)
 
-        // 3. M T, as (M T)^T = T^T M^T so that lane (g, c) ends with (M T)[t = c][q = 4 g + r], the
-        //    A operand of the output chain
-        v4f ut = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            ut = mfma4(sh_T[(4 * g + r) * kTS + cl], sh_M[cl * kTS + 4 * g + r], ut);
-        const float ua[4] = {ut[0], ut[1], ut[2], ut[3]};
-
-#pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            const int i = 16 * (wv * IBW + ib) + cl;
-            float zq[4];                   // Z[q = 4 g + r][i] = v_q[i] - (S kh_q)[i]
-#pragma unroll
-            for (int r = 0; r < 4; ++r) zq[r] = sh_v[(4 * g + r) * VS + i] - fz[ib][r];
-            // 4. outputs O = Qh S^T + (M T) Z
-            v4f uz = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) uz = mfma4(ua[r], zq[r], uz);
-            float ov[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ov[r] = qs[ib][r] + uz[r];
-            // keep these reads next to their chains rather than sunk into the stores below
-            asm volatile("" ::"v"(ov[0]), "v"(ov[1]), "v"(ov[2]), "v"(ov[3]));
-            float *oc = o0 + (size_t)t0 * BH * DV + i;
+            // 3. M T, as (M T)^T = T^T M^T so that lane (g, c) ends with (M T)[t = c][q = 4 g + r],
+            //    the A operand of the output chain
+            v4f ut = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (4 * g + r < ct) oc[(size_t)(4 * g + r) * BH * DV] = ov[r];
-            // 5. end of the chunk: U = T Z, S <- S diag(Gam_15) + U^T Kb, Kb_t = kt_t o Gam_15
-            const float4 tv = ld4(sh_T + cl * kTS + 4 * g);                  // T[t = c][4 g + r]
-            v4f cz = {0.f, 0.f, 0.f, 0.f};
-            cz = mfma4(tv.x, zq[0], cz);
-            cz = mfma4(tv.y, zq[1], cz);
-            cz = mfma4(tv.z, zq[2], cz);
-            cz = mfma4(tv.w, zq[3], cz);
+                ut = mfma4(sh_T[(4 * g + r) * kTS + cl], sh_M[cl * kTS + 4 * g + r], ut);
+            const float ua[4] = {ut[0], ut[1], ut[2], ut[3]};
+
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const float4 gs = ld4(sh_gam + 16 * kb + 4 * g);              // Gam_15 of the lane's columns
-                const float gk = sh_gam[16 * kb + cl];                         // Gam_15 of key 16 kb + c
-                v4f u = {gs.x * s[ib][kb].x, gs.y * s[ib][kb].y, gs.z * s[ib][kb].z, gs.w * s[ib][kb].w};
-                const float *kr = sh_kt + (4 * g) * KS + 16 * kb + cl;         // kt[t][16 kb + c]
-                u = mfma4(gk * kr[0], cz[0], u);
-                u = mfma4(gk * kr[KS], cz[1], u);
-                u = mfma4(gk * kr[2 * KS], cz[2], u);
-                u = mfma4(gk * kr[3 * KS], cz[3], u);
-                s[ib][kb] = make_float4(u[0], u[1], u[2], u[3]);
+            for (int ib = 0; ib < IBW; ++ib) {
+                const int i = 16 * (wv * IBW + ib) + cl;
+                float zq[4];                   // Z[q = 4 g + r][i] = v_q[i] - (S kh_q)[i]
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zq[r] = sh_v[(4 * g + r) * VS + i] - fz[ib][r];
+                // 4. outputs O = Qh S^T + (M T) Z
+                v4f uz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) uz = mfma4(ua[r], zq[r], uz);
+                float ov[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ov[r] = qs[ib][r] + uz[r];
+                // keep these reads next to their chains rather than sunk into the stores below
+                asm volatile("" ::"v"(ov[0]), "v"(ov[1]), "v"(ov[2]), "v"(ov[3]));
+                float *oc = o0 + (size_t)t0 * BH * DV + i;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r < ct) oc[(size_t)(4 * g + r) * BH * DV] = ov[r];
+                // 5. end of the chunk: U = T Z, S <- (S + U^T Kt) diag(Gam_15) (the column scale
+                //    taken after the update, the same as S diag(Gam_15) + U^T Kb)
+                const float4 tv = ld4(sh_T + cl * kTS + 4 * g);              // T[t = c][4 g + r]
+                v4f cz = {0.f, 0.f, 0.f, 0.f};
+                cz = mfma4(tv.x, zq[0], cz);
+                cz = mfma4(tv.y, zq[1], cz);
+                cz = mfma4(tv.z, zq[2], cz);
+                cz = mfma4(tv.w, zq[3], cz);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    v4f u = {s[ib][kb].x, s[ib][kb].y, s[ib][kb].z, s[ib][kb].w};
+                    const float *kr = sh_kt + (4 * g) * KS + 16 * kb + cl;     // kt[t][16 kb + c]
+                    u = mfma4(kr[0], cz[0], u);
+                    u = mfma4(kr[KS], cz[1], u);
+                    u = mfma4(kr[2 * KS], cz[2], u);
+                    u = mfma4(kr[3 * KS], cz[3], u);
+                    const float4 gs = ld4(sh_gam + 16 * kb + 4 * g);   // Gam_15, lane's columns
+                    s[ib][kb] = make_float4(gs.x * u[0], gs.y * u[1], gs.z * u[2], gs.w * u[3]);
+                }
             }
+            mfma_settle();
         }
-        mfma_settle();
-        if (more) rows.store_qka(smem, t);
+        if (more) derive(p ^ 1);
     }
 
     // the final state is the new checkpoint; the ring is empty
