@@ -62,6 +62,27 @@ __device__ __forceinline__ float4 mul4(float4 x, float4 y)
     return make_float4(x.x * y.x, x.y * y.y, x.z * y.z, x.w * y.w);
 }
 
+// The value of the lane D places lower in the same 16-lane row (a DPP row shift; lanes below D
+// get 0).
+template <int D>
+__device__ __forceinline__ float4 row_shr4(float4 v)
+{
+    auto sh = [](float x) {
+        const int r = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xF, 0xF, true);
+        return __int_as_float(r);
+    };
+    return make_float4(sh(v.x), sh(v.y), sh(v.z), sh(v.w));
+}
+
+// Step D of an inclusive product scan over groups of lanes aligned inside 16-lane rows (l = the
+// lane's index in its group).
+template <int D>
+__device__ __forceinline__ void scan_mul_step(float4 &x, int l)
+{
+    const float4 y = row_shr4<D>(x);
+    if (l >= D) x = mul4(x, y);
+}
+
 // The chunk's raw rows in registers between their load and their LDS store. Thread t holds the q,
 // k and gate units of channels 4 cg .. 4 cg + 3 (cg = t / LPC) for TPT consecutive tokens, so
 // that the LPC lanes of a channel group cover the chunk and the gate products are a scan across
@@ -73,7 +94,8 @@ struct KdaRows {
     static constexpr int TPB = KpShape<DV, DK>::TPB, KF = DK / 4, VF = DV / 4;
     static constexpr int TPT = kChunk * KF / TPB, LPC = kChunk / TPT;
     static constexpr int VQ = (kChunk * VF + TPB - 1) / TPB;
-    static_assert(TPT * TPB == kChunk * KF && (TPT == 1 || TPT == 2) && 64 % LPC == 0, "row map");
+    static_assert(TPT * TPB == kChunk * KF && (TPT == 1 || TPT == 2) && (LPC == 8 || LPC == 16),
+                  "row map: a channel group's lanes sit inside one 16-lane row");
     float4 q[TPT], k[TPT], a[TPT], v[VQ];
     float be;
 
@@ -113,14 +135,11 @@ struct KdaRows {
 #pragma unroll
         for (int i = 1; i < TPT; ++i) pr[i] = mul4(pr[i - 1], a[i]);
         float4 x = pr[TPT - 1];            // inclusive product scan over the group's lanes
-#pragma unroll
-        for (int d = 1; d < LPC; d *= 2) {
-            const float yx = __shfl_up(x.x, d, LPC), yy = __shfl_up(x.y, d, LPC);
-            const float yz = __shfl_up(x.z, d, LPC), yw = __shfl_up(x.w, d, LPC);
-            if (l >= d) x = mul4(x, make_float4(yx, yy, yz, yw));
-        }
-        float4 e = make_float4(__shfl_up(x.x, 1, LPC), __shfl_up(x.y, 1, LPC),
-                               __shfl_up(x.z, 1, LPC), __shfl_up(x.w, 1, LPC));
+        scan_mul_step<1>(x, l);
+        scan_mul_step<2>(x, l);
+        scan_mul_step<4>(x, l);
+        if constexpr (LPC == 16) scan_mul_step<8>(x, l);
+        float4 e = row_shr4<1>(x);         // exclusive: the earlier lanes' product
         if (l == 0) e = make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
