@@ -28,6 +28,7 @@
 #include "tile_order.h"
 #include "mfma_tile.h"
 #include "gdn_layout.h"
+#include "gdn_chunk.h"
 
 namespace rssm {
 namespace {
@@ -218,14 +219,153 @@ __device__ __forceinline__ void kda_fold_tile(TileRegs<DV, DK> &s,
             p += bfly<16>(p);
             p += __shfl_xor(p, 32);
             const float cf = be * (sh_v[j * RW::VS + row] - p);
+            int ko = j * RW::KS + 4 * g;
+            asm volatile("" : "+v"(ko));
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const float4 k4 = ld4(kr + 16 * kb);
+                const float4 k4 = ld4(sh_k + ko + 16 * kb);
                 float4 &x = s[ib][kb];
                 x.x += cf * k4.x; x.y += cf * k4.y; x.z += cf * k4.z; x.w += cf * k4.w;
             }
         }
     }
+}
+
+// The fold on the matrix cores. With Gam_j = a_0 o ... o a_j the gates' running product over the
+// entries (per key channel), kh_j = k_j o Gam_j, kt_j = k_j / Gam_j and A[t][j] = kh_t . kt_j, the n
+// entries applied in order give (the chunk form of the Kimi Delta Attention prefill)
+//     S <- (S + U^T Kt) diag(Gam_{n-1}),   U = T (V - Kh S^T),
+// with T the lower-triangular factor of the delta rule's WY form taken over A (gdn_chunk.h). The
+// ratios Gam_t / Gam_j sit on the two operands, so the form is taken when every channel's product
+// stays at or above 2^-64 (then 1 / Gam_j <= 2^64); otherwise, and for more than 16 entries, the
+// entries are folded one by one on the vector units (kda_fold_tile).
+constexpr float kMinGamFold = 0x1p-64f;
+
+// LDS floats of the matrix-core fold beside the staged rows: kh and kt rows [16][d_k+4], beta of 16
+// rows, the A and T blocks [16][20], Gam [d_k] and a flag per wave.
+template <int DV, int DK>
+__host__ __device__ constexpr int kda_mfold_floats()
+{
+    return 2 * kChunk * (DK + 4) + kChunk + 2 * kChunk * kTS + DK + 16;
+}
+
+// Fold entries 0..n-1 (rows staged in LDS as for kda_fold_tile, oldest first) into the register
+// tile, then hand the tile to `done` (which stores it). mf: whether the matrix-core form may be used
+// (its LDS `ext` of kda_mfold_floats floats is there); n and mf are uniform over the workgroup. All
+// threads call it; it holds two barriers on the matrix-core path, one on the other. Each path ends
+// in its own call of `done`, so that no tile value is live where the paths join (a join there
+// kept two copies of the tile in registers).
+template <int DV, int DK, typename Done>
+__device__ __forceinline__ void kda_fold_any(TileRegs<DV, DK> &s, const float *sh_k,
+                                             const float *sh_a, const float *sh_v,
+                                             const float *sh_be, int n, bool mf, float *ext,
+                                             Done done)
+{
+    using F = MfmaTile<DV, DK>;
+    using RW = Rows<DV, DK>;
+    constexpr int IBW = F::IBW, KB = F::KB, NW = F::NW, KS = RW::KS, VS = RW::VS;
+    constexpr int NA = KB >= 2 ? 2 : 1;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
+    float *sh_kh = ext;                        // [16][KS]
+    float *sh_kt = sh_kh + kChunk * KS;        // [16][KS]
+    float *sh_b = sh_kt + kChunk * KS;         // [16]  beta, 0 past n
+    float *sh_A = sh_b + kChunk;               // [16][kTS]
+    float *sh_T = sh_A + kChunk * kTS;         // [16][kTS]
+    float *sh_gam = sh_T + kChunk * kTS;       // [DK]
+    int *sh_flag = reinterpret_cast<int *>(sh_gam + DK);   // [NW]
+
+    // 1. one key channel per thread: the running product, kh and kt (zero rows past n), Gam_{n-1};
+    //    then one call site of the vector fold (a second inlined copy costs registers)
+    int slow = 1;
+    if (mf && n <= kChunk) {
+        bool bad = false;
+        if (t < DK) {
+            float gm = 1.f;
+            for (int j = 0; j < kChunk; ++j) {
+                float kh = 0.f, kt = 0.f;
+                if (j < n) {
+                    gm *= sh_a[j * KS + t];
+                    const float kv = sh_k[j * KS + t];
+                    kh = kv * gm;
+                    kt = kv * __builtin_amdgcn_rcpf(gm);
+                }
+                sh_kh[j * KS + t] = kh;
+                sh_kt[j * KS + t] = kt;
+            }
+            sh_gam[t] = gm;
+            bad = !(gm >= kMinGamFold);
+        }
+        if (t < kChunk) sh_b[t] = t < n ? sh_be[t] : 0.f;
+        const unsigned long long bw = __ballot(bad);
+        if (lane == 0) sh_flag[wv] = bw != 0;
+        __syncthreads();
+        slow = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) slow |= sh_flag[w];
+    }
+    if (slow) {
+        kda_fold_tile<DV, DK>(s, sh_k, sh_a, sh_v, sh_be, n);
+        done(s);
+        return;
+    }
+
+    // 2. wave 0: A = Kh Kt^T on the matrix cores and T in registers; every wave:
+    //    Z = V - Kh S^T for its i-blocks (rows past n zero)
+    if (wv == 0) {
+        const v4f ak = row_dots16<KB, KS, NA, false>(sh_kh, sh_kt);      // kh_{4g+r} . kt_c
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sh_A[(4 * g + r) * kTS + cl] = ak[r];
+        wave_sync_lds();
+        t_solve_regs<kChunk, kTS, kTS>(sh_A, sh_b, sh_T);
+    }
+    v4f fz[IBW];
+#pragma unroll
+    for (int ib = 0; ib < IBW; ++ib) {
+        const int i = 16 * (wv * IBW + ib) + cl;
+        v4f fp[NA];
+#pragma unroll
+        for (int p = 0; p < NA; ++p) fp[p] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const float4 kv = ld4(sh_kh + cl * KS + 16 * kb + 4 * g);
+            v4f &f = fp[kb % NA];
+            f = mfma4(kv.x, s[ib][kb].x, f);
+            f = mfma4(kv.y, s[ib][kb].y, f);
+            f = mfma4(kv.z, s[ib][kb].z, f);
+            f = mfma4(kv.w, s[ib][kb].w, f);
+        }
+        const v4f acc = tree_sum<NA>(fp);      // (S kh_q)[i] for q = 4 g + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int q = 4 * g + r;
+            fz[ib][r] = q < n ? sh_v[q * VS + i] - acc[r] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // 3. U = T Z, S <- (S + U^T Kt) diag(Gam_{n-1})
+#pragma unroll
+    for (int ib = 0; ib < IBW; ++ib) {
+        const float4 tv = ld4(sh_T + cl * kTS + 4 * g);                    // T[t = c][4 g + r]
+        v4f cz = {0.f, 0.f, 0.f, 0.f};
+        cz = mfma4(tv.x, fz[ib][0], cz);
+        cz = mfma4(tv.y, fz[ib][1], cz);
+        cz = mfma4(tv.z, fz[ib][2], cz);
+        cz = mfma4(tv.w, fz[ib][3], cz);       // U[t][i] for t = 4 g + r, i = 16 ib' + c
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            v4f u = {s[ib][kb].x, s[ib][kb].y, s[ib][kb].z, s[ib][kb].w};
+            const float *kr = sh_kt + (4 * g) * KS + 16 * kb + cl;           // kt[t][16 kb + c]
+            u = mfma4(kr[0], cz[0], u);
+            u = mfma4(kr[KS], cz[1], u);
+            u = mfma4(kr[2 * KS], cz[2], u);
+            u = mfma4(kr[3 * KS], cz[3], u);
+            const float4 gs = ld4(sh_gam + 16 * kb + 4 * g);
+            s[ib][kb] = make_float4(gs.x * u[0], gs.y * u[1], gs.z * u[2], gs.w * u[3]);
+        }
+    }
+    mfma_settle();
+    done(s);
 }
 
 // o[row] = S r (r in LDS, d_k floats) for the wave's rows, plus extra[row] (added by the g = 0
@@ -248,12 +388,19 @@ __device__ __forceinline__ float tile_gemv_row(const TileRegs<DV, DK> &s,
 // ------------------------------------------------------------------------------------------
 // decode
 // ------------------------------------------------------------------------------------------
+// Start of the matrix-core fold's LDS after rows of `floats` floats (16-byte aligned).
+__host__ __device__ constexpr int kda_ext_off(int floats) { return (floats + 3) & ~3; }
+
 template <int DV, int DK>
-__host__ __device__ constexpr int kda_decode_lds(int W)
+__host__ __device__ constexpr int kda_decode_lds(int W, bool fold)
 {
-    // rows of up to W + 1 entries (a fold after a full commit takes the ring and the token), the
-    // query, and per wave r [DK] and the coefficients [W + 1]
-    return Rows<DV, DK>::floats(W + 1) + DK + (MfmaTile<DV, DK>::NW) * (DK + 36);
+    // rows of up to W + 1 entries (a fold after a full commit takes the ring and the token); the
+    // replay adds the query and per wave r [DK] and the coefficients [W + 1], the step that folds
+    // the matrix-core fold's blocks (W <= 16)
+    const int rows = Rows<DV, DK>::floats(W + 1);
+    const int replay = rows + DK + (MfmaTile<DV, DK>::NW) * (DK + 36);
+    const int mfold = kda_ext_off(rows) + (W <= kChunk ? kda_mfold_floats<DV, DK>() : 0);
+    return fold && mfold > replay ? mfold : replay;
 }
 
 // Replay step (len + 1 < W). LOAD: read the tile here after the ring loads went out.
@@ -337,15 +484,17 @@ __device__ __forceinline__ void kda_fold_decode(const GdnStepArgs &a, const KTil
                                a.v + c.bh * DV, 0, sh_k, sh_a, sh_v};
     stage_rows<DV, DK, TPB>(er, n, [&] { ckpt_load<DV>(s, S0, t); });
     __syncthreads();
-    kda_fold_tile<DV, DK>(s, sh_k, sh_a, sh_v, sh_be, n);
-    ckpt_store<DV>(s, S0, t);
+    kda_fold_any<DV, DK>(s, sh_k, sh_a, sh_v, sh_be, n, W <= kChunk,
+                         smem + kda_ext_off(Rows<DV, DK>::floats(W + 1)), [&](TileRegs<DV, DK> &f) {
+        ckpt_store<DV>(f, S0, t);
 #pragma unroll
-    for (int ib = 0; ib < IBW; ++ib) {
-        float p = tile_gemv_row<DV, DK>(s, ib, qt);
-        p += bfly<16>(p);
-        p += __shfl_xor(p, 32);
-        if (g == 0) a.o[c.bh * DV + 16 * (wv * IBW + ib) + cl] = p;
-    }
+        for (int ib = 0; ib < IBW; ++ib) {
+            float p = tile_gemv_row<DV, DK>(f, ib, qt);
+            p += bfly<16>(p);
+            p += __shfl_xor(p, 32);
+            if (g == 0) a.o[c.bh * DV + 16 * (wv * IBW + ib) + cl] = p;
+        }
+    });
 }
 
 // Variants as the Gated DeltaNet decode: 0 = every sequence at (a.uhead, a.ulen), none folds;
@@ -389,7 +538,7 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (MODE == 2 ? KdaFold
 template <int DV, int DK>
 __host__ __device__ constexpr int kda_fold_lds(int W)
 {
-    return Rows<DV, DK>::floats(W);
+    return kda_ext_off(Rows<DV, DK>::floats(W)) + (W <= kChunk ? kda_mfold_floats<DV, DK>() : 0);
 }
 
 template <int DV, int DK>
@@ -430,17 +579,19 @@ __global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (KdaFoldOcc<DV, DK>:
     const EntryRows<DV, DK> er{a.ring, c, head, len, a.ring.k, a.ring.alpha, a.ring.v, 0, sh_k, sh_a, sh_v};
     stage_rows<DV, DK, TPB>(er, len, [&] { ckpt_load<DV>(s, S0, t); });
     __syncthreads();
-    kda_fold_tile<DV, DK>(s, sh_k, sh_a, sh_v, sh_be, len);
-    if (a.out) {
+    kda_fold_any<DV, DK>(s, sh_k, sh_a, sh_v, sh_be, len, W <= kChunk,
+                         smem + kda_ext_off(Rows<DV, DK>::floats(W)), [&](TileRegs<DV, DK> &f) {
+        if (a.out) {
 #pragma unroll
-        for (int ib = 0; ib < IBW; ++ib) {
-            float *p = a.out + c.bh * (size_t)(DV * DK) + mfma_tile_offset<DV, DK>(t, ib);
+            for (int ib = 0; ib < IBW; ++ib) {
+                float *p = a.out + c.bh * (size_t)(DV * DK) + mfma_tile_offset<DV, DK>(t, ib);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) st4(p + 16 * kb, s[ib][kb]);
+                for (int kb = 0; kb < KB; ++kb) st4(p + 16 * kb, f[ib][kb]);
+            }
+        } else {
+            ckpt_store<DV>(f, S0, t);
         }
-    } else {
-        ckpt_store<DV>(s, S0, t);
-    }
+    });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -656,7 +807,7 @@ template <int DV, int DK>
 hipError_t go_decode(const GdnStepArgs &a, int mode, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(TileShape<DV, DK>::TPB);
-    const size_t lds = 4 * (size_t)kda_decode_lds<DV, DK>(a.d.W);
+    const size_t lds = 4 * (size_t)kda_decode_lds<DV, DK>(a.d.W, mode == 2);
     if (mode == 0) hipLaunchKernelGGL((k_kda_decode<DV, DK, 0>), grid, block, lds, s, a);
     else if (mode == 1) hipLaunchKernelGGL((k_kda_decode<DV, DK, 1>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_kda_decode<DV, DK, 2>), grid, block, lds, s, a);
@@ -705,7 +856,7 @@ bool kda_supported(int DV, int DK)
 
 size_t kda_lds_bytes(int DV, int DK, int W, int K)
 {
-#define RSSM_C(v, k) if (DV == v && DK == k) { const size_t d = kda_decode_lds<v, k>(W), \
+#define RSSM_C(v, k) if (DV == v && DK == k) { const size_t d = kda_decode_lds<v, k>(W, true), \
     e = kda_verify_lds<v, k>(W, K); return 4 * (d > e ? d : e); }
     RSSM_KDA_SHAPES(RSSM_C)
 #undef RSSM_C

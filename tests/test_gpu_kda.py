@@ -320,6 +320,36 @@ def test_kda_prefill_after_buffered_entries():
         assert l == [0] * sh.batch and e == 0
 
 
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_kda_fold_vector_path_windows(d):
+    """Windows whose gate product in some key channel falls below 2^-64 (a run of gates 1e-6 in a
+    few channels, one gate of exactly 0) are folded entry by entry on the vector units, the rest of
+    the same launches on the matrix cores: every output, the materialised state (which folds the
+    buffered entries) and the bookkeeping after every step, W = 16."""
+    sh = wl.GDNShape(batch=2, nheads=3, d_k=d, d_v=d, window=16)
+    T = 40
+    say(f"kda fold vector-path windows d={d}")
+    s0 = wl.kda_state0(sh, 8)
+    ins = wl.kda_token_inputs(sh, 8, 0, ntok=T)
+    ins["alpha"][3:12, 0, 1, :3] = 1e-6         # first window of tile (0, 1)
+    ins["alpha"][20, 1, 2, d - 1] = 0.0         # second window of tile (1, 2)
+    dd = kda_dev_tokens(sh, ins, T)
+    ctx = _ctx(sh)
+    ctx.init_checkpoint(dev(s0))
+    model = Bookkeeping(sh.batch, sh.window)
+    ref = s0.astype(np.float64).copy()
+    o = torch.empty(sh.batch, sh.nheads, d, device="cuda")
+    mat = torch.empty(s0.shape, device="cuda")
+    for t in range(T):
+        ctx.decode_step(o, **{k: v[t] for k, v in dd.items()})
+        o_ref = _ref_step(ins, t, ref)
+        model.decode()
+        assert normwise_err(host(o), o_ref) < TOL, t
+        _check_bk(ctx, model)
+        ctx.materialize(mat)
+        assert normwise_err(host(mat), ref) < TOL, t
+
+
 def _prefill_against_oracle(sh, s0, ins, T):
     dd = kda_dev_tokens(sh, ins, T)
     ctx = _ctx(sh)
