@@ -265,7 +265,8 @@ __device__ __forceinline__ void kda_fold_any(TileRegs<DV, DK> &s, const float *s
     using RW = Rows<DV, DK>;
     constexpr int IBW = F::IBW, KB = F::KB, NW = F::NW, KS = RW::KS, VS = RW::VS;
     constexpr int NA = KB >= 2 ? 2 : 1;
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 4, cl = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
     float *sh_kh = ext;                        // [16][KS]
     float *sh_kt = sh_kh + kChunk * KS;        // [16][KS]
     float *sh_b = sh_kt + kChunk * KS;         // [16]  beta, 0 past n
