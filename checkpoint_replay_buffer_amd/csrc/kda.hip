@@ -613,8 +613,10 @@ __host__ __device__ constexpr int kda_verify_lds(int W, int K)
     return Rows<DV, DK>::floats(W16) + K16 * (DK + 4) + K16 * (W16 + 4);
 }
 
+// Compiled for eight waves per SIMD at 128 x 128 (at most 64 VGPRs, no spills): four workgroups per
+// compute unit, which its LDS allows at W <= 16 (three at 65 VGPRs).
 template <int DV, int DK, int NJB>
-__global__ void __launch_bounds__((TileShape<DV, DK>::TPB)) k_kda_verify(GdnStepArgs a)
+__global__ void __launch_bounds__((TileShape<DV, DK>::TPB), (TileShape<DV, DK>::TPB == 512 ? 8 : 1)) k_kda_verify(GdnStepArgs a)
 {
     using F = MfmaTile<DV, DK>;
     using RW = Rows<DV, DK>;
