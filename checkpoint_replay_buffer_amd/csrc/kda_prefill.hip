@@ -18,7 +18,8 @@
 // with T the lower-triangular factor of the delta rule's WY form (gdn_chunk.h) taken over A in
 // place of the Gram block;
 //     O = Qh S^T + M U,  M[t][j] = qh_t . kt_j for j <= t (else 0);
-// and the chunk ends in S diag(Gam_15) + U^T Kb, Kb_j = kt_j o Gam_15. Every product is a
+// and the chunk ends in S diag(Gam_15) + U^T Kb, Kb_j = kt_j o Gam_15, formed as
+// (S + U^T Kt) diag(Gam_15). Every product is a
 // v_mfma_f32_16x16x4_f32 chain on the register-resident tile of mfma_tile.h, as in the Gated
 // DeltaNet prefill. Splitting Gam_t / Gam_j over the two operands needs 1 / Gam_j to stay finite: a
 // chunk in which some channel's gate product falls below 2^-64 is applied token by token instead
@@ -241,7 +242,7 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
 
     // Barriers per chunk: (1) the chunk-form rows, beta, Gam_15 and the flags of this chunk are in
     // LDS (written at the end of the previous one), and every wave is done with the previous chunk
-    // (the value rows and the blocks may be rewritten); (3) the value rows and the A, T, M blocks
+    // (the value rows and the blocks may be rewritten); (2) the value rows and the A, T, M blocks
     // are in LDS. The next chunk's chunk-form rows go to the other buffer at the end of the chunk.
     for (int t0 = 0, n = 0; t0 < T; t0 += kChunk, ++n) {
         const int ct = T - t0 < kChunk ? T - t0 : kChunk, p = n & 1;
@@ -332,7 +333,7 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
                 products();
             }
             mfma_settle();
-            __syncthreads();                                                             // (3)
+            __syncthreads();                                                             // (2)
 
             // 3. M T, as (M T)^T = T^T M^T so that lane (g, c) ends with (M T)[t = c][q = 4 g + r],
             //    the A operand of the output chain
