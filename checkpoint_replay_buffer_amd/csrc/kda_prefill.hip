@@ -279,8 +279,10 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
                               o0 + (size_t)(t0 + j) * BH * DV);
         } else {
             // 2. the S-independent blocks first, so that their latency overlaps the other waves'
-            //    matrix work: wave 0 A and T, wave 1 the masked M (wave 0 does both when alone);
-            //    then every wave F = Kh S^T and Qs = Qh S^T for its i-blocks. Wave 0's forward
+            //    matrix work: wave hv A and T, the next wave the masked M (one wave does both when
+            //    alone); then every wave F = Kh S^T and Qs = Qh S^T for its i-blocks. The roles
+            //    move from wave to wave with the chunk and the tile, so that the two workgroups on a
+            //    compute unit do not both load the same SIMD with them. Wave hv's forward
             //    substitution sits in the same straight-line code as its products; its store of T
             //    comes after them.
             v4f fz[IBW], qs[IBW];
@@ -314,7 +316,8 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
                 for (int r = 0; r < 4; ++r)
                     sh_M[(4 * g + r) * kTS + cl] = cl <= 4 * g + r ? m[r] : 0.f;
             };
-            if (wv == 0) {
+            const int hv = (n + tile) % NW;    // the wave with the extra roles this chunk
+            if (wv == hv) {
                 if constexpr (NW == 1) m_block();
                 const v4f ak = row_dots16<KB, KS, NA, false>(sh_kh, sh_kt);  // kh_{4g+r} . kt_c
 #pragma unroll
@@ -329,7 +332,7 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
                 products();
                 t_store_cols<kChunk, kTS>(tq, sh_T);
             } else {
-                if (wv == 1) m_block();
+                if (wv == (hv + 1) % NW) m_block();
                 products();
             }
             mfma_settle();
