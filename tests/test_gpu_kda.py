@@ -451,11 +451,11 @@ def test_kda_prefill_serving_shape_sampled():
 # ---------------------------------------------------------------------------------------------
 
 def test_kda_serving_shape_sampled():
-    """Batch 256, 32 heads, 128 x 128, W = 16, 96 steps: sampled sequences against the oracle
-    every step, every sequence against the conventional kernel every 32 steps, the materialised
-    state and bookkeeping at the end."""
+    """Batch 256, 32 heads, 128 x 128, W = 16, 512 steps over a 32-slot token pool (the
+    benchmark's schedule): sampled sequences against the oracle every step, every sequence against
+    the conventional kernel every 32 steps, the materialised state and bookkeeping at the end."""
     sh = wl.KDA_SERVE
-    steps, pool_n = 96, 16
+    steps, pool_n = 512, 32
     say("kda serving shape: generating inputs")
     s0 = wl.kda_state0(sh, 0)
     slots = [wl.kda_token_inputs(sh, 0, s) for s in range(pool_n)]
