@@ -60,11 +60,19 @@ __device__ __forceinline__ float lane_of(float v, int lane)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Sum over the 64 lanes of the wave; every lane must take part.
+// Sum over the 64 lanes of the wave, returned wave-uniform: the DPP butterfly inside each 16-lane
+// row, then the four row sums read from lanes 0, 16, 32 and 48. No LDS crossbar round trip, which
+// the dependent chain of such sums in the recursion below would otherwise wait on at every entry.
+// Every lane must take part.
 __device__ __forceinline__ float wave_sum(float v)
 {
-    v = group_sum<32>(v);
-    return v + __shfl_xor(v, 32);
+    v = group_sum<16>(v);
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Columns of r per lane in the recursion: lane l holds columns CPL l .. CPL l + CPL - 1 (lanes
@@ -87,9 +95,10 @@ __device__ __forceinline__ float kda_recursion(const float *sh_k, const float *s
     const bool on = col < DK;
     float r0 = on ? qrow[col] : 0.f, r1 = (CPL == 2 && on) ? qrow[col + 1] : 0.f;
     float bc = 0.f;
-    for (int j = m - 1; j >= 0; --j) {
-        float k0 = 0.f, k1 = 0.f, a0 = 0.f, a1 = 0.f;
-        if (on) {
+    // the key and gate values of entry j, loaded one entry ahead of their use
+    auto rows = [&](int j, float &k0, float &k1, float &a0, float &a1) {
+        k0 = k1 = a0 = a1 = 0.f;
+        if (on && j >= 0) {
             if constexpr (CPL == 2) {
                 const float2 kv = *reinterpret_cast<const float2 *>(sh_k + j * KS + col);
                 const float2 av = *reinterpret_cast<const float2 *>(sh_a + j * KS + col);
@@ -99,6 +108,12 @@ __device__ __forceinline__ float kda_recursion(const float *sh_k, const float *s
                 a0 = sh_a[j * KS + col];
             }
         }
+    };
+    float nk0, nk1, na0, na1;
+    rows(m - 1, nk0, nk1, na0, na1);
+    for (int j = m - 1; j >= 0; --j) {
+        const float k0 = nk0, k1 = nk1, a0 = na0, a1 = na1;
+        rows(j - 1, nk0, nk1, na0, na1);
         const float c = wave_sum(k0 * r0 + k1 * r1);
         const float b = lane_of(bel, j) * c;
         if (lane == j) bc = b;
