@@ -113,6 +113,13 @@ __device__ __forceinline__ float4 sum_partials(const float4 (&p)[NW])
     }
 }
 
+// float4 at a byte offset from a base pointer: with a wave-uniform base the load takes the
+// scalar-base form and the lane offset stays one 32-bit register.
+__device__ __forceinline__ float4 ld4_at(const float *base, uint32_t off)
+{
+    return *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(base) + off);
+}
+
 // The chunk's rows of x, B, C and dt held in registers between their load and their LDS store.
 // Lane t takes float4 i = t + q TPB of the chunk's rows (row i / PF of x, i / NF of B and C). The
 // addresses are formed at each load from t and the (uniform) row bases, not kept in registers
@@ -149,6 +156,32 @@ struct ChunkRows {
         // a full chunk: lanes t >= 16 load a row too, and only lanes t < 16 keep theirs
         const int jt = ct == kChunk ? (t & (kChunk - 1)) : t;
         dt = ct == kChunk || t < ct ? db[(size_t)jt * BH] : 0.f;
+    }
+
+    // The same for a full chunk whose rows lie within 4 GiB of its first row: no predicates, and
+    // every address is the (uniform) row base plus a 32-bit lane offset in bytes.
+    __device__ __forceinline__ void load_full(const float *xb, const float *bb, const float *cb,
+                                              const float *db, uint32_t BH, uint32_t BG, int t)
+    {
+        asm volatile("" : "+v"(t));
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int i = t + q * TPB, j = i / PF, o = (i - j * PF) * 16;
+            if (XQ * TPB == kChunk * PF || i < kChunk * PF)
+                x[q] = ld4_at(xb, (uint32_t)j * (BH * (4u * P)) + (uint32_t)o);
+        }
+#pragma unroll
+        for (int q = 0; q < BQ; ++q) {
+            const int i = t + q * TPB, j = i / NF, o = (i - j * NF) * 16;
+            if (BQ * TPB == kChunk * NF || i < kChunk * NF) {
+                const uint32_t e = (uint32_t)j * (BG * (4u * N)) + (uint32_t)o;
+                b[q] = ld4_at(bb, e);
+                c[q] = ld4_at(cb, e);
+            }
+        }
+        // lanes t >= 16 load a row too, and only lanes t < 16 keep theirs
+        dt = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(db) +
+                                              (uint32_t)(t & (kChunk - 1)) * (4u * BH));
     }
 
     __device__ __forceinline__ void store(float *sh_x, float *sh_B, float *sh_C, float *sh_dt, int t) const
@@ -198,6 +231,9 @@ __global__ void __launch_bounds__((PrefillShape<P, N>::TPB), (PrefillShape<P, N>
     const int tile = blockIdx.x, b = tile / H, h = tile - b * H, g0 = h / (H / G);
     const size_t bh = (size_t)tile, bg = (size_t)b * G + g0;
     const size_t BH = (size_t)B * H, BG = (size_t)B * G;
+    // a chunk's rows span 16 token strides of B H (x, dt) or B G (B, C) rows: 32-bit byte
+    // offsets reach them all
+    const bool narrow = (BH * P > BG * N ? BH * P : BG * N) * 4 * kChunk <= 0xFFFFFFFFull;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, g = lane >> 4, cl = lane & 15;
     const float Ah = a.A[h], Dh = a.D[h];
 
@@ -218,9 +254,13 @@ __global__ void __launch_bounds__((PrefillShape<P, N>::TPB), (PrefillShape<P, N>
     tile_loaded(s);
 
     // One chunk of tokens t0 .. t0 + ct - 1. FULL (ct = 16, every chunk but a ragged last one)
-    // stores every output row without predicates, so the chunk is straight-line code.
-    auto chunk = [&](auto full, int t0, int buf) {
-        constexpr bool FULL = decltype(full)::value;
+    // stores every output row without predicates, so the chunk is straight-line code. NEXT_FULL:
+    // the next chunk is full too and its rows take the unpredicated 32-bit-offset load. Each
+    // kind of load has its own copy of the chunk: a load path that joins the other one would make
+    // the compiler wait, before the loads, for every memory operation still in flight (the
+    // previous chunk's output stores among them).
+    auto chunk = [&](auto full, auto next_full, int t0, int buf) {
+        constexpr bool FULL = decltype(full)::value, NEXT_FULL = decltype(next_full)::value;
         const int ct = FULL ? kChunk : T - t0;
         float *sh_x = smem + buf * BUF;
         float *sh_B = sh_x + kChunk * XS;
@@ -228,11 +268,13 @@ __global__ void __launch_bounds__((PrefillShape<P, N>::TPB), (PrefillShape<P, N>
         // wave stores the next chunk's, so they need one buffer; x and B are read after it too
         rows.store(sh_x, sh_B, sh_C, sh_dt, t);
         __syncthreads();
-        if (t0 + kChunk < T) {             // the next chunk's rows, in flight during this chunk
-            const size_t t1 = t0 + kChunk;
+        const size_t t1 = t0 + kChunk;    // the next chunk's rows, in flight during this chunk
+        if constexpr (NEXT_FULL)
+            rows.load_full(x0 + t1 * BH * P, b0 + t1 * BG * N, c0 + t1 * BG * N, d0 + t1 * BH,
+                           (uint32_t)BH, (uint32_t)BG, t);
+        else if ((int)t1 < T)
             rows.load(x0 + t1 * BH * P, b0 + t1 * BG * N, c0 + t1 * BG * N, d0 + t1 * BH, BH, BG,
                       T - (int)t1 < kChunk ? T - (int)t1 : kChunk, t);
-        }
 
         // 1. S-independent blocks first: every wave its share of B C^T (k-blocks wv KBW ..
         //    wv KBW + KBW - 1) and of the decay weights of the chunk
@@ -329,8 +371,11 @@ __global__ void __launch_bounds__((PrefillShape<P, N>::TPB), (PrefillShape<P, N>
         mfma_settle();
     };
     int t0 = 0, buf = 0;
-    for (; t0 + kChunk <= T; t0 += kChunk, buf ^= 1) chunk(std::true_type{}, t0, buf);
-    if (t0 < T) chunk(std::false_type{}, t0, buf);
+    if (narrow)
+        for (; t0 + 2 * kChunk <= T; t0 += kChunk, buf ^= 1)
+            chunk(std::true_type{}, std::true_type{}, t0, buf);
+    for (; t0 + kChunk <= T; t0 += kChunk, buf ^= 1) chunk(std::true_type{}, std::false_type{}, t0, buf);
+    if (t0 < T) chunk(std::false_type{}, std::false_type{}, t0, buf);
 
     // the final state is the new checkpoint (and its bf16 read copy); the ring is empty
 #pragma unroll
