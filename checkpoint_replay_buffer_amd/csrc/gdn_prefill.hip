@@ -95,7 +95,7 @@ struct GdnRows {
 #pragma unroll
         for (int i = 0; i < KQ; ++i) {
             const int u = t + i * TPB, j = u / KF, o = (u - j * KF) * 4;
-            if (u < kChunk * KF) {
+            if (KQ * TPB == kChunk * KF || u < kChunk * KF) {
                 st4(sh_q + j * KS + o, q[i]);
                 st4(sh_k + j * KS + o, k[i]);
             }
@@ -103,7 +103,7 @@ struct GdnRows {
 #pragma unroll
         for (int i = 0; i < VQ; ++i) {
             const int u = t + i * TPB, j = u / VF, o = (u - j * VF) * 4;
-            if (u < kChunk * VF) st4(sh_v + j * VS + o, v[i]);
+            if (VQ * TPB == kChunk * VF || u < kChunk * VF) st4(sh_v + j * VS + o, v[i]);
         }
         if (t < kChunk) {
             sh_be[t] = be;
@@ -112,7 +112,12 @@ struct GdnRows {
     }
 };
 
-template <int DV, int DK>
+// NARROW: 16 token rows of the outputs span less than 4 GiB, so a chunk's output stores go
+// through a buffer resource whose record range ends after the chunk's last real row: the stores of
+// padding rows fall outside it and are dropped, and every store issues unpredicated (a predicated
+// store leaves the compiler without a count of the stores in flight, and its wait for the next
+// chunk's rows then covers those stores too).
+template <int DV, int DK, bool NARROW>
 __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPrefillArgs a)
 {
     using F = MfmaTile<DV, DK, GpShape<DV, DK>::NW>;
@@ -231,6 +236,11 @@ __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPr
         for (int r = 0; r < 4; ++r)
             ut = mfma4(sh_T[(4 * g + r) * kTS + cl], sh_A[cl * kTS + 4 * g + r], ut);
         const float ua[4] = {ut[0], ut[1], ut[2], ut[3]};
+        // the chunk's output rows; records end after row ct - 1 of this tile
+        const __amdgpu_buffer_rsrc_t orows = __builtin_amdgcn_make_buffer_rsrc(
+            o0 + (size_t)t0 * BH * DV, 0,
+            NARROW ? (int)(((uint32_t)(ct - 1) * (uint32_t)(BH * DV) + (uint32_t)DV) * 4u) : 0,
+            0x00020000);
         const float ur[4] = {ut[0] * rr.x, ut[1] * rr.y, ut[2] * rr.z, ut[3] * rr.w};
         const float gmv[4] = {gm.x, gm.y, gm.z, gm.w}, rfv[4] = {rf.x, rf.y, rf.z, rf.w};
 
@@ -252,10 +262,18 @@ __global__ void __launch_bounds__((GpShape<DV, DK>::TPB), 2) k_gdn_prefill(GdnPr
             for (int r = 0; r < 4; ++r) ov[r] = gmv[r] * (qs[ib][r] - uf[r]) + uv[r];
             // keep these reads next to their chains rather than sunk into the stores below
             asm volatile("" ::"v"(ov[0]), "v"(ov[1]), "v"(ov[2]), "v"(ov[3]));
-            float *oc = o0 + (size_t)t0 * BH * DV + i;
+            if constexpr (NARROW) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * g + r < ct) oc[(size_t)(4 * g + r) * BH * DV] = ov[r];
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __float_as_uint(ov[r]), orows,
+                        (int)(((uint32_t)(4 * g + r) * (uint32_t)(BH * DV) + (uint32_t)i) * 4u), 0, 0);
+            } else {
+                float *oc = o0 + (size_t)t0 * BH * DV + i;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r < ct) oc[(size_t)(4 * g + r) * BH * DV] = ov[r];
+            }
             // 5. fold of the chunk: Z = R[15] o V - gam F, C = T Z, S <- gam S + C^T K
             float zf[4];
 #pragma unroll
@@ -294,7 +312,11 @@ hipError_t go_gdn_prefill(const GdnPrefillArgs &a, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(GpShape<DV, DK>::TPB);
     const size_t lds = 4 * (size_t)gp_lds_floats<DV, DK>();
-    hipLaunchKernelGGL((k_gdn_prefill<DV, DK>), grid, block, lds, s, a);
+    // 16 token rows of the outputs within 4 GiB: unpredicated output stores
+    if ((size_t)a.d.B * a.d.H * DV * 4 * kChunk <= 0xFFFFFFFFull)
+        hipLaunchKernelGGL((k_gdn_prefill<DV, DK, true>), grid, block, lds, s, a);
+    else
+        hipLaunchKernelGGL((k_gdn_prefill<DV, DK, false>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 

@@ -167,7 +167,7 @@ struct KdaRows {
 #pragma unroll
         for (int i = 0; i < VQ; ++i) {
             const int u = t + i * TPB, j = u / VF, o = (u - j * VF) * 4;
-            if (u < kChunk * VF) st4(sm + L::v + j * L::VS + o, v[i]);
+            if (VQ * TPB == kChunk * VF || u < kChunk * VF) st4(sm + L::v + j * L::VS + o, v[i]);
         }
     }
 };
@@ -209,7 +209,12 @@ __device__ __forceinline__ void token_step(float4 (&s)[F::IBW][F::KB], const flo
     }
 }
 
-template <int DV, int DK>
+// NARROW: 16 token rows of the outputs span less than 4 GiB, so a chunk's output stores go
+// through a buffer resource whose record range ends after the chunk's last real row: the stores of
+// padding rows fall outside it and are dropped, and every store issues unpredicated (a predicated
+// store leaves the compiler without a count of the stores in flight, and its wait for the next
+// chunk's rows then covers those stores too).
+template <int DV, int DK, bool NARROW>
 __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPrefillArgs a)
 {
     using F = MfmaTile<DV, DK, KpShape<DV, DK>::NW>;
@@ -345,6 +350,11 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
             for (int r = 0; r < 4; ++r)
                 ut = mfma4(sh_T[(4 * g + r) * kTS + cl], sh_M[cl * kTS + 4 * g + r], ut);
             const float ua[4] = {ut[0], ut[1], ut[2], ut[3]};
+            // the chunk's output rows; records end after row ct - 1 of this tile
+            const __amdgpu_buffer_rsrc_t orows = __builtin_amdgcn_make_buffer_rsrc(
+                o0 + (size_t)t0 * BH * DV, 0,
+                NARROW ? (int)(((uint32_t)(ct - 1) * (uint32_t)(BH * DV) + (uint32_t)DV) * 4u) : 0,
+                0x00020000);
 
 #pragma unroll
             for (int ib = 0; ib < IBW; ++ib) {
@@ -361,10 +371,18 @@ __global__ void __launch_bounds__((KpShape<DV, DK>::TPB), 2) k_kda_prefill(GdnPr
                 for (int r = 0; r < 4; ++r) ov[r] = qs[ib][r] + uz[r];
                 // keep these reads next to their chains rather than sunk into the stores below
                 asm volatile("" ::"v"(ov[0]), "v"(ov[1]), "v"(ov[2]), "v"(ov[3]));
-                float *oc = o0 + (size_t)t0 * BH * DV + i;
+                if constexpr (NARROW) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * g + r < ct) oc[(size_t)(4 * g + r) * BH * DV] = ov[r];
+                    for (int r = 0; r < 4; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __float_as_uint(ov[r]), orows,
+                            (int)(((uint32_t)(4 * g + r) * (uint32_t)(BH * DV) + (uint32_t)i) * 4u), 0, 0);
+                } else {
+                    float *oc = o0 + (size_t)t0 * BH * DV + i;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * g + r < ct) oc[(size_t)(4 * g + r) * BH * DV] = ov[r];
+                }
                 // 5. end of the chunk: U = T Z, S <- (S + U^T Kt) diag(Gam_15) (the column scale
                 //    taken after the update, the same as S diag(Gam_15) + U^T Kb)
                 const float4 tv = ld4(sh_T + cl * kTS + 4 * g);              // T[t = c][4 g + r]
@@ -404,7 +422,11 @@ hipError_t go_kda_prefill(const GdnPrefillArgs &a, hipStream_t s)
 {
     const dim3 grid(a.d.B * a.d.H), block(KpShape<DV, DK>::TPB);
     const size_t lds = 4 * (size_t)KpLds<DV, DK>::floats;
-    hipLaunchKernelGGL((k_kda_prefill<DV, DK>), grid, block, lds, s, a);
+    // 16 token rows of the outputs within 4 GiB: unpredicated output stores
+    if ((size_t)a.d.B * a.d.H * DV * 4 * kChunk <= 0xFFFFFFFFull)
+        hipLaunchKernelGGL((k_kda_prefill<DV, DK, true>), grid, block, lds, s, a);
+    else
+        hipLaunchKernelGGL((k_kda_prefill<DV, DK, false>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
