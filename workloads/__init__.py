@@ -179,3 +179,37 @@ M2_SPEC = M2Shape(batch=512, nheads=128, ngroups=128, head_dim=64, d_state=128, 
                   max_draft=6)
 GDN_SERVE = GDNShape(batch=256, nheads=32, d_k=128, d_v=128, window=16)
 KDA_SERVE = GDNShape(batch=256, nheads=32, d_k=128, d_v=128, window=16)
+
+
+def torch_prompt_inputs(kind: str, batch: int, nheads: int, dim_v: int, dim_k: int, ntok: int,
+                        seed: int, device="cuda"):
+    """Prompt inputs and an initial state drawn on the device with torch's seeded generator, in
+    float32, for shapes too large to draw on the host; the distributions are the ones above
+    (Mamba-2 with one B/C group per head). Token-major like the *_token_inputs functions. Returns
+    (inputs, state0); Mamba-2's A and D come from m2_params."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+
+    def nrm(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+
+    T, B, H = ntok, batch, nheads
+    if kind == "mamba2":
+        x = nrm(T, B, H, dim_v)
+        Bm = nrm(T, B, H, dim_k).mul_(1.0 / math.sqrt(dim_k))
+        C = nrm(T, B, H, dim_k).mul_(1.0 / math.sqrt(dim_k))
+        dt = torch.nn.functional.softplus(nrm(T, B, H).mul_(0.5).add_(-2.0))
+        ins = {"x": x, "B": Bm, "C": C, "dt": dt}
+    else:
+        q = nrm(T, B, H, dim_k)
+        q.div_(q.norm(dim=-1, keepdim=True))
+        k = nrm(T, B, H, dim_k)
+        k.div_(k.norm(dim=-1, keepdim=True))
+        v = nrm(T, B, H, dim_v)
+        beta = torch.sigmoid(nrm(T, B, H))
+        ga = nrm(T, B, H, dim_k) if kind == "kda" else nrm(T, B, H)
+        alpha = torch.exp(-torch.nn.functional.softplus(ga))
+        ins = {"q": q, "k": k, "v": v, "beta": beta, "alpha": alpha}
+    return ins, nrm(B, H, dim_v, dim_k).mul_(0.1)
