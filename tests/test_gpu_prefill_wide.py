@@ -74,3 +74,7 @@ def test_prefill_rows_beyond_4gib(kind, dv, dk):
         err = normwise_err(host(mat[b])[None], ref)
         say(f"  sequence {b}: state error {err:.2e}")
         assert err < TOL, (b, err)
+    ctx.close()
+    del ctx, y, mat
+    gc.collect()
+    torch.cuda.empty_cache()                 # the next tests need none of these 70 GB
